@@ -1,1 +1,223 @@
-"""Packed width-4 depthwise causal Conv1d (+ SiLU) for MI355X (gfx950)."""
+"""Packed width-4 depthwise causal Conv1d (+ SiLU) for MI355X (gfx950).
+
+Thin torch binding of the C ABI in include/conv1d.h: every function below only checks tensor
+metadata, marshals pointers, sizes and the current HIP stream, and calls the library; all of
+the computation runs in the hand-written HIP kernels of ``csrc/``.  bf16 tensors are
+``torch.bfloat16`` (or 16-bit integer views holding bf16 bits); taps and bias are
+``torch.float32`` or ``torch.bfloat16``.
+
+Entry points (same names as the C ABI):
+  conv1d_fwd           forward over packed rows: cu_seqlens / per-token sequence IDs / batch
+                       rows, optional slot pool (conv_state, cache_indices, has_initial_state)
+                       or caller history rows (history, has_history)
+  conv1d_state_update  one decode step per sequence against its slot
+  conv1d_bwd           dx, deterministic FP32 dweight / dbias, and d(history)
+"""
+import ctypes
+
+from . import _lib
+
+__all__ = ["conv1d_fwd", "conv1d_state_update", "conv1d_bwd", "conv1d_fwd_workspace_bytes",
+           "conv1d_bwd_workspace_bytes", "library_path"]
+
+library_path = _lib.LIB_PATH
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _bits_ok(t):
+    torch = _torch()
+    return t.dtype in (torch.bfloat16, torch.int16, torch.uint16) if hasattr(torch, "uint16") else \
+        t.dtype in (torch.bfloat16, torch.int16)
+
+
+def _rows2d(t, name, C=None):
+    if t.dim() != 2 or not _bits_ok(t):
+        raise ValueError(f"{name}: need a 2-D bf16 tensor")
+    if t.shape[0] > 0 and t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name}: channels must be contiguous")
+    if C is not None and t.shape[1] != C:
+        raise ValueError(f"{name}: expected {C} channels")
+    ld = t.stride(0) if t.shape[0] > 1 else t.shape[1]
+    return t.data_ptr(), max(ld, t.shape[1])
+
+
+def _taps(t, C, shape, name):
+    torch = _torch()
+    if t is None:
+        return None, 0
+    if tuple(t.shape) != shape or not t.is_contiguous():
+        raise ValueError(f"{name}: need a contiguous tensor of shape {shape}")
+    if t.dtype == torch.float32:
+        return t.data_ptr(), _lib.F32
+    if t.dtype == torch.bfloat16:
+        return t.data_ptr(), _lib.BF16
+    raise ValueError(f"{name}: dtype must be float32 or bfloat16")
+
+
+def _i32(t, name):
+    torch = _torch()
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError(f"{name}: need a contiguous int32 tensor")
+    return t.data_ptr()
+
+
+def _u8(t, name):
+    torch = _torch()
+    if t is None:
+        return None
+    if t.dtype not in (torch.bool, torch.uint8) or not t.is_contiguous():
+        raise ValueError(f"{name}: need a contiguous bool/uint8 tensor")
+    return t.data_ptr()
+
+
+def _seq(rows, cu_seqlens, seq_idx, seqlen):
+    s = _lib.Seq()
+    if cu_seqlens is not None:
+        s.cu_seqlens = _i32(cu_seqlens, "cu_seqlens")
+        s.nseq = cu_seqlens.numel() - 1
+        return s, s.nseq
+    s.seq_idx = _i32(seq_idx, "seq_idx")
+    s.seqlen = int(seqlen) if seqlen is not None else max(rows, 1)
+    return s, (rows // s.seqlen if seq_idx is None else -1)
+
+
+def _pool(conv_state, cache_indices, has_initial_state, C):
+    if conv_state is None:
+        return None
+    if conv_state.dim() != 3 or conv_state.shape[1] != C or not _bits_ok(conv_state):
+        raise ValueError("conv_state: need a bf16 [slots, C, L] tensor")
+    p = _lib.Pool()
+    p.ptr = conv_state.data_ptr()
+    p.slots, _, p.len = conv_state.shape
+    p.s_slot, p.s_chan, p.s_pos = conv_state.stride()
+    if conv_state.shape[0] == 1:
+        p.s_slot = max(p.s_slot, 1)
+    p.cache_indices = _i32(cache_indices, "cache_indices")
+    p.has_initial_state = _u8(has_initial_state, "has_initial_state")
+    return p
+
+
+def _hist(history, has_history, C):
+    if history is None:
+        return None
+    if history.dim() != 3 or tuple(history.shape[1:]) != (3, C) or not history.is_contiguous() or not _bits_ok(history):
+        raise ValueError("history: need a contiguous bf16 [nseq, 3, C] tensor")
+    h = _lib.Hist()
+    h.ptr = history.data_ptr()
+    h.has_history = _u8(has_history, "has_history")
+    return h
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ref(s):
+    return None if s is None else ctypes.byref(s)
+
+
+def conv1d_fwd_workspace_bytes(rows, C, nseq):
+    return int(_lib.load().conv1d_fwd_workspace_bytes(rows, C, nseq))
+
+
+def conv1d_bwd_workspace_bytes(rows, C):
+    return int(_lib.load().conv1d_bwd_workspace_bytes(rows, C))
+
+
+def conv1d_fwd(x, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqlen=None, conv_state=None,
+               cache_indices=None, has_initial_state=None, history=None, has_history=None, activation="silu",
+               out=None, workspace=None, stream=None):
+    """y = act(causal depthwise conv of x), packed rows; conv_state is updated in place."""
+    torch = _torch()
+    lib = _lib.load()
+    rows, C = x.shape
+    xp, x_ld = _rows2d(x, "x")
+    wp, wd = _taps(weight, C, (C, 4), "weight")
+    bp, bd = _taps(bias, C, (C,), "bias")
+    seq, nseq = _seq(rows, cu_seqlens, seq_idx, seqlen)
+    pool = _pool(conv_state, cache_indices, has_initial_state, C)
+    hist = _hist(history, has_history, C)
+    if out is None:
+        out = torch.empty((rows, C), dtype=torch.bfloat16, device=x.device)
+    yp, y_ld = _rows2d(out, "out", C)
+    if out.shape[0] != rows:
+        raise ValueError("out: must have as many rows as x")
+    ws = workspace.data_ptr() if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.conv1d_fwd(xp, rows, C, x_ld, wp, wd, bp, bd, ctypes.byref(seq), _ref(pool), _ref(hist),
+                        _lib.ACT[activation], yp, y_ld, ws, wsb, _stream(stream))
+    _lib.check(lib, st, "conv1d_fwd")
+    return out
+
+
+def conv1d_state_update(x, weight, bias=None, *, conv_state, cache_indices, activation="silu", out=None,
+                        stream=None):
+    """One decode token per sequence; conv_state positions 0..2 shift in place."""
+    torch = _torch()
+    lib = _lib.load()
+    nseq, C = x.shape
+    xp, x_ld = _rows2d(x, "x")
+    wp, wd = _taps(weight, C, (C, 4), "weight")
+    bp, bd = _taps(bias, C, (C,), "bias")
+    pool = _pool(conv_state, cache_indices, None, C)
+    if pool is None:
+        raise ValueError("conv_state is required")
+    if out is None:
+        out = torch.empty((nseq, C), dtype=torch.bfloat16, device=x.device)
+    yp, y_ld = _rows2d(out, "out", C)
+    st = lib.conv1d_state_update(xp, nseq, C, x_ld, wp, wd, bp, bd, ctypes.byref(pool), _lib.ACT[activation],
+                                 yp, y_ld, _stream(stream))
+    _lib.check(lib, st, "conv1d_state_update")
+    return out
+
+
+def conv1d_bwd(x, dy, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqlen=None, history=None,
+               has_history=None, activation="silu", dx=None, dweight=None, want_dbias=None, dbias=None,
+               want_dhistory=None, dhistory=None, workspace=None, stream=None):
+    """Returns (dx, dweight [C,4] fp32, dbias [C] fp32 or None, dhistory [nseq,3,C] or None)."""
+    torch = _torch()
+    lib = _lib.load()
+    rows, C = x.shape
+    xp, x_ld = _rows2d(x, "x")
+    dyp, dy_ld = _rows2d(dy, "dy", C)
+    wp, wd = _taps(weight, C, (C, 4), "weight")
+    bp, bd = _taps(bias, C, (C,), "bias")
+    seq, nseq = _seq(rows, cu_seqlens, seq_idx, seqlen)
+    hist = _hist(history, has_history, C)
+    dev = x.device
+    if dx is None:
+        dx = torch.empty((rows, C), dtype=torch.bfloat16, device=dev)
+    dxp, dx_ld = _rows2d(dx, "dx", C)
+    if dweight is None:
+        dweight = torch.empty((C, 4), dtype=torch.float32, device=dev)
+    if want_dbias is None:
+        want_dbias = bias is not None or dbias is not None
+    if want_dbias and dbias is None:
+        dbias = torch.empty((C,), dtype=torch.float32, device=dev)
+    if want_dhistory is None:
+        want_dhistory = history is not None or dhistory is not None
+    if want_dhistory and dhistory is None:
+        dhistory = torch.empty((max(nseq, 0), 3, C), dtype=torch.bfloat16, device=dev)
+    for t, name, dt in ((dweight, "dweight", torch.float32), (dbias, "dbias", torch.float32)):
+        if t is not None and (t.dtype != dt or not t.is_contiguous()):
+            raise ValueError(f"{name}: need a contiguous float32 tensor")
+    if workspace is None:
+        need = lib.conv1d_bwd_workspace_bytes(rows, C)
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size()
+    st = lib.conv1d_bwd(xp, dyp, rows, C, x_ld, dy_ld, wp, wd, bp, bd, ctypes.byref(seq), _ref(hist),
+                        _lib.ACT[activation], dxp, dx_ld, dweight.data_ptr(),
+                        None if dbias is None else dbias.data_ptr(),
+                        None if dhistory is None else dhistory.data_ptr(), workspace.data_ptr(), wsb,
+                        _stream(stream))
+    _lib.check(lib, st, "conv1d_bwd")
+    return dx, dweight, (dbias if want_dbias else None), (dhistory if want_dhistory else None)

@@ -1,0 +1,284 @@
+// conv1d_api.cpp -- the C ABI of include/conv1d.h: host-side validation and kernel launches.
+//
+// Every entry point checks what the host can check (pointers, dtypes, sizes, strides, layouts,
+// byte-range overlaps, workspace size) and returns CONV1D_EINVAL / CONV1D_EWORKSPACE before
+// anything is enqueued.  It never reads device memory and never synchronizes, so the calls are
+// stream-ordered and can be captured in a HIP graph (FlashInfer causal_conv1d_fn, Notes).
+#include "conv1d.h"
+
+#include <stdint.h>
+
+#include "conv1d_launch.h"
+
+using namespace cconv;
+
+namespace {
+
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+};
+
+Span span_rows(const void* p, int64_t rows, int64_t C, int64_t ld, int64_t esz) {
+  Span s;
+  if (!p || rows <= 0 || C <= 0) return s;
+  s.lo = reinterpret_cast<uintptr_t>(p);
+  s.hi = s.lo + (uintptr_t)(((rows - 1) * ld + C) * esz);
+  return s;
+}
+
+Span span_bytes(const void* p, int64_t bytes) {
+  Span s;
+  if (!p || bytes <= 0) return s;
+  s.lo = reinterpret_cast<uintptr_t>(p);
+  s.hi = s.lo + (uintptr_t)bytes;
+  return s;
+}
+
+bool overlap(const Span& a, const Span& b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+// Byte ranges of the sequence metadata (offsets / IDs) and of per-sequence arrays.
+Span span_seq(const conv1d_seq* s, int64_t rows) {
+  if (s->cu_seqlens) return span_bytes(s->cu_seqlens, (s->nseq + 1) * 4);
+  if (s->seq_idx) return span_bytes(s->seq_idx, rows * 4);
+  return Span{};
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int mode_of(const conv1d_seq* s) {
+  if (s->cu_seqlens) return MODE_CU;
+  return s->seq_idx ? MODE_IDX : MODE_BATCH;
+}
+
+// Sequence description: checks the form and returns the host-known sequence count (-1 = IDX).
+int check_seq(const conv1d_seq* s, int64_t rows, int64_t* nseq_out) {
+  if (!s) return CONV1D_EINVAL;
+  if (s->cu_seqlens) {
+    if (s->seq_idx || s->nseq < 0) return CONV1D_EINVAL;
+    *nseq_out = s->nseq;
+    return CONV1D_OK;
+  }
+  if (s->seqlen < 1 || rows % s->seqlen != 0) return CONV1D_EINVAL;
+  *nseq_out = s->seq_idx ? -1 : rows / s->seqlen;
+  return CONV1D_OK;
+}
+
+bool dtype_ok(int d) { return d == CONV1D_BF16 || d == CONV1D_F32; }
+int64_t dsize(int d) { return d == CONV1D_F32 ? 4 : 2; }
+
+// Pool layout: [slots, C, len] with the channel or history axis contiguous, no self-overlap
+// inside a slot and no overlap between slots (causal_conv1d_fn, Parameters conv_state).
+int check_pool(const conv1d_pool* p, int64_t C, int64_t nseq, Span* out) {
+  if (p->len < 3 || p->slots < 1 || p->s_slot < 1 || p->s_chan < 1 || p->s_pos < 1) return CONV1D_EINVAL;
+  if (p->s_chan != 1 && p->s_pos != 1) return CONV1D_EINVAL;
+  if (p->s_pos == 1 && C > 1 && p->s_chan < p->len) return CONV1D_EINVAL;  // (c, j) must not alias
+  if (p->s_chan == 1 && p->s_pos != 1 && p->s_pos < C) return CONV1D_EINVAL;
+  if (p->s_chan == 1 && p->s_pos == 1 && C > 1) return CONV1D_EINVAL;
+  const int64_t extent = (C - 1) * p->s_chan + (p->len - 1) * p->s_pos + 1;
+  if (p->slots > 1 && p->s_slot < extent) return CONV1D_EINVAL;  // slots must not overlap
+  if (nseq > 0 && !p->cache_indices) return CONV1D_EINVAL;
+  *out = span_bytes(p->ptr, ((p->slots - 1) * p->s_slot + extent) * 2);
+  return CONV1D_OK;
+}
+
+// ws was sized by the launcher; the partial slabs need FP32 alignment
+constexpr size_t kWsAlign = 256;
+
+uint32_t ceil_div(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
+
+}  // namespace
+
+extern "C" {
+
+size_t conv1d_fwd_workspace_bytes(int64_t rows, int64_t C, int64_t nseq) {
+  (void)rows;
+  (void)C;
+  (void)nseq;
+  return 0;  // uniform row tiles with an in-kernel sequence lookup: no chunk map
+}
+
+size_t conv1d_bwd_workspace_bytes(int64_t rows, int64_t C) {
+  if (rows <= 0 || C <= 0) return 0;
+  const size_t nrb = (size_t)((rows + kBwdRowsPerBlock - 1) / kBwdRowsPerBlock);
+  const size_t bytes = nrb * 5u * (size_t)C * sizeof(float);
+  return (bytes + kWsAlign - 1) / kWsAlign * kWsAlign;
+}
+
+const char* conv1d_status_str(int status) {
+  switch (status) {
+    case CONV1D_OK: return "ok";
+    case CONV1D_EINVAL: return "invalid argument (host-checkable precondition failed; nothing launched)";
+    case CONV1D_EWORKSPACE: return "workspace missing or too small";
+    case CONV1D_EUNSUPPORTED: return "unsupported configuration";
+    case CONV1D_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void* w, int w_dtype,
+               const void* b, int b_dtype, const conv1d_seq* seq, const conv1d_pool* pool,
+               const conv1d_hist* hist, int act, void* y, int64_t y_ld, void* ws, size_t ws_bytes,
+               hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (rows < 0 || C < 1 || x_ld < C || y_ld < C || !w || !dtype_ok(w_dtype)) return CONV1D_EINVAL;
+  if (b && !dtype_ok(b_dtype)) return CONV1D_EINVAL;
+  if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
+  if (rows > 0 && (!x || !y)) return CONV1D_EINVAL;
+  int64_t nseq = 0;
+  if (check_seq(seq, rows, &nseq) != CONV1D_OK) return CONV1D_EINVAL;
+  const int mode = mode_of(seq);
+  const bool use_pool = pool && pool->ptr;
+  const bool use_hist = hist && hist->ptr;
+  if (use_pool && use_hist) return CONV1D_EINVAL;
+  if ((use_pool || use_hist) && mode == MODE_IDX) return CONV1D_EINVAL;
+
+  const Span sx = span_rows(x, rows, C, x_ld, 2), sy = span_rows(y, rows, C, y_ld, 2);
+  const Span sw = span_bytes(w, 4 * C * dsize(w_dtype)), sb = span_bytes(b, C * dsize(b_dtype));
+  Span sp, sh;
+  if (use_pool && check_pool(pool, C, nseq, &sp) != CONV1D_OK) return CONV1D_EINVAL;
+  if (use_hist) sh = span_bytes(hist->ptr, nseq * 3 * C * 2);
+  // out must not share storage with any operand; the pool must not alias the other operands
+  const Span sm = span_seq(seq, rows);
+  const Span sci = use_pool ? span_bytes(pool->cache_indices, nseq * 4) : Span{};
+  const Span shi = use_pool ? span_bytes(pool->has_initial_state, nseq) : Span{};
+  const Span shh = use_hist ? span_bytes(hist->has_history, nseq) : Span{};
+  const Span ins[8] = {sx, sw, sb, sh, sm, sci, shi, shh};
+  for (const Span& in : ins)
+    if (overlap(sy, in) || overlap(sp, in)) return CONV1D_EINVAL;
+  if (overlap(sy, sp)) return CONV1D_EINVAL;
+  if (rows == 0) return CONV1D_OK;
+
+  const bool vec = (C % 8 == 0) && (x_ld % 8 == 0) && (y_ld % 8 == 0) && aligned(x, 16) && aligned(y, 16) &&
+                   (!use_hist || aligned(hist->ptr, 16));
+  const uint64_t nblk = (uint64_t)ceil_div(C, 512) * ceil_div(rows, kFwdRowsPerBlock);
+  if (nblk > 0x7fffffffull) return CONV1D_EINVAL;
+
+  FwdArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.y = static_cast<uint16_t*>(y);
+  a.x_ld = x_ld;
+  a.y_ld = y_ld;
+  a.rows = rows;
+  a.C = C;
+  a.w = w;
+  a.b = b;
+  a.w_f32 = w_dtype == CONV1D_F32;
+  a.b_f32 = b_dtype == CONV1D_F32;
+  a.seq = SeqArgs{seq->cu_seqlens, mode == MODE_BATCH ? nseq : seq->nseq, seq->seq_idx, seq->seqlen};
+  if (use_pool)
+    a.pool = PoolArgs{static_cast<uint16_t*>(pool->ptr), pool->slots, pool->s_slot, pool->s_chan, pool->s_pos,
+                      pool->cache_indices, pool->has_initial_state};
+  if (use_hist) a.hist = HistArgs{static_cast<const uint16_t*>(hist->ptr), hist->has_history};
+  a.n_strips = ceil_div(C, 512);
+  a.n_rowblocks = ceil_div(rows, kFwdRowsPerBlock);
+  return launch_fwd(a, mode, vec, act == CONV1D_ACT_SILU, stream) == hipSuccess ? CONV1D_OK : CONV1D_EHIP;
+}
+
+int conv1d_state_update(const void* x, int64_t nseq, int64_t C, int64_t x_ld, const void* w, int w_dtype,
+                        const void* b, int b_dtype, const conv1d_pool* pool, int act, void* y, int64_t y_ld,
+                        hipStream_t stream) {
+  if (nseq < 0 || C < 1 || x_ld < C || y_ld < C || !w || !dtype_ok(w_dtype)) return CONV1D_EINVAL;
+  if (b && !dtype_ok(b_dtype)) return CONV1D_EINVAL;
+  if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
+  if (!pool || !pool->ptr) return CONV1D_EINVAL;
+  if (nseq > 0 && (!x || !y)) return CONV1D_EINVAL;
+  Span sp;
+  if (check_pool(pool, C, nseq, &sp) != CONV1D_OK) return CONV1D_EINVAL;
+  const Span sx = span_rows(x, nseq, C, x_ld, 2), sy = span_rows(y, nseq, C, y_ld, 2);
+  const Span sw = span_bytes(w, 4 * C * dsize(w_dtype)), sb = span_bytes(b, C * dsize(b_dtype));
+  const Span sci = span_bytes(pool->cache_indices, nseq * 4);
+  const Span ins[4] = {sx, sw, sb, sci};
+  for (const Span& in : ins)
+    if (overlap(sy, in) || overlap(sp, in)) return CONV1D_EINVAL;
+  if (overlap(sy, sp)) return CONV1D_EINVAL;
+  if (nseq == 0) return CONV1D_OK;
+  if ((uint64_t)nseq * ceil_div(C, 8) / 256 > 0x7fffffffull) return CONV1D_EINVAL;
+  const bool vec = (C % 8 == 0) && (x_ld % 8 == 0) && (y_ld % 8 == 0) && aligned(x, 16) && aligned(y, 16);
+  DecodeArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.y = static_cast<uint16_t*>(y);
+  a.x_ld = x_ld;
+  a.y_ld = y_ld;
+  a.nseq = nseq;
+  a.C = C;
+  a.w = w;
+  a.b = b;
+  a.w_f32 = w_dtype == CONV1D_F32;
+  a.b_f32 = b_dtype == CONV1D_F32;
+  a.pool = PoolArgs{static_cast<uint16_t*>(pool->ptr), pool->slots, pool->s_slot, pool->s_chan, pool->s_pos,
+                    pool->cache_indices, nullptr};
+  return launch_decode(a, vec, act == CONV1D_ACT_SILU, stream) == hipSuccess ? CONV1D_OK : CONV1D_EHIP;
+}
+
+int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x_ld, int64_t dy_ld,
+               const void* w, int w_dtype, const void* b, int b_dtype, const conv1d_seq* seq,
+               const conv1d_hist* hist, int act, void* dx, int64_t dx_ld, float* dw, float* db,
+               void* dhist, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (rows < 0 || C < 1 || x_ld < C || dy_ld < C || dx_ld < C || !w || !dtype_ok(w_dtype) || !dw)
+    return CONV1D_EINVAL;
+  if (b && !dtype_ok(b_dtype)) return CONV1D_EINVAL;
+  if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
+  if (rows > 0 && (!x || !dy || !dx)) return CONV1D_EINVAL;
+  int64_t nseq = 0;
+  if (check_seq(seq, rows, &nseq) != CONV1D_OK) return CONV1D_EINVAL;
+  const int mode = mode_of(seq);
+  const bool use_hist = hist && hist->ptr;
+  if (use_hist && mode == MODE_IDX) return CONV1D_EINVAL;
+  if (dhist && !use_hist) return CONV1D_EINVAL;
+  const size_t need = conv1d_bwd_workspace_bytes(rows, C);
+  if (ws_bytes < need || (need > 0 && !ws)) return CONV1D_EWORKSPACE;
+  if (ws && !aligned(ws, 16)) return CONV1D_EINVAL;
+
+  const Span sx = span_rows(x, rows, C, x_ld, 2), sdy = span_rows(dy, rows, C, dy_ld, 2);
+  const Span sdx = span_rows(dx, rows, C, dx_ld, 2);
+  const Span sw = span_bytes(w, 4 * C * dsize(w_dtype)), sb = span_bytes(b, C * dsize(b_dtype));
+  const Span sdw = span_bytes(dw, 4 * C * 4), sdb = span_bytes(db, C * 4);
+  const Span sh = use_hist ? span_bytes(hist->ptr, nseq * 3 * C * 2) : Span{};
+  const Span sdh = dhist ? span_bytes(dhist, nseq * 3 * C * 2) : Span{};
+  const Span sws = span_bytes(ws, (int64_t)need);
+  const Span sm = span_seq(seq, rows);
+  const Span shh = use_hist ? span_bytes(hist->has_history, nseq) : Span{};
+  const Span outs[5] = {sdx, sdw, sdb, sdh, sws};
+  const Span ins[7] = {sx, sdy, sw, sb, sh, sm, shh};
+  for (int i = 0; i < 5; ++i) {
+    for (int j = 0; j < 7; ++j)
+      if (overlap(outs[i], ins[j])) return CONV1D_EINVAL;
+    for (int j = i + 1; j < 5; ++j)
+      if (overlap(outs[i], outs[j])) return CONV1D_EINVAL;
+  }
+
+  const bool vec = (C % 8 == 0) && (x_ld % 8 == 0) && (dy_ld % 8 == 0) && (dx_ld % 8 == 0) && aligned(x, 16) &&
+                   aligned(dy, 16) && aligned(dx, 16) && (!use_hist || aligned(hist->ptr, 16)) &&
+                   (!dhist || aligned(dhist, 16));
+  const uint64_t nblk = (uint64_t)ceil_div(C, 512) * ceil_div(rows, kBwdRowsPerBlock);
+  if (nblk > 0x7fffffffull || (uint64_t)(5 * C + (nseq > 0 ? nseq : 0) * C) / 256 > 0x7fffffffull)
+    return CONV1D_EINVAL;
+
+  BwdArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.dy = static_cast<const uint16_t*>(dy);
+  a.dx = static_cast<uint16_t*>(dx);
+  a.x_ld = x_ld;
+  a.dy_ld = dy_ld;
+  a.dx_ld = dx_ld;
+  a.rows = rows;
+  a.C = C;
+  a.w = w;
+  a.b = b;
+  a.w_f32 = w_dtype == CONV1D_F32;
+  a.b_f32 = b_dtype == CONV1D_F32;
+  a.seq = SeqArgs{seq->cu_seqlens, mode == MODE_BATCH ? nseq : seq->nseq, seq->seq_idx, seq->seqlen};
+  if (use_hist) a.hist = HistArgs{static_cast<const uint16_t*>(hist->ptr), hist->has_history};
+  a.dhist = static_cast<uint16_t*>(dhist);
+  a.part = static_cast<float*>(ws);
+  a.dw = dw;
+  a.db = db;
+  a.n_strips = ceil_div(C, 512);
+  a.n_rowblocks = ceil_div(rows, kBwdRowsPerBlock);
+  return launch_bwd(a, mode, vec, act == CONV1D_ACT_SILU, stream) == hipSuccess ? CONV1D_OK : CONV1D_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,257 @@
+// conv1d_device.h -- device-side building blocks of the gfx950 kernels (library-internal).
+//
+// Data layout: activations are channel-last bf16 rows.  One lane owns CPL consecutive channels
+// of a row (CPL = 8: one 16-byte global_load_dwordx4 per row), a 64-lane wave covers 64*CPL
+// channels of the same row, so every row access of a wave is one contiguous, fully coalesced
+// 64*CPL*2-byte segment.  The four waves of a block own four consecutive row ranges of the
+// same channel strip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "conv1d_launch.h"
+
+namespace cconv {
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWave * kWaves;
+
+// ------------------------------------------------------------------ bf16 packing
+template <int CPL>
+struct Pk {
+  uint32_t d[CPL / 2];  // CPL bf16 values, two per dword, channel order low half first
+};
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Two FP32 values -> two bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+template <int CPL>
+__device__ __forceinline__ void unpack(const Pk<CPL>& p, float (&f)[CPL]) {
+#pragma unroll
+  for (int j = 0; j < CPL / 2; ++j) {
+    f[2 * j] = bf16_lo(p.d[j]);
+    f[2 * j + 1] = bf16_hi(p.d[j]);
+  }
+}
+
+template <int CPL>
+__device__ __forceinline__ Pk<CPL> pack(const float (&f)[CPL]) {
+  Pk<CPL> p;
+#pragma unroll
+  for (int j = 0; j < CPL / 2; ++j) p.d[j] = pack_bf16x2(f[2 * j], f[2 * j + 1]);
+  return p;
+}
+
+template <int CPL>
+__device__ __forceinline__ Pk<CPL> zero_pk() {
+  Pk<CPL> p;
+#pragma unroll
+  for (int j = 0; j < CPL / 2; ++j) p.d[j] = 0u;
+  return p;
+}
+
+// ------------------------------------------------------------------ row loads / stores
+// VEC: C % CPL == 0 and every row start is 16-byte (CPL = 8) / 8-byte (CPL = 4) aligned, so an
+// active lane's CPL channels are one aligned vector.  Otherwise element-wise with bounds.
+template <int CPL, bool VEC>
+__device__ __forceinline__ Pk<CPL> load_row(const uint16_t* __restrict__ row, int64_t c0, int64_t C) {
+  Pk<CPL> p;
+  if constexpr (VEC) {
+    if constexpr (CPL == 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + c0);
+      p.d[0] = v.x; p.d[1] = v.y; p.d[2] = v.z; p.d[3] = v.w;
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(row + c0);
+      p.d[0] = v.x; p.d[1] = v.y;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < CPL / 2; ++j) {
+      const uint32_t lo = (c0 + 2 * j < C) ? row[c0 + 2 * j] : 0u;
+      const uint32_t hi = (c0 + 2 * j + 1 < C) ? row[c0 + 2 * j + 1] : 0u;
+      p.d[j] = lo | (hi << 16);
+    }
+  }
+  return p;
+}
+
+template <int CPL, bool VEC>
+__device__ __forceinline__ void store_row(uint16_t* __restrict__ row, int64_t c0, int64_t C, const Pk<CPL>& p) {
+  if constexpr (VEC) {
+    if constexpr (CPL == 8) {
+      *reinterpret_cast<uint4*>(row + c0) = make_uint4(p.d[0], p.d[1], p.d[2], p.d[3]);
+    } else {
+      *reinterpret_cast<uint2*>(row + c0) = make_uint2(p.d[0], p.d[1]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < CPL / 2; ++j) {
+      if (c0 + 2 * j < C) row[c0 + 2 * j] = (uint16_t)(p.d[j] & 0xffffu);
+      if (c0 + 2 * j + 1 < C) row[c0 + 2 * j + 1] = (uint16_t)(p.d[j] >> 16);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ taps
+template <int CPL>
+__device__ __forceinline__ void load_taps(const void* w, int w_f32, const void* b, int b_f32, int64_t c0,
+                                          int64_t C, float (&wk)[4][CPL], float (&bias)[CPL]) {
+#pragma unroll
+  for (int ch = 0; ch < CPL; ++ch) {
+    const int64_t c = c0 + ch;
+    const bool ok = c < C;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float v = 0.f;
+      if (ok) v = w_f32 ? static_cast<const float*>(w)[c * 4 + k]
+                        : __uint_as_float((uint32_t)static_cast<const uint16_t*>(w)[c * 4 + k] << 16);
+      wk[k][ch] = v;
+    }
+    float bv = 0.f;
+    if (ok && b) bv = b_f32 ? static_cast<const float*>(b)[c]
+                            : __uint_as_float((uint32_t)static_cast<const uint16_t*>(b)[c] << 16);
+    bias[ch] = bv;
+  }
+}
+
+// Three-row window w = [oldest, middle, newest]: drop the oldest, append row p.  Windows are
+// built by shifting rows into the sequence history (never by a runtime register index).
+template <int CPL>
+__device__ __forceinline__ void shift_in(float (&w)[3][CPL], const Pk<CPL>& p) {
+  float f[CPL];
+  unpack(p, f);
+#pragma unroll
+  for (int ch = 0; ch < CPL; ++ch) {
+    w[0][ch] = w[1][ch];
+    w[1][ch] = w[2][ch];
+    w[2][ch] = f[ch];
+  }
+}
+
+// ------------------------------------------------------------------ activation
+// sigmoid via the hardware exp2 and reciprocal (about 1 ulp each): far below bf16 rounding.
+__device__ __forceinline__ float sigmoid_f32(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+// ------------------------------------------------------------------ XCD-aware block order
+// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).  Give every XCD one
+// contiguous range of logical tiles, so neighbouring row tiles of a channel strip (which share
+// halo rows) run on the same XCD at about the same time.
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t nb) {
+  constexpr uint32_t X = 8;
+  const uint32_t q = nb / X, r = nb % X, xcd = b % X, idx = b / X;
+  return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
+
+// ------------------------------------------------------------------ sequence walking
+// All row indices below are wave-uniform: every lane of a wave works on the same row.
+struct SeqDesc {
+  int64_t s, e;  // rows [s, e) of the sequence (IDX mode: e exact up to the scan limit)
+  int64_t idx;   // sequence index (CU / BATCH modes), -1 in IDX mode
+};
+
+// Last row (exclusive) that belongs to some sequence, clamped to [0, rows].
+template <int MODE>
+__device__ __forceinline__ int64_t data_end(const SeqArgs& q, int64_t rows) {
+  if constexpr (MODE == MODE_CU) {
+    int64_t e = q.cu[q.nseq];
+    return e < 0 ? 0 : (e > rows ? rows : e);
+  } else {
+    return rows;
+  }
+}
+
+__device__ __forceinline__ int64_t cu_at(const SeqArgs& q, int64_t i, int64_t dend) {
+  int64_t v = q.cu[i];
+  return v < 0 ? 0 : (v > dend ? dend : v);
+}
+
+// IDX mode: does row t (0 <= t < rows) start a sequence?
+__device__ __forceinline__ bool idx_is_start(const SeqArgs& q, int64_t t) {
+  return (t % q.seqlen == 0) || (q.seq_idx[t] != q.seq_idx[t - 1]);  // t == 0 is caught first
+}
+
+// IDX mode: first sequence start in (t, limit), or limit.  64 rows per step, one row per lane.
+__device__ __forceinline__ int64_t idx_next_start(const SeqArgs& q, int64_t t, int64_t limit) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int64_t base = t + 1; base < limit; base += kWave) {
+    const int64_t r = base + lane;
+    bool st = false;
+    if (r < limit) st = idx_is_start(q, r);
+    const uint64_t m = __ballot(st);
+    if (m) return base + (int64_t)__builtin_ctzll(m);
+  }
+  return limit;
+}
+
+// The sequence containing row t (t < dend).  `limit` bounds the IDX-mode forward scan.
+template <int MODE>
+__device__ __forceinline__ SeqDesc seq_of_row(const SeqArgs& q, int64_t t, int64_t dend, int64_t limit) {
+  SeqDesc d;
+  if constexpr (MODE == MODE_CU) {
+    // largest i in [0, nseq) with cu[i] <= t; then cu[i+1] > t
+    int64_t lo = 0, hi = q.nseq - 1;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) >> 1;
+      if (cu_at(q, mid, dend) <= t) lo = mid; else hi = mid - 1;
+    }
+    d.idx = lo;
+    d.s = cu_at(q, lo, dend);
+    d.e = cu_at(q, lo + 1, dend);
+    if (d.e <= t) d.e = t + 1;  // only for metadata that breaks the contract: stay in bounds
+  } else if constexpr (MODE == MODE_BATCH) {
+    d.idx = t / q.seqlen;
+    d.s = d.idx * q.seqlen;
+    d.e = d.s + q.seqlen;
+    if (d.e > dend) d.e = dend;
+  } else {
+    // only the distance to the sequence start up to 3 rows matters: d.s = t - min(dist, 3)
+    int64_t dist = 3;
+    if (idx_is_start(q, t)) dist = 0;
+    else if (idx_is_start(q, t - 1)) dist = 1;
+    else if (idx_is_start(q, t - 2)) dist = 2;
+    d.s = t - dist;
+    d.idx = -1;
+    d.e = idx_next_start(q, t, limit);
+  }
+  return d;
+}
+
+// The sequence that starts right where `cur` ended (cur.e < dend).  Empty sequences are skipped.
+template <int MODE>
+__device__ __forceinline__ SeqDesc next_seq(const SeqArgs& q, const SeqDesc& cur, int64_t dend, int64_t limit) {
+  SeqDesc d;
+  const int64_t t = cur.e;
+  if constexpr (MODE == MODE_CU) {
+    int64_t i = cur.idx + 1;
+    while (i + 1 < q.nseq && cu_at(q, i + 1, dend) <= t) ++i;
+    d.idx = i;
+    d.s = t;
+    d.e = cu_at(q, i + 1, dend);
+    if (d.e <= t) d.e = t + 1;
+  } else if constexpr (MODE == MODE_BATCH) {
+    d.idx = cur.idx + 1;
+    d.s = t;
+    d.e = t + q.seqlen;
+    if (d.e > dend) d.e = dend;
+  } else {
+    d.idx = -1;
+    d.s = t;
+    d.e = idx_next_start(q, t, limit);
+  }
+  return d;
+}
+
+}  // namespace cconv

@@ -1,0 +1,87 @@
+// conv1d_launch.h -- library-internal launch parameters shared by the host entry points
+// (conv1d_api.cpp) and the kernels.  Everything here is plain data: pointers are device
+// pointers that the host has validated but never dereferences.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cconv {
+
+// Rows per wave and per block (4 waves) of the forward and backward kernels.  The backward's
+// per-block dweight partials live in the workspace, one [5, C] FP32 slab per row block.
+constexpr int kFwdRowsPerWave = 32;
+constexpr int kBwdRowsPerWave = 64;
+constexpr int kFwdRowsPerBlock = 4 * kFwdRowsPerWave;
+constexpr int kBwdRowsPerBlock = 4 * kBwdRowsPerWave;
+
+// How rows split into sequences: cu_seqlens offsets, per-token sequence IDs, or batch rows.
+enum { MODE_CU = 0, MODE_IDX = 1, MODE_BATCH = 2 };
+
+struct SeqArgs {
+  const int32_t* cu;       // [nseq + 1] or nullptr
+  int64_t nseq;            // number of sequences (cu form or batch-row form)
+  const int32_t* seq_idx;  // [rows] or nullptr
+  int64_t seqlen;          // batch-row length (IDX / BATCH forms)
+};
+
+struct PoolArgs {
+  uint16_t* ptr;  // nullptr: no pool
+  int64_t slots, s_slot, s_chan, s_pos;
+  const int32_t* cache_indices;
+  const uint8_t* has_init;
+};
+
+struct HistArgs {
+  const uint16_t* ptr;  // nullptr: no history rows; else contiguous [nseq, 3, C]
+  const uint8_t* has_hist;
+};
+
+struct FwdArgs {
+  const uint16_t* x;
+  uint16_t* y;
+  int64_t x_ld, y_ld, rows, C;
+  const void* w;
+  const void* b;
+  int w_f32, b_f32;
+  SeqArgs seq;
+  PoolArgs pool;
+  HistArgs hist;
+  uint32_t n_strips, n_rowblocks;
+};
+
+struct DecodeArgs {
+  const uint16_t* x;
+  uint16_t* y;
+  int64_t x_ld, y_ld, nseq, C;
+  const void* w;
+  const void* b;
+  int w_f32, b_f32;
+  PoolArgs pool;
+  uint32_t n_strips;
+};
+
+struct BwdArgs {
+  const uint16_t* x;
+  const uint16_t* dy;
+  uint16_t* dx;
+  int64_t x_ld, dy_ld, dx_ld, rows, C;
+  const void* w;
+  const void* b;
+  int w_f32, b_f32;
+  SeqArgs seq;
+  HistArgs hist;
+  uint16_t* dhist;  // nullptr: not requested
+  float* part;      // workspace: [n_rowblocks, 5, C] FP32 per-block partials
+  float* dw;        // [C, 4]
+  float* db;        // [C] or nullptr
+  uint32_t n_strips, n_rowblocks;
+};
+
+// Launchers (return hipError_t of the launch).  mode: 0 = cu_seqlens, 1 = seq_idx, 2 = batch rows.
+hipError_t launch_fwd(const FwdArgs& a, int mode, bool vec, bool silu, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, bool vec, bool silu, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int mode, bool vec, bool silu, hipStream_t stream);
+
+}  // namespace cconv

@@ -1,0 +1,152 @@
+/*
+ * conv1d.h -- C ABI of the MI355X (gfx950) packed width-4 depthwise causal Conv1d (+ SiLU).
+ *
+ * The operation (FlashInfer docs, flashinfer.mamba.causal_conv1d_fn, Parameters and Notes):
+ * for every packed sequence with rows [s, e) and channel c, with the extended sequence
+ *     u[-3], u[-2], u[-1] = the sequence's history (zeros unless stated otherwise),
+ *     u[t] = x[s + t]                                              (raw bf16 inputs),
+ *     z[t] = b[c] + w[c][0]*u[t-3] + w[c][1]*u[t-2] + w[c][2]*u[t-1] + w[c][3]*u[t]
+ * accumulated in FP32 (bias first, then taps 0..3 as fused multiply-adds; tap 3 multiplies the
+ * current token), and y[s + t][c] = act(z[t]) rounded to bf16 (round to nearest even), where
+ * act is SiLU (z * sigmoid(z), FP32) or the identity (the Megatron-Core page
+ * core.ssm.causal_conv1d.causal_conv1d_cp makes bias and activation optional).
+ *
+ * Conventions shared by every entry point:
+ *   - All data pointers are DEVICE pointers; the caller owns every buffer.  The library never
+ *     allocates, never reads device memory on the host, never synchronizes, and keeps no
+ *     mutable global state: every call only enqueues kernels on `stream` (a hipStream_t, NULL =
+ *     the null stream), so calls can be captured in a HIP graph and replayed with device
+ *     metadata (offsets, slots, flags) changed in place within the same capacities
+ *     (causal_conv1d_fn, Notes).
+ *   - bf16 tensors are 16-bit bf16 bit patterns.  x, y, dy, dx are row-major [rows, C] with a
+ *     row stride (`*_ld`, in elements, >= C) and contiguous channels.
+ *   - Taps w are a contiguous [C, 4] array of FP32 or bf16 (`w_dtype`); the optional bias is a
+ *     contiguous [C] array of FP32 or bf16 (`b_dtype`), NULL for none
+ *     (causal_conv1d_fn, Parameters weight and bias).
+ *   - Host-checkable preconditions are validated before anything is enqueued; a violation
+ *     returns CONV1D_EINVAL (or CONV1D_EWORKSPACE) and launches nothing.  Device-side values
+ *     (offsets, sequence IDs, slot numbers) are the caller's constraint and are not checked:
+ *     offsets must start at 0, be nondecreasing and end at most at `rows`; live slots must be
+ *     unique and in [0, slots); sequence IDs must be non-negative (causal_conv1d_fn, Notes;
+ *     causal_conv1d_cp, Parameters global_seq_idx).  Violating them is undefined behaviour.
+ *   - Any C >= 1 and any row stride are accepted.  When C, the strides and the pointers allow
+ *     16-byte vectors a vectorized kernel runs, otherwise an element-wise one; results are
+ *     identical.
+ *   - Two calls that run concurrently must not share live slots or workspaces.
+ */
+#ifndef CONV1D_H
+#define CONV1D_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CONV1D_OK = 0,
+  CONV1D_EINVAL = 1,      /* a host-checkable precondition failed; nothing was launched     */
+  CONV1D_EWORKSPACE = 2,  /* workspace missing or smaller than the *_workspace_bytes query  */
+  CONV1D_EUNSUPPORTED = 3,/* reserved; not returned by this version                         */
+  CONV1D_EHIP = 4         /* the HIP runtime reported a launch error                        */
+} conv1d_status;
+
+typedef enum { CONV1D_BF16 = 0, CONV1D_F32 = 1 } conv1d_dtype;
+typedef enum { CONV1D_ACT_NONE = 0, CONV1D_ACT_SILU = 1 } conv1d_act;
+
+/* How the packed rows split into independent sequences; the convolution state resets at every
+   sequence start.  Exactly one form is used:
+   - cu_seqlens != NULL: int32 [nseq + 1] offsets, sequence i = rows [cu[i], cu[i+1]); rows at
+     or after cu[nseq] belong to no sequence and are never written; empty sequences are allowed
+     (causal_conv1d_fn, Parameters cu_seqlens).  seq_idx must be NULL.
+   - seq_idx != NULL: int32 [rows] per-token sequence IDs (>= 0) inside batch rows of `seqlen`
+     rows (rows % seqlen == 0); a sequence starts at every batch-row start and wherever the ID
+     differs from the previous row's (causal_conv1d_cp, Parameters x and global_seq_idx).
+   - both NULL: every batch row of `seqlen` rows is one sequence (rows % seqlen == 0). */
+typedef struct {
+  const int32_t* cu_seqlens;
+  int64_t nseq;
+  const int32_t* seq_idx;
+  int64_t seqlen;
+} conv1d_seq;
+
+/* In-place bf16 state pool [slots, C, len] (causal_conv1d_fn, Parameters conv_state,
+   cache_indices, has_initial_state).  Element (slot, c, j) is at
+   ptr + slot*s_slot + c*s_chan + j*s_pos (strides in elements); either s_chan == 1 or
+   s_pos == 1, and slots must not overlap.  History position j (j = 0, 1, 2) holds the raw
+   input 3 - j rows before the sequence's first row (oldest first).
+   cache_indices: int32 [nseq] slot of each sequence; -1 gives +0 output rows and no state
+   access.  has_initial_state: uint8 [nseq] (NULL = all false); true reads positions 0..2 as
+   the history, false starts from zeros.  After the call, positions 0..2 of the slot of every
+   live nonempty sequence hold the last three values of its extended sequence u; positions
+   >= 3, other slots and slots of empty sequences are unchanged.  Needs the cu_seqlens or the
+   batch-row form (the host must know nseq). */
+typedef struct {
+  void* ptr;
+  int64_t slots, len, s_slot, s_chan, s_pos;
+  const int32_t* cache_indices;
+  const uint8_t* has_initial_state;
+} conv1d_pool;
+
+/* Caller-supplied history rows for the context-parallel share of one GPU
+   (flashinfer.cake_causal_conv1d_train.cake_causal_conv1d_kcp, summary: a fragment that
+   continues a document reads the preceding fragment's rows instead of zeros).  ptr: contiguous
+   bf16 [nseq, 3, C]; row j of entry i is the raw input 3 - j rows before sequence i's first
+   row.  has_history: uint8 [nseq], NULL = every sequence reads its rows; sequences with 0 start
+   from zeros.  Needs the cu_seqlens or the batch-row form. */
+typedef struct {
+  const void* ptr;
+  const uint8_t* has_history;
+} conv1d_hist;
+
+/* Forward over packed rows (causal_conv1d_fn; causal_conv1d_cp; cake_causal_conv1d_kcp).
+   x, y: bf16 [rows, C] with strides x_ld, y_ld.  seq: required.  pool, hist: optional
+   (NULL), not both.  act: conv1d_act.  y must not overlap x, w, b, the pool or hist; rows of y
+   outside every sequence are not written.  ws/ws_bytes: unused (0 bytes needed; may be NULL).
+   Returns a conv1d_status. */
+int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void* w, int w_dtype,
+               const void* b, int b_dtype, const conv1d_seq* seq, const conv1d_pool* pool,
+               const conv1d_hist* hist, int act, void* y, int64_t y_ld, void* ws, size_t ws_bytes,
+               hipStream_t stream);
+
+/* One decode step per sequence (causal_conv1d_fn, Notes: the step after prefill).  x, y: bf16
+   [nseq, C] (one new token per sequence).  For a live slot: y = act(b + w . [h0, h1, h2, x])
+   with the slot's positions 0..2 as h, then positions 0..2 become [h1, h2, x]; slot -1 gives
+   +0 and no state access.  Equal, bit for bit, to conv1d_fwd on unit-length sequences with
+   has_initial_state all true.  pool is required (its has_initial_state field is ignored). */
+int conv1d_state_update(const void* x, int64_t nseq, int64_t C, int64_t x_ld, const void* w,
+                        int w_dtype, const void* b, int b_dtype, const conv1d_pool* pool, int act,
+                        void* y, int64_t y_ld, hipStream_t stream);
+
+/* Training backward (cake_causal_conv1d_kcp, Returns: dx and a deterministic FP32 dweight;
+   causal_conv1d_cp).  Given dy = dL/dy (bf16 [rows, C], stride dy_ld), recomputes the forward
+   z and writes
+     dx   bf16 [rows, C] (stride dx_ld): dL/dx, rows outside every sequence untouched;
+     dw   FP32 [C, 4]: dL/dw, contiguous (required);
+     db   FP32 [C]: dL/db (NULL to skip; computed whether or not b is given);
+     dhist bf16 [nseq, 3, C]: dL/d(history rows) for sequences that read history rows
+          (requires hist; NULL to skip; rows of other sequences untouched).
+   dw and db are sums of per-tile FP32 partials combined in a fixed order by a second kernel
+   (no atomics), so they are bitwise identical from run to run and independent of the
+   workspace address.  ws: device scratch of at least conv1d_bwd_workspace_bytes(rows, C)
+   bytes, 16-byte aligned, not overlapping any operand.  No pool. */
+int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x_ld, int64_t dy_ld,
+               const void* w, int w_dtype, const void* b, int b_dtype, const conv1d_seq* seq,
+               const conv1d_hist* hist, int act, void* dx, int64_t dx_ld, float* dw, float* db,
+               void* dhist, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace sizes in bytes (host-only, pure functions of the capacities). */
+size_t conv1d_fwd_workspace_bytes(int64_t rows, int64_t C, int64_t nseq);
+size_t conv1d_bwd_workspace_bytes(int64_t rows, int64_t C);
+
+/* Static description of a status code. */
+const char* conv1d_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV1D_H */

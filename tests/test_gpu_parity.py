@@ -1,0 +1,186 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Covers the five workloads at full size (forward; backward where the workload trains), sweeps of
+small random problems that span several row tiles with ragged tails, the scalar (unaligned)
+path, both pool layouts, and the degenerate cases (no rows, no sequences, empty sequences,
+sequences of 1..3 rows on tile boundaries, all-sentinel batches).
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import gpu_harness as gh  # noqa: E402
+from causal_depthwise_conv1d_width_amd import workloads as wl  # noqa: E402
+
+
+def _print_case(name, **kw):
+    print(f"[gpu] {name} {kw}", flush=True)
+
+
+# ------------------------------------------------------------------ the five workloads
+def test_config1_forward(oracle):
+    case = wl.config_1()
+    _print_case(case["name"])
+    gh.check_fwd(oracle, case)
+
+
+@pytest.mark.parametrize("layout", ["hist", "chan"])
+def test_config2_forward_pool(oracle, layout):
+    case = wl.config_2(layout)
+    _print_case(case["name"])
+    y, pool = gh.check_fwd(oracle, case)
+    # the empty sequence keeps its slot untouched; the sentinel's slot too
+    ci = case["cache_indices"]
+    assert np.array_equal(pool[ci[case["empty"]]], case["pool"][ci[case["empty"]]])
+
+
+def test_config3_forward_pool_padding(oracle):
+    case = wl.config_3()
+    _print_case(case["name"])
+    y, _ = gh.check_fwd(oracle, case)
+    assert (y[32512:] == wl.OUT_FILL).all(), "padding rows after the last offset must stay untouched"
+
+
+def test_config4_forward_backward(oracle):
+    case = wl.config_4()
+    _print_case(case["name"])
+    gh.check_fwd(oracle, case)
+    gh.check_bwd(oracle, case)
+
+
+def test_config5_forward_backward(oracle):
+    case = wl.config_5()
+    _print_case(case["name"])
+    gh.check_fwd(oracle, case)
+    gh.check_bwd(oracle, case)
+
+
+# ------------------------------------------------------------------ sweeps
+def _sweep_cases(seed, n, mode):
+    rng = np.random.default_rng(seed)
+    out = []
+    for q in range(n):
+        C = int(rng.choice([1, 3, 8, 13, 64, 520, 1032, 1024]))
+        layout = [None, "hist", "chan"][q % 3] if mode == "cu" else None
+        case = wl.random_case(rng, C=C, nseq=int(rng.integers(0, 9)), max_len=int(rng.choice([3, 40, 300])),
+                              mode=mode, pool_layout_name=layout, with_hist=(mode == "cu" and layout is None and q % 2 == 0),
+                              L=int(rng.choice([3, 4, 6])), w_f32=bool(q % 2), act="silu" if q % 5 else "none",
+                              sentinel=(q % 3 == 1), force_empty=(q % 4 == 1))
+        case["name"] = f"sweep-{mode}-{seed}-{q}-C{C}"
+        out.append(case)
+    return out
+
+
+@pytest.mark.parametrize("mode", ["cu", "idx"])
+def test_sweep_forward(oracle, mode):
+    for case in _sweep_cases(100 if mode == "cu" else 200, 30, mode):
+        _print_case(case["name"], rows=case["x"].shape[0])
+        gh.check_fwd(oracle, case)
+
+
+@pytest.mark.parametrize("mode", ["cu", "idx"])
+def test_sweep_backward(oracle, mode):
+    for case in _sweep_cases(300 if mode == "cu" else 400, 30, mode):
+        case.pop("pool", None)
+        case.pop("cache_indices", None)
+        case.pop("has_initial_state", None)
+        _print_case(case["name"], rows=case["x"].shape[0])
+        gh.check_bwd(oracle, case)
+
+
+def _boundary_case(rng, C, lengths, layout="hist", hist=False, act="silu", pad=5):
+    """Sequences whose first rows land on wave (32/64-row) and block (128/256-row) boundaries."""
+    lengths = np.asarray(lengths, np.int64)
+    cu = np.zeros(len(lengths) + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    rows = int(cu[-1]) + pad
+    n = len(lengths)
+    case = dict(name=f"boundary-C{C}-{layout}-{'hist' if hist else 'pool'}", act=act, cu_seqlens=cu,
+                x=wl.normal_bf16(rng, (rows, C)), w=wl.uniform_f32(rng, (C, 4)),
+                b=(rng.standard_normal(C) * 0.1).astype(np.float32), dy=wl.normal_bf16(rng, (rows, C)))
+    if hist:
+        case["hist"] = wl.normal_bf16(rng, (n, 3, C))
+        case["has_history"] = (rng.random(n) < 0.7).astype(np.uint8)
+    elif layout is not None:
+        case["pool"] = wl.pool_layout(wl.normal_bf16(rng, (n + 3, C, 4)), layout)
+        ci = rng.permutation(n + 3)[:n].astype(np.int32)
+        ci[::7] = -1
+        case["cache_indices"] = ci
+        case["has_initial_state"] = (rng.random(n) < 0.8).astype(np.uint8)
+    return case
+
+
+def _boundary_lengths():
+    # prefix lengths chosen so sequence starts fall 1, 2, 3 rows before/after multiples of 32 and
+    # 64, with sequences of length 1, 2, 3 and 4 straddling them
+    return [31, 1, 1, 1, 28, 2, 2, 62, 3, 29, 4, 1, 93, 2, 1, 127, 3, 3, 1, 125, 1, 2, 254, 5, 0, 0, 2, 3, 60]
+
+
+@pytest.mark.parametrize("layout", ["hist", "chan", None])
+def test_tile_boundary_sequences_forward(oracle, layout):
+    rng = np.random.default_rng(7)
+    for C in (512, 24, 5):
+        case = _boundary_case(rng, C, _boundary_lengths(), layout=layout, hist=(layout is None))
+        _print_case(case["name"])
+        gh.check_fwd(oracle, case)
+
+
+def test_tile_boundary_sequences_backward(oracle):
+    rng = np.random.default_rng(8)
+    for C in (512, 24, 5):
+        case = _boundary_case(rng, C, _boundary_lengths(), layout=None, hist=True)
+        _print_case(case["name"])
+        gh.check_bwd(oracle, case)
+        case.pop("hist")
+        case.pop("has_history")
+        gh.check_bwd(oracle, case)
+
+
+def test_degenerate_inputs(oracle):
+    rng = np.random.default_rng(9)
+    C = 16
+    w = wl.uniform_f32(rng, (C, 4))
+    # no rows at all
+    for cu in (np.array([0], np.int32), np.array([0, 0, 0], np.int32)):
+        case = dict(name="empty", x=np.zeros((0, C), np.uint16), w=w, b=None, cu_seqlens=cu,
+                    dy=np.zeros((0, C), np.uint16), act="silu")
+        gh.check_fwd(oracle, case)
+        gh.check_bwd(oracle, case)
+    # rows but no sequence / only empty sequences: nothing written, dweight = 0
+    for cu in (np.array([0], np.int32), np.array([0, 0, 0], np.int32)):
+        case = dict(name="padding-only", x=wl.normal_bf16(rng, (9, C)), w=w, b=None, cu_seqlens=cu,
+                    dy=wl.normal_bf16(rng, (9, C)), act="silu")
+        y, _ = gh.check_fwd(oracle, case)
+        assert (y == wl.OUT_FILL).all()
+        dx, dw, _, _ = gh.check_bwd(oracle, case)
+        assert (dw == 0).all() and (dx == wl.OUT_FILL).all()
+    # all sentinels: zero rows, pool untouched
+    cu = np.array([0, 3, 9, 10], np.int32)
+    pool = wl.normal_bf16(rng, (4, C, 4))
+    case = dict(name="all-sentinel", x=wl.normal_bf16(rng, (12, C)), w=w, b=None, cu_seqlens=cu, pool=pool,
+                cache_indices=np.array([-1, -1, -1], np.int32), has_initial_state=np.ones(3, np.uint8), act="silu")
+    y, p = gh.check_fwd(oracle, case)
+    assert (y[:10] == 0).all() and np.array_equal(p, pool)
+    # empty fragment with history rows: d(history) = 0
+    cu = np.array([0, 4, 4, 9], np.int32)
+    case = dict(name="empty-fragment-hist", x=wl.normal_bf16(rng, (9, C)), w=w, b=None, cu_seqlens=cu,
+                hist=wl.normal_bf16(rng, (3, 3, C)), has_history=np.ones(3, np.uint8),
+                dy=wl.normal_bf16(rng, (9, C)), act="silu")
+    dx, dw, _, dh = gh.check_bwd(oracle, case)
+    assert (dh[1] == 0).all()
+
+
+def test_batch_rows_form(oracle):
+    """Neither offsets nor IDs: every batch row of `seqlen` rows is one sequence."""
+    rng = np.random.default_rng(10)
+    C, B, T = 64, 5, 77
+    case = dict(name="batch-rows", x=wl.normal_bf16(rng, (B * T, C)), w=wl.uniform_f32(rng, (C, 4)),
+                b=(rng.standard_normal(C) * 0.1).astype(np.float32), seqlen=T, dy=wl.normal_bf16(rng, (B * T, C)),
+                act="silu")
+    gh.check_fwd(oracle, case)
+    gh.check_bwd(oracle, case)
