@@ -1,0 +1,346 @@
+"""Benchmark: effective HBM GB/s of the packed causal conv1d (+ SiLU), forward and backward.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one pass of the whole hot path over one batch of the context-parallel workload (the
+largest single-GPU training workload): the forward (sequence lookup, history rows, stencil,
+SiLU) and the backward (recompute, dx, per-block dweight partials + ordered reduce,
+d(history)) over x [16384, 5632] bf16 in 12 fragments, 8 with 3 history rows.  Inputs are
+resident in HBM before the timed region.  Steady state, as inside a training or serving loop:
+the timed calls run back to back on one stream over a ring of independent buffer sets (4 for the
+step workload, about 3 GB), so no call finds its operands in the 256 MB Infinity Cache and every
+call's writes evict the previous calls' dirty lines, i.e. each written byte is paid for in HBM.
+HIP events on the stream the library launches on bracket each batch of calls; `value` =
+algorithmic bytes of K steps / the batch time.  Effective bytes count what the method must move,
+each once (activations read and written, history rows, taps, gradients); halo re-reads and the
+dweight partial workspace are overhead and not counted.
+
+The same JSON line also carries every other workload (forward of the small and pool-prefill
+workloads, forward and backward of the per-token-ID training workload, a decode step), a plain
+bf16 copy as the practical bandwidth ceiling, the roofline object of the dominant call and the
+CPU oracle timed on the host as a baseline.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
+METRIC = "effective GB/s (fwd, bwd) of packed causal conv1d+SiLU; % of HBM peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_conv1d_bwd_kernel_cp_share.md")
+KERNEL_SOURCES = ["conv1d_device.h", "conv1d_launch.h", "conv1d_fwd.hip", "conv1d_bwd.hip", "conv1d_api.cpp"]
+
+
+# ------------------------------------------------------------------ algorithmic bytes
+def _tap_bytes(a):
+    return 0 if a is None else a.size * a.itemsize
+
+
+def _segments(case):
+    rows = case["x"].shape[0]
+    if case.get("cu_seqlens") is not None:
+        cu = case["cu_seqlens"].astype(np.int64)
+        return [(int(cu[i]), int(cu[i + 1]), i) for i in range(len(cu) - 1)], int(cu[-1]), len(cu) - 1
+    return None, rows, 0
+
+
+def fwd_bytes(case):
+    """2C per row read (live sequences) + 2C per row written + 6C per history read / state write
+    + taps + bias + metadata."""
+    rows, C = case["x"].shape
+    segs, r_out, nseq = _segments(case)
+    r_read, n_state = r_out, 0
+    meta = 0
+    if segs is not None:
+        meta += (nseq + 1) * 4
+        if case.get("pool") is not None:
+            ci, hi = case["cache_indices"], case["has_initial_state"]
+            meta += nseq * 4 + nseq
+            r_read = sum(e - s for s, e, i in segs if ci[i] >= 0)
+            n_state = sum((1 + int(hi[i])) for s, e, i in segs if ci[i] >= 0 and e > s)
+        if case.get("hist") is not None:
+            hh = case.get("has_history")
+            meta += nseq
+            n_state = sum(1 for s, e, i in segs if e > s and (hh is None or hh[i]))
+    if case.get("seq_idx") is not None:
+        meta += rows * 4
+    return (2 * C * r_read + 2 * C * r_out + 6 * C * n_state + _tap_bytes(case["w"]) + _tap_bytes(case.get("b"))
+            + meta)
+
+
+def bwd_bytes(case):
+    """6C per row (x, dy read; dx written) + 6C per history row set read and its gradient written
+    + taps + bias + dweight (+ dbias) + metadata."""
+    rows, C = case["x"].shape
+    segs, r, nseq = _segments(case)
+    n_hist, meta = 0, 0
+    if segs is not None:
+        meta += (nseq + 1) * 4
+        if case.get("hist") is not None:
+            hh = case.get("has_history")
+            meta += nseq
+            n_hist = sum(1 for s, e, i in segs if hh is None or hh[i])
+    if case.get("seq_idx") is not None:
+        meta += rows * 4
+    has_b = case.get("b") is not None
+    return (6 * C * r + 12 * C * n_hist + _tap_bytes(case["w"]) + _tap_bytes(case.get("b")) + 16 * C
+            + (4 * C if has_b else 0) + meta)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "causal_depthwise_conv1d_width_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per conv1d_bwd call from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; else None."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
+    m_bytes = re.search(r"hbm_bytes_per_call:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+# ------------------------------------------------------------------ GPU side
+class Gpu:
+    def __init__(self):
+        import torch
+
+        import causal_depthwise_conv1d_width_amd as cc
+        from causal_depthwise_conv1d_width_amd import _lib
+        _lib.load()  # fail loudly if the HIP library is missing
+        self.torch, self.cc = torch, cc
+        self.dev = torch.device("cuda", 0)
+        self.stream = torch.cuda.current_stream()
+
+    def bits(self, a):
+        t = self.torch
+        return t.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(t.bfloat16).to(self.dev)
+
+    def taps(self, a):
+        if a is None:
+            return None
+        return self.bits(a) if a.dtype == np.uint16 else self.torch.from_numpy(a).to(self.dev)
+
+    def i32(self, a):
+        return None if a is None else self.torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(self.dev)
+
+    def u8(self, a):
+        return None if a is None else self.torch.from_numpy(np.ascontiguousarray(a, np.uint8)).to(self.dev)
+
+    def pool(self, a):
+        t = self.torch
+        st = tuple(s // 2 for s in a.strides)
+        p = t.empty_strided(a.shape, st, dtype=t.bfloat16, device=self.dev)
+        p.copy_(self.bits(np.ascontiguousarray(a)).view(a.shape))
+        return p
+
+    def prepare(self, case):
+        """Device copies of a workload plus preallocated outputs: calls allocate nothing."""
+        t = self.torch
+        rows, C = case["x"].shape
+        d = dict(x=self.bits(case["x"]), w=self.taps(case["w"]), b=self.taps(case.get("b")),
+                 cu=self.i32(case.get("cu_seqlens")), seq_idx=self.i32(case.get("seq_idx")),
+                 seqlen=case.get("seqlen"), act=case.get("act", "silu"))
+        d["y"] = t.empty((rows, C), dtype=t.bfloat16, device=self.dev)
+        if case.get("pool") is not None:
+            d["pool"] = self.pool(case["pool"])
+            d["ci"], d["hi"] = self.i32(case["cache_indices"]), self.u8(case["has_initial_state"])
+        if case.get("hist") is not None:
+            d["hist"], d["hh"] = self.bits(case["hist"]), self.u8(case.get("has_history"))
+            d["dhist"] = t.empty_like(d["hist"])
+        if case.get("dy") is not None:
+            d["dy"] = self.bits(case["dy"])
+            d["dx"] = t.empty((rows, C), dtype=t.bfloat16, device=self.dev)
+            d["dw"] = t.empty((C, 4), dtype=t.float32, device=self.dev)
+            d["db"] = t.empty((C,), dtype=t.float32, device=self.dev) if case.get("b") is not None else None
+            need = self.cc.conv1d_bwd_workspace_bytes(rows, C)
+            d["ws"] = t.empty((max(need, 1),), dtype=t.uint8, device=self.dev)
+        return d
+
+    def fwd(self, d):
+        # repeated prefills keep updating the pool in place: same reads and writes every call
+        return self.cc.conv1d_fwd(d["x"], d["w"], d["b"], cu_seqlens=d["cu"], seq_idx=d["seq_idx"],
+                                  seqlen=d["seqlen"], conv_state=d.get("pool"), cache_indices=d.get("ci"),
+                                  has_initial_state=d.get("hi"), history=d.get("hist"),
+                                  has_history=d.get("hh"), activation=d["act"], out=d["y"])
+
+    def bwd(self, d):
+        return self.cc.conv1d_bwd(d["x"], d["dy"], d["w"], d["b"], cu_seqlens=d["cu"], seq_idx=d["seq_idx"],
+                                  seqlen=d["seqlen"], history=d.get("hist"), has_history=d.get("hh"),
+                                  activation=d["act"], dx=d["dx"], dweight=d["dw"], dbias=d["db"],
+                                  want_dbias=d["db"] is not None, dhistory=d.get("dhist"),
+                                  want_dhistory="dhist" in d, workspace=d["ws"])
+
+    def ring(self, calls, k, warmup):
+        """Mean milliseconds per call over k back-to-back passes of `calls` (a list of zero-argument
+        callables cycling through independent buffer sets), bracketed by two HIP events."""
+        t = self.torch
+        for i in range(warmup * len(calls)):
+            calls[i % len(calls)]()
+        ev0, ev1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        ev0.record(self.stream)
+        for i in range(k):
+            calls[i % len(calls)]()
+        ev1.record(self.stream)
+        t.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / k
+
+    def copy_ceiling(self, nbytes=1 << 30):
+        """A plain bf16 device copy of nbytes (torch's copy kernel) under the same steady state:
+        the practical HBM ceiling for a read-once / write-once stream."""
+        t = self.torch
+        bufs = [(t.empty(nbytes // 2, dtype=t.bfloat16, device=self.dev).normal_(),
+                 t.empty(nbytes // 2, dtype=t.bfloat16, device=self.dev)) for _ in range(2)]
+        ms = self.ring([lambda a=a, b=b: b.copy_(a) for a, b in bufs], 20, 3)
+        return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def gbps(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+def cpu_baseline(case, max_seconds=30.0):
+    """The oracle as it stands (plain C loops, OpenMP over channel blocks) on the host cores: one
+    warm pass, then timed passes of forward + backward until ~10 s of wall time have passed."""
+    from oracle import Oracle
+    o = Oracle()
+    kw = dict(cu_seqlens=case.get("cu_seqlens"), seq_idx=case.get("seq_idx"), seqlen=case.get("seqlen"),
+              hist=case.get("hist"), has_history=case.get("has_history"), act=case.get("act", "silu"))
+    o.fwd(case["x"], case["w"], case.get("b"), **kw)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        o.fwd(case["x"], case["w"], case.get("b"), **kw)
+        o.bwd(case["x"], case["dy"], case["w"], case.get("b"), **kw)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > 10.0 or len(times) >= 20 or sum(times) > max_seconds:
+            break
+    sec = sorted(times)[len(times) // 2]
+    nbytes = fwd_bytes(case) + bwd_bytes(case)
+    return {"value": round(nbytes / sec / 1e9, 3), "unit": "GB/s", "cores": o.threads(), "kind": "oracle",
+            "sample": f"the full step workload (fwd + bwd over x [16384, 5632]), median of {len(times)} timed passes "
+                      f"after one warm pass; {sec:.3f} s per pass",
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true", help="skip the other workloads and the copy ceiling")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU: the multi-GPU context-parallel exchange is "
+                                   "designed but not built; run with --gpus 1"}), flush=True)
+        sys.exit(2)
+
+    from causal_depthwise_conv1d_width_amd import workloads as wl
+    g = Gpu()
+    torch = g.torch
+
+    case = wl.config_5()
+    sets = [g.prepare(case) for _ in range(4)]
+    fb, bb = fwd_bytes(case), bwd_bytes(case)
+    # step k: forward on set k % 4, backward on set (k + 2) % 4 -> consecutive calls never share data
+    step_calls = []
+    for k in range(4):
+        step_calls.append(lambda k=k: g.fwd(sets[k]))
+        step_calls.append(lambda k=k: g.bwd(sets[(k + 2) % 4]))
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    mean_step = 2 * g.ring(step_calls, 2 * args.steps, args.warmup)
+    wall = time.perf_counter() - w0
+    mean_f = g.ring([lambda k=k: g.fwd(sets[k]) for k in range(4)], args.steps, 2)
+    mean_b = g.ring([lambda k=k: g.bwd(sets[k]) for k in range(4)], args.steps, 2)
+    value = gbps(fb + bb, mean_step)
+
+    traffic = stored_traffic()
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(mean_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "storage_dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "context-parallel share: x [16384, 5632] bf16 in 12 fragments (8 read 3 history "
+                               "rows), fp32 taps, no bias, SiLU; forward + backward (dx, dweight, d(history))",
+                   "rows": 16384, "channels": 5632, "fragments": 12, "with_history": 8},
+        "fwd": {"GBps": round(gbps(fb, mean_f), 1), "pct_of_peak": round(100 * gbps(fb, mean_f) / PEAK_HBM_GBPS, 2),
+                "ms": round(mean_f, 4), "bytes": fb},
+        "bwd": {"GBps": round(gbps(bb, mean_b), 1), "pct_of_peak": round(100 * gbps(bb, mean_b) / PEAK_HBM_GBPS, 2),
+                "ms": round(mean_b, 4), "bytes": bb},
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
+        "roofline": {"bound": "hbm", "kernel": "conv1d_bwd call (conv1d_bwd_kernel + conv1d_bwd_reduce_kernel)",
+                     "achieved": round(gbps(bb, mean_b), 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps(bb, mean_b) / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": bb},
+    }
+
+    if not args.no_extras:
+        extras = {"copy_ceiling_GBps": round(g.copy_ceiling(), 1)}
+        for k in (1, 2, 3, 4):
+            c = wl.CONFIGS[k]()
+            nb = fwd_bytes(c)
+            nsets = int(min(8, max(2, -(-(1 << 30) // nb))))
+            dd = [g.prepare(c) for _ in range(nsets)]
+            ms = g.ring([lambda d=d: g.fwd(d) for d in dd], 20, 3)
+            r = {"fwd_GBps": round(gbps(nb, ms), 1), "fwd_us": round(1e3 * ms, 2), "fwd_bytes": nb}
+            if c.get("dy") is not None:
+                nbb = bwd_bytes(c)
+                msb = g.ring([lambda d=d: g.bwd(d) for d in dd], 20, 3)
+                r.update({"bwd_GBps": round(gbps(nbb, msb), 1), "bwd_us": round(1e3 * msb, 2), "bwd_bytes": nbb})
+            extras[c["name"]] = r
+            del dd
+            if k == 3:  # decode step: one token for each of the 64 live slots of the prefill pool
+                C = c["x"].shape[1]
+                x1 = g.bits(c["x"][:64])
+                pool = g.pool(c["pool"])
+                ci = g.i32(c["cache_indices"])
+                y1 = torch.empty_like(x1)
+                w, b = g.taps(c["w"]), g.taps(c["b"])
+                msd = g.ring([lambda: g.cc.conv1d_state_update(x1, w, b, conv_state=pool, cache_indices=ci, out=y1)],
+                             50, 3)
+                nbd = 64 * C * 2 * 2 + 64 * C * 2 * 6 + 4 * C * 4 + C * 4 + 64 * 4
+                extras["decode_N64_C5632"] = {"GBps": round(gbps(nbd, msd), 1), "us": round(1e3 * msd, 2),
+                                              "bytes": nbd}
+        out["workloads"] = extras
+        out["step_workload"] = case["name"]
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

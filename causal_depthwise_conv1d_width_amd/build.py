@@ -23,14 +23,14 @@ def hipcc_flags():
             "-Wall", "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-def build(out=LIB, jobs=4, verbose=False):
-    objdir = os.path.join(PKG, "_build")
+def build(out=LIB, jobs=4, verbose=False, defines=()):
+    objdir = os.path.join(PKG, "_build", os.path.basename(out))
     os.makedirs(objdir, exist_ok=True)
     objs, procs = [], []
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = ["hipcc", *hipcc_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = ["hipcc", *hipcc_flags(), *[f"-D{d}" for d in defines], *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd))
         procs.append(subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True))

@@ -8,17 +8,18 @@
 //     dw_k   = sum_t dz[t] u[t-3+k],  db = sum_t dz[t]
 //     dh_j   = sum_{tau <= j} w_{j-tau} dz[s+tau]   (history row j of a continuing fragment)
 //
-// Tiling: as the forward (4 waves x 64 lanes, lane = CPL channels), kBwdRowsPerWave rows per
-// wave.  A wave needs x rows [ta-3, tb+3) and dy rows [ta, tb+3).  Before the block barrier
-// each wave stages its first three and last three x/dy rows in LDS; the boundary buffers
-// between waves then serve both neighbours (look-behind x for the next wave, look-ahead x/dy for
-// the previous one) and the owner itself, so inside a block each row leaves HBM once.
+// Tiling: as the forward (waves side by side in channels, lane = 8 channels), with kBwdRows-row
+// ranges.  A wave needs x rows [ta-3, tb+3) and dy rows [ta, tb+3); its own rows are streamed
+// once (non-temporal), the three look-behind and three look-ahead rows belong to the
+// neighbouring row ranges, which stream them at the same time on the same XCD, so those few
+// reads are served by L2.
 //
 // dweight/dbias are deterministic by construction: each lane accumulates its channels over its
-// rows in row order (FP32), the four waves of a block are added in wave order through LDS, the
-// block's [5, C] partial goes to the workspace, and a second kernel adds the partials of all
-// row blocks in ascending block order.  No atomics anywhere, so the bits depend only on the
-// input values and the row-block size, never on scheduling or on the workspace address.
+// rows in row order (FP32) and owns those channels for the whole row range, so the range's
+// [5, C] partial is written straight from registers to the workspace, and a second kernel adds
+// the partials of all row ranges in ascending range order.  No atomics anywhere, so the bits
+// depend only on the input values and the range length, never on scheduling or on the
+// workspace address.
 #include "conv1d_device.h"
 
 namespace cconv {
@@ -36,76 +37,135 @@ __device__ __forceinline__ void load_hist_rows(const HistArgs& hist, int64_t idx
   }
 }
 
+#ifndef CCONV_BWD_CHUNK
+#define CCONV_BWD_CHUNK 4
+#endif
+#ifndef CCONV_BWD_PIPELINE
+#define CCONV_BWD_PIPELINE 1
+#endif
+#ifndef CCONV_BWD_WAVES_PER_EU
+#define CCONV_BWD_WAVES_PER_EU 1
+#endif
+
+// Per-lane state of the backward stream (CPL channels).
+template <int CPL>
+struct BwdState {
+  float wk[4][CPL], bias[CPL];
+  float u[4][CPL];    // extended-sequence ring, slot = (row - run start) mod 4
+  float g[4][CPL];    // dz ring, same slots
+  float acc[5][CPL];  // dw_0..3, db partial sums over the wave's rows
+  float dh[3][CPL];   // d(history) of a head fragment
+};
+
+// One real row q (ring slot r): recompute z, dz = dy * act'(z); dweight/dbias sums when `own`.
+template <int CPL, bool SILU>
+__device__ __forceinline__ void bwd_row(BwdState<CPL>& st, const Pk<CPL>& xr, const Pk<CPL>& gr, int r, bool own) {
+  unpack(xr, st.u[r % 4]);
+  float dyv[CPL];
+  unpack(gr, dyv);
+#pragma unroll
+  for (int ch = 0; ch < CPL; ++ch) {
+    float z = st.bias[ch];
+    z = __builtin_fmaf(st.wk[0][ch], st.u[(r + 1) % 4][ch], z);
+    z = __builtin_fmaf(st.wk[1][ch], st.u[(r + 2) % 4][ch], z);
+    z = __builtin_fmaf(st.wk[2][ch], st.u[(r + 3) % 4][ch], z);
+    z = __builtin_fmaf(st.wk[3][ch], st.u[r % 4][ch], z);
+    float dz = dyv[ch];
+    if (SILU) {
+      const float sg = sigmoid_f32(z);
+      dz = dz * (sg * __builtin_fmaf(z, 1.0f - sg, 1.0f));
+    }
+    st.g[r % 4][ch] = dz;
+  }
+  if (own) {
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch) {
+      st.acc[0][ch] = __builtin_fmaf(st.g[r % 4][ch], st.u[(r + 1) % 4][ch], st.acc[0][ch]);
+      st.acc[1][ch] = __builtin_fmaf(st.g[r % 4][ch], st.u[(r + 2) % 4][ch], st.acc[1][ch]);
+      st.acc[2][ch] = __builtin_fmaf(st.g[r % 4][ch], st.u[(r + 3) % 4][ch], st.acc[2][ch]);
+      st.acc[3][ch] = __builtin_fmaf(st.g[r % 4][ch], st.u[r % 4][ch], st.acc[3][ch]);
+      st.acc[4][ch] += st.g[r % 4][ch];
+    }
+  }
+}
+
+// dx of the row three steps back: w3 dz[q-3] + w2 dz[q-2] + w1 dz[q-1] + w0 dz[q]
+template <int CPL>
+__device__ __forceinline__ Pk<CPL> bwd_dx(const BwdState<CPL>& st, int r) {
+  float d[CPL];
+#pragma unroll
+  for (int ch = 0; ch < CPL; ++ch) {
+    float v = st.wk[3][ch] * st.g[(r + 1) % 4][ch];
+    v = __builtin_fmaf(st.wk[2][ch], st.g[(r + 2) % 4][ch], v);
+    v = __builtin_fmaf(st.wk[1][ch], st.g[(r + 3) % 4][ch], v);
+    v = __builtin_fmaf(st.wk[0][ch], st.g[r % 4][ch], v);
+    d[ch] = v;
+  }
+  return pack(d);
+}
+
+// head of a continuing fragment: dh_j += w_{j-r} dz[s+r] for j >= r (r = 0, 1, 2)
+template <int CPL>
+__device__ __forceinline__ void bwd_dhist(BwdState<CPL>& st, int r) {
+#pragma unroll
+  for (int j = r; j < 3; ++j)
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch) st.dh[j][ch] = __builtin_fmaf(st.wk[j - r][ch], st.g[r % 4][ch], st.dh[j][ch]);
+}
+
+// CH own rows starting at q0 (every lane active, all rows real and owned).
+template <int CPL, bool VEC, int CH, bool SILU>
+__device__ __forceinline__ void bwd_chunk(BwdState<CPL>& st, const Pk<CPL> (&X)[CH], const Pk<CPL> (&G)[CH],
+                                          const BwdArgs& a, int64_t q0, int64_t t, int64_t c0, bool want_dh) {
+#pragma unroll
+  for (int r = 0; r < CH; ++r) {
+    bwd_row<CPL, SILU>(st, X[r], G[r], r, true);
+    if (r < 3 && want_dh && q0 == t) bwd_dhist<CPL>(st, r);
+    if (q0 + r - 3 >= t) store_row<CPL, VEC, true>(a.dx + (q0 + r - 3) * a.dx_ld, c0, a.C, bwd_dx<CPL>(st, r));
+  }
+}
+
+template <int CPL, bool VEC, int CH>
+__device__ __forceinline__ void bwd_load(Pk<CPL> (&X)[CH], Pk<CPL> (&G)[CH], const BwdArgs& a, int64_t q0, int64_t qlast,
+                                         int64_t c0) {
+#pragma unroll
+  for (int r = 0; r < CH; ++r) {
+    const int64_t q = q0 + r < qlast ? q0 + r : qlast;
+    X[r] = load_row<CPL, VEC, true>(a.x + q * a.x_ld, c0, a.C);
+    G[r] = load_row<CPL, VEC, true>(a.dy + q * a.dy_ld, c0, a.C);
+  }
+}
+
 template <int CPL, bool VEC, int MODE, bool SILU>
-__global__ void __launch_bounds__(kThreads) conv1d_bwd_kernel(const BwdArgs a) {
-  constexpr int KW = kBwdRowsPerWave;
-  constexpr int CH = 4;  // rows per unrolled chunk (the 4-slot rings)
-  // boundary buffers: bx[b][k] holds row (start of wave b) - 3 + k, k = 0..5
-  __shared__ Pk<CPL> bx[kWaves + 1][6][kWave];
-  __shared__ Pk<CPL> bdy[kWaves + 1][6][kWave];
+__global__ void __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(CCONV_BWD_WAVES_PER_EU)))
+conv1d_bwd_kernel(const BwdArgs a) {
+  constexpr int CH = CCONV_BWD_CHUNK;  // rows per unrolled chunk (a multiple of the 4-slot rings)
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
-  const uint32_t strip = tile / a.n_rowblocks, rb = tile % a.n_rowblocks;
+  uint32_t strip, rb;
+  tile_coords(xcd_tile(blockIdx.x, gridDim.x), a.n_strips, strip, rb);
   const int64_t C = a.C;
-  const int64_t c0 = (int64_t)strip * (kWave * CPL) + lane * CPL;
+  const int64_t wc0 = (int64_t)strip * kBlockChannels + (int64_t)wave * kWaveChannels;
+  if (wc0 >= C) return;  // the whole wave is past the last channel: no partial to write
+  const int64_t c0 = wc0 + lane * CPL;
   const bool active = c0 < C;
+  const bool full = VEC && wc0 + kWaveChannels <= C;  // every lane of the wave is active
   const int64_t dend = data_end<MODE>(a.seq, a.rows);
 
-  int64_t ta = (int64_t)rb * kBwdRowsPerBlock + (int64_t)wave * KW;
-  int64_t tb = ta + KW;
+  int64_t ta = (int64_t)rb * kBwdRows;
+  int64_t tb = ta + kBwdRows;
   ta = ta < dend ? ta : dend;
   tb = tb < dend ? tb : dend;
 
-  // ---- stage halos: own first / last three rows, plus the block's outer look-behind/ahead
-  if (active) {
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const int64_t rf = ta + j;
-      if (rf < tb) {
-        bx[wave][3 + j][lane] = load_row<CPL, VEC>(a.x + rf * a.x_ld, c0, C);
-        bdy[wave][3 + j][lane] = load_row<CPL, VEC>(a.dy + rf * a.dy_ld, c0, C);
-      }
-      const int64_t rl = tb - 3 + j;
-      if (rl >= ta) {
-        bx[wave + 1][j][lane] = load_row<CPL, VEC>(a.x + rl * a.x_ld, c0, C);
-        bdy[wave + 1][j][lane] = load_row<CPL, VEC>(a.dy + rl * a.dy_ld, c0, C);
-      }
-      if (wave == 0) {
-        const int64_t rb0 = ta - 3 + j;
-        if (rb0 >= 0 && ta < tb) bx[0][j][lane] = load_row<CPL, VEC>(a.x + rb0 * a.x_ld, c0, C);
-      }
-      if (wave == kWaves - 1) {
-        const int64_t ra = tb + j;
-        if (ra < dend && ta < tb) {
-          bx[kWaves][3 + j][lane] = load_row<CPL, VEC>(a.x + ra * a.x_ld, c0, C);
-          bdy[kWaves][3 + j][lane] = load_row<CPL, VEC>(a.dy + ra * a.dy_ld, c0, C);
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  float acc[5][CPL];  // dw_0..3, db partial sums of this lane
+  BwdState<CPL> st;
 #pragma unroll
   for (int k = 0; k < 5; ++k)
 #pragma unroll
-    for (int ch = 0; ch < CPL; ++ch) acc[k][ch] = 0.f;
+    for (int ch = 0; ch < CPL; ++ch) st.acc[k][ch] = 0.f;
 
   if (ta < tb) {
-    float wk[4][CPL], bias[CPL];
-    load_taps<CPL>(a.w, a.w_f32, a.b, a.b_f32, c0, C, wk, bias);
-
-    // x / dy of a wave-uniform row q, from the boundary buffers when staged, else from HBM
-    auto src = [&](int64_t q, const uint16_t* base, int64_t ld, Pk<CPL> (*buf)[6][kWave]) -> Pk<CPL> {
-      if (q >= ta - 3 && q < ta + 3) return buf[wave][q - ta + 3][lane];
-      if (q >= tb - 3 && q < tb + 3) return buf[wave + 1][q - tb + 3][lane];
-      return load_row<CPL, VEC>(base + q * ld, c0, C);
-    };
-
-    float u[4][CPL];  // extended-sequence ring, slot = (row - run start) mod 4
-    float g[4][CPL];  // dz ring, same slots
+    load_taps<CPL>(a.w, a.w_f32, a.b, a.b_f32, c0, C, st.wk, st.bias);
     const int64_t lim = (tb + 3 < dend) ? tb + 3 : dend;  // IDX scans need ends up to tb+3
     SeqDesc sd = seq_of_row<MODE>(a.seq, ta, dend, lim);
     int64_t t = ta;
@@ -123,23 +183,20 @@ __global__ void __launch_bounds__(kThreads) conv1d_bwd_kernel(const BwdArgs a) {
 #pragma unroll
           for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
       }
-      {
-        // window rows t-3..t-1: the history, then the last `dist` rows of the same sequence
-        for (int64_t k = 3 - dist; k < 3; ++k) {
-          Pk<CPL> p = zero_pk<CPL>();
-          if (active) p = src(t - 3 + k, a.x, a.x_ld, bx);
-          shift_in<CPL>(h, p);
-        }
-#pragma unroll
-        for (int j = 0; j < 3; ++j)
-#pragma unroll
-          for (int ch = 0; ch < CPL; ++ch) u[j + 1][ch] = h[j][ch];
+      // window rows t-3..t-1: the history, then the last `dist` rows of the same sequence
+      // (the previous row range streamed them moments earlier on this XCD: cached loads)
+      for (int64_t k = 3 - dist; k < 3; ++k) {
+        Pk<CPL> p = zero_pk<CPL>();
+        if (active) p = load_row<CPL, VEC>(a.x + (t - 3 + k) * a.x_ld, c0, C);
+        shift_in<CPL>(h, p);
       }
-      float dh[3][CPL];
 #pragma unroll
       for (int j = 0; j < 3; ++j)
 #pragma unroll
-        for (int ch = 0; ch < CPL; ++ch) dh[j][ch] = 0.f;
+        for (int ch = 0; ch < CPL; ++ch) {
+          st.u[j + 1][ch] = h[j][ch];
+          st.dh[j][ch] = 0.f;
+        }
 
       const int64_t t_end = sd.e < tb ? sd.e : tb;  // rows of this run that the wave owns
       int64_t la_end = t_end;                        // plus same-sequence look-ahead rows
@@ -147,7 +204,33 @@ __global__ void __launch_bounds__(kThreads) conv1d_bwd_kernel(const BwdArgs a) {
       if (la_end > dend) la_end = dend;
       const int64_t steps_end = t_end + 3;  // three trailing steps finish the last dx rows
 
-      for (int64_t q0 = t; q0 < steps_end; q0 += CH) {
+      // full chunks of own rows, software-pipelined with two register buffers (see the forward)
+      const int nfull = (full && CCONV_BWD_PIPELINE) ? (int)((t_end - t) / CH) : 0;
+      int64_t q0 = t;
+      if (nfull > 0) {
+        // two register buffers, unrolled by two chunks, next chunk's loads always issued (rows
+        // past the last full chunk re-read its last row): see the forward kernel
+        const int64_t qlast = t + (int64_t)nfull * CH - 1;
+        Pk<CPL> XA[CH], GA[CH], XB[CH], GB[CH];
+        bwd_load<CPL, VEC, CH>(XA, GA, a, q0, qlast, c0);
+        for (int j = 0;; j += 2, q0 += 2 * CH) {
+          bwd_load<CPL, VEC, CH>(XB, GB, a, q0 + CH, qlast, c0);
+          bwd_chunk<CPL, VEC, CH, SILU>(st, XA, GA, a, q0, t, c0, want_dh);
+          if (j + 1 >= nfull) {
+            q0 += CH;
+            break;
+          }
+          bwd_load<CPL, VEC, CH>(XA, GA, a, q0 + 2 * CH, qlast, c0);
+          bwd_chunk<CPL, VEC, CH, SILU>(st, XB, GB, a, q0 + CH, t, c0, want_dh);
+          if (j + 2 >= nfull) {
+            q0 += 2 * CH;
+            break;
+          }
+        }
+      }
+      // the rest: remaining own rows, look-ahead rows of the same sequence, and three trailing
+      // steps (dz = 0 past the sequence's end) that finish the last dx rows
+      for (; q0 < steps_end; q0 += CH) {
         Pk<CPL> xr[CH], gr[CH];
 #pragma unroll
         for (int r = 0; r < CH; ++r) {
@@ -155,8 +238,13 @@ __global__ void __launch_bounds__(kThreads) conv1d_bwd_kernel(const BwdArgs a) {
           xr[r] = zero_pk<CPL>();
           gr[r] = zero_pk<CPL>();
           if (q < la_end && active) {
-            xr[r] = src(q, a.x, a.x_ld, bx);
-            gr[r] = src(q, a.dy, a.dy_ld, bdy);
+            if (q < t_end) {  // own rows: read once, streamed
+              xr[r] = load_row<CPL, VEC, true>(a.x + q * a.x_ld, c0, C);
+              gr[r] = load_row<CPL, VEC, true>(a.dy + q * a.dy_ld, c0, C);
+            } else {  // look-ahead rows, owned by the next row range
+              xr[r] = load_row<CPL, VEC>(a.x + q * a.x_ld, c0, C);
+              gr[r] = load_row<CPL, VEC>(a.dy + q * a.dy_ld, c0, C);
+            }
           }
         }
 #pragma unroll
@@ -164,56 +252,15 @@ __global__ void __launch_bounds__(kThreads) conv1d_bwd_kernel(const BwdArgs a) {
           const int64_t q = q0 + r;
           if (q < steps_end) {
             if (q < la_end) {
-              unpack(xr[r], u[r % 4]);
-              float dyv[CPL];
-              unpack(gr[r], dyv);
-#pragma unroll
-              for (int ch = 0; ch < CPL; ++ch) {
-                float z = bias[ch];
-                z = __builtin_fmaf(wk[0][ch], u[(r + 1) % 4][ch], z);
-                z = __builtin_fmaf(wk[1][ch], u[(r + 2) % 4][ch], z);
-                z = __builtin_fmaf(wk[2][ch], u[(r + 3) % 4][ch], z);
-                z = __builtin_fmaf(wk[3][ch], u[r % 4][ch], z);
-                float dz = dyv[ch];
-                if (SILU) {
-                  const float sg = sigmoid_f32(z);
-                  dz = dz * (sg * __builtin_fmaf(z, 1.0f - sg, 1.0f));
-                }
-                g[r % 4][ch] = dz;
-              }
-              if (q < t_end) {
-#pragma unroll
-                for (int ch = 0; ch < CPL; ++ch) {
-                  acc[0][ch] = __builtin_fmaf(g[r % 4][ch], u[(r + 1) % 4][ch], acc[0][ch]);
-                  acc[1][ch] = __builtin_fmaf(g[r % 4][ch], u[(r + 2) % 4][ch], acc[1][ch]);
-                  acc[2][ch] = __builtin_fmaf(g[r % 4][ch], u[(r + 3) % 4][ch], acc[2][ch]);
-                  acc[3][ch] = __builtin_fmaf(g[r % 4][ch], u[r % 4][ch], acc[3][ch]);
-                  acc[4][ch] += g[r % 4][ch];
-                }
-              }
+              bwd_row<CPL, SILU>(st, xr[r], gr[r], r, q < t_end);
             } else {
 #pragma unroll
-              for (int ch = 0; ch < CPL; ++ch) g[r % 4][ch] = 0.f;  // past the sequence's end
+              for (int ch = 0; ch < CPL; ++ch) st.g[r % 4][ch] = 0.f;  // past the sequence's end
             }
-            if (r < 3 && want_dh && q0 == t) {
-              // head of a continuing fragment: dh_j += w_{j-r} dz[s+r] for j >= r
-#pragma unroll
-              for (int j = r; j < 3; ++j)
-#pragma unroll
-                for (int ch = 0; ch < CPL; ++ch) dh[j][ch] = __builtin_fmaf(wk[j - r][ch], g[r % 4][ch], dh[j][ch]);
-            }
+            if (r < 3 && want_dh && q0 == t) bwd_dhist<CPL>(st, r);
             if (q - 3 >= t) {
-              // dx[q-3] = w3 dz[q-3] + w2 dz[q-2] + w1 dz[q-1] + w0 dz[q]
-              float d[CPL];
-#pragma unroll
-              for (int ch = 0; ch < CPL; ++ch) {
-                float v = wk[3][ch] * g[(r + 1) % 4][ch];
-                v = __builtin_fmaf(wk[2][ch], g[(r + 2) % 4][ch], v);
-                v = __builtin_fmaf(wk[1][ch], g[(r + 3) % 4][ch], v);
-                v = __builtin_fmaf(wk[0][ch], g[r % 4][ch], v);
-                d[ch] = v;
-              }
-              if (active) store_row<CPL, VEC>(a.dx + (q - 3) * a.dx_ld, c0, C, pack(d));
+              const Pk<CPL> d = bwd_dx<CPL>(st, r);
+              if (active) store_row<CPL, VEC, true>(a.dx + (q - 3) * a.dx_ld, c0, C, d);
             }
           }
         }
@@ -221,7 +268,7 @@ __global__ void __launch_bounds__(kThreads) conv1d_bwd_kernel(const BwdArgs a) {
       if constexpr (MODE != MODE_IDX) {
         if (want_dh && active) {
 #pragma unroll
-          for (int j = 0; j < 3; ++j) store_row<CPL, VEC>(a.dhist + (sd.idx * 3 + j) * C, c0, C, pack(dh[j]));
+          for (int j = 0; j < 3; ++j) store_row<CPL, VEC>(a.dhist + (sd.idx * 3 + j) * C, c0, C, pack(st.dh[j]));
         }
       }
       t = t_end;
@@ -231,26 +278,20 @@ __global__ void __launch_bounds__(kThreads) conv1d_bwd_kernel(const BwdArgs a) {
     }
   }
 
-  // ---- block partial: waves 1..3 hand their sums to wave 0 through LDS, added in wave order
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(&bx[0][0][0]);  // reuse: 3 x 5*CPL x 64 floats
-  if (wave > 0) {
-#pragma unroll
-    for (int k = 0; k < 5; ++k)
-#pragma unroll
-      for (int ch = 0; ch < CPL; ++ch) red[((wave - 1) * 5 * CPL + k * CPL + ch) * kWave + lane] = acc[k][ch];
-  }
-  __syncthreads();
-  if (wave == 0 && active) {
+  // ---- this lane's partial sums for its channels over this row range (every range writes one,
+  // empty ranges write zeros, so the reduce can read all of them)
+  if (active) {
 #pragma unroll
     for (int k = 0; k < 5; ++k) {
       float* dst = a.part + ((int64_t)rb * 5 + k) * C + c0;
+      if constexpr (VEC) {
 #pragma unroll
-      for (int ch = 0; ch < CPL; ++ch) {
-        float s = acc[k][ch];
+        for (int q = 0; q < CPL; q += 4)
+          *reinterpret_cast<f32x4*>(dst + q) = f32x4{st.acc[k][q], st.acc[k][q + 1], st.acc[k][q + 2], st.acc[k][q + 3]};
+      } else {
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) s += red[((w - 1) * 5 * CPL + k * CPL + ch) * kWave + lane];
-        if (c0 + ch < C) dst[ch] = s;
+        for (int ch = 0; ch < CPL; ++ch)
+          if (c0 + ch < C) dst[ch] = st.acc[k][ch];
       }
     }
   }
@@ -258,8 +299,8 @@ __global__ void __launch_bounds__(kThreads) conv1d_bwd_kernel(const BwdArgs a) {
 
 // Ordered reduce: out[k][c] = sum over row blocks 0, 1, ..., n-1 of part[block][k][c].  One
 // thread per (k, c); the extra threads write zero d(history) rows of empty continuing fragments.
-__global__ void __launch_bounds__(kThreads) conv1d_bwd_reduce_kernel(const BwdArgs a, int64_t nhist_zero) {
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+__global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_reduce_kernel(const BwdArgs a, int64_t nhist_zero) {
+  const int64_t gid = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
   const int64_t C = a.C;
   if (gid < 5 * C) {
     const int64_t k = gid / C, c = gid - k * C;
@@ -291,7 +332,7 @@ __global__ void __launch_bounds__(kThreads) conv1d_bwd_reduce_kernel(const BwdAr
 }
 
 // ------------------------------------------------------------------ launchers
-constexpr int kCpl = 8;
+constexpr int kCpl = kChannelsPerLane;
 
 template <int MODE, bool VEC, bool SILU>
 static hipError_t bwd_go(const BwdArgs& a, hipStream_t s) {
@@ -299,16 +340,16 @@ static hipError_t bwd_go(const BwdArgs& a, hipStream_t s) {
   if (blocks) {
     void* args[] = {const_cast<BwdArgs*>(&a)};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&conv1d_bwd_kernel<kCpl, VEC, MODE, SILU>),
-                                   dim3(blocks), dim3(kThreads), args, 0, s);
+                                   dim3(blocks), dim3(kBlockThreads), args, 0, s);
     if (e != hipSuccess) return e;
   }
   // empty fragments that read history rows still get a (zero) d(history)
   const int64_t nz = (a.dhist && MODE == MODE_CU) ? a.seq.nseq : 0;
   const int64_t threads = 5 * a.C + nz * a.C;
-  const uint32_t rblocks = (uint32_t)((threads + kThreads - 1) / kThreads);
+  const uint32_t rblocks = (uint32_t)((threads + kBlockThreads - 1) / kBlockThreads);
   int64_t nz_arg = nz;
   void* rargs[] = {const_cast<BwdArgs*>(&a), &nz_arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&conv1d_bwd_reduce_kernel), dim3(rblocks), dim3(kThreads),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&conv1d_bwd_reduce_kernel), dim3(rblocks), dim3(kBlockThreads),
                          rargs, 0, s);
 }
 

@@ -2,9 +2,8 @@
 //
 // Data layout: activations are channel-last bf16 rows.  One lane owns CPL consecutive channels
 // of a row (CPL = 8: one 16-byte global_load_dwordx4 per row), a 64-lane wave covers 64*CPL
-// channels of the same row, so every row access of a wave is one contiguous, fully coalesced
-// 64*CPL*2-byte segment.  The four waves of a block own four consecutive row ranges of the
-// same channel strip.
+// channels of the same row, and the waves of a block sit side by side, so one row access of a
+// block is one contiguous, fully coalesced segment of kBlockChannels*2 bytes.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,8 +14,6 @@
 namespace cconv {
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
-constexpr int kThreads = kWave * kWaves;
 
 // ------------------------------------------------------------------ bf16 packing
 template <int CPL>
@@ -25,6 +22,7 @@ struct Pk {
 };
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
@@ -62,17 +60,33 @@ __device__ __forceinline__ Pk<CPL> zero_pk() {
 }
 
 // ------------------------------------------------------------------ row loads / stores
+#ifndef CCONV_NT_LOADS
+#define CCONV_NT_LOADS 1
+#endif
+#ifndef CCONV_NT_STORES
+#define CCONV_NT_STORES 1
+#endif
 // VEC: C % CPL == 0 and every row start is 16-byte (CPL = 8) / 8-byte (CPL = 4) aligned, so an
 // active lane's CPL channels are one aligned vector.  Otherwise element-wise with bounds.
-template <int CPL, bool VEC>
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// STREAM: the row is read exactly once here (non-temporal hint: do not keep it in the caches).
+template <int CPL, bool VEC, bool STREAM = false>
 __device__ __forceinline__ Pk<CPL> load_row(const uint16_t* __restrict__ row, int64_t c0, int64_t C) {
   Pk<CPL> p;
   if constexpr (VEC) {
     if constexpr (CPL == 8) {
-      const uint4 v = *reinterpret_cast<const uint4*>(row + c0);
+      const u32x4* src = reinterpret_cast<const u32x4*>(row + c0);
+      u32x4 v;
+      if constexpr (STREAM && CCONV_NT_LOADS) v = __builtin_nontemporal_load(src);
+      else v = *src;
       p.d[0] = v.x; p.d[1] = v.y; p.d[2] = v.z; p.d[3] = v.w;
     } else {
-      const uint2 v = *reinterpret_cast<const uint2*>(row + c0);
+      const u32x2* src = reinterpret_cast<const u32x2*>(row + c0);
+      u32x2 v;
+      if constexpr (STREAM && CCONV_NT_LOADS) v = __builtin_nontemporal_load(src);
+      else v = *src;
       p.d[0] = v.x; p.d[1] = v.y;
     }
   } else {
@@ -86,13 +100,19 @@ __device__ __forceinline__ Pk<CPL> load_row(const uint16_t* __restrict__ row, in
   return p;
 }
 
-template <int CPL, bool VEC>
+template <int CPL, bool VEC, bool STREAM = false>
 __device__ __forceinline__ void store_row(uint16_t* __restrict__ row, int64_t c0, int64_t C, const Pk<CPL>& p) {
   if constexpr (VEC) {
     if constexpr (CPL == 8) {
-      *reinterpret_cast<uint4*>(row + c0) = make_uint4(p.d[0], p.d[1], p.d[2], p.d[3]);
+      u32x4 v = {p.d[0], p.d[1], p.d[2], p.d[3]};
+      u32x4* dst = reinterpret_cast<u32x4*>(row + c0);
+      if constexpr (STREAM && CCONV_NT_STORES) __builtin_nontemporal_store(v, dst);
+      else *dst = v;
     } else {
-      *reinterpret_cast<uint2*>(row + c0) = make_uint2(p.d[0], p.d[1]);
+      u32x2 v = {p.d[0], p.d[1]};
+      u32x2* dst = reinterpret_cast<u32x2*>(row + c0);
+      if constexpr (STREAM && CCONV_NT_STORES) __builtin_nontemporal_store(v, dst);
+      else *dst = v;
     }
   } else {
 #pragma unroll
@@ -149,6 +169,13 @@ __device__ __forceinline__ float sigmoid_f32(float z) {
 // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).  Give every XCD one
 // contiguous range of logical tiles, so neighbouring row tiles of a channel strip (which share
 // halo rows) run on the same XCD at about the same time.
+// Logical tiles are ordered row-range major (tile = row_range * n_strips + strip), so the
+// channel strips of the same rows, which share DRAM pages, run side by side.
+__device__ __forceinline__ void tile_coords(uint32_t tile, uint32_t n_strips, uint32_t& strip, uint32_t& rb) {
+  strip = tile % n_strips;
+  rb = tile / n_strips;
+}
+
 __device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t nb) {
   constexpr uint32_t X = 8;
   const uint32_t q = nb / X, r = nb % X, xcd = b % X, idx = b / X;

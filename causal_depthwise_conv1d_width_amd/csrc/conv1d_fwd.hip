@@ -6,21 +6,25 @@
 // cake_causal_conv1d_kcp.
 //
 // Forward tiling (HBM-bound stencil, no MFMA):
-//   block  = 4 waves x 64 lanes; lane = CPL consecutive channels; block = one 64*CPL-channel
-//            strip x kFwdRowsPerBlock rows, wave w owning rows [r0 + w*KW, r0 + (w+1)*KW).
-//   halo   = the three rows before a wave's first row.  Each wave stages its own last three
-//            x rows in LDS before the block barrier; the next wave reads its halo from there
-//            and the owner reads them back at its end, so inside a block every x row leaves
-//            HBM once.  At a sequence start the halo is the sequence's history instead: pool
-//            positions 0..2, caller history rows, or zeros.
+//   block  = kWavesPerBlock waves side by side; lane = 8 consecutive channels; a block covers
+//            kBlockChannels channels of a kFwdRows-row range, so each row it touches is one
+//            contiguous segment.  Logical tiles run row-range major and each XCD gets one
+//            contiguous slice of them, so the row ranges next to each other (which share the
+//            three halo rows) and the channel strips of the same rows run together.
+//   stream = every wave walks its rows top to bottom in unrolled 8-row chunks: 8 non-temporal
+//            16-byte loads in flight per lane, then 8 stencil rows, 8 non-temporal stores.
+//   halo   = the three rows before a wave's first row: raw inputs of the same sequence (cached
+//            loads; the neighbouring range streamed them moments earlier on the same XCD), or
+//            at a sequence start the sequence's history (pool positions 0..2, caller history
+//            rows, or zeros).
 //   taps   = FP32 in registers; z = b, then four FMAs in tap order 0..3 (tap 3 = current row).
-//   window = a 4-slot register ring indexed by row mod 4 inside fully unrolled 8-row chunks,
-//            so the sliding window costs no register moves.
+//   window = a 4-slot register ring indexed by row mod 4 inside the unrolled chunk, so the
+//            sliding window costs no register moves.
 //   pool   = the wave that holds a sequence's first row is the only one that reads or writes
-//            its slot.  With a pool, row-range boundaries that fall on the first three rows of
-//            a sequence move to that sequence's fourth row (or its end), so no other wave or
-//            block ever needs the slot's old history, and the head writes the final state
-//            (the last three raw values of the extended sequence) right after reading it.
+//            its slot (for its channels).  With a pool, row-range boundaries that fall on the
+//            first three rows of a sequence move to that sequence's fourth row (or its end), so
+//            no other wave ever needs the slot's old history, and the head writes the final
+//            state (the last three raw values of the extended sequence) right after reading it.
 #include "conv1d_device.h"
 
 namespace cconv {
@@ -100,40 +104,90 @@ __device__ __forceinline__ int64_t owner_boundary(const SeqArgs& q, int64_t r, i
   }
 }
 
+// CH consecutive rows starting at q0 (rows past qlast re-read row qlast), every lane active,
+// streamed (non-temporal).
+template <int CPL, bool VEC, int CH>
+__device__ __forceinline__ void load_chunk(Pk<CPL> (&buf)[CH], const uint16_t* __restrict__ x, int64_t ld, int64_t q0,
+                                           int64_t qlast, int64_t c0, int64_t C) {
+#pragma unroll
+  for (int r = 0; r < CH; ++r) {
+    const int64_t q = q0 + r < qlast ? q0 + r : qlast;
+    buf[r] = load_row<CPL, VEC, true>(x + q * ld, c0, C);
+  }
+}
+
+template <int CPL, bool SILU>
+__device__ __forceinline__ Pk<CPL> stencil_row(const float (&wk)[4][CPL], const float (&bias)[CPL],
+                                               const float (&u)[4][CPL], int r);
+
+// CH rows starting at q0 from a loaded buffer: ring update, stencil, streamed store (all lanes).
+template <int CPL, bool VEC, int CH, bool SILU>
+__device__ __forceinline__ void stencil_chunk(const Pk<CPL> (&buf)[CH], uint16_t* __restrict__ y, int64_t ld,
+                                              int64_t q0, int64_t c0, int64_t C, const float (&wk)[4][CPL],
+                                              const float (&bias)[CPL], float (&u)[4][CPL]) {
+#pragma unroll
+  for (int r = 0; r < CH; ++r) {
+    unpack(buf[r], u[r % 4]);
+    store_row<CPL, VEC, true>(y + (q0 + r) * ld, c0, C, stencil_row<CPL, SILU>(wk, bias, u, r));
+  }
+}
+
+// One output row from the ring: u[(r+1)%4], u[(r+2)%4], u[(r+3)%4] are rows t-3, t-2, t-1 and
+// u[r%4] the current row.  z = b, then the four taps in order (FMA), FP32; y = act(z) in bf16.
+template <int CPL, bool SILU>
+__device__ __forceinline__ Pk<CPL> stencil_row(const float (&wk)[4][CPL], const float (&bias)[CPL],
+                                               const float (&u)[4][CPL], int r) {
+  float out[CPL];
+#pragma unroll
+  for (int ch = 0; ch < CPL; ++ch) {
+    float z = bias[ch];
+    z = __builtin_fmaf(wk[0][ch], u[(r + 1) % 4][ch], z);
+    z = __builtin_fmaf(wk[1][ch], u[(r + 2) % 4][ch], z);
+    z = __builtin_fmaf(wk[2][ch], u[(r + 3) % 4][ch], z);
+    z = __builtin_fmaf(wk[3][ch], u[r % 4][ch], z);
+    out[ch] = SILU ? z * sigmoid_f32(z) : z;
+  }
+  return pack(out);
+}
+
 // ------------------------------------------------------------------ forward kernel
+#ifndef CCONV_FWD_CHUNK
+#define CCONV_FWD_CHUNK 8
+#endif
+#ifndef CCONV_FWD_PIPELINE
+#define CCONV_FWD_PIPELINE 1
+#endif
+#ifndef CCONV_FWD_WAVES_PER_EU
+#define CCONV_FWD_WAVES_PER_EU 1
+#endif
+
 template <int CPL, bool VEC, int MODE, bool SILU>
-__global__ void __launch_bounds__(kThreads) conv1d_fwd_kernel(const FwdArgs a) {
-  constexpr int KW = kFwdRowsPerWave;
-  constexpr int CH = 8;  // rows per unrolled chunk; a multiple of the 4-slot ring
-  __shared__ Pk<CPL> stage[kWaves][3][kWave];
+__global__ void __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(CCONV_FWD_WAVES_PER_EU)))
+conv1d_fwd_kernel(const FwdArgs a) {
+  constexpr int CH = CCONV_FWD_CHUNK;  // rows per unrolled chunk; a multiple of the 4-slot ring
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
-  const uint32_t strip = tile / a.n_rowblocks, rb = tile % a.n_rowblocks;
+  uint32_t strip, rb;
+  tile_coords(xcd_tile(blockIdx.x, gridDim.x), a.n_strips, strip, rb);
   const int64_t C = a.C;
-  const int64_t c0 = (int64_t)strip * (kWave * CPL) + lane * CPL;
+  const int64_t wc0 = (int64_t)strip * kBlockChannels + (int64_t)wave * kWaveChannels;
+  if (wc0 >= C) return;  // the whole wave is past the last channel
+  const int64_t c0 = wc0 + lane * CPL;
   const bool active = c0 < C;
+  const bool full = VEC && wc0 + kWaveChannels <= C;  // every lane of the wave is active
   const int64_t dend = data_end<MODE>(a.seq, a.rows);
   const bool has_pool = a.pool.ptr != nullptr;
 
-  int64_t ta = (int64_t)rb * kFwdRowsPerBlock + (int64_t)wave * KW;
-  int64_t tb = ta + KW;
+  int64_t ta = (int64_t)rb * kFwdRows;
+  int64_t tb = ta + kFwdRows;
   if (has_pool) {
     ta = owner_boundary<MODE>(a.seq, ta, dend);
     tb = owner_boundary<MODE>(a.seq, tb, dend);
   }
   ta = ta < dend ? ta : dend;
   tb = tb < dend ? tb : dend;
-
-  // stage this wave's last three rows for the next wave (and for itself at its end)
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int64_t r = tb - 3 + j;
-    if (r >= ta && active) stage[wave][j][lane] = load_row<CPL, VEC>(a.x + r * a.x_ld, c0, C);
-  }
-  __syncthreads();
-  if (ta >= tb) return;  // no barrier below this point
+  if (ta >= tb) return;
 
   float wk[4][CPL], bias[CPL];
   load_taps<CPL>(a.w, a.w_f32, a.b, a.b_f32, c0, C, wk, bias);
@@ -157,7 +211,7 @@ __global__ void __launch_bounds__(kThreads) conv1d_fwd_kernel(const FwdArgs a) {
       // -1 slot: +0 output, no state access, no input read
       const Pk<CPL> zero = zero_pk<CPL>();
       if (active)
-        for (int64_t q = t; q < run_end; ++q) store_row<CPL, VEC>(a.y + q * a.y_ld, c0, C, zero);
+        for (int64_t q = t; q < run_end; ++q) store_row<CPL, VEC, true>(a.y + q * a.y_ld, c0, C, zero);
     } else {
       float h[3][CPL];
       if constexpr (MODE != MODE_IDX) {
@@ -169,55 +223,68 @@ __global__ void __launch_bounds__(kThreads) conv1d_fwd_kernel(const FwdArgs a) {
           for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
       }
       // window rows t-3, t-2, t-1 -> ring slots 1, 2, 3: the history, then the last `dist`
-      // input rows of the same sequence shifted in (dist > 0 only on the first run)
-      {
-        float win[3][CPL];
-#pragma unroll
-        for (int j = 0; j < 3; ++j)
-#pragma unroll
-          for (int ch = 0; ch < CPL; ++ch) win[j][ch] = h[j][ch];
-        for (int64_t k = 3 - dist; k < 3; ++k) {
-          Pk<CPL> p = zero_pk<CPL>();
-          if (active) p = (wave > 0) ? stage[wave - 1][k][lane]
-                                     : load_row<CPL, VEC>(a.x + (t - 3 + k) * a.x_ld, c0, C);
-          shift_in<CPL>(win, p);
-        }
-#pragma unroll
-        for (int j = 0; j < 3; ++j)
-#pragma unroll
-          for (int ch = 0; ch < CPL; ++ch) u[j + 1][ch] = win[j][ch];
+      // input rows of the same sequence shifted in (dist > 0 only on the first run; those rows
+      // were just streamed by the neighbouring row range on this XCD, so they come from L2)
+      for (int64_t k = 3 - dist; k < 3; ++k) {
+        Pk<CPL> p = zero_pk<CPL>();
+        if (active) p = load_row<CPL, VEC>(a.x + (t - 3 + k) * a.x_ld, c0, C);
+        shift_in<CPL>(h, p);
       }
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch) u[j + 1][ch] = h[j][ch];
       if constexpr (MODE != MODE_IDX) {
+        // at the sequence's first row dist == 0, so h still holds the untouched history
         if (has_pool && t == sd.s && sd.e > sd.s) pool_writeback<CPL, VEC>(a, slot, sd, h, c0, active);
       }
 
-      for (int64_t q0 = t; q0 < run_end; q0 += CH) {
-        const int64_t n = run_end - q0;
+      // full chunks: software-pipelined, the next chunk's loads are in flight while this chunk
+      // computes and stores; lanes past the last channel only occur in the last wave of a strip,
+      // which takes the predicated tail path for everything
+      const int64_t nrun = run_end - t;
+      const int nfull = (full && CCONV_FWD_PIPELINE) ? (int)(nrun / CH) : 0;
+      int64_t q0 = t;
+      if (nfull > 0) {
+        // Two register buffers, unrolled by two chunks: chunk j+1's loads are issued before
+        // chunk j's stores, so waiting for a chunk's data never waits for the stores issued
+        // before it (the vector memory counter is in order).  The next chunk's loads are issued
+        // unconditionally; past the last full chunk they re-read the last row (a cache hit), so
+        // every path back to the loop head carries the same outstanding loads and the compiler's
+        // wait counts stay exact.
+        const int64_t qlast = t + (int64_t)nfull * CH - 1;
+        Pk<CPL> A[CH], B[CH];
+        load_chunk<CPL, VEC, CH>(A, a.x, a.x_ld, q0, qlast, c0, C);
+        for (int j = 0;; j += 2, q0 += 2 * CH) {
+          load_chunk<CPL, VEC, CH>(B, a.x, a.x_ld, q0 + CH, qlast, c0, C);
+          stencil_chunk<CPL, VEC, CH, SILU>(A, a.y, a.y_ld, q0, c0, C, wk, bias, u);
+          if (j + 1 >= nfull) {
+            q0 += CH;
+            break;
+          }
+          load_chunk<CPL, VEC, CH>(A, a.x, a.x_ld, q0 + 2 * CH, qlast, c0, C);
+          stencil_chunk<CPL, VEC, CH, SILU>(B, a.y, a.y_ld, q0 + CH, c0, C, wk, bias, u);
+          if (j + 2 >= nfull) {
+            q0 += 2 * CH;
+            break;
+          }
+        }
+      }
+      // tail (and partially active waves): rows one chunk at a time with uniform row predicates
+      for (; q0 < run_end; q0 += CH) {
+        const int n = (int)(run_end - q0 < CH ? run_end - q0 : CH);
         Pk<CPL> xr[CH];
 #pragma unroll
         for (int r = 0; r < CH; ++r) {
           xr[r] = zero_pk<CPL>();
-          if (r < n && active) {
-            const int64_t row = q0 + r;
-            if (row >= tb - 3) xr[r] = stage[wave][row - (tb - 3)][lane];
-            else xr[r] = load_row<CPL, VEC>(a.x + row * a.x_ld, c0, C);
-          }
+          if (r < n && active) xr[r] = load_row<CPL, VEC, true>(a.x + (q0 + r) * a.x_ld, c0, C);
         }
 #pragma unroll
         for (int r = 0; r < CH; ++r) {
           if (r < n) {
             unpack(xr[r], u[r % 4]);
-            float out[CPL];
-#pragma unroll
-            for (int ch = 0; ch < CPL; ++ch) {
-              float z = bias[ch];
-              z = __builtin_fmaf(wk[0][ch], u[(r + 1) % 4][ch], z);
-              z = __builtin_fmaf(wk[1][ch], u[(r + 2) % 4][ch], z);
-              z = __builtin_fmaf(wk[2][ch], u[(r + 3) % 4][ch], z);
-              z = __builtin_fmaf(wk[3][ch], u[r % 4][ch], z);
-              out[ch] = SILU ? z * sigmoid_f32(z) : z;
-            }
-            if (active) store_row<CPL, VEC>(a.y + (q0 + r) * a.y_ld, c0, C, pack(out));
+            const Pk<CPL> out = stencil_row<CPL, SILU>(wk, bias, u, r);
+            if (active) store_row<CPL, VEC, true>(a.y + (q0 + r) * a.y_ld, c0, C, out);
           }
         }
       }
@@ -233,8 +300,8 @@ __global__ void __launch_bounds__(kThreads) conv1d_fwd_kernel(const FwdArgs a) {
 // One thread per (sequence, CPL-channel group).  y = act(b + w . [h0, h1, h2, x]), then the
 // slot's positions 0..2 become [h1, h2, x]; slot -1 gives +0 and touches nothing.
 template <int CPL, bool VEC, bool SILU>
-__global__ void __launch_bounds__(kThreads) conv1d_decode_kernel(const DecodeArgs a) {
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+__global__ void __launch_bounds__(kBlockThreads) conv1d_decode_kernel(const DecodeArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
   const int64_t groups = (a.C + CPL - 1) / CPL;
   if (gid >= a.nseq * groups) return;
   const int64_t i = gid / groups;
@@ -283,13 +350,14 @@ __global__ void __launch_bounds__(kThreads) conv1d_decode_kernel(const DecodeArg
 }
 
 // ------------------------------------------------------------------ launchers
-constexpr int kCpl = 8;
+constexpr int kCpl = kChannelsPerLane;
 
 template <int MODE, bool VEC, bool SILU>
 static hipError_t fwd_go(const FwdArgs& a, hipStream_t s) {
   const uint32_t blocks = a.n_strips * a.n_rowblocks;
-  hipLaunchKernelGGL((conv1d_fwd_kernel<kCpl, VEC, MODE, SILU>), dim3(blocks), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  void* args[] = {const_cast<FwdArgs*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&conv1d_fwd_kernel<kCpl, VEC, MODE, SILU>), dim3(blocks),
+                         dim3(kBlockThreads), args, 0, s);
 }
 
 template <int MODE>
@@ -310,9 +378,10 @@ hipError_t launch_fwd(const FwdArgs& a, int mode, bool vec, bool silu, hipStream
 template <bool VEC, bool SILU>
 static hipError_t decode_go(const DecodeArgs& a, hipStream_t s) {
   const int64_t groups = (a.C + kCpl - 1) / kCpl;
-  const int64_t blocks = (a.nseq * groups + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL((conv1d_decode_kernel<kCpl, VEC, SILU>), dim3((uint32_t)blocks), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  const int64_t blocks = (a.nseq * groups + kBlockThreads - 1) / kBlockThreads;
+  void* args[] = {const_cast<DecodeArgs*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&conv1d_decode_kernel<kCpl, VEC, SILU>),
+                         dim3((uint32_t)blocks), dim3(kBlockThreads), args, 0, s);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool vec, bool silu, hipStream_t s) {

@@ -9,12 +9,29 @@
 
 namespace cconv {
 
-// Rows per wave and per block (4 waves) of the forward and backward kernels.  The backward's
-// per-block dweight partials live in the workspace, one [5, C] FP32 slab per row block.
-constexpr int kFwdRowsPerWave = 32;
-constexpr int kBwdRowsPerWave = 64;
-constexpr int kFwdRowsPerBlock = 4 * kFwdRowsPerWave;
-constexpr int kBwdRowsPerBlock = 4 * kBwdRowsPerWave;
+// Tiling.  A block is kWavesPerBlock waves side by side in channels: lane = 8 channels, wave =
+// 512 channels, block = kBlockChannels channels of one row range.  Every wave streams the rows
+// of its range top to bottom.  The forward uses kFwdRows-row ranges; the backward kBwdRows-row
+// ranges, and writes one [5, C] FP32 dweight/dbias partial per range to the workspace.
+#ifndef CCONV_WAVES_PER_BLOCK
+#define CCONV_WAVES_PER_BLOCK 4
+#endif
+#ifndef CCONV_FWD_ROWS
+#define CCONV_FWD_ROWS 128
+#endif
+#ifndef CCONV_BWD_ROWS
+#define CCONV_BWD_ROWS 128
+#endif
+#ifndef CCONV_CPL
+#define CCONV_CPL 4
+#endif
+constexpr int kChannelsPerLane = CCONV_CPL;
+constexpr int kWavesPerBlock = CCONV_WAVES_PER_BLOCK;
+constexpr int kBlockThreads = 64 * kWavesPerBlock;
+constexpr int kWaveChannels = 64 * kChannelsPerLane;
+constexpr int kBlockChannels = kWavesPerBlock * kWaveChannels;
+constexpr int kFwdRows = CCONV_FWD_ROWS;
+constexpr int kBwdRows = CCONV_BWD_ROWS;
 
 // How rows split into sequences: cu_seqlens offsets, per-token sequence IDs, or batch rows.
 enum { MODE_CU = 0, MODE_IDX = 1, MODE_BATCH = 2 };

@@ -27,9 +27,11 @@ OUT_FILL = 0x7FC1  # a NaN pattern the kernels never produce: marks rows that mu
 def to_bf16_bits(a):
     """float32 -> bf16 bit patterns, round to nearest even (inputs are finite)."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = u + 0x7FFF + ((u >> 16) & 1)
-    return (u >> 16).astype(np.uint16)
+    u = a.view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    r = u + np.uint32(0x7FFF)  # no uint32 overflow for finite values
+    r += lsb
+    return (r >> 16).astype(np.uint16)
 
 
 def bf16_bits_to_f32(b):
