@@ -261,7 +261,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads and the copy ceiling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-only-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB three times (counter calibration)")
     args = ap.parse_args()
+    if args.copy_only_mib:
+        import torch
+        a = torch.empty(args.copy_only_mib << 19, dtype=torch.bfloat16, device="cuda").normal_()
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": a.numel() * 2, "copies": 3}), flush=True)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build runs on one GPU: the multi-GPU context-parallel exchange is "
