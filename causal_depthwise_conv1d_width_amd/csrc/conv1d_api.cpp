@@ -254,7 +254,7 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
                    aligned(dy, 16) && aligned(dx, 16) && (!use_hist || aligned(hist->ptr, 16)) &&
                    (!dhist || aligned(dhist, 16));
   const uint64_t nblk = (uint64_t)ceil_div(C, kBlockChannels) * ceil_div(rows, kBwdRows);
-  if (nblk > 0x7fffffffull || (uint64_t)(5 * C + (nseq > 0 ? nseq : 0) * C) / 256 > 0x7fffffffull)
+  if (nblk > 0x7fffffffull || (uint64_t)((20 + (nseq > 0 ? nseq : 0)) * C) / 256 > 0x7fffffffull)
     return CONV1D_EINVAL;
 
   BwdArgs a{};

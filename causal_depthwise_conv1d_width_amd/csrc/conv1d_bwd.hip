@@ -54,7 +54,6 @@ struct BwdState {
   float u[4][CPL];    // extended-sequence ring, slot = (row - run start) mod 4
   float g[4][CPL];    // dz ring, same slots
   float acc[5][CPL];  // dw_0..3, db partial sums over the wave's rows
-  float dh[3][CPL];   // d(history) of a head fragment
 };
 
 // One real row q (ring slot r): recompute z, dz = dy * act'(z); dweight/dbias sums when `own`.
@@ -106,22 +105,35 @@ __device__ __forceinline__ Pk<CPL> bwd_dx(const BwdState<CPL>& st, int r) {
 
 // head of a continuing fragment: dh_j += w_{j-r} dz[s+r] for j >= r (r = 0, 1, 2)
 template <int CPL>
-__device__ __forceinline__ void bwd_dhist(BwdState<CPL>& st, int r) {
+__device__ __forceinline__ void bwd_dhist(const BwdState<CPL>& st, float (&dh)[3][CPL], int r) {
 #pragma unroll
   for (int j = r; j < 3; ++j)
 #pragma unroll
-    for (int ch = 0; ch < CPL; ++ch) st.dh[j][ch] = __builtin_fmaf(st.wk[j - r][ch], st.g[r % 4][ch], st.dh[j][ch]);
+    for (int ch = 0; ch < CPL; ++ch) dh[j][ch] = __builtin_fmaf(st.wk[j - r][ch], st.g[r % 4][ch], dh[j][ch]);
 }
 
-// CH own rows starting at q0 (every lane active, all rows real and owned).
-template <int CPL, bool VEC, int CH, bool SILU>
+// CH own rows starting at q0 (every lane active, all rows real and owned).  FIRST: q0 is the
+// run's first row, so rows q0-3..q0-1 get no dx here, and a head fragment's d(history), which
+// needs dz of the sequence's first three rows only, is finished and stored in this chunk.
+template <int CPL, bool VEC, int CH, bool SILU, bool FIRST>
 __device__ __forceinline__ void bwd_chunk(BwdState<CPL>& st, const Pk<CPL> (&X)[CH], const Pk<CPL> (&G)[CH],
-                                          const BwdArgs& a, int64_t q0, int64_t t, int64_t c0, bool want_dh) {
+                                          const BwdArgs& a, int64_t q0, int64_t c0, bool want_dh, int64_t hidx) {
+  static_assert(CH >= 3, "the first chunk must hold a sequence's first three rows");
 #pragma unroll
   for (int r = 0; r < CH; ++r) {
     bwd_row<CPL, SILU>(st, X[r], G[r], r, true);
-    if (r < 3 && want_dh && q0 == t) bwd_dhist<CPL>(st, r);
-    if (q0 + r - 3 >= t) store_row<CPL, VEC, true>(a.dx + (q0 + r - 3) * a.dx_ld, c0, a.C, bwd_dx<CPL>(st, r));
+    if (FIRST && r == 2 && want_dh) {
+      float dh[3][CPL];
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch) dh[j][ch] = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < 3; ++rr) bwd_dhist<CPL>(st, dh, rr);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) store_row<CPL, VEC>(a.dhist + (hidx * 3 + j) * a.C, c0, a.C, pack(dh[j]));
+    }
+    if (!FIRST || r >= 3) store_row<CPL, VEC, true>(a.dx + (q0 + r - 3) * a.dx_ld, c0, a.C, bwd_dx<CPL>(st, r));
   }
 }
 
@@ -193,10 +205,7 @@ conv1d_bwd_kernel(const BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 3; ++j)
 #pragma unroll
-        for (int ch = 0; ch < CPL; ++ch) {
-          st.u[j + 1][ch] = h[j][ch];
-          st.dh[j][ch] = 0.f;
-        }
+        for (int ch = 0; ch < CPL; ++ch) st.u[j + 1][ch] = h[j][ch];
 
       const int64_t t_end = sd.e < tb ? sd.e : tb;  // rows of this run that the wave owns
       int64_t la_end = t_end;                        // plus same-sequence look-ahead rows
@@ -207,29 +216,38 @@ conv1d_bwd_kernel(const BwdArgs a) {
       // full chunks of own rows, software-pipelined with two register buffers (see the forward)
       const int nfull = (full && CCONV_BWD_PIPELINE) ? (int)((t_end - t) / CH) : 0;
       int64_t q0 = t;
+      bool dh_done = false;
       if (nfull > 0) {
         // two register buffers, unrolled by two chunks, next chunk's loads always issued (rows
         // past the last full chunk re-read its last row): see the forward kernel
         const int64_t qlast = t + (int64_t)nfull * CH - 1;
         Pk<CPL> XA[CH], GA[CH], XB[CH], GB[CH];
         bwd_load<CPL, VEC, CH>(XA, GA, a, q0, qlast, c0);
-        for (int j = 0;; j += 2, q0 += 2 * CH) {
-          bwd_load<CPL, VEC, CH>(XB, GB, a, q0 + CH, qlast, c0);
-          bwd_chunk<CPL, VEC, CH, SILU>(st, XA, GA, a, q0, t, c0, want_dh);
-          if (j + 1 >= nfull) {
+        bwd_load<CPL, VEC, CH>(XB, GB, a, q0 + CH, qlast, c0);
+        bwd_chunk<CPL, VEC, CH, SILU, true>(st, XA, GA, a, q0, c0, want_dh, sd.idx);
+        dh_done = true;
+        for (int j = 1;; j += 2, q0 += 2 * CH) {
+          if (j >= nfull) {
             q0 += CH;
             break;
           }
           bwd_load<CPL, VEC, CH>(XA, GA, a, q0 + 2 * CH, qlast, c0);
-          bwd_chunk<CPL, VEC, CH, SILU>(st, XB, GB, a, q0 + CH, t, c0, want_dh);
-          if (j + 2 >= nfull) {
+          bwd_chunk<CPL, VEC, CH, SILU, false>(st, XB, GB, a, q0 + CH, c0, want_dh, sd.idx);
+          if (j + 1 >= nfull) {
             q0 += 2 * CH;
             break;
           }
+          bwd_load<CPL, VEC, CH>(XB, GB, a, q0 + 3 * CH, qlast, c0);
+          bwd_chunk<CPL, VEC, CH, SILU, false>(st, XA, GA, a, q0 + 2 * CH, c0, want_dh, sd.idx);
         }
       }
       // the rest: remaining own rows, look-ahead rows of the same sequence, and three trailing
       // steps (dz = 0 past the sequence's end) that finish the last dx rows
+      float dh[3][CPL];
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch) dh[j][ch] = 0.f;
       for (; q0 < steps_end; q0 += CH) {
         Pk<CPL> xr[CH], gr[CH];
 #pragma unroll
@@ -257,7 +275,7 @@ conv1d_bwd_kernel(const BwdArgs a) {
 #pragma unroll
               for (int ch = 0; ch < CPL; ++ch) st.g[r % 4][ch] = 0.f;  // past the sequence's end
             }
-            if (r < 3 && want_dh && q0 == t) bwd_dhist<CPL>(st, r);
+            if (r < 3 && want_dh && q0 == t) bwd_dhist<CPL>(st, dh, r);
             if (q - 3 >= t) {
               const Pk<CPL> d = bwd_dx<CPL>(st, r);
               if (active) store_row<CPL, VEC, true>(a.dx + (q - 3) * a.dx_ld, c0, C, d);
@@ -266,9 +284,9 @@ conv1d_bwd_kernel(const BwdArgs a) {
         }
       }
       if constexpr (MODE != MODE_IDX) {
-        if (want_dh && active) {
+        if (want_dh && active && !dh_done) {
 #pragma unroll
-          for (int j = 0; j < 3; ++j) store_row<CPL, VEC>(a.dhist + (sd.idx * 3 + j) * C, c0, C, pack(st.dh[j]));
+          for (int j = 0; j < 3; ++j) store_row<CPL, VEC>(a.dhist + (sd.idx * 3 + j) * C, c0, C, pack(dh[j]));
         }
       }
       t = t_end;
@@ -284,10 +302,12 @@ conv1d_bwd_kernel(const BwdArgs a) {
 #pragma unroll
     for (int k = 0; k < 5; ++k) {
       float* dst = a.part + ((int64_t)rb * 5 + k) * C + c0;
-      if constexpr (VEC) {
+      if constexpr (VEC && CPL >= 4) {
 #pragma unroll
         for (int q = 0; q < CPL; q += 4)
           *reinterpret_cast<f32x4*>(dst + q) = f32x4{st.acc[k][q], st.acc[k][q + 1], st.acc[k][q + 2], st.acc[k][q + 3]};
+      } else if constexpr (VEC) {
+        *reinterpret_cast<f32x2*>(dst) = f32x2{st.acc[k][0], st.acc[k][1]};
       } else {
 #pragma unroll
         for (int ch = 0; ch < CPL; ++ch)
@@ -297,33 +317,48 @@ conv1d_bwd_kernel(const BwdArgs a) {
   }
 }
 
-// Ordered reduce: out[k][c] = sum over row blocks 0, 1, ..., n-1 of part[block][k][c].  One
-// thread per (k, c); the extra threads write zero d(history) rows of empty continuing fragments.
-__global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_reduce_kernel(const BwdArgs a, int64_t nhist_zero) {
-  const int64_t gid = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+// Ordered reduce of the per-range partials: out[o] = sum over row ranges p of part[p][o], for
+// the flattened o = k*C + c (k = 0..3 dweight taps, 4 = dbias).  A wave owns 16 consecutive o;
+// lane l sums the ranges p = l/16, l/16 + 4, l/16 + 8, ... in ascending order (each load of
+// the wave reads four 64-byte runs), then a fixed two-level butterfly across lanes l, l^16,
+// l^32, l^48 adds the four interleaved subsets:  (s0 + s1) + (s2 + s3).  The order is fixed, so
+// dweight/dbias are bitwise reproducible; no atomics.  The remaining threads write zero
+// d(history) rows of empty continuing fragments.
+__global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_reduce_kernel(const BwdArgs a, int64_t nhist_zero,
+                                                                           int64_t n_red_waves) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t gwave = ((int64_t)blockIdx.x * kBlockThreads + threadIdx.x) / kWave;
   const int64_t C = a.C;
-  if (gid < 5 * C) {
-    const int64_t k = gid / C, c = gid - k * C;
-    if (k == 4 && !a.db) return;
-    const float* p = a.part + k * C + c;
-    const int64_t stride = 5 * C;
-    float s = 0.f;
+  const int64_t nout = 5 * C;
+  if (gwave < n_red_waves) {
+    const int64_t o = gwave * 16 + (lane & 15);
+    const int sub = lane >> 4;
+    const bool ok = o < nout;
     const int64_t n = a.n_rowblocks;
-    int64_t i = 0;
-    for (; i + 8 <= n; i += 8) {
-      float v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = p[(i + j) * stride];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s += v[j];
+    float s = 0.f;
+    if (ok) {
+      const float* p = a.part + o;
+      int64_t i = sub;
+      for (; i + 12 < n; i += 16) {
+        const float v0 = p[i * nout], v1 = p[(i + 4) * nout], v2 = p[(i + 8) * nout], v3 = p[(i + 12) * nout];
+        s += v0;
+        s += v1;
+        s += v2;
+        s += v3;
+      }
+      for (; i < n; i += 4) s += p[i * nout];
     }
-    for (; i < n; ++i) s += p[i * stride];
-    if (k < 4) a.dw[c * 4 + k] = s;
-    else a.db[c] = s;
+    s += __shfl_xor(s, 16);  // s0+s1 (lanes 0-31), s2+s3 (lanes 32-63); fp add commutes exactly
+    s += __shfl_xor(s, 32);  // (s0+s1) + (s2+s3) on every lane
+    if (ok && lane < 16) {
+      const int64_t k = o / C, c = o - k * C;
+      if (k < 4) a.dw[c * 4 + k] = s;
+      else if (a.db) a.db[c] = s;
+    }
     return;
   }
-  const int64_t hid = gid - 5 * C;
-  if (hid >= nhist_zero * C) return;
+  const int64_t hid = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x - n_red_waves * kWave;
+  if (hid < 0 || hid >= nhist_zero * C) return;
   const int64_t i = hid / C, c = hid - i * C;
   if (a.hist.has_hist && !a.hist.has_hist[i]) return;
   if (a.seq.cu[i + 1] != a.seq.cu[i]) return;  // nonempty: written by the tile kernel
@@ -345,10 +380,11 @@ static hipError_t bwd_go(const BwdArgs& a, hipStream_t s) {
   }
   // empty fragments that read history rows still get a (zero) d(history)
   const int64_t nz = (a.dhist && MODE == MODE_CU) ? a.seq.nseq : 0;
-  const int64_t threads = 5 * a.C + nz * a.C;
+  int64_t n_red_waves = (5 * a.C + 15) / 16;
+  const int64_t threads = n_red_waves * kWave + nz * a.C;
   const uint32_t rblocks = (uint32_t)((threads + kBlockThreads - 1) / kBlockThreads);
   int64_t nz_arg = nz;
-  void* rargs[] = {const_cast<BwdArgs*>(&a), &nz_arg};
+  void* rargs[] = {const_cast<BwdArgs*>(&a), &nz_arg, &n_red_waves};
   return hipLaunchKernel(reinterpret_cast<const void*>(&conv1d_bwd_reduce_kernel), dim3(rblocks), dim3(kBlockThreads),
                          rargs, 0, s);
 }

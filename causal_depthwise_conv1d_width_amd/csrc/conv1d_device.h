@@ -82,12 +82,16 @@ __device__ __forceinline__ Pk<CPL> load_row(const uint16_t* __restrict__ row, in
       if constexpr (STREAM && CCONV_NT_LOADS) v = __builtin_nontemporal_load(src);
       else v = *src;
       p.d[0] = v.x; p.d[1] = v.y; p.d[2] = v.z; p.d[3] = v.w;
-    } else {
+    } else if constexpr (CPL == 4) {
       const u32x2* src = reinterpret_cast<const u32x2*>(row + c0);
       u32x2 v;
       if constexpr (STREAM && CCONV_NT_LOADS) v = __builtin_nontemporal_load(src);
       else v = *src;
       p.d[0] = v.x; p.d[1] = v.y;
+    } else {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(row + c0);
+      if constexpr (STREAM && CCONV_NT_LOADS) p.d[0] = __builtin_nontemporal_load(src);
+      else p.d[0] = *src;
     }
   } else {
 #pragma unroll
@@ -108,11 +112,15 @@ __device__ __forceinline__ void store_row(uint16_t* __restrict__ row, int64_t c0
       u32x4* dst = reinterpret_cast<u32x4*>(row + c0);
       if constexpr (STREAM && CCONV_NT_STORES) __builtin_nontemporal_store(v, dst);
       else *dst = v;
-    } else {
+    } else if constexpr (CPL == 4) {
       u32x2 v = {p.d[0], p.d[1]};
       u32x2* dst = reinterpret_cast<u32x2*>(row + c0);
       if constexpr (STREAM && CCONV_NT_STORES) __builtin_nontemporal_store(v, dst);
       else *dst = v;
+    } else {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(row + c0);
+      if constexpr (STREAM && CCONV_NT_STORES) __builtin_nontemporal_store(p.d[0], dst);
+      else *dst = p.d[0];
     }
   } else {
 #pragma unroll

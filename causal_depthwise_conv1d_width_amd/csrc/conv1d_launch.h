@@ -20,10 +20,10 @@ namespace cconv {
 #define CCONV_FWD_ROWS 128
 #endif
 #ifndef CCONV_BWD_ROWS
-#define CCONV_BWD_ROWS 128
+#define CCONV_BWD_ROWS 256
 #endif
 #ifndef CCONV_CPL
-#define CCONV_CPL 4
+#define CCONV_CPL 2
 #endif
 constexpr int kChannelsPerLane = CCONV_CPL;
 constexpr int kWavesPerBlock = CCONV_WAVES_PER_BLOCK;

@@ -1,0 +1,248 @@
+"""GPU properties beyond element-wise parity: determinism, decode = unit prefill, chunked prefill,
+the context-parallel split, HIP-graph capture and replay with edited metadata, strided rows and
+64-bit row offsets.  Everything goes through the C ABI (the torch binding only marshals)."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import gpu_harness as gh  # noqa: E402
+import causal_depthwise_conv1d_width_amd as cc  # noqa: E402
+from causal_depthwise_conv1d_width_amd import workloads as wl  # noqa: E402
+
+
+def say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def test_dweight_bitwise_reproducible():
+    """Ten backward runs, fresh and garbage-filled workspaces, another stream: identical dw/db bits."""
+    say("determinism config4/config5")
+    for case in (wl.config_4(), wl.config_5()):
+        x, dy = gh.dev_bits(case["x"]), gh.dev_bits(case["dy"])
+        w, b = gh.dev_taps(case["w"]), gh.dev_taps(case.get("b"))
+        kw = dict(cu_seqlens=gh.dev_i32(case.get("cu_seqlens")), seq_idx=gh.dev_i32(case.get("seq_idx")),
+                  seqlen=case.get("seqlen"), history=gh.dev_bits(case["hist"]) if case.get("hist") is not None else None,
+                  has_history=gh.dev_u8(case.get("has_history")), want_dbias=True)
+        need = cc.conv1d_bwd_workspace_bytes(*case["x"].shape)
+        ref = None
+        side = torch.cuda.Stream()
+        for run in range(10):
+            ws = torch.empty(need + 4096, dtype=torch.uint8, device="cuda")
+            ws.fill_(run * 37 % 256)
+            ws = ws[256 * (run % 4):]  # different, still aligned, addresses
+            stream = side if run % 2 else None
+            with torch.cuda.stream(side if run % 2 else torch.cuda.current_stream()):
+                _, dw, db, _ = cc.conv1d_bwd(x, dy, w, b, workspace=ws, stream=stream, **kw)
+            torch.cuda.synchronize()
+            bits = (dw.view(torch.int32).cpu().numpy(), db.view(torch.int32).cpu().numpy())
+            if ref is None:
+                ref = bits
+            else:
+                assert np.array_equal(bits[0], ref[0]) and np.array_equal(bits[1], ref[1]), f"run {run} differs"
+
+
+def test_forward_recompute_bitwise_identical():
+    say("forward recompute")
+    case = wl.config_5()
+    y1, _ = gh.gpu_fwd(case)
+    y2, _ = gh.gpu_fwd(case)
+    assert np.array_equal(y1, y2)
+
+
+@pytest.mark.parametrize("layout", ["hist", "chan"])
+def test_decode_matches_oracle_and_unit_prefill(oracle, layout):
+    say(f"decode {layout}")
+    rng = np.random.default_rng(31)
+    for C, N, L in ((5632, 64, 4), (13, 9, 3), (1024, 7, 6)):
+        x = wl.normal_bf16(rng, (N, C))
+        w = wl.uniform_f32(rng, (C, 4))
+        b = (rng.standard_normal(C) * 0.1).astype(np.float32)
+        vals = wl.normal_bf16(rng, (N + 5, C, L))
+        ci = rng.permutation(N + 5)[:N].astype(np.int32)
+        ci[1] = -1
+        pool = gh.dev_pool(wl.pool_layout(vals.copy(), layout))
+        y = cc.conv1d_state_update(gh.dev_bits(x), gh.dev_taps(w), gh.dev_taps(b), conv_state=pool,
+                                   cache_indices=gh.dev_i32(ci))
+        torch.cuda.synchronize()
+        ref_pool = wl.pool_layout(vals.copy(), layout)
+        yr = oracle.state_update(x, w, b, pool=ref_pool, cache_indices=ci)
+        gh.assert_bf16_close(gh.host_bits(y), yr, "decode y")
+        assert np.array_equal(gh.host_pool(pool), ref_pool), "decode state shift"
+        # the same step as a prefill of unit-length sequences: identical bits
+        case = dict(x=x, w=w, b=b, cu_seqlens=np.arange(N + 1, dtype=np.int32), pool=wl.pool_layout(vals.copy(), layout),
+                    cache_indices=ci, has_initial_state=np.ones(N, np.uint8), act="silu")
+        yf, pf = gh.gpu_fwd(case)
+        assert np.array_equal(yf, gh.host_bits(y)) and np.array_equal(pf, ref_pool)
+
+
+def test_chunked_prefill_equals_one_call():
+    say("chunked prefill")
+    rng = np.random.default_rng(32)
+    C, n = 1536, 600
+    x = wl.normal_bf16(rng, (n, C))
+    w = wl.uniform_f32(rng, (C, 4))
+    b = (rng.standard_normal(C) * 0.1).astype(np.float32)
+    vals = wl.normal_bf16(rng, (2, C, 4))
+    ci, hi = np.array([1], np.int32), np.array([1], np.uint8)
+    full = dict(x=x, w=w, b=b, cu_seqlens=np.array([0, n], np.int32), pool=vals.copy(), cache_indices=ci,
+                has_initial_state=hi, act="silu")
+    y_full, p_full = gh.gpu_fwd(full)
+    for cut in (1, 2, 3, 127, 128, 129, 300):
+        pool = gh.dev_pool(vals.copy())
+        ys = []
+        for lo, hi_ in ((0, cut), (cut, n)):
+            y = cc.conv1d_fwd(gh.dev_bits(x[lo:hi_]), gh.dev_taps(w), gh.dev_taps(b),
+                              cu_seqlens=gh.dev_i32(np.array([0, hi_ - lo])), conv_state=pool,
+                              cache_indices=gh.dev_i32(ci), has_initial_state=gh.dev_u8(hi))
+            ys.append(gh.host_bits(y))
+        torch.cuda.synchronize()
+        assert np.array_equal(np.concatenate(ys), y_full), f"cut {cut}"
+        assert np.array_equal(gh.host_pool(pool), p_full)
+
+
+def test_context_parallel_split_on_gpu():
+    """Fragments with the previous fragment's last three rows as history = the unsplit batch (y
+    bit-exact); dx of the unsplit call on those rows = local dx + d(history); dw adds up."""
+    say("cp split")
+    rng = np.random.default_rng(33)
+    C, S, cut = 2048, 1000, 437
+    x, dy = wl.normal_bf16(rng, (S, C)), wl.normal_bf16(rng, (S, C))
+    w = wl.uniform_f32(rng, (C, 4))
+    whole = dict(x=x, w=w, b=None, cu_seqlens=np.array([0, S], np.int32), dy=dy, act="silu")
+    y_u, _ = gh.gpu_fwd(whole)
+    dx_u, dw_u, _, _ = gh.gpu_bwd(whole)
+    hist = np.zeros((2, 3, C), np.uint16)
+    hist[1] = x[cut - 3:cut]
+    frag = dict(x=x, w=w, b=None, cu_seqlens=np.array([0, cut, S], np.int32), hist=hist,
+                has_history=np.array([0, 1], np.uint8), dy=dy, act="silu")
+    y_f, _ = gh.gpu_fwd(frag)
+    assert np.array_equal(y_f, y_u)
+    dx_f, dw_f, _, dh = gh.gpu_bwd(frag)
+    assert np.array_equal(dx_f[cut:], dx_u[cut:])
+    a, h, ref = gh.f32(dx_f[cut - 3:cut]), gh.f32(dh[1]), gh.f32(dx_u[cut - 3:cut])
+    assert np.all(np.abs(a + h - ref) <= 2.0 ** -8 * (np.abs(a) + np.abs(h) + np.abs(ref)) + 1e-6)
+    gh.assert_w_close(dw_f, dw_u, "dw over fragments")
+
+
+def test_hip_graph_replay_with_edited_metadata(oracle):
+    """Capture forward + backward once; between replays rewrite cu_seqlens / cache_indices /
+    has_initial_state / has_history in place (same capacities) and check every replay."""
+    say("graph capture")
+    rng = np.random.default_rng(34)
+    C, rows, N = 1024, 700, 5
+    x, dy = wl.normal_bf16(rng, (rows, C)), wl.normal_bf16(rng, (rows, C))
+    w = wl.uniform_f32(rng, (C, 4))
+    b = (rng.standard_normal(C) * 0.1).astype(np.float32)
+    vals = wl.normal_bf16(rng, (8, C, 4))
+    hist = wl.normal_bf16(rng, (N, 3, C))
+    dev = dict(x=gh.dev_bits(x), dy=gh.dev_bits(dy), w=gh.dev_taps(w), b=gh.dev_taps(b), hist=gh.dev_bits(hist),
+               cu=torch.zeros(N + 1, dtype=torch.int32, device="cuda"), ci=torch.zeros(N, dtype=torch.int32, device="cuda"),
+               hi=torch.zeros(N, dtype=torch.uint8, device="cuda"), hh=torch.zeros(N, dtype=torch.uint8, device="cuda"),
+               pool=gh.dev_pool(vals.copy()), y=torch.empty(rows, C, dtype=torch.bfloat16, device="cuda"),
+               y2=torch.empty(rows, C, dtype=torch.bfloat16, device="cuda"),
+               dx=torch.empty(rows, C, dtype=torch.bfloat16, device="cuda"),
+               dw=torch.empty(C, 4, dtype=torch.float32, device="cuda"),
+               db=torch.empty(C, dtype=torch.float32, device="cuda"),
+               dh=torch.empty(N, 3, C, dtype=torch.bfloat16, device="cuda"),
+               ws=torch.empty(cc.conv1d_bwd_workspace_bytes(rows, C), dtype=torch.uint8, device="cuda"))
+
+    def metadata():
+        lengths = rng.integers(0, 200, size=N)
+        lengths = np.minimum(lengths, rows // N)
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        ci = rng.permutation(8)[:N].astype(np.int32)
+        ci[int(rng.integers(0, N))] = -1
+        return cu, ci, (rng.random(N) < 0.5).astype(np.uint8), (rng.random(N) < 0.5).astype(np.uint8)
+
+    def run():
+        cc.conv1d_fwd(dev["x"], dev["w"], dev["b"], cu_seqlens=dev["cu"], conv_state=dev["pool"],
+                      cache_indices=dev["ci"], has_initial_state=dev["hi"], out=dev["y"])
+        cc.conv1d_fwd(dev["x"], dev["w"], dev["b"], cu_seqlens=dev["cu"], history=dev["hist"],
+                      has_history=dev["hh"], out=dev["y2"])
+        cc.conv1d_bwd(dev["x"], dev["dy"], dev["w"], dev["b"], cu_seqlens=dev["cu"], history=dev["hist"],
+                      has_history=dev["hh"], dx=dev["dx"], dweight=dev["dw"], dbias=dev["db"], dhistory=dev["dh"],
+                      workspace=dev["ws"])
+
+    meta = metadata()
+    for t, m in zip((dev["cu"], dev["ci"], dev["hi"], dev["hh"]), meta):
+        t.copy_(torch.from_numpy(m))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()  # warm up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for replay in range(4):
+        cu, ci, hi, hh = metadata()
+        for t, m in zip((dev["cu"], dev["ci"], dev["hi"], dev["hh"]), (cu, ci, hi, hh)):
+            t.copy_(torch.from_numpy(m))
+        pool_before = gh.host_pool(dev["pool"])
+        dev["y"].fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref_pool = pool_before.copy()
+        yr = oracle.fwd(x, w, b, cu_seqlens=cu, pool=ref_pool, cache_indices=ci, has_initial_state=hi, fill=0)
+        yg = gh.host_bits(dev["y"])
+        gh.assert_bf16_close(yg[: cu[-1]], yr[: cu[-1]], f"replay {replay}: y")
+        assert np.array_equal(gh.host_pool(dev["pool"]), ref_pool), f"replay {replay}: pool"
+        yr2 = oracle.fwd(x, w, b, cu_seqlens=cu, hist=hist, has_history=hh)
+        gh.assert_bf16_close(gh.host_bits(dev["y2"])[: cu[-1]], yr2[: cu[-1]], f"replay {replay}: y (history)")
+        dxr, dwr, dbr, dhr = oracle.bwd(x, dy, w, b, cu_seqlens=cu, hist=hist, has_history=hh)
+        gh.assert_bf16_close(gh.host_bits(dev["dx"])[: cu[-1]], dxr[: cu[-1]], f"replay {replay}: dx")
+        gh.assert_w_close(dev["dw"].cpu().numpy(), dwr, f"replay {replay}: dw")
+        gh.assert_w_close(dev["db"].cpu().numpy(), dbr, f"replay {replay}: db")
+        dhg = gh.host_bits(dev["dh"]).reshape(N, 3, C)
+        for i in np.flatnonzero(hh):
+            gh.assert_bf16_close(dhg[i], dhr[i], f"replay {replay}: dhist")
+
+
+def test_strided_rows_and_scalar_path(oracle):
+    """Row strides larger than C (a channel slice of a wider tensor) and misaligned rows."""
+    say("strided rows")
+    rng = np.random.default_rng(35)
+    for C, ld, off in ((512, 640, 0), (512, 600, 8), (24, 27, 1), (1000, 1000, 3)):
+        rows = 333
+        full = wl.normal_bf16(rng, (rows, ld + off))
+        xs = full[:, off:off + C]
+        cu = np.array([0, 100, 101, 333], np.int32)
+        w = wl.uniform_f32(rng, (C, 4))
+        hist = wl.normal_bf16(rng, (3, 3, C))
+        xdev = gh.dev_bits(full)[:, off:off + C]
+        out_full = torch.empty(rows, ld + 5, dtype=torch.bfloat16, device="cuda")
+        out = out_full[:, 5:5 + C]
+        y = cc.conv1d_fwd(xdev, gh.dev_taps(w), None, cu_seqlens=gh.dev_i32(cu), history=gh.dev_bits(hist), out=out)
+        torch.cuda.synchronize()
+        yr = oracle.fwd(np.ascontiguousarray(xs), w, None, cu_seqlens=cu, hist=hist)
+        gh.assert_bf16_close(gh.host_bits(y), yr, f"strided C={C} ld={ld} off={off}")
+
+
+def test_64bit_row_offsets(oracle):
+    """rows * C beyond 2^31 elements: row offsets must not wrap.  Checked on sampled channels."""
+    say("64-bit offsets")
+    rng = np.random.default_rng(36)
+    rows, C = 4096 * 33, 16384  # 2.2e9 elements, 4.4 GB per tensor
+    x = torch.empty(rows, C, dtype=torch.bfloat16, device="cuda")
+    x.normal_(generator=torch.Generator(device="cuda").manual_seed(7))
+    cu = np.array([0, 5, 70000, rows - 3, rows], np.int32)
+    w = wl.uniform_f32(rng, (C, 4))
+    y = cc.conv1d_fwd(x, gh.dev_taps(w), None, cu_seqlens=gh.dev_i32(cu))
+    torch.cuda.synchronize()
+    cols = np.array([0, 1, 777, 8191, 16383])
+    tail = slice(rows - 70000, rows)
+    xs = gh.host_bits(x[:, cols].contiguous())
+    ys = gh.host_bits(y[:, cols].contiguous())
+    yr = oracle.fwd(xs, np.ascontiguousarray(w[cols]), None, cu_seqlens=cu)
+    gh.assert_bf16_close(ys[tail], yr[tail], "far rows")
+    gh.assert_bf16_close(ys[:4096], yr[:4096], "near rows")
+    del x, y
+    torch.cuda.empty_cache()
