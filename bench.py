@@ -10,8 +10,10 @@ resident in HBM before the timed region.  Steady state, as inside a training or 
 the timed calls run back to back on one stream over a ring of independent buffer sets (4 for the
 step workload, about 3 GB), so no call finds its operands in the 256 MB Infinity Cache and every
 call's writes evict the previous calls' dirty lines, i.e. each written byte is paid for in HBM.
-HIP events on the stream the library launches on bracket each batch of calls; `value` =
-algorithmic bytes of K steps / the batch time.  Effective bytes count what the method must move,
+W untimed warm-up steps come first (default 200, about 45 ms: after an idle gap the clocks need
+some 20 ms of sustained load to settle, and a shorter warm-up times the ramp).  HIP events on the
+stream the library launches on bracket each batch of calls; `value` = algorithmic bytes of K
+steps / the batch time.  Effective bytes count what the method must move,
 each once (activations read and written, history rows, taps, gradients); halo re-reads and the
 dweight partial workspace are overhead and not counted.
 
@@ -188,19 +190,33 @@ class Gpu:
                                   want_dbias=d["db"] is not None, dhistory=d.get("dhist"),
                                   want_dhistory="dhist" in d, workspace=d["ws"])
 
-    def ring(self, calls, k, warmup):
-        """Mean milliseconds per call over k back-to-back passes of `calls` (a list of zero-argument
-        callables cycling through independent buffer sets), bracketed by two HIP events."""
+    def ring(self, calls, k, warmup, warm_ms=0.0, wall=None):
+        """Mean milliseconds per call over k back-to-back calls cycling through `calls` (zero-argument
+        callables over independent buffer sets), bracketed by two HIP events on the library's stream.
+        Untimed first: `warmup` calls, then whole passes until `warm_ms` of wall time have gone by
+        (the clocks need some 20 ms of sustained load to settle after an idle gap).  If `wall` is a
+        list, the host wall time of the timed calls (seconds) is appended to it."""
         t = self.torch
-        for i in range(warmup * len(calls)):
+        for i in range(warmup):
             calls[i % len(calls)]()
+        if warm_ms > 0:
+            t0 = time.perf_counter()
+            while True:
+                for c in calls:
+                    c()
+                t.cuda.synchronize()
+                if (time.perf_counter() - t0) * 1e3 >= warm_ms:
+                    break
         ev0, ev1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         t.cuda.synchronize()
+        w0 = time.perf_counter()
         ev0.record(self.stream)
         for i in range(k):
             calls[i % len(calls)]()
         ev1.record(self.stream)
         t.cuda.synchronize()
+        if wall is not None:
+            wall.append(time.perf_counter() - w0)
         return ev0.elapsed_time(ev1) / k
 
     def copy_ceiling(self, nbytes=1 << 30):
@@ -209,7 +225,7 @@ class Gpu:
         t = self.torch
         bufs = [(t.empty(nbytes // 2, dtype=t.bfloat16, device=self.dev).normal_(),
                  t.empty(nbytes // 2, dtype=t.bfloat16, device=self.dev)) for _ in range(2)]
-        ms = self.ring([lambda a=a, b=b: b.copy_(a) for a, b in bufs], 20, 3)
+        ms = self.ring([lambda a=a, b=b: b.copy_(a) for a, b in bufs], 40, 0, warm_ms=40)
         return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
@@ -257,8 +273,8 @@ def _cpu_model():
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-extras", action="store_true", help="skip the other workloads and the copy ceiling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only-mib", type=int, default=0,
@@ -291,12 +307,11 @@ def main():
     for k in range(4):
         step_calls.append(lambda k=k: g.fwd(sets[k]))
         step_calls.append(lambda k=k: g.bwd(sets[(k + 2) % 4]))
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    mean_step = 2 * g.ring(step_calls, 2 * args.steps, args.warmup)
-    wall = time.perf_counter() - w0
-    mean_f = g.ring([lambda k=k: g.fwd(sets[k]) for k in range(4)], args.steps, 2)
-    mean_b = g.ring([lambda k=k: g.bwd(sets[k]) for k in range(4)], args.steps, 2)
+    walls = []
+    mean_step = 2 * g.ring(step_calls, 2 * args.steps, 2 * args.warmup, wall=walls)
+    wall = walls[0]
+    mean_f = g.ring([lambda k=k: g.fwd(sets[k]) for k in range(4)], args.steps, 20)
+    mean_b = g.ring([lambda k=k: g.bwd(sets[k]) for k in range(4)], args.steps, 20)
     value = gbps(fb + bb, mean_step)
 
     traffic = stored_traffic()
@@ -326,11 +341,11 @@ def main():
             nb = fwd_bytes(c)
             nsets = int(min(8, max(2, -(-(1 << 30) // nb))))
             dd = [g.prepare(c) for _ in range(nsets)]
-            ms = g.ring([lambda d=d: g.fwd(d) for d in dd], 20, 3)
+            ms = g.ring([lambda d=d: g.fwd(d) for d in dd], 40, 0, warm_ms=40)
             r = {"fwd_GBps": round(gbps(nb, ms), 1), "fwd_us": round(1e3 * ms, 2), "fwd_bytes": nb}
             if c.get("dy") is not None:
                 nbb = bwd_bytes(c)
-                msb = g.ring([lambda d=d: g.bwd(d) for d in dd], 20, 3)
+                msb = g.ring([lambda d=d: g.bwd(d) for d in dd], 40, 0, warm_ms=40)
                 r.update({"bwd_GBps": round(gbps(nbb, msb), 1), "bwd_us": round(1e3 * msb, 2), "bwd_bytes": nbb})
             extras[c["name"]] = r
             del dd

@@ -101,7 +101,8 @@ size_t conv1d_fwd_workspace_bytes(int64_t rows, int64_t C, int64_t nseq) {
 
 size_t conv1d_bwd_workspace_bytes(int64_t rows, int64_t C) {
   if (rows <= 0 || C <= 0) return 0;
-  const size_t nrb = (size_t)((rows + kBwdRows - 1) / kBwdRows);
+  const int64_t rr = range_rows_for(rows, ceil_div(C, kBlockChannels), kBwdBlocks, kBwdFixedRows);
+  const size_t nrb = (size_t)((rows + rr - 1) / rr);
   const size_t bytes = nrb * 5u * (size_t)C * sizeof(float);
   return (bytes + kWsAlign - 1) / kWsAlign * kWsAlign;
 }
@@ -153,7 +154,8 @@ int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void*
 
   const bool vec = (C % 8 == 0) && (x_ld % 8 == 0) && (y_ld % 8 == 0) && aligned(x, 16) && aligned(y, 16) &&
                    (!use_hist || aligned(hist->ptr, 16));
-  const uint64_t nblk = (uint64_t)ceil_div(C, kBlockChannels) * ceil_div(rows, kFwdRows);
+  const int64_t rr = range_rows_for(rows, ceil_div(C, kBlockChannels), kFwdBlocks, kFwdFixedRows);
+  const uint64_t nblk = (uint64_t)ceil_div(C, kBlockChannels) * ceil_div(rows, rr);
   if (nblk > 0x7fffffffull) return CONV1D_EINVAL;
 
   FwdArgs a{};
@@ -172,8 +174,9 @@ int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void*
     a.pool = PoolArgs{static_cast<uint16_t*>(pool->ptr), pool->slots, pool->s_slot, pool->s_chan, pool->s_pos,
                       pool->cache_indices, pool->has_initial_state};
   if (use_hist) a.hist = HistArgs{static_cast<const uint16_t*>(hist->ptr), hist->has_history};
+  a.range_rows = rr;
   a.n_strips = ceil_div(C, kBlockChannels);
-  a.n_rowblocks = ceil_div(rows, kFwdRows);
+  a.n_rowblocks = ceil_div(rows, rr);
   return launch_fwd(a, mode, vec, act == CONV1D_ACT_SILU, stream) == hipSuccess ? CONV1D_OK : CONV1D_EHIP;
 }
 
@@ -253,7 +256,8 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
   const bool vec = (C % 8 == 0) && (x_ld % 8 == 0) && (dy_ld % 8 == 0) && (dx_ld % 8 == 0) && aligned(x, 16) &&
                    aligned(dy, 16) && aligned(dx, 16) && (!use_hist || aligned(hist->ptr, 16)) &&
                    (!dhist || aligned(dhist, 16));
-  const uint64_t nblk = (uint64_t)ceil_div(C, kBlockChannels) * ceil_div(rows, kBwdRows);
+  const int64_t rr = range_rows_for(rows, ceil_div(C, kBlockChannels), kBwdBlocks, kBwdFixedRows);
+  const uint64_t nblk = (uint64_t)ceil_div(C, kBlockChannels) * ceil_div(rows, rr);
   if (nblk > 0x7fffffffull || (uint64_t)((20 + (nseq > 0 ? nseq : 0)) * C) / 256 > 0x7fffffffull)
     return CONV1D_EINVAL;
 
@@ -276,8 +280,9 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
   a.part = static_cast<float*>(ws);
   a.dw = dw;
   a.db = db;
+  a.range_rows = rr;
   a.n_strips = ceil_div(C, kBlockChannels);
-  a.n_rowblocks = ceil_div(rows, kBwdRows);
+  a.n_rowblocks = ceil_div(rows, rr);
   return launch_bwd(a, mode, vec, act == CONV1D_ACT_SILU, stream) == hipSuccess ? CONV1D_OK : CONV1D_EHIP;
 }
 

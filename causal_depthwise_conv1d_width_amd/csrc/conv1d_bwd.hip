@@ -8,11 +8,14 @@
 //     dw_k   = sum_t dz[t] u[t-3+k],  db = sum_t dz[t]
 //     dh_j   = sum_{tau <= j} w_{j-tau} dz[s+tau]   (history row j of a continuing fragment)
 //
-// Tiling: as the forward (waves side by side in channels, lane = 8 channels), with kBwdRows-row
-// ranges.  A wave needs x rows [ta-3, tb+3) and dy rows [ta, tb+3); its own rows are streamed
-// once (non-temporal), the three look-behind and three look-ahead rows belong to the
-// neighbouring row ranges, which stream them at the same time on the same XCD, so those few
-// reads are served by L2.
+// Tiling: as the forward (waves side by side in channels, lane = CPL channels, one launch of
+// about kBwdBlocks equal row ranges).  A wave streams x and dy over its own rows [ta, tb) and up
+// to three look-ahead rows of the sequence that holds row tb - 1; the three look-behind and the
+// look-ahead rows belong to the neighbouring ranges (cached loads).  The step at row q produces
+// the value w3 dz[q-3] + w2 dz[q-2] + w1 dz[q-1] + w0 dz[q] of row q - 3: dx when q - 3 is a row
+// of q's sequence, d(history) row j when q - 3 is the sequence's history row j (the dz ring holds
+// zeros before a sequence's start).  Where a sequence ends, the values of its last three rows
+// are flushed with the dz of later rows left out, and the stream goes straight on.
 //
 // dweight/dbias are deterministic by construction: each lane accumulates its channels over its
 // rows in row order (FP32) and owns those channels for the whole row range, so the range's
@@ -42,9 +45,6 @@ __device__ __forceinline__ void load_hist_rows(const HistArgs& hist, int64_t idx
 #endif
 #ifndef CCONV_BWD_PIPELINE
 #define CCONV_BWD_PIPELINE 1
-#endif
-#ifndef CCONV_BWD_WAVES_PER_EU
-#define CCONV_BWD_WAVES_PER_EU 1
 #endif
 
 // Per-lane state of the backward stream (CPL channels).
@@ -88,10 +88,11 @@ __device__ __forceinline__ void bwd_row(BwdState<CPL>& st, const Pk<CPL>& xr, co
   }
 }
 
-// dx of the row three steps back: w3 dz[q-3] + w2 dz[q-2] + w1 dz[q-1] + w0 dz[q]
+// The value of row p = q - 3 at step q (ring slot r of row q): w3 dz[p] + w2 dz[p+1] + w1 dz[p+2]
+// + w0 dz[p+3].  Ring slots of rows before a sequence's start hold dz = 0, so for the three rows
+// before a sequence this is the gradient of its history rows.
 template <int CPL>
-__device__ __forceinline__ Pk<CPL> bwd_dx(const BwdState<CPL>& st, int r) {
-  float d[CPL];
+__device__ __forceinline__ void bwd_back(const BwdState<CPL>& st, int r, float (&d)[CPL]) {
 #pragma unroll
   for (int ch = 0; ch < CPL; ++ch) {
     float v = st.wk[3][ch] * st.g[(r + 1) % 4][ch];
@@ -100,40 +101,117 @@ __device__ __forceinline__ Pk<CPL> bwd_dx(const BwdState<CPL>& st, int r) {
     v = __builtin_fmaf(st.wk[0][ch], st.g[r % 4][ch], v);
     d[ch] = v;
   }
-  return pack(d);
 }
 
-// head of a continuing fragment: dh_j += w_{j-r} dz[s+r] for j >= r (r = 0, 1, 2)
-template <int CPL>
-__device__ __forceinline__ void bwd_dhist(const BwdState<CPL>& st, float (&dh)[3][CPL], int r) {
-#pragma unroll
-  for (int j = r; j < 3; ++j)
-#pragma unroll
-    for (int ch = 0; ch < CPL; ++ch) dh[j][ch] = __builtin_fmaf(st.wk[j - r][ch], st.g[r % 4][ch], dh[j][ch]);
+// The sequence a wave is streaming, and whether this wave writes its d(history) rows (it holds
+// the sequence's first row and the sequence reads caller history rows).
+struct BwdSeq {
+  SeqDesc sd;
+  bool dh;
+};
+
+// Where the value of row p goes: dx when p is a row of the current sequence inside the wave's own
+// range [ta, tb); d(history) row p - s + 3 when p is one of the three history rows of a sequence
+// whose head this wave streams; nowhere otherwise (rows of the neighbouring ranges).
+template <int CPL, bool VEC>
+__device__ __forceinline__ void bwd_route(const BwdArgs& a, const BwdSeq& cs, int64_t p, int64_t ta, int64_t tb,
+                                          const float (&v)[CPL], int64_t c0, bool active) {
+  if (p >= cs.sd.s) {
+    if (p >= ta && p < tb && active) store_row<CPL, VEC, true>(a.dx + p * a.dx_ld, c0, a.C, pack(v));
+  } else if (cs.dh && active) {
+    store_row<CPL, VEC>(a.dhist + (cs.sd.idx * 3 + (p - cs.sd.s + 3)) * a.C, c0, a.C, pack(v));
+  }
 }
 
-// CH own rows starting at q0 (every lane active, all rows real and owned).  FIRST: q0 is the
-// run's first row, so rows q0-3..q0-1 get no dx here, and a head fragment's d(history), which
-// needs dz of the sequence's first three rows only, is finished and stored in this chunk.
-template <int CPL, bool VEC, int CH, bool SILU, bool FIRST>
-__device__ __forceinline__ void bwd_chunk(BwdState<CPL>& st, const Pk<CPL> (&X)[CH], const Pk<CPL> (&G)[CH],
-                                          const BwdArgs& a, int64_t q0, int64_t c0, bool want_dh, int64_t hidx) {
-  static_assert(CH >= 3, "the first chunk must hold a sequence's first three rows");
+// The current sequence ends right before row e (ring slot r): the values of its last three rows
+// e-3, e-2, e-1 only take dz of rows before e.
+template <int CPL, bool VEC>
+__device__ __forceinline__ void bwd_flush(const BwdArgs& a, const BwdState<CPL>& st, const BwdSeq& cs, int r, int64_t e,
+                                          int64_t ta, int64_t tb, int64_t c0, bool active) {
+  float v3[CPL], v2[CPL], v1[CPL];
+#pragma unroll
+  for (int ch = 0; ch < CPL; ++ch) {
+    const float g3 = st.g[(r + 1) % 4][ch], g2 = st.g[(r + 2) % 4][ch], g1 = st.g[(r + 3) % 4][ch];
+    v3[ch] = __builtin_fmaf(st.wk[1][ch], g1, __builtin_fmaf(st.wk[2][ch], g2, st.wk[3][ch] * g3));
+    v2[ch] = __builtin_fmaf(st.wk[2][ch], g1, st.wk[3][ch] * g2);
+    v1[ch] = st.wk[3][ch] * g1;
+  }
+  bwd_route<CPL, VEC>(a, cs, e - 3, ta, tb, v3, c0, active);
+  bwd_route<CPL, VEC>(a, cs, e - 2, ta, tb, v2, c0, active);
+  bwd_route<CPL, VEC>(a, cs, e - 1, ta, tb, v1, c0, active);
+}
+
+template <int MODE>
+__device__ __forceinline__ bool bwd_wants_dh(const BwdArgs& a, const SeqDesc& sd) {
+  if constexpr (MODE == MODE_IDX) {
+    return false;  // caller history rows need the cu_seqlens or batch-row form
+  } else {
+    return a.dhist && (!a.hist.has_hist || a.hist.has_hist[sd.idx]);
+  }
+}
+
+// Row q = cs.sd.s (ring slot r), the first row of a sequence, is next: the three window slots
+// take its history and dz = 0.
+template <int CPL, bool VEC, int MODE>
+__device__ __forceinline__ void bwd_enter(const BwdArgs& a, BwdState<CPL>& st, BwdSeq& cs, int r, int64_t c0,
+                                          bool active) {
+  float h[3][CPL];
+  if constexpr (MODE != MODE_IDX) {
+    load_hist_rows<CPL, VEC>(a.hist, cs.sd.idx, c0, a.C, active, h);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
+  }
+  cs.dh = bwd_wants_dh<MODE>(a, cs.sd);
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch) {
+      st.u[(r + 1 + j) % 4][ch] = h[j][ch];
+      st.g[(r + 1 + j) % 4][ch] = 0.f;
+    }
+}
+
+// CH rows starting at q0 (ring slot of row q0 + r is r mod 4).  The stream covers the own rows
+// [ta, tb) and then up to three look-ahead rows of the sequence that holds row tb - 1, which
+// finish the last dx rows; it ends (done) at that sequence's end or at tb + 3.  A chunk of own
+// rows of one sequence, at least three rows past both its start and the range start, is a
+// straight recompute-and-dx; any other chunk takes the row-by-row path.
+template <int CPL, bool VEC, int MODE, int CH, bool SILU>
+__device__ __forceinline__ void bwd_chunk(const BwdArgs& a, BwdState<CPL>& st, BwdSeq& cs, const Pk<CPL> (&X)[CH],
+                                          const Pk<CPL> (&G)[CH], int64_t q0, int64_t ta, int64_t tb, int64_t dend,
+                                          int64_t lim, int64_t c0, bool active, bool& done) {
+  if (q0 + CH <= tb && cs.sd.e >= q0 + CH && q0 >= cs.sd.s + 3 && q0 >= ta + 3) {
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+      bwd_row<CPL, SILU>(st, X[r], G[r], r, true);
+      float d[CPL];
+      bwd_back<CPL>(st, r, d);
+      if (active) store_row<CPL, VEC, true>(a.dx + (q0 + r - 3) * a.dx_ld, c0, a.C, pack(d));
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < CH; ++r) {
-    bwd_row<CPL, SILU>(st, X[r], G[r], r, true);
-    if (FIRST && r == 2 && want_dh) {
-      float dh[3][CPL];
-#pragma unroll
-      for (int j = 0; j < 3; ++j)
-#pragma unroll
-        for (int ch = 0; ch < CPL; ++ch) dh[j][ch] = 0.f;
-#pragma unroll
-      for (int rr = 0; rr < 3; ++rr) bwd_dhist<CPL>(st, dh, rr);
-#pragma unroll
-      for (int j = 0; j < 3; ++j) store_row<CPL, VEC>(a.dhist + (hidx * 3 + j) * a.C, c0, a.C, pack(dh[j]));
+    const int64_t q = q0 + r;
+    if (!done && q == cs.sd.e) {
+      bwd_flush<CPL, VEC>(a, st, cs, r, q, ta, tb, c0, active);
+      if (q >= tb) {
+        done = true;
+      } else {
+        cs.sd = next_seq<MODE>(a.seq, cs.sd, dend, lim);
+        bwd_enter<CPL, VEC, MODE>(a, st, cs, r, c0, active);
+      }
     }
-    if (!FIRST || r >= 3) store_row<CPL, VEC, true>(a.dx + (q0 + r - 3) * a.dx_ld, c0, a.C, bwd_dx<CPL>(st, r));
+    if (!done && q >= tb + 3) done = true;
+    if (!done) {
+      bwd_row<CPL, SILU>(st, X[r], G[r], r, q < tb);
+      float d[CPL];
+      bwd_back<CPL>(st, r, d);
+      bwd_route<CPL, VEC>(a, cs, q - 3, ta, tb, d, c0, active);
+    }
   }
 }
 
@@ -149,9 +227,9 @@ __device__ __forceinline__ void bwd_load(Pk<CPL> (&X)[CH], Pk<CPL> (&G)[CH], con
 }
 
 template <int CPL, bool VEC, int MODE, bool SILU>
-__global__ void __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(CCONV_BWD_WAVES_PER_EU)))
-conv1d_bwd_kernel(const BwdArgs a) {
+__global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_kernel(const BwdArgs a) {
   constexpr int CH = CCONV_BWD_CHUNK;  // rows per unrolled chunk (a multiple of the 4-slot rings)
+  static_assert(CH % 4 == 0, "chunks must keep the ring slot of a row fixed");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -165,8 +243,8 @@ conv1d_bwd_kernel(const BwdArgs a) {
   const bool full = VEC && wc0 + kWaveChannels <= C;  // every lane of the wave is active
   const int64_t dend = data_end<MODE>(a.seq, a.rows);
 
-  int64_t ta = (int64_t)rb * kBwdRows;
-  int64_t tb = ta + kBwdRows;
+  int64_t ta = (int64_t)rb * a.range_rows;
+  int64_t tb = ta + a.range_rows;
   ta = ta < dend ? ta : dend;
   tb = tb < dend ? tb : dend;
 
@@ -178,121 +256,82 @@ conv1d_bwd_kernel(const BwdArgs a) {
 
   if (ta < tb) {
     load_taps<CPL>(a.w, a.w_f32, a.b, a.b_f32, c0, C, st.wk, st.bias);
-    const int64_t lim = (tb + 3 < dend) ? tb + 3 : dend;  // IDX scans need ends up to tb+3
-    SeqDesc sd = seq_of_row<MODE>(a.seq, ta, dend, lim);
-    int64_t t = ta;
-    bool first = true;
-    while (true) {
-      const int64_t dist = first ? (t - sd.s < 3 ? t - sd.s : 3) : 0;
-      float h[3][CPL];
-      bool want_dh = false;
-      if constexpr (MODE != MODE_IDX) {
-        load_hist_rows<CPL, VEC>(a.hist, dist < 3 ? sd.idx : -1, c0, C, active, h);
-        want_dh = a.dhist && t == sd.s && (!a.hist.has_hist || a.hist.has_hist[sd.idx]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 3; ++j)
-#pragma unroll
-          for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
-      }
-      // window rows t-3..t-1: the history, then the last `dist` rows of the same sequence
-      // (the previous row range streamed them moments earlier on this XCD: cached loads)
-      for (int64_t k = 3 - dist; k < 3; ++k) {
-        Pk<CPL> p = zero_pk<CPL>();
-        if (active) p = load_row<CPL, VEC>(a.x + (t - 3 + k) * a.x_ld, c0, C);
-        shift_in<CPL>(h, p);
-      }
+    const int64_t lim = (tb + 3 < dend) ? tb + 3 : dend;  // sequence ends matter up to tb + 3
+
+    // full chunks of own rows, software-pipelined with two register buffers (see the forward)
+    const int nfull = (full && CCONV_BWD_PIPELINE) ? (int)((tb - ta) / CH) : 0;
+    const int64_t qlast = ta + (int64_t)nfull * CH - 1;
+    int64_t q0 = ta;
+    Pk<CPL> XA[CH], GA[CH], XB[CH], GB[CH];
+    if (nfull > 0) bwd_load<CPL, VEC, CH>(XA, GA, a, q0, qlast, c0);  // in flight during the set-up
+
+    // the sequence holding row ta and the window rows ta-3 .. ta-1
+    BwdSeq cs;
+    cs.sd = seq_of_row<MODE>(a.seq, ta, dend, lim);
+    const int64_t dist = ta - cs.sd.s < 3 ? ta - cs.sd.s : 3;
+    Pk<CPL> wrow[3];
+    load_window<CPL, VEC>(wrow, a.x, a.x_ld, ta, dist, c0, C, active);
+    float h[3][CPL];
+    cs.dh = false;
+    if constexpr (MODE != MODE_IDX) {
+      load_hist_rows<CPL, VEC>(a.hist, dist < 3 ? cs.sd.idx : -1, c0, C, active, h);
+      if (dist == 0) cs.dh = bwd_wants_dh<MODE>(a, cs.sd);
+    } else {
 #pragma unroll
       for (int j = 0; j < 3; ++j)
 #pragma unroll
-        for (int ch = 0; ch < CPL; ++ch) st.u[j + 1][ch] = h[j][ch];
+        for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
+    }
+    // window rows ta-3..ta-1: the history, then the last `dist` rows of the same sequence (the
+    // previous row range streamed them moments earlier on this XCD: cached loads); dz = 0 there
+    shift_window<CPL>(h, wrow, dist);
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int ch = 0; ch < CPL; ++ch) st.u[j + 1][ch] = h[j][ch];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int ch = 0; ch < CPL; ++ch) st.g[j][ch] = 0.f;
 
-      const int64_t t_end = sd.e < tb ? sd.e : tb;  // rows of this run that the wave owns
-      int64_t la_end = t_end;                        // plus same-sequence look-ahead rows
-      if (t_end == tb) la_end = (sd.e < tb + 3) ? sd.e : tb + 3;
-      if (la_end > dend) la_end = dend;
-      const int64_t steps_end = t_end + 3;  // three trailing steps finish the last dx rows
-
-      // full chunks of own rows, software-pipelined with two register buffers (see the forward)
-      const int nfull = (full && CCONV_BWD_PIPELINE) ? (int)((t_end - t) / CH) : 0;
-      int64_t q0 = t;
-      bool dh_done = false;
-      if (nfull > 0) {
-        // two register buffers, unrolled by two chunks, next chunk's loads always issued (rows
-        // past the last full chunk re-read its last row): see the forward kernel
-        const int64_t qlast = t + (int64_t)nfull * CH - 1;
-        Pk<CPL> XA[CH], GA[CH], XB[CH], GB[CH];
-        bwd_load<CPL, VEC, CH>(XA, GA, a, q0, qlast, c0);
+    bool done = false;
+    if (nfull > 0) {
+      // two register buffers, unrolled by two chunks, next chunk's loads always issued (rows
+      // past the last full chunk re-read its last row): see the forward kernel
+      for (int j = 0;; j += 2, q0 += 2 * CH) {
         bwd_load<CPL, VEC, CH>(XB, GB, a, q0 + CH, qlast, c0);
-        bwd_chunk<CPL, VEC, CH, SILU, true>(st, XA, GA, a, q0, c0, want_dh, sd.idx);
-        dh_done = true;
-        for (int j = 1;; j += 2, q0 += 2 * CH) {
-          if (j >= nfull) {
-            q0 += CH;
-            break;
-          }
-          bwd_load<CPL, VEC, CH>(XA, GA, a, q0 + 2 * CH, qlast, c0);
-          bwd_chunk<CPL, VEC, CH, SILU, false>(st, XB, GB, a, q0 + CH, c0, want_dh, sd.idx);
-          if (j + 1 >= nfull) {
-            q0 += 2 * CH;
-            break;
-          }
-          bwd_load<CPL, VEC, CH>(XB, GB, a, q0 + 3 * CH, qlast, c0);
-          bwd_chunk<CPL, VEC, CH, SILU, false>(st, XA, GA, a, q0 + 2 * CH, c0, want_dh, sd.idx);
+        bwd_chunk<CPL, VEC, MODE, CH, SILU>(a, st, cs, XA, GA, q0, ta, tb, dend, lim, c0, active, done);
+        if (j + 1 >= nfull) {
+          q0 += CH;
+          break;
+        }
+        bwd_load<CPL, VEC, CH>(XA, GA, a, q0 + 2 * CH, qlast, c0);
+        bwd_chunk<CPL, VEC, MODE, CH, SILU>(a, st, cs, XB, GB, q0 + CH, ta, tb, dend, lim, c0, active, done);
+        if (j + 2 >= nfull) {
+          q0 += 2 * CH;
+          break;
         }
       }
-      // the rest: remaining own rows, look-ahead rows of the same sequence, and three trailing
-      // steps (dz = 0 past the sequence's end) that finish the last dx rows
-      float dh[3][CPL];
+    }
+    // the rest: remaining own rows (and partially active waves), then the look-ahead rows, which
+    // the next row range streams at the same time (cached loads)
+    for (; !done; q0 += CH) {
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
-#pragma unroll
-        for (int ch = 0; ch < CPL; ++ch) dh[j][ch] = 0.f;
-      for (; q0 < steps_end; q0 += CH) {
-        Pk<CPL> xr[CH], gr[CH];
-#pragma unroll
-        for (int r = 0; r < CH; ++r) {
-          const int64_t q = q0 + r;
-          xr[r] = zero_pk<CPL>();
-          gr[r] = zero_pk<CPL>();
-          if (q < la_end && active) {
-            if (q < t_end) {  // own rows: read once, streamed
-              xr[r] = load_row<CPL, VEC, true>(a.x + q * a.x_ld, c0, C);
-              gr[r] = load_row<CPL, VEC, true>(a.dy + q * a.dy_ld, c0, C);
-            } else {  // look-ahead rows, owned by the next row range
-              xr[r] = load_row<CPL, VEC>(a.x + q * a.x_ld, c0, C);
-              gr[r] = load_row<CPL, VEC>(a.dy + q * a.dy_ld, c0, C);
-            }
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < CH; ++r) {
-          const int64_t q = q0 + r;
-          if (q < steps_end) {
-            if (q < la_end) {
-              bwd_row<CPL, SILU>(st, xr[r], gr[r], r, q < t_end);
-            } else {
-#pragma unroll
-              for (int ch = 0; ch < CPL; ++ch) st.g[r % 4][ch] = 0.f;  // past the sequence's end
-            }
-            if (r < 3 && want_dh && q0 == t) bwd_dhist<CPL>(st, dh, r);
-            if (q - 3 >= t) {
-              const Pk<CPL> d = bwd_dx<CPL>(st, r);
-              if (active) store_row<CPL, VEC, true>(a.dx + (q - 3) * a.dx_ld, c0, C, d);
-            }
+      for (int r = 0; r < CH; ++r) {
+        const int64_t q = q0 + r;
+        XA[r] = zero_pk<CPL>();
+        GA[r] = zero_pk<CPL>();
+        if (active && q < lim) {
+          if (q < tb) {
+            XA[r] = load_row<CPL, VEC, true>(a.x + q * a.x_ld, c0, C);
+            GA[r] = load_row<CPL, VEC, true>(a.dy + q * a.dy_ld, c0, C);
+          } else {
+            XA[r] = load_row<CPL, VEC>(a.x + q * a.x_ld, c0, C);
+            GA[r] = load_row<CPL, VEC>(a.dy + q * a.dy_ld, c0, C);
           }
         }
       }
-      if constexpr (MODE != MODE_IDX) {
-        if (want_dh && active && !dh_done) {
-#pragma unroll
-          for (int j = 0; j < 3; ++j) store_row<CPL, VEC>(a.dhist + (sd.idx * 3 + j) * C, c0, C, pack(dh[j]));
-        }
-      }
-      t = t_end;
-      if (t >= tb) break;
-      sd = next_seq<MODE>(a.seq, sd, dend, lim);
-      first = false;
+      bwd_chunk<CPL, VEC, MODE, CH, SILU>(a, st, cs, XA, GA, q0, ta, tb, dend, lim, c0, active, done);
     }
   }
 

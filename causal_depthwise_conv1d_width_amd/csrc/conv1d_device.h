@@ -167,6 +167,27 @@ __device__ __forceinline__ void shift_in(float (&w)[3][CPL], const Pk<CPL>& p) {
   }
 }
 
+// Window rows t-3 .. t-1 of a run that starts `dist` rows (0..3) into its sequence: the last
+// `dist` of them are inputs of the same sequence.  Every load is issued before any is used, so
+// the halo costs one memory round trip.
+template <int CPL, bool VEC>
+__device__ __forceinline__ void load_window(Pk<CPL> (&p)[3], const uint16_t* __restrict__ x, int64_t ld, int64_t t,
+                                            int64_t dist, int64_t c0, int64_t C, bool active) {
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    p[j] = zero_pk<CPL>();
+    if (active && j >= 3 - dist) p[j] = load_row<CPL, VEC>(x + (t - 3 + j) * ld, c0, C);
+  }
+}
+
+// h = the sequence's history positions 0..2; shift in the window rows load_window fetched.
+template <int CPL>
+__device__ __forceinline__ void shift_window(float (&h)[3][CPL], const Pk<CPL> (&p)[3], int64_t dist) {
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    if (j >= 3 - dist) shift_in<CPL>(h, p[j]);
+}
+
 // ------------------------------------------------------------------ activation
 // sigmoid via the hardware exp2 and reciprocal (about 1 ulp each): far below bf16 rounding.
 __device__ __forceinline__ float sigmoid_f32(float z) {
@@ -235,16 +256,29 @@ __device__ __forceinline__ int64_t idx_next_start(const SeqArgs& q, int64_t t, i
 template <int MODE>
 __device__ __forceinline__ SeqDesc seq_of_row(const SeqArgs& q, int64_t t, int64_t dend, int64_t limit) {
   SeqDesc d;
+  const int lane = threadIdx.x & (kWave - 1);
   if constexpr (MODE == MODE_CU) {
-    // largest i in [0, nseq) with cu[i] <= t; then cu[i+1] > t
-    int64_t lo = 0, hi = q.nseq - 1;
-    while (lo < hi) {
-      const int64_t mid = (lo + hi + 1) >> 1;
-      if (cu_at(q, mid, dend) <= t) lo = mid; else hi = mid - 1;
+    // largest i in [0, nseq) with cu[i] <= t, by a 64-ary search: lane l reads cu[lo + l*stride]
+    // (one load per lane per level, a single level while nseq <= 63), the highest lane whose
+    // offset is <= t narrows the interval.  Lane 0 is taken as the floor without a test, as the
+    // offsets start at 0.  The last level also hands over cu[i + 1] from the next lane.
+    int64_t lo = 0, n = q.nseq;  // the answer lies in [lo, lo + n)
+    while (true) {
+      const int64_t stride = n < kWave ? 1 : (n + kWave - 2) / (kWave - 1);
+      const int64_t off = (int64_t)lane * stride;
+      int32_t v = 0;
+      if (off <= n) v = (int32_t)cu_at(q, lo + off, dend);  // lo + n <= nseq: in bounds
+      const uint64_t m = __ballot(lane == 0 || (off < n && v <= t));
+      const int k = 63 - __builtin_clzll(m);
+      if (stride == 1) {
+        d.idx = lo + k;
+        d.s = __builtin_amdgcn_readlane(v, k);  // k is wave-uniform: scalar results
+        d.e = __builtin_amdgcn_readlane(v, k + 1 < kWave ? k + 1 : k);
+        break;
+      }
+      lo += (int64_t)k * stride;
+      n = n - (int64_t)k * stride < stride ? n - (int64_t)k * stride : stride;
     }
-    d.idx = lo;
-    d.s = cu_at(q, lo, dend);
-    d.e = cu_at(q, lo + 1, dend);
     if (d.e <= t) d.e = t + 1;  // only for metadata that breaks the contract: stay in bounds
   } else if constexpr (MODE == MODE_BATCH) {
     d.idx = t / q.seqlen;
@@ -252,14 +286,19 @@ __device__ __forceinline__ SeqDesc seq_of_row(const SeqArgs& q, int64_t t, int64
     d.e = d.s + q.seqlen;
     if (d.e > dend) d.e = dend;
   } else {
-    // only the distance to the sequence start up to 3 rows matters: d.s = t - min(dist, 3)
-    int64_t dist = 3;
-    if (idx_is_start(q, t)) dist = 0;
-    else if (idx_is_start(q, t - 1)) dist = 1;
-    else if (idx_is_start(q, t - 2)) dist = 2;
+    // only the distance to the sequence start up to 3 matters (d.s = t - min(dist, 3)), and the
+    // next start below `limit`: lane l tests row t - 3 + l, one pass covers rows t-3 .. t+60
+    const int64_t r = t - 3 + lane;
+    bool st = false;
+    if (r >= 0 && (lane <= 3 || r < limit)) st = idx_is_start(q, r);
+    const uint64_t m = __ballot(st);
+    const uint64_t back = m & 0xEull;  // rows t-2, t-1, t
+    const int64_t dist = back ? 3 - (63 - __builtin_clzll(back)) : 3;
     d.s = t - dist;
     d.idx = -1;
-    d.e = idx_next_start(q, t, limit);
+    const uint64_t ahead = m >> 4;  // rows t+1 ..
+    if (ahead) d.e = t + 1 + (int64_t)__builtin_ctzll(ahead);
+    else d.e = t + 61 < limit ? idx_next_start(q, t + 60, limit) : limit;
   }
   return d;
 }
@@ -272,6 +311,7 @@ __device__ __forceinline__ SeqDesc next_seq(const SeqArgs& q, const SeqDesc& cur
   if constexpr (MODE == MODE_CU) {
     int64_t i = cur.idx + 1;
     while (i + 1 < q.nseq && cu_at(q, i + 1, dend) <= t) ++i;
+    if (i >= q.nseq) i = q.nseq - 1;  // only for metadata that breaks the contract: stay in bounds
     d.idx = i;
     d.s = t;
     d.e = cu_at(q, i + 1, dend);

@@ -6,20 +6,22 @@
 // cake_causal_conv1d_kcp.
 //
 // Forward tiling (HBM-bound stencil, no MFMA):
-//   block  = kWavesPerBlock waves side by side; lane = 8 consecutive channels; a block covers
-//            kBlockChannels channels of a kFwdRows-row range, so each row it touches is one
-//            contiguous segment.  Logical tiles run row-range major and each XCD gets one
-//            contiguous slice of them, so the row ranges next to each other (which share the
-//            three halo rows) and the channel strips of the same rows run together.
-//   stream = every wave walks its rows top to bottom in unrolled 8-row chunks: 8 non-temporal
-//            16-byte loads in flight per lane, then 8 stencil rows, 8 non-temporal stores.
-//   halo   = the three rows before a wave's first row: raw inputs of the same sequence (cached
-//            loads; the neighbouring range streamed them moments earlier on the same XCD), or
-//            at a sequence start the sequence's history (pool positions 0..2, caller history
-//            rows, or zeros).
-//   taps   = FP32 in registers; z = b, then four FMAs in tap order 0..3 (tap 3 = current row).
+//   block  = kWavesPerBlock waves side by side; lane = CPL consecutive channels; a block covers
+//            kBlockChannels channels of one row range, so each row it touches is one contiguous
+//            segment.  The range length is set per launch so that one launch is about
+//            kFwdBlocks equal blocks, all resident at once.  Logical tiles run row-range major
+//            and each XCD gets one contiguous slice of them.
+//   stream = every wave walks its whole range top to bottom in unrolled chunks, software-
+//            pipelined with two register buffers (the next chunk's non-temporal loads are in
+//            flight while this chunk computes and stores), straight across sequence boundaries:
+//            the loads never depend on where sequences start, only the window does.
 //   window = a 4-slot register ring indexed by row mod 4 inside the unrolled chunk, so the
-//            sliding window costs no register moves.
+//            sliding window costs no register moves.  Where a sequence starts inside a chunk,
+//            its three window slots are re-seeded from that sequence's history (pool positions
+//            0..2, caller history rows, or zeros) right before its first row.
+//   halo   = at the range start, the three rows before it: raw inputs of the same sequence
+//            (cached loads), or the sequence's history at its first row.
+//   taps   = FP32 in registers; z = b, then four FMAs in tap order 0..3 (tap 3 = current row).
 //   pool   = the wave that holds a sequence's first row is the only one that reads or writes
 //            its slot (for its channels).  With a pool, row-range boundaries that fall on the
 //            first three rows of a sequence move to that sequence's fourth row (or its end), so
@@ -120,18 +122,6 @@ template <int CPL, bool SILU>
 __device__ __forceinline__ Pk<CPL> stencil_row(const float (&wk)[4][CPL], const float (&bias)[CPL],
                                                const float (&u)[4][CPL], int r);
 
-// CH rows starting at q0 from a loaded buffer: ring update, stencil, streamed store (all lanes).
-template <int CPL, bool VEC, int CH, bool SILU>
-__device__ __forceinline__ void stencil_chunk(const Pk<CPL> (&buf)[CH], uint16_t* __restrict__ y, int64_t ld,
-                                              int64_t q0, int64_t c0, int64_t C, const float (&wk)[4][CPL],
-                                              const float (&bias)[CPL], float (&u)[4][CPL]) {
-#pragma unroll
-  for (int r = 0; r < CH; ++r) {
-    unpack(buf[r], u[r % 4]);
-    store_row<CPL, VEC, true>(y + (q0 + r) * ld, c0, C, stencil_row<CPL, SILU>(wk, bias, u, r));
-  }
-}
-
 // One output row from the ring: u[(r+1)%4], u[(r+2)%4], u[(r+3)%4] are rows t-3, t-2, t-1 and
 // u[r%4] the current row.  z = b, then the four taps in order (FMA), FP32; y = act(z) in bf16.
 template <int CPL, bool SILU>
@@ -152,19 +142,98 @@ __device__ __forceinline__ Pk<CPL> stencil_row(const float (&wk)[4][CPL], const 
 
 // ------------------------------------------------------------------ forward kernel
 #ifndef CCONV_FWD_CHUNK
-#define CCONV_FWD_CHUNK 8
+#define CCONV_FWD_CHUNK 4
 #endif
 #ifndef CCONV_FWD_PIPELINE
 #define CCONV_FWD_PIPELINE 1
 #endif
-#ifndef CCONV_FWD_WAVES_PER_EU
-#define CCONV_FWD_WAVES_PER_EU 1
-#endif
+
+// The sequence a wave is streaming: its rows, its pool slot, and whether its output is forced to
+// zero (a -1 slot).
+struct FwdSeq {
+  SeqDesc sd;
+  int32_t slot;
+  bool zero;
+};
+
+template <int MODE>
+__device__ __forceinline__ void fwd_slot(const FwdArgs& a, FwdSeq& cs) {
+  cs.slot = -1;
+  cs.zero = false;
+  if constexpr (MODE != MODE_IDX) {
+    if (a.pool.ptr) {
+      cs.slot = a.pool.cache_indices[cs.sd.idx];
+      cs.zero = !(cs.slot >= 0 && cs.slot < a.pool.slots);  // -1 (other values are out of contract)
+    }
+  }
+}
+
+// Row q = cs.sd.s, the first row of a sequence, is next: h <- its history, and with a pool the
+// head writes the sequence's final state (the head wave is the only one that touches the slot).
+template <int CPL, bool VEC, int MODE>
+__device__ __forceinline__ void fwd_enter(const FwdArgs& a, FwdSeq& cs, int64_t c0, bool active, float (&h)[3][CPL]) {
+  fwd_slot<MODE>(a, cs);
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
+  if constexpr (MODE != MODE_IDX) {
+    if (!cs.zero) {
+      load_history<CPL, VEC>(a.pool, a.hist, cs.sd.idx, cs.slot, true, c0, a.C, active, h);
+      if (a.pool.ptr && cs.sd.e > cs.sd.s) pool_writeback<CPL, VEC>(a, cs.slot, cs.sd, h, c0, active);
+    }
+  }
+}
+
+// n (<= CH) rows starting at q0 from a loaded buffer.  Ring slot of row q is (q - range start)
+// mod 4 = r mod 4, as q0 - range start is a multiple of CH.  A chunk inside one sequence is a
+// straight stencil; a chunk where sequences start re-seeds the three window slots from the new
+// sequence's history right before its first row.
+template <int CPL, bool VEC, int MODE, int CH, bool SILU>
+__device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)[CH], int n, int64_t q0, int64_t tb,
+                                          int64_t dend, FwdSeq& cs, int64_t c0, bool active,
+                                          const float (&wk)[4][CPL], const float (&bias)[CPL], float (&u)[4][CPL]) {
+  if (n == CH && cs.sd.e >= q0 + CH) {
+    if (cs.zero) {
+      if (active) {
+#pragma unroll
+        for (int r = 0; r < CH; ++r) store_row<CPL, VEC, true>(a.y + (q0 + r) * a.y_ld, c0, a.C, zero_pk<CPL>());
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < CH; ++r) {
+        unpack(buf[r], u[r % 4]);
+        const Pk<CPL> out = stencil_row<CPL, SILU>(wk, bias, u, r);
+        if (active) store_row<CPL, VEC, true>(a.y + (q0 + r) * a.y_ld, c0, a.C, out);
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int r = 0; r < CH; ++r) {
+    if (r < n) {
+      const int64_t q = q0 + r;
+      if (q == cs.sd.e) {  // a new sequence starts at row q (empty ones are skipped)
+        cs.sd = next_seq<MODE>(a.seq, cs.sd, dend, tb);
+        float h[3][CPL];
+        fwd_enter<CPL, VEC, MODE>(a, cs, c0, active, h);
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+          for (int ch = 0; ch < CPL; ++ch) u[(r + 1 + j) % 4][ch] = h[j][ch];
+      }
+      unpack(buf[r], u[r % 4]);
+      Pk<CPL> out = zero_pk<CPL>();
+      if (!cs.zero) out = stencil_row<CPL, SILU>(wk, bias, u, r);
+      if (active) store_row<CPL, VEC, true>(a.y + q * a.y_ld, c0, a.C, out);
+    }
+  }
+}
 
 template <int CPL, bool VEC, int MODE, bool SILU>
-__global__ void __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(CCONV_FWD_WAVES_PER_EU)))
-conv1d_fwd_kernel(const FwdArgs a) {
+__global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs a) {
   constexpr int CH = CCONV_FWD_CHUNK;  // rows per unrolled chunk; a multiple of the 4-slot ring
+  static_assert(CH % 4 == 0, "chunks must keep the ring slot of a row fixed");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -179,8 +248,8 @@ conv1d_fwd_kernel(const FwdArgs a) {
   const int64_t dend = data_end<MODE>(a.seq, a.rows);
   const bool has_pool = a.pool.ptr != nullptr;
 
-  int64_t ta = (int64_t)rb * kFwdRows;
-  int64_t tb = ta + kFwdRows;
+  int64_t ta = (int64_t)rb * a.range_rows;
+  int64_t tb = ta + a.range_rows;
   if (has_pool) {
     ta = owner_boundary<MODE>(a.seq, ta, dend);
     tb = owner_boundary<MODE>(a.seq, tb, dend);
@@ -192,107 +261,75 @@ conv1d_fwd_kernel(const FwdArgs a) {
   float wk[4][CPL], bias[CPL];
   load_taps<CPL>(a.w, a.w_f32, a.b, a.b_f32, c0, C, wk, bias);
 
-  float u[4][CPL];  // ring of the extended sequence: row q lives in slot (q - run start) mod 4
-  SeqDesc sd = seq_of_row<MODE>(a.seq, ta, dend, tb);
-  int64_t t = ta;
-  bool first = true;
-  while (true) {
-    const int64_t dist = first ? (t - sd.s < 3 ? t - sd.s : 3) : 0;
-    int32_t slot = -1;
-    bool sentinel = false;
-    if constexpr (MODE != MODE_IDX) {
-      if (has_pool) {
-        slot = a.pool.cache_indices[sd.idx];
-        sentinel = !(slot >= 0 && slot < a.pool.slots);  // -1 (other values are out of contract)
-      }
-    }
-    const int64_t run_end = sd.e < tb ? sd.e : tb;
-    if (sentinel) {
-      // -1 slot: +0 output, no state access, no input read
-      const Pk<CPL> zero = zero_pk<CPL>();
-      if (active)
-        for (int64_t q = t; q < run_end; ++q) store_row<CPL, VEC, true>(a.y + q * a.y_ld, c0, C, zero);
-    } else {
-      float h[3][CPL];
-      if constexpr (MODE != MODE_IDX) {
-        load_history<CPL, VEC>(a.pool, a.hist, dist < 3 ? sd.idx : -1, slot, true, c0, C, active, h);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 3; ++j)
-#pragma unroll
-          for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
-      }
-      // window rows t-3, t-2, t-1 -> ring slots 1, 2, 3: the history, then the last `dist`
-      // input rows of the same sequence shifted in (dist > 0 only on the first run; those rows
-      // were just streamed by the neighbouring row range on this XCD, so they come from L2)
-      for (int64_t k = 3 - dist; k < 3; ++k) {
-        Pk<CPL> p = zero_pk<CPL>();
-        if (active) p = load_row<CPL, VEC>(a.x + (t - 3 + k) * a.x_ld, c0, C);
-        shift_in<CPL>(h, p);
-      }
-#pragma unroll
-      for (int j = 0; j < 3; ++j)
-#pragma unroll
-        for (int ch = 0; ch < CPL; ++ch) u[j + 1][ch] = h[j][ch];
-      if constexpr (MODE != MODE_IDX) {
-        // at the sequence's first row dist == 0, so h still holds the untouched history
-        if (has_pool && t == sd.s && sd.e > sd.s) pool_writeback<CPL, VEC>(a, slot, sd, h, c0, active);
-      }
+  // full chunks are software-pipelined over the whole range; lanes past the last channel only
+  // occur in the last wave of a strip, which takes the predicated path for everything
+  const int nfull = (full && CCONV_FWD_PIPELINE) ? (int)((tb - ta) / CH) : 0;
+  const int64_t qlast = ta + (int64_t)nfull * CH - 1;
+  int64_t q0 = ta;
+  Pk<CPL> A[CH], B[CH];
+  if (nfull > 0) load_chunk<CPL, VEC, CH>(A, a.x, a.x_ld, q0, qlast, c0, C);  // in flight during the set-up
 
-      // full chunks: software-pipelined, the next chunk's loads are in flight while this chunk
-      // computes and stores; lanes past the last channel only occur in the last wave of a strip,
-      // which takes the predicated tail path for everything
-      const int64_t nrun = run_end - t;
-      const int nfull = (full && CCONV_FWD_PIPELINE) ? (int)(nrun / CH) : 0;
-      int64_t q0 = t;
-      if (nfull > 0) {
-        // Two register buffers, unrolled by two chunks: chunk j+1's loads are issued before
-        // chunk j's stores, so waiting for a chunk's data never waits for the stores issued
-        // before it (the vector memory counter is in order).  The next chunk's loads are issued
-        // unconditionally; past the last full chunk they re-read the last row (a cache hit), so
-        // every path back to the loop head carries the same outstanding loads and the compiler's
-        // wait counts stay exact.
-        const int64_t qlast = t + (int64_t)nfull * CH - 1;
-        Pk<CPL> A[CH], B[CH];
-        load_chunk<CPL, VEC, CH>(A, a.x, a.x_ld, q0, qlast, c0, C);
-        for (int j = 0;; j += 2, q0 += 2 * CH) {
-          load_chunk<CPL, VEC, CH>(B, a.x, a.x_ld, q0 + CH, qlast, c0, C);
-          stencil_chunk<CPL, VEC, CH, SILU>(A, a.y, a.y_ld, q0, c0, C, wk, bias, u);
-          if (j + 1 >= nfull) {
-            q0 += CH;
-            break;
-          }
-          load_chunk<CPL, VEC, CH>(A, a.x, a.x_ld, q0 + 2 * CH, qlast, c0, C);
-          stencil_chunk<CPL, VEC, CH, SILU>(B, a.y, a.y_ld, q0 + CH, c0, C, wk, bias, u);
-          if (j + 2 >= nfull) {
-            q0 += 2 * CH;
-            break;
-          }
-        }
+  // the sequence holding row ta and the window rows ta-3 .. ta-1
+  FwdSeq cs;
+  cs.sd = seq_of_row<MODE>(a.seq, ta, dend, tb);
+  const int64_t dist = ta - cs.sd.s < 3 ? ta - cs.sd.s : 3;  // window rows from the same sequence
+  float h[3][CPL];
+  Pk<CPL> wrow[3];
+  load_window<CPL, VEC>(wrow, a.x, a.x_ld, ta, dist, c0, C, active);
+  if (dist == 0) {
+    fwd_enter<CPL, VEC, MODE>(a, cs, c0, active, h);
+  } else {
+    // mid-sequence start: with a pool, range boundaries never fall on a sequence's rows 1 and 2,
+    // so dist == 3 and the slot is not touched (only its -1 status matters)
+    fwd_slot<MODE>(a, cs);
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
+    if constexpr (MODE != MODE_IDX) {
+      if (!cs.zero && dist < 3) load_history<CPL, VEC>(a.pool, a.hist, cs.sd.idx, cs.slot, true, c0, C, active, h);
+    }
+  }
+  // window rows ta-3, ta-2, ta-1 -> ring slots 1, 2, 3: the history, then the last `dist` input
+  // rows of the same sequence (the neighbouring range streamed them moments earlier on this XCD,
+  // so they come from L2)
+  shift_window<CPL>(h, wrow, dist);
+  float u[4][CPL];
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch) u[j + 1][ch] = h[j][ch];
+
+  if (nfull > 0) {
+    // Two register buffers, unrolled by two chunks: chunk j+1's loads are issued before chunk j's
+    // stores, so waiting for a chunk's data never waits for the stores issued before it (the
+    // vector memory counter is in order).  The next chunk's loads are issued unconditionally;
+    // past the last full chunk they re-read the last row (a cache hit), so every path back to the
+    // loop head carries the same outstanding loads and the compiler's wait counts stay exact.
+    for (int j = 0;; j += 2, q0 += 2 * CH) {
+      load_chunk<CPL, VEC, CH>(B, a.x, a.x_ld, q0 + CH, qlast, c0, C);
+      fwd_chunk<CPL, VEC, MODE, CH, SILU>(a, A, CH, q0, tb, dend, cs, c0, active, wk, bias, u);
+      if (j + 1 >= nfull) {
+        q0 += CH;
+        break;
       }
-      // tail (and partially active waves): rows one chunk at a time with uniform row predicates
-      for (; q0 < run_end; q0 += CH) {
-        const int n = (int)(run_end - q0 < CH ? run_end - q0 : CH);
-        Pk<CPL> xr[CH];
-#pragma unroll
-        for (int r = 0; r < CH; ++r) {
-          xr[r] = zero_pk<CPL>();
-          if (r < n && active) xr[r] = load_row<CPL, VEC, true>(a.x + (q0 + r) * a.x_ld, c0, C);
-        }
-#pragma unroll
-        for (int r = 0; r < CH; ++r) {
-          if (r < n) {
-            unpack(xr[r], u[r % 4]);
-            const Pk<CPL> out = stencil_row<CPL, SILU>(wk, bias, u, r);
-            if (active) store_row<CPL, VEC, true>(a.y + (q0 + r) * a.y_ld, c0, C, out);
-          }
-        }
+      load_chunk<CPL, VEC, CH>(A, a.x, a.x_ld, q0 + 2 * CH, qlast, c0, C);
+      fwd_chunk<CPL, VEC, MODE, CH, SILU>(a, B, CH, q0 + CH, tb, dend, cs, c0, active, wk, bias, u);
+      if (j + 2 >= nfull) {
+        q0 += 2 * CH;
+        break;
       }
     }
-    t = run_end;
-    if (t >= tb) break;
-    sd = next_seq<MODE>(a.seq, sd, dend, tb);
-    first = false;
+  }
+  // the rest (and partially active waves): one chunk at a time with uniform row predicates
+  for (; q0 < tb; q0 += CH) {
+    const int n = (int)(tb - q0 < CH ? tb - q0 : CH);
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+      A[r] = zero_pk<CPL>();
+      if (r < n && active) A[r] = load_row<CPL, VEC, true>(a.x + (q0 + r) * a.x_ld, c0, C);
+    }
+    fwd_chunk<CPL, VEC, MODE, CH, SILU>(a, A, n, q0, tb, dend, cs, c0, active, wk, bias, u);
   }
 }
 

@@ -9,18 +9,20 @@
 
 namespace cconv {
 
-// Tiling.  A block is kWavesPerBlock waves side by side in channels: lane = 8 channels, wave =
-// 512 channels, block = kBlockChannels channels of one row range.  Every wave streams the rows
-// of its range top to bottom.  The forward uses kFwdRows-row ranges; the backward kBwdRows-row
-// ranges, and writes one [5, C] FP32 dweight/dbias partial per range to the workspace.
+// Tiling.  A block is kWavesPerBlock waves side by side in channels: lane = CPL channels, wave =
+// 64*CPL channels, block = kBlockChannels channels of one row range.  Every wave streams the rows
+// of its range top to bottom, straight across sequence boundaries.  The range length is chosen
+// per launch (range_rows) so that one launch is about kFwdBlocks / kBwdBlocks blocks: with 256
+// CUs that is a single wave of resident blocks of equal work, no tail of late blocks.  The
+// backward writes one [5, C] FP32 dweight/dbias partial per range to the workspace.
 #ifndef CCONV_WAVES_PER_BLOCK
 #define CCONV_WAVES_PER_BLOCK 4
 #endif
-#ifndef CCONV_FWD_ROWS
-#define CCONV_FWD_ROWS 128
+#ifndef CCONV_FWD_BLOCKS
+#define CCONV_FWD_BLOCKS 1024
 #endif
-#ifndef CCONV_BWD_ROWS
-#define CCONV_BWD_ROWS 256
+#ifndef CCONV_BWD_BLOCKS
+#define CCONV_BWD_BLOCKS 1024
 #endif
 #ifndef CCONV_CPL
 #define CCONV_CPL 2
@@ -30,8 +32,28 @@ constexpr int kWavesPerBlock = CCONV_WAVES_PER_BLOCK;
 constexpr int kBlockThreads = 64 * kWavesPerBlock;
 constexpr int kWaveChannels = 64 * kChannelsPerLane;
 constexpr int kBlockChannels = kWavesPerBlock * kWaveChannels;
-constexpr int kFwdRows = CCONV_FWD_ROWS;
-constexpr int kBwdRows = CCONV_BWD_ROWS;
+#ifndef CCONV_FWD_FIXED_ROWS
+#define CCONV_FWD_FIXED_ROWS 0
+#endif
+#ifndef CCONV_BWD_FIXED_ROWS
+#define CCONV_BWD_FIXED_ROWS 0
+#endif
+constexpr int64_t kFwdBlocks = CCONV_FWD_BLOCKS;
+constexpr int64_t kBwdBlocks = CCONV_BWD_BLOCKS;
+constexpr int64_t kFwdFixedRows = CCONV_FWD_FIXED_ROWS;
+constexpr int64_t kBwdFixedRows = CCONV_BWD_FIXED_ROWS;
+constexpr int64_t kRangeAlign = 8;  // range lengths are multiples of 8 rows
+
+// Rows per range for `rows` rows of `n_strips` channel strips and a target block count.  A
+// positive `fixed` length overrides the target (a build-time tuning knob).
+inline int64_t range_rows_for(int64_t rows, int64_t n_strips, int64_t target_blocks, int64_t fixed = 0) {
+  if (fixed > 0) return fixed;
+  int64_t per_strip = target_blocks / (n_strips > 0 ? n_strips : 1);
+  if (per_strip < 1) per_strip = 1;
+  int64_t r = (rows + per_strip - 1) / per_strip;
+  r = (r + kRangeAlign - 1) / kRangeAlign * kRangeAlign;
+  return r > 0 ? r : kRangeAlign;
+}
 
 // How rows split into sequences: cu_seqlens offsets, per-token sequence IDs, or batch rows.
 enum { MODE_CU = 0, MODE_IDX = 1, MODE_BATCH = 2 };
@@ -65,6 +87,7 @@ struct FwdArgs {
   SeqArgs seq;
   PoolArgs pool;
   HistArgs hist;
+  int64_t range_rows;  // rows per row range
   uint32_t n_strips, n_rowblocks;
 };
 
@@ -93,6 +116,7 @@ struct BwdArgs {
   float* part;      // workspace: [n_rowblocks, 5, C] FP32 per-block partials
   float* dw;        // [C, 4]
   float* db;        // [C] or nullptr
+  int64_t range_rows;  // rows per row range
   uint32_t n_strips, n_rowblocks;
 };
 

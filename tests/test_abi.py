@@ -52,10 +52,17 @@ def test_status_strings(lib):
 def test_workspace_sizes(lib):
     assert lib.conv1d_fwd_workspace_bytes(32768, 5632, 64) == 0
     assert lib.conv1d_bwd_workspace_bytes(0, 64) == 0
-    for rows, C in ((1, 1), (16384, 5632), (16384, 4096), (1000, 13)):
+    # one FP32 partial per (row range, tap or bias, channel), rounded up to 256 bytes; the number
+    # of ranges is at least one and at most one per row, and bounded by the launch's block budget
+    for rows, C in ((1, 1), (16384, 5632), (16384, 4096), (1000, 13), (777, 3), (1 << 20, 1), (5, 100000)):
         need = lib.conv1d_bwd_workspace_bytes(rows, C)
-        slabs = -(-rows // 128)
-        assert need >= slabs * 5 * C * 4 and need % 256 == 0 and need - slabs * 5 * C * 4 < 256
+        assert need % 256 == 0
+        per_range = 5 * C * 4
+        ranges = [n for n in range(1, min(rows, 4096) + 1) if 0 <= need - n * per_range < 256]
+        assert ranges and (per_range < 256 or len(ranges) == 1), (rows, C, need)
+        n = ranges[0]
+        strips = -(-C // 512)
+        assert n * strips <= max(4096, strips), (rows, C, n)
 
 
 # ------------------------------------------------------------------ fake device buffers
