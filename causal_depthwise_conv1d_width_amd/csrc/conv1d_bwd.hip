@@ -179,7 +179,7 @@ __device__ __forceinline__ void bwd_enter(const BwdArgs& a, BwdState<CPL>& st, B
 // finish the last dx rows; it ends (done) at that sequence's end or at tb + 3.  A chunk of own
 // rows of one sequence, at least three rows past both its start and the range start, is a
 // straight recompute-and-dx; any other chunk takes the row-by-row path.
-template <int CPL, bool VEC, int MODE, int CH, bool SILU>
+template <int CPL, bool VEC, int MODE, int CH, bool SILU, bool FULL>
 __device__ __forceinline__ void bwd_chunk(const BwdArgs& a, BwdState<CPL>& st, BwdSeq& cs, const Pk<CPL> (&X)[CH],
                                           const Pk<CPL> (&G)[CH], int64_t q0, int64_t ta, int64_t tb, int64_t dend,
                                           int64_t lim, int64_t c0, bool active, bool& done) {
@@ -189,7 +189,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdArgs& a, BwdState<CPL>& st, B
       bwd_row<CPL, SILU>(st, X[r], G[r], r, true);
       float d[CPL];
       bwd_back<CPL>(st, r, d);
-      if (active) store_row<CPL, VEC, true>(a.dx + (q0 + r - 3) * a.dx_ld, c0, a.C, pack(d));
+      if (FULL || active) store_row<CPL, VEC, true>(a.dx + (q0 + r - 3) * a.dx_ld, c0, a.C, pack(d));
     }
     return;
   }
@@ -226,8 +226,17 @@ __device__ __forceinline__ void bwd_load(Pk<CPL> (&X)[CH], Pk<CPL> (&G)[CH], con
   }
 }
 
+#ifndef CCONV_BWD_WAVES_PER_EU
+#define CCONV_BWD_WAVES_PER_EU 0
+#endif
+#if CCONV_BWD_WAVES_PER_EU > 0
+#define CCONV_BWD_OCCUPANCY __attribute__((amdgpu_waves_per_eu(CCONV_BWD_WAVES_PER_EU)))
+#else
+#define CCONV_BWD_OCCUPANCY
+#endif
+
 template <int CPL, bool VEC, int MODE, bool SILU>
-__global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_kernel(const BwdArgs a) {
+__global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_kernel(const BwdArgs a) {
   constexpr int CH = CCONV_BWD_CHUNK;  // rows per unrolled chunk (a multiple of the 4-slot rings)
   static_assert(CH % 4 == 0, "chunks must keep the ring slot of a row fixed");
 
@@ -300,13 +309,13 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_kernel(const BwdArgs
       // past the last full chunk re-read its last row): see the forward kernel
       for (int j = 0;; j += 2, q0 += 2 * CH) {
         bwd_load<CPL, VEC, CH>(XB, GB, a, q0 + CH, qlast, c0);
-        bwd_chunk<CPL, VEC, MODE, CH, SILU>(a, st, cs, XA, GA, q0, ta, tb, dend, lim, c0, active, done);
+        bwd_chunk<CPL, VEC, MODE, CH, SILU, true>(a, st, cs, XA, GA, q0, ta, tb, dend, lim, c0, active, done);
         if (j + 1 >= nfull) {
           q0 += CH;
           break;
         }
         bwd_load<CPL, VEC, CH>(XA, GA, a, q0 + 2 * CH, qlast, c0);
-        bwd_chunk<CPL, VEC, MODE, CH, SILU>(a, st, cs, XB, GB, q0 + CH, ta, tb, dend, lim, c0, active, done);
+        bwd_chunk<CPL, VEC, MODE, CH, SILU, true>(a, st, cs, XB, GB, q0 + CH, ta, tb, dend, lim, c0, active, done);
         if (j + 2 >= nfull) {
           q0 += 2 * CH;
           break;
@@ -331,7 +340,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_kernel(const BwdArgs
           }
         }
       }
-      bwd_chunk<CPL, VEC, MODE, CH, SILU>(a, st, cs, XA, GA, q0, ta, tb, dend, lim, c0, active, done);
+      bwd_chunk<CPL, VEC, MODE, CH, SILU, false>(a, st, cs, XA, GA, q0, ta, tb, dend, lim, c0, active, done);
     }
   }
 

@@ -189,13 +189,13 @@ __device__ __forceinline__ void fwd_enter(const FwdArgs& a, FwdSeq& cs, int64_t 
 // mod 4 = r mod 4, as q0 - range start is a multiple of CH.  A chunk inside one sequence is a
 // straight stencil; a chunk where sequences start re-seeds the three window slots from the new
 // sequence's history right before its first row.
-template <int CPL, bool VEC, int MODE, int CH, bool SILU>
+template <int CPL, bool VEC, int MODE, int CH, bool SILU, bool FULL>
 __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)[CH], int n, int64_t q0, int64_t tb,
                                           int64_t dend, FwdSeq& cs, int64_t c0, bool active,
                                           const float (&wk)[4][CPL], const float (&bias)[CPL], float (&u)[4][CPL]) {
   if (n == CH && cs.sd.e >= q0 + CH) {
     if (cs.zero) {
-      if (active) {
+      if (FULL || active) {
 #pragma unroll
         for (int r = 0; r < CH; ++r) store_row<CPL, VEC, true>(a.y + (q0 + r) * a.y_ld, c0, a.C, zero_pk<CPL>());
       }
@@ -204,7 +204,7 @@ __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)
       for (int r = 0; r < CH; ++r) {
         unpack(buf[r], u[r % 4]);
         const Pk<CPL> out = stencil_row<CPL, SILU>(wk, bias, u, r);
-        if (active) store_row<CPL, VEC, true>(a.y + (q0 + r) * a.y_ld, c0, a.C, out);
+        if (FULL || active) store_row<CPL, VEC, true>(a.y + (q0 + r) * a.y_ld, c0, a.C, out);
       }
     }
     return;
@@ -225,7 +225,7 @@ __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)
       unpack(buf[r], u[r % 4]);
       Pk<CPL> out = zero_pk<CPL>();
       if (!cs.zero) out = stencil_row<CPL, SILU>(wk, bias, u, r);
-      if (active) store_row<CPL, VEC, true>(a.y + q * a.y_ld, c0, a.C, out);
+      if (FULL || active) store_row<CPL, VEC, true>(a.y + q * a.y_ld, c0, a.C, out);
     }
   }
 }
@@ -308,13 +308,13 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
     // loop head carries the same outstanding loads and the compiler's wait counts stay exact.
     for (int j = 0;; j += 2, q0 += 2 * CH) {
       load_chunk<CPL, VEC, CH>(B, a.x, a.x_ld, q0 + CH, qlast, c0, C);
-      fwd_chunk<CPL, VEC, MODE, CH, SILU>(a, A, CH, q0, tb, dend, cs, c0, active, wk, bias, u);
+      fwd_chunk<CPL, VEC, MODE, CH, SILU, true>(a, A, CH, q0, tb, dend, cs, c0, active, wk, bias, u);
       if (j + 1 >= nfull) {
         q0 += CH;
         break;
       }
       load_chunk<CPL, VEC, CH>(A, a.x, a.x_ld, q0 + 2 * CH, qlast, c0, C);
-      fwd_chunk<CPL, VEC, MODE, CH, SILU>(a, B, CH, q0 + CH, tb, dend, cs, c0, active, wk, bias, u);
+      fwd_chunk<CPL, VEC, MODE, CH, SILU, true>(a, B, CH, q0 + CH, tb, dend, cs, c0, active, wk, bias, u);
       if (j + 2 >= nfull) {
         q0 += 2 * CH;
         break;
@@ -329,7 +329,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
       A[r] = zero_pk<CPL>();
       if (r < n && active) A[r] = load_row<CPL, VEC, true>(a.x + (q0 + r) * a.x_ld, c0, C);
     }
-    fwd_chunk<CPL, VEC, MODE, CH, SILU>(a, A, n, q0, tb, dend, cs, c0, active, wk, bias, u);
+    fwd_chunk<CPL, VEC, MODE, CH, SILU, false>(a, A, n, q0, tb, dend, cs, c0, active, wk, bias, u);
   }
 }
 
