@@ -62,6 +62,9 @@ class Oracle:
         lib.oracle_state_update.argtypes = [_p, _i64, _i64, _i64, _p, _int, _p, _int, _p, _i64,
                                             _i64, _i64, _i64, _i64, _p, _int, _p, _i64]
         lib.oracle_state_update.restype = _int
+        lib.oracle_spec_update.argtypes = [_p, _i64, _i64, _i64, _i64, _p, _int, _p, _int, _p, _i64,
+                                           _i64, _i64, _i64, _i64, _p, _p, _int, _p, _i64]
+        lib.oracle_spec_update.restype = _int
         lib.oracle_round_double_to_bf16.argtypes = [ctypes.c_double]
         lib.oracle_round_double_to_bf16.restype = ctypes.c_uint16
         lib.oracle_round_float_to_bf16.argtypes = [ctypes.c_float]
@@ -141,6 +144,25 @@ class Oracle:
                                           _ptr(y), C)
         if rc != 0:
             raise OracleError(f"oracle_state_update rejected its input (code {rc})")
+        return y
+
+    def spec_update(self, x, w, b=None, *, pool, cache_indices, accepted=None, act="silu", fill=0x7FC1):
+        """Speculative multi-token update: x [nseq, K, C] bf16 bits, `accepted` [nseq] int32 (None =
+        all 1); returns y [nseq, K, C] and updates `pool` in place (see oracle_spec_update)."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        if x.ndim != 3:
+            raise ValueError("x must be [nseq, K, C]")
+        nseq, K, C = x.shape
+        w, wf = _taps(w, C, "weight", (C, 4))
+        b, bf = _taps(b, C, "bias", (C,))
+        pl, slots, L, ss, sc, sp = self._pool(pool, C)
+        ci = np.ascontiguousarray(cache_indices, dtype=np.int32)
+        acc = None if accepted is None else np.ascontiguousarray(accepted, dtype=np.int32)
+        y = np.full((nseq, K, C), fill, dtype=np.uint16)
+        rc = self.lib.oracle_spec_update(_ptr(x), nseq, K, C, C, _ptr(w), wf, _ptr(b), bf, _ptr(pl), slots, L,
+                                         ss, sc, sp, _ptr(ci), _ptr(acc), {"none": 0, "silu": 1}[act], _ptr(y), C)
+        if rc != 0:
+            raise OracleError(f"oracle_spec_update rejected its input (code {rc})")
         return y
 
     # ------------------------------------------------------------------ backward

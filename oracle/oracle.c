@@ -314,6 +314,68 @@ int oracle_state_update(const uint16_t* x, int64_t nseq, int64_t C, int64_t x_ld
   return OR_OK;
 }
 
+/* ================================================================ speculative multi-token update
+   Reading of flashinfer.mamba.causal_conv1d_fn, Notes (the first speculative update after a
+   prefill uses accepted count 1), stated in the design notes:
+     - a slot's positions hold raw inputs, oldest first;
+     - a step feeds K tokens x_1..x_K per sequence, and `accepted` says how many tokens of the
+       previous step were kept, so the three raw values before x_1 sit at positions a-1, a, a+1
+       (after a prefill a = 1: positions 0..2, where the prefill leaves them);
+     - y_k is the stencil over the extended sequence u = [h0, h1, h2, x_1, ..., x_K];
+     - afterwards positions 0..K+1 hold u[1..K+2], the last K + 2 raw values.  Whatever prefix a'
+       of these K tokens the next step accepts, the three values before its first token are then
+       at positions a'-1 .. a'+1.
+   Positions >= K + 2 are left alone, a -1 slot gives +0 and no state access, K = 1 with a = 1 is
+   the ordinary decode step.  Needs L >= K + 2 and 1 <= a <= L - 2 for every live sequence. */
+int oracle_spec_update(const uint16_t* x, int64_t nseq, int64_t K, int64_t C, int64_t x_ld,
+                       const void* w, int w_f32, const void* b, int b_f32, uint16_t* pool,
+                       int64_t slots, int64_t len, int64_t s_slot, int64_t s_chan, int64_t s_pos,
+                       const int32_t* cache_indices, const int32_t* accepted, int act, uint16_t* y,
+                       int64_t y_ld) {
+  if (!w || !pool || !cache_indices || C < 1 || K < 1 || x_ld < C || y_ld < C || nseq < 0 ||
+      (act != 0 && act != 1))
+    return OR_INVALID;
+  if (nseq > 0 && (!x || !y)) return OR_INVALID;
+  if (len < K + 2) return OR_INVALID;
+  ctx_t k = {pool, slots, len, s_slot, s_chan, s_pos, cache_indices, NULL, NULL, NULL};
+  if (validate_pool(&k, nseq, C) != OR_OK) return OR_INVALID;
+  for (int64_t i = 0; i < nseq; ++i) {
+    int32_t a = accepted ? accepted[i] : 1;
+    if (cache_indices[i] != -1 && (a < 1 || a > len - 2)) return OR_INVALID;
+  }
+  uint16_t* u = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(K + 3));
+  if (!u) return OR_NOMEM;
+  for (int64_t i = 0; i < nseq; ++i) {
+    int32_t slot = cache_indices[i];
+    int64_t a = accepted ? accepted[i] : 1;
+    for (int64_t c = 0; c < C; ++c) {
+      if (slot == -1) {
+        for (int64_t t = 0; t < K; ++t) y[(i * K + t) * y_ld + c] = 0;
+        continue;
+      }
+      uint16_t* h = pool + slot * s_slot + c * s_chan;
+      for (int j = 0; j < 3; ++j) u[j] = h[(a - 1 + j) * s_pos];
+      for (int64_t t = 0; t < K; ++t) u[3 + t] = x[(i * K + t) * x_ld + c];
+      for (int64_t t = 0; t < K; ++t) {
+        float z = stencil_f32(b ? load_tap(b, b_f32, c) : 0.0f, load_tap(w, w_f32, c * 4 + 0),
+                              load_tap(w, w_f32, c * 4 + 1), load_tap(w, w_f32, c * 4 + 2),
+                              load_tap(w, w_f32, c * 4 + 3), bf16_bits_to_float(u[t]),
+                              bf16_bits_to_float(u[t + 1]), bf16_bits_to_float(u[t + 2]),
+                              bf16_bits_to_float(u[t + 3]));
+        if (act == 1) {
+          double zd = (double)z;
+          y[(i * K + t) * y_ld + c] = double_to_bf16_rne(zd * sigmoid_d(zd));
+        } else {
+          y[(i * K + t) * y_ld + c] = float_to_bf16_rne(z);
+        }
+      }
+      for (int64_t j = 0; j < K + 2; ++j) h[j * s_pos] = u[j + 1];
+    }
+  }
+  free(u);
+  return OR_OK;
+}
+
 /* ================================================================ backward
    Given dy = dL/dy, produce dx = dL/dx (bf16), dw[c][k] = dL/dw (float), db[c] = dL/db (float,
    when db != NULL) and, for sequences that read caller history rows, dhist[i][j][c] = dL/dh_j

@@ -18,7 +18,7 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def oracle():
     from oracle import DEFAULT_LIB, Oracle
-    if not os.path.exists(DEFAULT_LIB):
-        from oracle.build import build
+    from oracle.build import SRC, build
+    if not os.path.exists(DEFAULT_LIB) or os.path.getmtime(DEFAULT_LIB) < os.path.getmtime(SRC):
         build()
     return Oracle()

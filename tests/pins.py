@@ -367,10 +367,99 @@ def pin_cp_fragments_backward(o, seed=21):
     _close(dw_f, dw_u, 1e-5, 1e-5, "dw over fragments")
 
 
+def _spec_setup(rng, N, K, C, L, layout, w_bf16):
+    x = wl.normal_bf16(rng, (N, K, C))
+    w = wl.to_bf16_bits(wl.uniform_f32(rng, (C, 4))) if w_bf16 else wl.uniform_f32(rng, (C, 4))
+    b = (rng.standard_normal(C) * 0.1).astype(np.float32)
+    slots = N + 3
+    pool = wl.pool_layout(wl.normal_bf16(rng, (slots, C, L)), layout)
+    ci = rng.permutation(slots)[:N].astype(np.int32)
+    if N > 1:
+        ci[1] = -1
+    acc = rng.integers(1, L - 1, size=N).astype(np.int32)  # 1 .. L-2
+    return x, w, b, pool, ci, acc
+
+
+def pin_spec_update_bruteforce(o, seed=22):
+    """Speculative K-token update (reading of the causal_conv1d_fn Notes): the K outputs of each
+    sequence are the dense Toeplitz forward of its K tokens with history rows read at pool
+    positions a-1, a, a+1; afterwards positions 0..K+1 hold the last K+2 raw values of
+    [history, tokens]; later positions, and every -1 slot, stay untouched; -1 outputs are +0."""
+    rng = np.random.default_rng(seed)
+    for layout in ("hist", "chan"):
+        for K, L, act in ((1, 3, "silu"), (2, 4, "none"), (3, 8, "silu"), (5, 7, "silu"), (4, 6, "none")):
+            N, C = 5, 7
+            x, w, b, pool, ci, acc = _spec_setup(rng, N, K, C, L, layout, w_bf16=(K % 2 == 0))
+            pool0 = pool.copy()
+            hist = np.zeros((N, 3, C), np.uint16)
+            for i in range(N):
+                if ci[i] >= 0:
+                    hist[i] = pool0[ci[i], :, acc[i] - 1:acc[i] + 2].T
+            case = dict(x=x.reshape(N * K, C), w=w, b=b, cu_seqlens=np.arange(0, N * K + 1, K, dtype=np.int32),
+                        hist=hist, has_history=np.ones(N, np.uint8), act=act)
+            _, yref, _, _ = bf.forward_f64(case)
+            yref = yref.numpy().reshape(N, K, C)
+            y = o.spec_update(x, w, b, pool=pool, cache_indices=ci, accepted=acc, act=act)
+            expect = pool0.copy()
+            for i in range(N):
+                if ci[i] < 0:
+                    assert (y[i] == 0).all(), "a -1 slot gives +0"
+                    continue
+                _close(bf.f64(y[i]), yref[i], 2.0 ** -8, 1e-5, f"spec update y (K={K}, L={L})")
+                ext = np.concatenate([hist[i], x[i]], axis=0)  # [K + 3, C] raw bits
+                expect[ci[i], :, 0:K + 2] = ext[1:].T
+            assert np.array_equal(pool, expect), f"spec update state write-back (K={K}, L={L}, {layout})"
+
+
+def pin_spec_protocol_equals_prefill(o, seed=23):
+    """Speculative decoding end to end: prefill, then steps of K tokens where each step reports how
+    many tokens of the previous step were accepted (1 for the first step after the prefill).  Every
+    step's outputs must equal the dense forward over the accepted stream so far followed by that
+    step's tokens; K = 1 steps with accepted count 1 must equal the decode step bit for bit."""
+    rng = np.random.default_rng(seed)
+    N, C, K, L = 3, 6, 4, 6
+    w = wl.uniform_f32(rng, (C, 4))
+    b = (rng.standard_normal(C) * 0.1).astype(np.float32)
+    for layout in ("hist", "chan"):
+        lengths = [int(v) for v in rng.integers(1, 6, size=N)]
+        cu = np.zeros(N + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(lengths)
+        xp = wl.normal_bf16(rng, (int(cu[-1]), C))
+        pool = wl.pool_layout(wl.normal_bf16(rng, (N + 2, C, L)), layout)
+        ci = np.array([2, 0, 3], dtype=np.int32)
+        o.fwd(xp, w, b, cu_seqlens=cu, pool=pool, cache_indices=ci, has_initial_state=np.zeros(N, np.uint8))
+        streams = [xp[cu[i]:cu[i + 1]] for i in range(N)]  # accepted raw tokens of each sequence so far
+        acc = np.ones(N, dtype=np.int32)
+        prev = None
+        for step in range(4):
+            xs = wl.normal_bf16(rng, (N, K, C))
+            if prev is not None:
+                for i in range(N):
+                    streams[i] = np.concatenate([streams[i], prev[i, :acc[i]]], axis=0)
+            y = o.spec_update(xs, w, b, pool=pool, cache_indices=ci, accepted=acc)
+            for i in range(N):
+                full = np.concatenate([streams[i], xs[i]], axis=0)
+                n = full.shape[0]
+                case = dict(x=full, w=w, b=b, cu_seqlens=np.array([0, n], np.int32), act="silu")
+                _, yref, _, _ = bf.forward_f64(case)
+                _close(bf.f64(y[i]), yref.numpy()[n - K:], 2.0 ** -8, 1e-5, f"spec protocol step {step}")
+            prev = xs
+            acc = rng.integers(1, K + 1, size=N).astype(np.int32)
+    # K = 1, accepted 1: the decode step
+    x1 = wl.normal_bf16(rng, (4, 1, C))
+    vals = wl.normal_bf16(rng, (6, C, 3))
+    ci = np.array([4, -1, 0, 2], dtype=np.int32)
+    p1, p2 = vals.copy(), vals.copy()
+    y1 = o.spec_update(x1, w, b, pool=p1, cache_indices=ci)
+    y2 = o.state_update(x1[:, 0], w, b, pool=p2, cache_indices=ci)
+    assert np.array_equal(y1[:, 0], y2) and np.array_equal(p1, p2), "K = 1 spec update == decode step"
+
+
 ALL_PINS = [pin_rounding, pin_forward_bruteforce, pin_forward_conv1d_library, pin_forward_closed_forms,
             pin_segment_invariants, pin_pool_invariants, pin_decode_equals_unit_prefill,
             pin_cp_fragments_forward, pin_backward_autograd, pin_backward_finite_differences,
-            pin_backward_linear_closed_form, pin_cp_fragments_backward]
+            pin_backward_linear_closed_form, pin_cp_fragments_backward, pin_spec_update_bruteforce,
+            pin_spec_protocol_equals_prefill]
 
 
 def golden_dyadic():

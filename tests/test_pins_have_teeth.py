@@ -33,6 +33,13 @@ MUTATIONS = {
     "pool_strides_transposed": ("return k->pool[slot * k->s_slot + c * k->s_chan + j * k->s_pos];",
                                 "return k->pool[slot * k->s_slot + c * k->s_pos + j * k->s_chan];"),
     "double_rounding_kept": ("if (r != 0.0) {", "if (0) {"),
+    "spec_history_reversed": ("u[j] = h[(a - 1 + j) * s_pos];", "u[j] = h[(a + 1 - j) * s_pos];"),
+    "spec_accepted_ignored": ("u[j] = h[(a - 1 + j) * s_pos];", "u[j] = h[j * s_pos];"),
+    "spec_writeback_unshifted": ("for (int64_t j = 0; j < K + 2; ++j) h[j * s_pos] = u[j + 1];",
+                                 "for (int64_t j = 0; j < K + 2; ++j) h[j * s_pos] = u[j];"),
+    "spec_writeback_short": ("for (int64_t j = 0; j < K + 2; ++j) h[j * s_pos] = u[j + 1];",
+                             "for (int64_t j = 0; j < K + 1; ++j) h[j * s_pos] = u[j + 1];"),
+    "spec_token_stride": ("u[3 + t] = x[(i * K + t) * x_ld + c];", "u[3 + t] = x[(i + t) * x_ld + c];"),
     "dx_mask_dropped_at_end": ("if (tau < n) acc += (double)wf[kk] * dz[tau];", "if (tau < n && tau + 1 < n) acc += (double)wf[kk] * dz[tau];"),
 }
 
