@@ -11,13 +11,14 @@ Entry points (same names as the C ABI):
                        rows, optional slot pool (conv_state, cache_indices, has_initial_state)
                        or caller history rows (history, has_history)
   conv1d_state_update  one decode step per sequence against its slot
+  conv1d_state_update_spec  K speculative tokens per sequence, history read at the accepted offset
   conv1d_bwd           dx, deterministic FP32 dweight / dbias, and d(history)
 """
 import ctypes
 
 from . import _lib
 
-__all__ = ["conv1d_fwd", "conv1d_state_update", "conv1d_bwd", "conv1d_fwd_workspace_bytes",
+__all__ = ["conv1d_fwd", "conv1d_state_update", "conv1d_state_update_spec", "conv1d_bwd", "conv1d_fwd_workspace_bytes",
            "conv1d_bwd_workspace_bytes", "library_path"]
 
 library_path = _lib.LIB_PATH
@@ -177,6 +178,45 @@ def conv1d_state_update(x, weight, bias=None, *, conv_state, cache_indices, acti
     st = lib.conv1d_state_update(xp, nseq, C, x_ld, wp, wd, bp, bd, ctypes.byref(pool), _lib.ACT[activation],
                                  yp, y_ld, _stream(stream))
     _lib.check(lib, st, "conv1d_state_update")
+    return out
+
+
+def _tokens3d(t, name, C=None):
+    """[nseq, K, C] bf16 with contiguous channels and one uniform row stride across (nseq, K)."""
+    if t.dim() != 3 or not _bits_ok(t):
+        raise ValueError(f"{name}: need a 3-D bf16 tensor [nseq, K, C]")
+    n, K, c = t.shape
+    if C is not None and c != C:
+        raise ValueError(f"{name}: expected {C} channels")
+    if n * K > 0 and c > 1 and t.stride(2) != 1:
+        raise ValueError(f"{name}: channels must be contiguous")
+    ld = t.stride(1) if K > 1 else (t.stride(0) if n > 1 else c)
+    if n > 1 and K > 1 and t.stride(0) != K * t.stride(1):
+        raise ValueError(f"{name}: tokens of consecutive sequences must be evenly spaced rows")
+    return t.data_ptr(), max(ld, c)
+
+
+def conv1d_state_update_spec(x, weight, bias=None, *, conv_state, cache_indices, num_accepted=None,
+                             activation="silu", out=None, stream=None):
+    """K speculative tokens per sequence, x [nseq, K, C]; the history is read at pool positions
+    a-1 .. a+1 for num_accepted a (int32 [nseq], None = all 1) and positions 0..K+1 are rewritten
+    in place with the last K + 2 raw values."""
+    torch = _torch()
+    lib = _lib.load()
+    nseq, K, C = x.shape
+    xp, x_ld = _tokens3d(x, "x")
+    wp, wd = _taps(weight, C, (C, 4), "weight")
+    bp, bd = _taps(bias, C, (C,), "bias")
+    pool = _pool(conv_state, cache_indices, None, C)
+    if pool is None:
+        raise ValueError("conv_state is required")
+    if out is None:
+        out = torch.empty((nseq, K, C), dtype=torch.bfloat16, device=x.device)
+    yp, y_ld = _tokens3d(out, "out", C)
+    acc = _i32(num_accepted, "num_accepted")
+    st = lib.conv1d_state_update_spec(xp, nseq, K, C, x_ld, wp, wd, bp, bd, ctypes.byref(pool), acc,
+                                      _lib.ACT[activation], yp, y_ld, _stream(stream))
+    _lib.check(lib, st, "conv1d_state_update_spec")
     return out
 
 

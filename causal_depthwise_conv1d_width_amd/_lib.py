@@ -34,6 +34,8 @@ SIGNATURES = {
                            ctypes.POINTER(Pool), ctypes.POINTER(Hist), c_int, c_p, c_i64, c_p, c_size, c_p]),
     "conv1d_state_update": (c_int, [c_p, c_i64, c_i64, c_i64, c_p, c_int, c_p, c_int, ctypes.POINTER(Pool),
                                     c_int, c_p, c_i64, c_p]),
+    "conv1d_state_update_spec": (c_int, [c_p, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_p, c_int,
+                                         ctypes.POINTER(Pool), c_p, c_int, c_p, c_i64, c_p]),
     "conv1d_bwd": (c_int, [c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_p, c_int, ctypes.POINTER(Seq),
                            ctypes.POINTER(Hist), c_int, c_p, c_i64, c_p, c_p, c_p, c_p, c_size, c_p]),
     "conv1d_fwd_workspace_bytes": (c_size, [c_i64, c_i64, c_i64]),

@@ -171,7 +171,7 @@ int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void*
   a.b_f32 = b_dtype == CONV1D_F32;
   a.seq = SeqArgs{seq->cu_seqlens, mode == MODE_BATCH ? nseq : seq->nseq, seq->seq_idx, seq->seqlen};
   if (use_pool)
-    a.pool = PoolArgs{static_cast<uint16_t*>(pool->ptr), pool->slots, pool->s_slot, pool->s_chan, pool->s_pos,
+    a.pool = PoolArgs{static_cast<uint16_t*>(pool->ptr), pool->slots, pool->len, pool->s_slot, pool->s_chan, pool->s_pos,
                       pool->cache_indices, pool->has_initial_state};
   if (use_hist) a.hist = HistArgs{static_cast<const uint16_t*>(hist->ptr), hist->has_history};
   a.range_rows = rr;
@@ -180,25 +180,31 @@ int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void*
   return launch_fwd(a, mode, vec, act == CONV1D_ACT_SILU, stream) == hipSuccess ? CONV1D_OK : CONV1D_EHIP;
 }
 
-int conv1d_state_update(const void* x, int64_t nseq, int64_t C, int64_t x_ld, const void* w, int w_dtype,
-                        const void* b, int b_dtype, const conv1d_pool* pool, int act, void* y, int64_t y_ld,
-                        hipStream_t stream) {
-  if (nseq < 0 || C < 1 || x_ld < C || y_ld < C || !w || !dtype_ok(w_dtype)) return CONV1D_EINVAL;
+// Decode and speculative update share one host path and one kernel (K = 1, all accepted = 1 is
+// the decode step).
+static int state_update_common(const void* x, int64_t nseq, int64_t K, int64_t C, int64_t x_ld, const void* w,
+                               int w_dtype, const void* b, int b_dtype, const conv1d_pool* pool,
+                               const int32_t* accepted, int act, void* y, int64_t y_ld, hipStream_t stream) {
+  if (nseq < 0 || K < 1 || C < 1 || x_ld < C || y_ld < C || !w || !dtype_ok(w_dtype)) return CONV1D_EINVAL;
   if (b && !dtype_ok(b_dtype)) return CONV1D_EINVAL;
   if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
   if (!pool || !pool->ptr) return CONV1D_EINVAL;
   if (nseq > 0 && (!x || !y)) return CONV1D_EINVAL;
+  if (nseq > INT64_MAX / K) return CONV1D_EINVAL;
   Span sp;
   if (check_pool(pool, C, nseq, &sp) != CONV1D_OK) return CONV1D_EINVAL;
-  const Span sx = span_rows(x, nseq, C, x_ld, 2), sy = span_rows(y, nseq, C, y_ld, 2);
+  if (pool->len < K + 2) return CONV1D_EINVAL;
+  const int64_t rows = nseq * K;
+  const Span sx = span_rows(x, rows, C, x_ld, 2), sy = span_rows(y, rows, C, y_ld, 2);
   const Span sw = span_bytes(w, 4 * C * dsize(w_dtype)), sb = span_bytes(b, C * dsize(b_dtype));
   const Span sci = span_bytes(pool->cache_indices, nseq * 4);
-  const Span ins[4] = {sx, sw, sb, sci};
+  const Span sacc = span_bytes(accepted, nseq * 4);
+  const Span ins[5] = {sx, sw, sb, sci, sacc};
   for (const Span& in : ins)
     if (overlap(sy, in) || overlap(sp, in)) return CONV1D_EINVAL;
   if (overlap(sy, sp)) return CONV1D_EINVAL;
   if (nseq == 0) return CONV1D_OK;
-  if ((uint64_t)nseq * ceil_div(C, 8) / 256 > 0x7fffffffull) return CONV1D_EINVAL;
+  if ((uint64_t)nseq * ceil_div(C, kChannelsPerLane) / kBlockThreads > 0x7fffffffull) return CONV1D_EINVAL;
   const bool vec = (C % 8 == 0) && (x_ld % 8 == 0) && (y_ld % 8 == 0) && aligned(x, 16) && aligned(y, 16);
   DecodeArgs a{};
   a.x = static_cast<const uint16_t*>(x);
@@ -206,14 +212,28 @@ int conv1d_state_update(const void* x, int64_t nseq, int64_t C, int64_t x_ld, co
   a.x_ld = x_ld;
   a.y_ld = y_ld;
   a.nseq = nseq;
+  a.K = K;
   a.C = C;
   a.w = w;
   a.b = b;
   a.w_f32 = w_dtype == CONV1D_F32;
   a.b_f32 = b_dtype == CONV1D_F32;
-  a.pool = PoolArgs{static_cast<uint16_t*>(pool->ptr), pool->slots, pool->s_slot, pool->s_chan, pool->s_pos,
+  a.pool = PoolArgs{static_cast<uint16_t*>(pool->ptr), pool->slots, pool->len, pool->s_slot, pool->s_chan, pool->s_pos,
                     pool->cache_indices, nullptr};
+  a.accepted = accepted;
   return launch_decode(a, vec, act == CONV1D_ACT_SILU, stream) == hipSuccess ? CONV1D_OK : CONV1D_EHIP;
+}
+
+int conv1d_state_update(const void* x, int64_t nseq, int64_t C, int64_t x_ld, const void* w, int w_dtype,
+                        const void* b, int b_dtype, const conv1d_pool* pool, int act, void* y, int64_t y_ld,
+                        hipStream_t stream) {
+  return state_update_common(x, nseq, 1, C, x_ld, w, w_dtype, b, b_dtype, pool, nullptr, act, y, y_ld, stream);
+}
+
+int conv1d_state_update_spec(const void* x, int64_t nseq, int64_t K, int64_t C, int64_t x_ld, const void* w,
+                             int w_dtype, const void* b, int b_dtype, const conv1d_pool* pool,
+                             const int32_t* num_accepted, int act, void* y, int64_t y_ld, hipStream_t stream) {
+  return state_update_common(x, nseq, K, C, x_ld, w, w_dtype, b, b_dtype, pool, num_accepted, act, y, y_ld, stream);
 }
 
 int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x_ld, int64_t dy_ld,

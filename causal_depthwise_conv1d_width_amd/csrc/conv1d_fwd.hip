@@ -333,9 +333,13 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
   }
 }
 
-// ------------------------------------------------------------------ decode kernel
-// One thread per (sequence, CPL-channel group).  y = act(b + w . [h0, h1, h2, x]), then the
-// slot's positions 0..2 become [h1, h2, x]; slot -1 gives +0 and touches nothing.
+// ------------------------------------------------------------------ decode / speculative update
+// One thread per (sequence, CPL-channel group), K tokens per sequence (K = 1: the decode step).
+// The history is pool positions a-1 .. a+1 for the sequence's accepted count a (1 without one);
+// y_t = act(b + w . window) over the extended sequence [h0, h1, h2, x_1 .. x_K]; afterwards
+// positions 0 .. K+1 hold its last K + 2 raw values.  All three history values are in registers
+// before the first write, and each thread owns its channels of the slot, so the in-place shift
+// needs no ordering between threads.
 template <int CPL, bool VEC, bool SILU>
 __global__ void __launch_bounds__(kBlockThreads) conv1d_decode_kernel(const DecodeArgs a) {
   const int64_t gid = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
@@ -343,45 +347,70 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_decode_kernel(const Deco
   if (gid >= a.nseq * groups) return;
   const int64_t i = gid / groups;
   const int64_t c0 = (gid - i * groups) * CPL;
-  const int64_t C = a.C;
+  const int64_t C = a.C, K = a.K;
   const int32_t slot = a.pool.cache_indices[i];
   if (!(slot >= 0 && slot < a.pool.slots)) {
-    store_row<CPL, VEC>(a.y + i * a.y_ld, c0, C, zero_pk<CPL>());
+    for (int64_t t = 0; t < K; ++t) store_row<CPL, VEC>(a.y + (i * K + t) * a.y_ld, c0, C, zero_pk<CPL>());
     return;
   }
+  int64_t o = a.accepted ? (int64_t)a.accepted[i] - 1 : 0;  // first history position
+  const int64_t omax = a.pool.len - 3;                       // out-of-contract counts are clamped
+  o = o < 0 ? 0 : (o > omax ? omax : o);
   float wk[4][CPL], bias[CPL];
   load_taps<CPL>(a.w, a.w_f32, a.b, a.b_f32, c0, C, wk, bias);
-  float xv[CPL];
-  unpack(load_row<CPL, VEC>(a.x + i * a.x_ld, c0, C), xv);
   uint16_t* base = a.pool.ptr + (int64_t)slot * a.pool.s_slot;
-  float out[CPL];
   uint16_t hb[3][CPL];
+  float u[3][CPL];
 #pragma unroll
   for (int ch = 0; ch < CPL; ++ch) {
     const int64_t c = c0 + ch;
-    float h[3] = {0.f, 0.f, 0.f};
-    if (c < C) {
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        hb[j][ch] = base[c * a.pool.s_chan + j * a.pool.s_pos];
-        h[j] = __uint_as_float((uint32_t)hb[j][ch] << 16);
-      }
+    for (int j = 0; j < 3; ++j) {
+      hb[j][ch] = c < C ? base[c * a.pool.s_chan + (o + j) * a.pool.s_pos] : (uint16_t)0;
+      u[j][ch] = __uint_as_float((uint32_t)hb[j][ch] << 16);
     }
-    float z = bias[ch];
-    z = __builtin_fmaf(wk[0][ch], h[0], z);
-    z = __builtin_fmaf(wk[1][ch], h[1], z);
-    z = __builtin_fmaf(wk[2][ch], h[2], z);
-    z = __builtin_fmaf(wk[3][ch], xv[ch], z);
-    out[ch] = SILU ? z * sigmoid_f32(z) : z;
   }
-  store_row<CPL, VEC>(a.y + i * a.y_ld, c0, C, pack(out));
 #pragma unroll
   for (int ch = 0; ch < CPL; ++ch) {
     const int64_t c = c0 + ch;
     if (c < C) {
-      base[c * a.pool.s_chan + 0 * a.pool.s_pos] = hb[1][ch];
-      base[c * a.pool.s_chan + 1 * a.pool.s_pos] = hb[2][ch];
-      base[c * a.pool.s_chan + 2 * a.pool.s_pos] = (uint16_t)(__float_as_uint(xv[ch]) >> 16);
+      base[c * a.pool.s_chan] = hb[1][ch];
+      base[c * a.pool.s_chan + a.pool.s_pos] = hb[2][ch];
+    }
+  }
+  // tokens in groups of four: the four row loads are issued together, one round trip per group
+  for (int64_t t0 = 0; t0 < K; t0 += 4) {
+    float xv[4][CPL];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      Pk<CPL> p = zero_pk<CPL>();
+      if (t0 + j < K) p = load_row<CPL, VEC>(a.x + (i * K + t0 + j) * a.x_ld, c0, C);
+      unpack(p, xv[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (t0 + j < K) {
+        const int64_t t = t0 + j;
+        float out[CPL];
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch) {
+          float z = bias[ch];
+          z = __builtin_fmaf(wk[0][ch], u[0][ch], z);
+          z = __builtin_fmaf(wk[1][ch], u[1][ch], z);
+          z = __builtin_fmaf(wk[2][ch], u[2][ch], z);
+          z = __builtin_fmaf(wk[3][ch], xv[j][ch], z);
+          out[ch] = SILU ? z * sigmoid_f32(z) : z;
+        }
+        store_row<CPL, VEC>(a.y + (i * K + t) * a.y_ld, c0, C, pack(out));
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch) {
+          const int64_t c = c0 + ch;
+          if (c < C) base[c * a.pool.s_chan + (t + 2) * a.pool.s_pos] = (uint16_t)(__float_as_uint(xv[j][ch]) >> 16);
+          u[0][ch] = u[1][ch];
+          u[1][ch] = u[2][ch];
+          u[2][ch] = xv[j][ch];
+        }
+      }
     }
   }
 }

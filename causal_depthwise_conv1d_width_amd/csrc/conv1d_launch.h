@@ -67,7 +67,7 @@ struct SeqArgs {
 
 struct PoolArgs {
   uint16_t* ptr;  // nullptr: no pool
-  int64_t slots, s_slot, s_chan, s_pos;
+  int64_t slots, len, s_slot, s_chan, s_pos;
   const int32_t* cache_indices;
   const uint8_t* has_init;
 };
@@ -92,14 +92,14 @@ struct FwdArgs {
 };
 
 struct DecodeArgs {
-  const uint16_t* x;
+  const uint16_t* x;  // token t of sequence i is row i*K + t
   uint16_t* y;
-  int64_t x_ld, y_ld, nseq, C;
+  int64_t x_ld, y_ld, nseq, K, C;
   const void* w;
   const void* b;
   int w_f32, b_f32;
-  PoolArgs pool;
-  uint32_t n_strips;
+  PoolArgs pool;            // pool.len >= K + 2
+  const int32_t* accepted;  // [nseq] or nullptr (all 1): history at positions a-1 .. a+1
 };
 
 struct BwdArgs {

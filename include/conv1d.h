@@ -121,6 +121,25 @@ int conv1d_state_update(const void* x, int64_t nseq, int64_t C, int64_t x_ld, co
                         int w_dtype, const void* b, int b_dtype, const conv1d_pool* pool, int act,
                         void* y, int64_t y_ld, hipStream_t stream);
 
+/* Speculative multi-token update (causal_conv1d_fn, Notes: the first speculative update after
+   a prefill uses accepted count 1).  Reading: each of nseq sequences feeds K tokens, and
+   num_accepted[i] = a tells how many tokens of the previous update were kept, so the three raw
+   history values sit at pool positions a-1, a, a+1 (a = 1 right after a prefill: positions
+   0..2, where conv1d_fwd leaves them).  Token t of sequence i is row i*K + t of x and y (bf16,
+   strides x_ld, y_ld): y = act(b + w . window) over the extended sequence [h0, h1, h2, x_1..x_K].
+   Afterwards positions 0..K+1 of the slot hold its last K + 2 raw values, so whichever prefix a'
+   of these K tokens the next update accepts finds its history at positions a'-1 .. a'+1;
+   positions >= K + 2 are untouched.  Slot -1 gives +0 and no state access.  K = 1 with every
+   a = 1 is conv1d_state_update.
+   pool: required, len >= K + 2 (its has_initial_state field is ignored: the history is always
+   read).  num_accepted: device int32 [nseq], or NULL for all 1; values must lie in [1, len - 2]
+   (device data is never read on the host: values outside are clamped into that range).
+   y must not overlap x, w, b, num_accepted or the pool.  Returns a conv1d_status. */
+int conv1d_state_update_spec(const void* x, int64_t nseq, int64_t K, int64_t C, int64_t x_ld,
+                             const void* w, int w_dtype, const void* b, int b_dtype,
+                             const conv1d_pool* pool, const int32_t* num_accepted, int act, void* y,
+                             int64_t y_ld, hipStream_t stream);
+
 /* Training backward (cake_causal_conv1d_kcp, Returns: dx and a deterministic FP32 dweight;
    causal_conv1d_cp).  Given dy = dL/dy (bf16 [rows, C], stride dy_ld), recomputes the forward
    z and writes

@@ -25,7 +25,9 @@
  *   - the FP32 accumulation is z = fma(w3,u[t], fma(w2,u[t-1], fma(w1,u[t-2], fma(w0,u[t-3], b))));
  *   - SiLU is z*sigmoid(z), evaluated in double from that FP32 z, rounded once to bf16 (RNE);
  *   - the backward is computed in double from the same FP32 z; dweight/dbias are rounded to
- *     float once at the end; dx and d(history) are rounded to bf16 (RNE) once.
+ *     float once at the end; dx and d(history) are rounded to bf16 (RNE) once;
+ *   - the speculative update (causal_conv1d_fn, Notes: accepted count 1 after a prefill) reads
+ *     its history at positions a-1 .. a+1 and leaves the last K + 2 raw values at 0 .. K+1.
  *
  * The loops below follow the definition directly: per segment, per channel, build the extended
  * sequence u = [h0, h1, h2, x[s], ..., x[e-1]] and apply the stencil.  OpenMP only splits the

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for required in ("conv1d_fwd", "conv1d_state_update", "conv1d_bwd"):
+    for required in ("conv1d_fwd", "conv1d_state_update", "conv1d_state_update_spec", "conv1d_bwd"):
         assert required in names
     assert set(names) == set(_lib.SIGNATURES), "binding signatures must cover exactly the header"
 
@@ -222,3 +222,24 @@ def test_state_update_rejects_bad_arguments(lib):
     p2 = pool_hist_layout(f, 8, C, 2)
     assert args(p2, f(8 * C * 2)) == EINVAL
     assert args(p, ctypes.c_void_p(p.ptr + 32)) == EINVAL
+
+
+def test_spec_update_rejects_bad_arguments(lib):
+    f = Fake()
+    C, n, K = 64, 8, 3
+    def call(pool, y=None, K=K, acc=None, x=None, nseq=n):
+        xp = f(nseq * K * C * 2) if x is None else x
+        yp = f(nseq * K * C * 2) if y is None else y
+        return lib.conv1d_state_update_spec(xp, nseq, K, C, C, f(C * 16), 1, None, 1,
+                                            None if pool is None else ctypes.byref(pool), acc, 1, yp, C, None)
+    assert call(None) == EINVAL                                    # pool required
+    assert call(pool_hist_layout(f, 16, C, 4)) == EINVAL           # len < K + 2
+    assert call(pool_hist_layout(f, 16, C, 5), K=0) == EINVAL      # K >= 1
+    p = pool_hist_layout(f, 16, C, 5)
+    assert call(p, y=ctypes.c_void_p(p.ptr + 64)) == EINVAL        # out overlaps the pool
+    p = pool_hist_layout(f, 16, C, 5)
+    y = f(n * K * C * 2)
+    assert call(p, y=y, acc=ctypes.c_void_p(y.value + 8)) == EINVAL  # out overlaps num_accepted
+    x = f(n * K * C * 2)
+    assert call(pool_hist_layout(f, 16, C, 5), x=x, y=ctypes.c_void_p(x.value + 2 * C * K)) == EINVAL
+    assert call(pool_hist_layout(f, 16, C, 5), nseq=-1) == EINVAL
