@@ -165,6 +165,28 @@ class Oracle:
             raise OracleError(f"oracle_spec_update rejected its input (code {rc})")
         return y
 
+    # ------------------------------------------------------------------ channels-first layout
+    # [B, D, T] with T contiguous: every (b, d) row is one sequence with zero history.  The
+    # operation is the channel-last one on the transposed array, so these wrappers transpose to
+    # [B*T, D], run the batch-row form (seqlen = T) and transpose back.
+    def fwd_cf(self, x, w, b=None, *, act="silu", nthreads=0):
+        x = np.asarray(x, dtype=np.uint16)
+        B, D, T = x.shape
+        if B * T == 0:
+            return np.zeros((B, D, T), dtype=np.uint16)
+        xl = np.ascontiguousarray(x.transpose(0, 2, 1)).reshape(B * T, D)
+        yl = self.fwd(xl, w, b, seqlen=T, act=act, nthreads=nthreads)
+        return np.ascontiguousarray(yl.reshape(B, T, D).transpose(0, 2, 1))
+
+    def bwd_cf(self, x, dy, w, b=None, *, act="silu", want_db=None, nthreads=0):
+        """(dx bits [B, D, T], dw float32 [D, 4], db float32 [D] or None)."""
+        x = np.asarray(x, dtype=np.uint16)
+        B, D, T = x.shape
+        xl = np.ascontiguousarray(x.transpose(0, 2, 1)).reshape(B * T, D)
+        dyl = np.ascontiguousarray(np.asarray(dy, dtype=np.uint16).transpose(0, 2, 1)).reshape(B * T, D)
+        dx, dw, db, _ = self.bwd(xl, dyl, w, b, seqlen=max(T, 1), act=act, want_db=want_db, nthreads=nthreads)
+        return np.ascontiguousarray(dx.reshape(B, T, D).transpose(0, 2, 1)), dw, db
+
     # ------------------------------------------------------------------ backward
     def bwd(self, x, dy, w, b=None, *, cu_seqlens=None, seq_idx=None, seqlen=None, hist=None,
             has_history=None, act="silu", want_db=None, want_dhist=None, fill=0x7FC1, nthreads=0):

@@ -455,11 +455,40 @@ def pin_spec_protocol_equals_prefill(o, seed=23):
     assert np.array_equal(y1[:, 0], y2) and np.array_equal(p1, p2), "K = 1 spec update == decode step"
 
 
+def pin_channels_first_conv1d(o, seed=24):
+    """Channels-first [B, D, T] (the layout the Megatron determinism note contrasts with channel-
+    last): each (b, d) row is one sequence with zero history.  Forward = torch's grouped conv1d with
+    three zeros of left padding in float64, then SiLU; backward = its autograd."""
+    import torch.nn.functional as F
+    rng = np.random.default_rng(seed)
+    for B, D, T, act, w_bf16, bias in ((2, 5, 9, "silu", False, True), (3, 4, 1, "silu", True, False),
+                                       (1, 7, 13, "none", False, True), (2, 3, 2, "silu", False, False),
+                                       (2, 6, 40, "silu", True, True)):
+        x = wl.normal_bf16(rng, (B, D, T))
+        dy = wl.normal_bf16(rng, (B, D, T))
+        w = wl.to_bf16_bits(wl.uniform_f32(rng, (D, 4))) if w_bf16 else wl.uniform_f32(rng, (D, 4))
+        b = (rng.standard_normal(D) * 0.1).astype(np.float32) if bias else None
+        xt = torch.tensor(bf.f64(x), requires_grad=True)
+        wt = torch.tensor(bf.taps_f64(w), requires_grad=True)
+        bt = torch.tensor(b.astype(np.float64) if bias else np.zeros(D), requires_grad=True)
+        z = F.conv1d(F.pad(xt, (3, 0)), wt[:, None, :], bias=bt, groups=D)
+        yt = z * torch.sigmoid(z) if act == "silu" else z
+        y = o.fwd_cf(x, w, b, act=act)
+        _close(bf.f64(y), yt.detach().numpy(), 2.0 ** -8, 1e-5, "channels-first y vs grouped conv1d")
+        (yt * torch.tensor(bf.f64(dy))).sum().backward()
+        dx, dw, db = o.bwd_cf(x, dy, w, b, act=act, want_db=True)
+        _close(bf.f64(dx), xt.grad.numpy(), 2.0 ** -8, 1e-5, "channels-first dx vs autograd")
+        gw = wt.grad.numpy()
+        _close(dw, gw, 1e-5, 1e-5 * (1.0 + np.abs(gw).max()), "channels-first dw vs autograd")
+        gb = bt.grad.numpy()
+        _close(db, gb, 1e-5, 1e-5 * (1.0 + np.abs(gb).max()), "channels-first db vs autograd")
+
+
 ALL_PINS = [pin_rounding, pin_forward_bruteforce, pin_forward_conv1d_library, pin_forward_closed_forms,
             pin_segment_invariants, pin_pool_invariants, pin_decode_equals_unit_prefill,
             pin_cp_fragments_forward, pin_backward_autograd, pin_backward_finite_differences,
             pin_backward_linear_closed_form, pin_cp_fragments_backward, pin_spec_update_bruteforce,
-            pin_spec_protocol_equals_prefill]
+            pin_spec_protocol_equals_prefill, pin_channels_first_conv1d]
 
 
 def golden_dyadic():
