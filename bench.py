@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
 METRIC = "effective GB/s (fwd, bwd) of packed causal conv1d+SiLU; % of HBM peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_conv1d_bwd_kernel_cp_share.md")
-KERNEL_SOURCES = ["conv1d_device.h", "conv1d_launch.h", "conv1d_fwd.hip", "conv1d_bwd.hip", "conv1d_api.cpp"]
+KERNEL_SOURCES = ["conv1d_device.h", "conv1d_launch.h", "conv1d_fwd.hip", "conv1d_bwd.hip", "conv1d_cf.hip", "conv1d_api.cpp"]
 
 
 # ------------------------------------------------------------------ algorithmic bytes
@@ -404,6 +404,29 @@ def main():
                 nbs = 2 * 64 * K * C * 2 + 64 * C * 2 * (3 + K + 2) + 4 * C * 4 + C * 4 + 2 * 64 * 4
                 extras["spec_update_N64_K4_C5632"] = {"GBps": round(gbps(nbs, mss), 1), "us": round(1e3 * mss, 2),
                                                       "bytes": nbs}
+        # channels-first [B, D, T]: the per-token-ID training shape (4 x 4096 x 4096), one sequence per row
+        rng = np.random.default_rng(1007)
+        B, D, T = 4, 4096, 4096
+        wcf = g.taps(wl.uniform_f32(rng, (D, 4)))
+        bcf = g.taps((rng.standard_normal(D) * 0.1).astype(np.float32))
+        cfs = []
+        for _ in range(4):
+            xcf = g.bits(wl.normal_bf16(rng, (B, D, T)))
+            cfs.append(dict(x=xcf, dy=g.bits(wl.normal_bf16(rng, (B, D, T))), y=torch.empty_like(xcf),
+                            dx=torch.empty_like(xcf), dw=torch.empty((D, 4), dtype=torch.float32, device=g.dev),
+                            db=torch.empty((D,), dtype=torch.float32, device=g.dev),
+                            ws=torch.empty((g.cc.conv1d_bwd_cf_workspace_bytes(B, D),), dtype=torch.uint8,
+                                           device=g.dev)))
+        nbf = B * D * T * 2 * 2 + D * 16 + D * 4
+        nbb = B * D * T * 2 * 3 + D * 16 + D * 4 + D * 16 + D * 4
+        msf = g.ring([lambda d=d: g.cc.conv1d_fwd_cf(d["x"], wcf, bcf, out=d["y"]) for d in cfs], 40, 0, warm_ms=40)
+        msb = g.ring([lambda d=d: g.cc.conv1d_bwd_cf(d["x"], d["dy"], wcf, bcf, dx=d["dx"], dweight=d["dw"],
+                                                     dbias=d["db"], want_dbias=True, workspace=d["ws"])
+                      for d in cfs], 40, 0, warm_ms=40)
+        extras["channels_first_B4_D4096_T4096"] = {"fwd_GBps": round(gbps(nbf, msf), 1), "fwd_us": round(1e3 * msf, 2),
+                                                   "fwd_bytes": nbf, "bwd_GBps": round(gbps(nbb, msb), 1),
+                                                   "bwd_us": round(1e3 * msb, 2), "bwd_bytes": nbb}
+        del cfs
         out["workloads"] = extras
         out["step_workload"] = case["name"]
     if not args.no_cpu_baseline:

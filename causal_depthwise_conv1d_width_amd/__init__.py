@@ -13,12 +13,15 @@ Entry points (same names as the C ABI):
   conv1d_state_update  one decode step per sequence against its slot
   conv1d_state_update_spec  K speculative tokens per sequence, history read at the accepted offset
   conv1d_bwd           dx, deterministic FP32 dweight / dbias, and d(history)
+  conv1d_fwd_cf / conv1d_bwd_cf  the channels-first layout [B, D, T] (T contiguous, one sequence
+                       per (b, d) row, zero history)
 """
 import ctypes
 
 from . import _lib
 
-__all__ = ["conv1d_fwd", "conv1d_state_update", "conv1d_state_update_spec", "conv1d_bwd", "conv1d_fwd_workspace_bytes",
+__all__ = ["conv1d_fwd", "conv1d_state_update", "conv1d_state_update_spec", "conv1d_bwd", "conv1d_fwd_cf",
+           "conv1d_bwd_cf", "conv1d_bwd_cf_workspace_bytes", "conv1d_fwd_workspace_bytes",
            "conv1d_bwd_workspace_bytes", "library_path"]
 
 library_path = _lib.LIB_PATH
@@ -261,3 +264,65 @@ def conv1d_bwd(x, dy, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqle
                         _stream(stream))
     _lib.check(lib, st, "conv1d_bwd")
     return dx, dweight, (dbias if want_dbias else None), (dhistory if want_dhistory else None)
+
+
+# ------------------------------------------------------------------ channels-first [B, D, T]
+def _cf3d(t, name, shape=None):
+    if t.dim() != 3 or not _bits_ok(t):
+        raise ValueError(f"{name}: need a 3-D bf16 tensor [B, D, T]")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}")
+    if t.shape[2] > 1 and t.stride(2) != 1:
+        raise ValueError(f"{name}: the time axis must be contiguous")
+    return t.data_ptr(), t.stride(0), t.stride(1)
+
+
+def conv1d_bwd_cf_workspace_bytes(B, D):
+    return int(_lib.load().conv1d_bwd_cf_workspace_bytes(B, D))
+
+
+def conv1d_fwd_cf(x, weight, bias=None, *, activation="silu", out=None, stream=None):
+    """y = act(causal width-4 conv along T) for x [B, D, T]; every (b, d) row is one sequence."""
+    torch = _torch()
+    lib = _lib.load()
+    B, D, T = x.shape
+    xp, xsb, xsd = _cf3d(x, "x")
+    wp, wd = _taps(weight, D, (D, 4), "weight")
+    bp, bd = _taps(bias, D, (D,), "bias")
+    if out is None:
+        out = torch.empty((B, D, T), dtype=torch.bfloat16, device=x.device)
+    yp, ysb, ysd = _cf3d(out, "out", (B, D, T))
+    st = lib.conv1d_fwd_cf(xp, B, D, T, xsb, xsd, wp, wd, bp, bd, _lib.ACT[activation], yp, ysb, ysd,
+                           _stream(stream))
+    _lib.check(lib, st, "conv1d_fwd_cf")
+    return out
+
+
+def conv1d_bwd_cf(x, dy, weight, bias=None, *, activation="silu", dx=None, dweight=None, want_dbias=None,
+                  dbias=None, workspace=None, stream=None):
+    """(dx [B, D, T], dweight [D, 4] fp32, dbias [D] fp32 or None) for the channels-first layout."""
+    torch = _torch()
+    lib = _lib.load()
+    B, D, T = x.shape
+    xp, xsb, xsd = _cf3d(x, "x")
+    dyp, dysb, dysd = _cf3d(dy, "dy", (B, D, T))
+    wp, wd = _taps(weight, D, (D, 4), "weight")
+    bp, bd = _taps(bias, D, (D,), "bias")
+    dev = x.device
+    if dx is None:
+        dx = torch.empty((B, D, T), dtype=torch.bfloat16, device=dev)
+    dxp, dxsb, dxsd = _cf3d(dx, "dx", (B, D, T))
+    if dweight is None:
+        dweight = torch.empty((D, 4), dtype=torch.float32, device=dev)
+    if want_dbias is None:
+        want_dbias = bias is not None
+    if want_dbias and dbias is None:
+        dbias = torch.empty((D,), dtype=torch.float32, device=dev)
+    need = lib.conv1d_bwd_cf_workspace_bytes(B, D)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    st = lib.conv1d_bwd_cf(xp, dyp, B, D, T, xsb, xsd, dysb, dysd, wp, wd, bp, bd, _lib.ACT[activation], dxp,
+                           dxsb, dxsd, dweight.data_ptr(), dbias.data_ptr() if want_dbias else None,
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check(lib, st, "conv1d_bwd_cf")
+    return dx, dweight, (dbias if want_dbias else None)

@@ -38,6 +38,11 @@ SIGNATURES = {
                                          ctypes.POINTER(Pool), c_p, c_int, c_p, c_i64, c_p]),
     "conv1d_bwd": (c_int, [c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_p, c_int, ctypes.POINTER(Seq),
                            ctypes.POINTER(Hist), c_int, c_p, c_i64, c_p, c_p, c_p, c_p, c_size, c_p]),
+    "conv1d_fwd_cf": (c_int, [c_p, c_i64, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_p, c_int, c_int, c_p, c_i64,
+                              c_i64, c_p]),
+    "conv1d_bwd_cf": (c_int, [c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_p, c_int,
+                              c_int, c_p, c_i64, c_i64, c_p, c_p, c_p, c_size, c_p]),
+    "conv1d_bwd_cf_workspace_bytes": (c_size, [c_i64, c_i64]),
     "conv1d_fwd_workspace_bytes": (c_size, [c_i64, c_i64, c_i64]),
     "conv1d_bwd_workspace_bytes": (c_size, [c_i64, c_i64]),
     "conv1d_status_str": (ctypes.c_char_p, [c_int]),

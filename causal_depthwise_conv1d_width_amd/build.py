@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcausal_conv1d.so")
-SOURCES = ["conv1d_fwd.hip", "conv1d_bwd.hip", "conv1d_api.cpp"]
+SOURCES = ["conv1d_fwd.hip", "conv1d_bwd.hip", "conv1d_cf.hip", "conv1d_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -83,6 +83,18 @@ int check_pool(const conv1d_pool* p, int64_t C, int64_t nseq, Span* out) {
   return CONV1D_OK;
 }
 
+// Channels-first array [B, D, T]: rows (b, d) at b * sb + d * sd, T contiguous, no two rows overlapping.
+bool cf_layout_ok(int64_t B, int64_t D, int64_t T, int64_t sb, int64_t sd) {
+  if (D > 1 && sd < T) return false;
+  if (B > 1 && sb < (D - 1) * sd + T) return false;
+  return sb >= 0 && sd >= 0;
+}
+
+Span span_cf(const void* p, int64_t B, int64_t D, int64_t T, int64_t sb, int64_t sd) {
+  if (!p || B <= 0 || D <= 0 || T <= 0) return Span{};
+  return span_bytes(p, ((B - 1) * sb + (D - 1) * sd + T) * 2);
+}
+
 // ws was sized by the launcher; the partial slabs need FP32 alignment
 constexpr size_t kWsAlign = 256;
 
@@ -104,6 +116,12 @@ size_t conv1d_bwd_workspace_bytes(int64_t rows, int64_t C) {
   const int64_t rr = range_rows_for(rows, ceil_div(C, kBlockChannels), kBwdBlocks, kBwdFixedRows);
   const size_t nrb = (size_t)((rows + rr - 1) / rr);
   const size_t bytes = nrb * 5u * (size_t)C * sizeof(float);
+  return (bytes + kWsAlign - 1) / kWsAlign * kWsAlign;
+}
+
+size_t conv1d_bwd_cf_workspace_bytes(int64_t B, int64_t D) {
+  if (B <= 0 || D <= 0) return 0;
+  const size_t bytes = (size_t)B * 5u * (size_t)D * sizeof(float);
   return (bytes + kWsAlign - 1) / kWsAlign * kWsAlign;
 }
 
@@ -304,6 +322,95 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
   a.n_strips = ceil_div(C, kBlockChannels);
   a.n_rowblocks = ceil_div(rows, rr);
   return launch_bwd(a, mode, vec, act == CONV1D_ACT_SILU, stream) == hipSuccess ? CONV1D_OK : CONV1D_EHIP;
+}
+
+int conv1d_fwd_cf(const void* x, int64_t B, int64_t D, int64_t T, int64_t x_sb, int64_t x_sd, const void* w,
+                  int w_dtype, const void* b, int b_dtype, int act, void* y, int64_t y_sb, int64_t y_sd,
+                  hipStream_t stream) {
+  if (B < 0 || D < 1 || T < 0 || !w || !dtype_ok(w_dtype)) return CONV1D_EINVAL;
+  if (b && !dtype_ok(b_dtype)) return CONV1D_EINVAL;
+  if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
+  if (!cf_layout_ok(B, D, T, x_sb, x_sd) || !cf_layout_ok(B, D, T, y_sb, y_sd)) return CONV1D_EINVAL;
+  if (B * T > 0 && (!x || !y)) return CONV1D_EINVAL;
+  const Span sx = span_cf(x, B, D, T, x_sb, x_sd), sy = span_cf(y, B, D, T, y_sb, y_sd);
+  const Span sw = span_bytes(w, 4 * D * dsize(w_dtype)), sb = span_bytes(b, D * dsize(b_dtype));
+  if (overlap(sy, sx) || overlap(sy, sw) || overlap(sy, sb)) return CONV1D_EINVAL;
+  if (B * T == 0) return CONV1D_OK;
+  if ((uint64_t)(B * D + 3) / 4 > 0x7fffffffull) return CONV1D_EINVAL;
+  const bool vec = T % 8 == 0 && x_sb % 8 == 0 && x_sd % 8 == 0 && y_sb % 8 == 0 && y_sd % 8 == 0 &&
+                   aligned(x, 16) && aligned(y, 16);
+  CfArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.out = static_cast<uint16_t*>(y);
+  a.B = B;
+  a.D = D;
+  a.T = T;
+  a.x_sb = x_sb;
+  a.x_sd = x_sd;
+  a.o_sb = y_sb;
+  a.o_sd = y_sd;
+  a.w = w;
+  a.b = b;
+  a.w_f32 = w_dtype == CONV1D_F32;
+  a.b_f32 = b_dtype == CONV1D_F32;
+  return launch_fwd_cf(a, vec, act == CONV1D_ACT_SILU, stream) == hipSuccess ? CONV1D_OK : CONV1D_EHIP;
+}
+
+int conv1d_bwd_cf(const void* x, const void* dy, int64_t B, int64_t D, int64_t T, int64_t x_sb, int64_t x_sd,
+                  int64_t dy_sb, int64_t dy_sd, const void* w, int w_dtype, const void* b, int b_dtype, int act,
+                  void* dx, int64_t dx_sb, int64_t dx_sd, float* dw, float* db, void* ws, size_t ws_bytes,
+                  hipStream_t stream) {
+  if (B < 0 || D < 1 || T < 0 || !w || !dtype_ok(w_dtype) || !dw) return CONV1D_EINVAL;
+  if (b && !dtype_ok(b_dtype)) return CONV1D_EINVAL;
+  if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
+  if (!cf_layout_ok(B, D, T, x_sb, x_sd) || !cf_layout_ok(B, D, T, dy_sb, dy_sd) ||
+      !cf_layout_ok(B, D, T, dx_sb, dx_sd))
+    return CONV1D_EINVAL;
+  if (B * T > 0 && (!x || !dy || !dx)) return CONV1D_EINVAL;
+  const size_t need = conv1d_bwd_cf_workspace_bytes(B, D);
+  if (ws_bytes < need || (need > 0 && !ws)) return CONV1D_EWORKSPACE;
+  if (ws && !aligned(ws, 16)) return CONV1D_EINVAL;
+  const Span sx = span_cf(x, B, D, T, x_sb, x_sd), sdy = span_cf(dy, B, D, T, dy_sb, dy_sd);
+  const Span sdx = span_cf(dx, B, D, T, dx_sb, dx_sd);
+  const Span sw = span_bytes(w, 4 * D * dsize(w_dtype)), sb = span_bytes(b, D * dsize(b_dtype));
+  const Span sdw = span_bytes(dw, 4 * D * 4), sdb = span_bytes(db, D * 4), sws = span_bytes(ws, (int64_t)need);
+  const Span outs[4] = {sdx, sdw, sdb, sws};
+  const Span ins[4] = {sx, sdy, sw, sb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (overlap(outs[i], ins[j])) return CONV1D_EINVAL;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return CONV1D_EINVAL;
+  }
+  if ((uint64_t)(B * D + 3) / 4 > 0x7fffffffull || (uint64_t)(20 * D) / 256 > 0x7fffffffull) return CONV1D_EINVAL;
+  const bool vec = T % 8 == 0 && x_sb % 8 == 0 && x_sd % 8 == 0 && dy_sb % 8 == 0 && dy_sd % 8 == 0 &&
+                   dx_sb % 8 == 0 && dx_sd % 8 == 0 && aligned(x, 16) && aligned(dy, 16) && aligned(dx, 16);
+  CfArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.dy = static_cast<const uint16_t*>(dy);
+  a.out = static_cast<uint16_t*>(dx);
+  a.B = B;
+  a.D = D;
+  a.T = T;
+  a.x_sb = x_sb;
+  a.x_sd = x_sd;
+  a.dy_sb = dy_sb;
+  a.dy_sd = dy_sd;
+  a.o_sb = dx_sb;
+  a.o_sd = dx_sd;
+  a.w = w;
+  a.b = b;
+  a.w_f32 = w_dtype == CONV1D_F32;
+  a.b_f32 = b_dtype == CONV1D_F32;
+  a.part = static_cast<float*>(ws);
+  if (launch_bwd_cf(a, vec, act == CONV1D_ACT_SILU, stream) != hipSuccess) return CONV1D_EHIP;
+  BwdArgs r{};
+  r.C = D;
+  r.part = a.part;
+  r.dw = dw;
+  r.db = db;
+  r.n_rowblocks = (uint32_t)B;
+  return launch_reduce(r, stream) == hipSuccess ? CONV1D_OK : CONV1D_EHIP;
 }
 
 }  // extern "C"

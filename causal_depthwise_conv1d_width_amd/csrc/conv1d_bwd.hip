@@ -443,6 +443,16 @@ static hipError_t bwd_mode(const BwdArgs& a, bool vec, bool silu, hipStream_t s)
   return silu ? bwd_go<MODE, false, true>(a, s) : bwd_go<MODE, false, false>(a, s);
 }
 
+hipError_t launch_reduce(const BwdArgs& a, hipStream_t s) {
+  int64_t n_red_waves = (5 * a.C + 15) / 16;
+  const int64_t threads = n_red_waves * kWave;
+  const uint32_t rblocks = (uint32_t)((threads + kBlockThreads - 1) / kBlockThreads);
+  int64_t nz_arg = 0;
+  void* rargs[] = {const_cast<BwdArgs*>(&a), &nz_arg, &n_red_waves};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&conv1d_bwd_reduce_kernel), dim3(rblocks), dim3(kBlockThreads),
+                         rargs, 0, s);
+}
+
 hipError_t launch_bwd(const BwdArgs& a, int mode, bool vec, bool silu, hipStream_t s) {
   switch (mode) {
     case MODE_CU: return bwd_mode<MODE_CU>(a, vec, silu, s);

@@ -120,9 +120,28 @@ struct BwdArgs {
   uint32_t n_strips, n_rowblocks;
 };
 
+// Channels-first [B, D, T] (T contiguous): every (b, d) row is one sequence with zero history.
+// Forward: y = act(conv(x)).  Backward: dx, and one FP32 [5, D] dweight/dbias partial per batch
+// row in `part` ([B, 5, D]), combined by the ordered reduce.
+struct CfArgs {
+  const uint16_t* x;
+  const uint16_t* dy;  // backward only
+  uint16_t* out;       // forward: y; backward: dx
+  int64_t B, D, T;
+  int64_t x_sb, x_sd, dy_sb, dy_sd, o_sb, o_sd;
+  const void* w;
+  const void* b;
+  int w_f32, b_f32;
+  float* part;  // backward only
+};
+
 // Launchers (return hipError_t of the launch).  mode: 0 = cu_seqlens, 1 = seq_idx, 2 = batch rows.
 hipError_t launch_fwd(const FwdArgs& a, int mode, bool vec, bool silu, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, bool vec, bool silu, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, int mode, bool vec, bool silu, hipStream_t stream);
+// the ordered reduce alone: dw / db from a.part over a.n_rowblocks partials of a.C channels
+hipError_t launch_reduce(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_cf(const CfArgs& a, bool vec, bool silu, hipStream_t stream);
+hipError_t launch_bwd_cf(const CfArgs& a, bool vec, bool silu, hipStream_t stream);
 
 }  // namespace cconv

@@ -157,9 +157,30 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
                const conv1d_hist* hist, int act, void* dx, int64_t dx_ld, float* dw, float* db,
                void* dhist, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Channels-first layout [B, D, T], T contiguous (core.ssm.causal_conv1d,
+   assert_causal_conv1d_deterministic names it: there a dweight element takes one contribution
+   per batch row instead of batch * ceil(seqlen / 128)).  Every (b, d) row is one sequence with
+   zero history; the operation is the same width-4 stencil (z = b, taps 0..3, tap 3 on the current
+   step, FP32, then act).  Strides are in elements: row (b, d) starts at b * sb + d * sd; rows
+   must not overlap (sd >= T, sb >= (D - 1) * sd + T).  x, y, dy, dx: bf16.  y / dx must not
+   overlap any input.  Returns a conv1d_status. */
+int conv1d_fwd_cf(const void* x, int64_t B, int64_t D, int64_t T, int64_t x_sb, int64_t x_sd, const void* w,
+                  int w_dtype, const void* b, int b_dtype, int act, void* y, int64_t y_sb, int64_t y_sd,
+                  hipStream_t stream);
+
+/* Channels-first backward: dx [B, D, T] bf16, dw FP32 [D, 4] (required), db FP32 [D] (NULL to
+   skip).  One FP32 partial per (batch row, channel) goes to ws, and a second kernel adds the B
+   partials of each channel in a fixed order, so dw and db are bitwise reproducible.  ws: at least
+   conv1d_bwd_cf_workspace_bytes(B, D) bytes, 16-byte aligned, not overlapping any operand. */
+int conv1d_bwd_cf(const void* x, const void* dy, int64_t B, int64_t D, int64_t T, int64_t x_sb, int64_t x_sd,
+                  int64_t dy_sb, int64_t dy_sd, const void* w, int w_dtype, const void* b, int b_dtype, int act,
+                  void* dx, int64_t dx_sb, int64_t dx_sd, float* dw, float* db, void* ws, size_t ws_bytes,
+                  hipStream_t stream);
+
 /* Workspace sizes in bytes (host-only, pure functions of the capacities). */
 size_t conv1d_fwd_workspace_bytes(int64_t rows, int64_t C, int64_t nseq);
 size_t conv1d_bwd_workspace_bytes(int64_t rows, int64_t C);
+size_t conv1d_bwd_cf_workspace_bytes(int64_t B, int64_t D);
 
 /* Static description of a status code. */
 const char* conv1d_status_str(int status);

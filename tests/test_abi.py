@@ -243,3 +243,35 @@ def test_spec_update_rejects_bad_arguments(lib):
     x = f(n * K * C * 2)
     assert call(pool_hist_layout(f, 16, C, 5), x=x, y=ctypes.c_void_p(x.value + 2 * C * K)) == EINVAL
     assert call(pool_hist_layout(f, 16, C, 5), nseq=-1) == EINVAL
+
+
+def test_channels_first_rejects_bad_arguments(lib):
+    f = Fake()
+    B, D, T = 2, 16, 64
+    def fwd_cf(x=None, y=None, xs=(D * T, T), ys=(D * T, T), w=True, act=1, B=B, D=D, T=T):
+        xp = f(B * D * T * 2) if x is None else x
+        yp = f(B * D * T * 2) if y is None else y
+        return lib.conv1d_fwd_cf(xp, B, D, T, xs[0], xs[1], f(D * 16) if w else None, 1, None, 1, act, yp,
+                                 ys[0], ys[1], None)
+    assert fwd_cf(w=False) == EINVAL
+    assert fwd_cf(act=5) == EINVAL
+    assert fwd_cf(D=0) == EINVAL
+    assert fwd_cf(xs=(D * T, T - 1)) == EINVAL          # rows of one batch overlap
+    assert fwd_cf(ys=(T, T)) == EINVAL                  # batches overlap
+    x = f(B * D * T * 2)
+    assert fwd_cf(x=x, y=ctypes.c_void_p(x.value + 64)) == EINVAL  # out overlaps x
+    need = lib.conv1d_bwd_cf_workspace_bytes(B, D)
+    assert need >= B * 5 * D * 4 and need % 256 == 0
+    assert lib.conv1d_bwd_cf_workspace_bytes(0, D) == 0
+    def bwd_cf(ws_bytes=None, ws=True, dw=True, dx=None, dy=None):
+        dyp = f(B * D * T * 2) if dy is None else dy
+        dxp = f(B * D * T * 2) if dx is None else dx
+        nb = need if ws_bytes is None else ws_bytes
+        return lib.conv1d_bwd_cf(f(B * D * T * 2), dyp, B, D, T, D * T, T, D * T, T, f(D * 16), 1, None, 1, 1, dxp,
+                                 D * T, T, f(D * 16) if dw else None, None, f(need) if ws is True else ws, nb, None)
+    assert bwd_cf(ws_bytes=need - 1) == EWORKSPACE
+    assert bwd_cf(ws=None) == EWORKSPACE
+    assert bwd_cf(dw=False) == EINVAL
+    assert bwd_cf(ws=ctypes.c_void_p(f(need + 64).value + 4)) == EINVAL  # misaligned workspace
+    dy = f(B * D * T * 2)
+    assert bwd_cf(dy=dy, dx=ctypes.c_void_p(dy.value + 32)) == EINVAL  # dx overlaps dy
