@@ -274,12 +274,12 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
     Pk<CPL> XA[CH], GA[CH], XB[CH], GB[CH];
     if (nfull > 0) bwd_load<CPL, VEC, CH>(XA, GA, a, q0, qlast, c0);  // in flight during the set-up
 
-    // the sequence holding row ta and the window rows ta-3 .. ta-1
+    // the window rows ta-3 .. ta-1 and the sequence holding row ta
+    Pk<CPL> wrow[3];
+    load_window<CPL, VEC>(wrow, a.x, a.x_ld, ta, c0, C, active);
     BwdSeq cs;
     cs.sd = seq_of_row<MODE>(a.seq, ta, dend, lim);
     const int64_t dist = ta - cs.sd.s < 3 ? ta - cs.sd.s : 3;
-    Pk<CPL> wrow[3];
-    load_window<CPL, VEC>(wrow, a.x, a.x_ld, ta, dist, c0, C, active);
     float h[3][CPL];
     cs.dh = false;
     if constexpr (MODE != MODE_IDX) {

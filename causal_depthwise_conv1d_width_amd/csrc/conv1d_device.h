@@ -167,16 +167,16 @@ __device__ __forceinline__ void shift_in(float (&w)[3][CPL], const Pk<CPL>& p) {
   }
 }
 
-// Window rows t-3 .. t-1 of a run that starts `dist` rows (0..3) into its sequence: the last
-// `dist` of them are inputs of the same sequence.  Every load is issued before any is used, so
-// the halo costs one memory round trip.
+// Rows t-3 .. t-1 (those >= 0), loaded before the sequence lookup says how many of them belong
+// to t's sequence, so the lookup, these loads and the first chunk share one memory round trip;
+// shift_window keeps only the last `dist` of them.
 template <int CPL, bool VEC>
 __device__ __forceinline__ void load_window(Pk<CPL> (&p)[3], const uint16_t* __restrict__ x, int64_t ld, int64_t t,
-                                            int64_t dist, int64_t c0, int64_t C, bool active) {
+                                            int64_t c0, int64_t C, bool active) {
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     p[j] = zero_pk<CPL>();
-    if (active && j >= 3 - dist) p[j] = load_row<CPL, VEC>(x + (t - 3 + j) * ld, c0, C);
+    if (active && t - 3 + j >= 0) p[j] = load_row<CPL, VEC>(x + (t - 3 + j) * ld, c0, C);
   }
 }
 

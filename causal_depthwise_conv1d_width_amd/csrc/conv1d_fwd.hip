@@ -269,13 +269,13 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
   Pk<CPL> A[CH], B[CH];
   if (nfull > 0) load_chunk<CPL, VEC, CH>(A, a.x, a.x_ld, q0, qlast, c0, C);  // in flight during the set-up
 
-  // the sequence holding row ta and the window rows ta-3 .. ta-1
+  // the window rows ta-3 .. ta-1 and the sequence holding row ta
+  Pk<CPL> wrow[3];
+  load_window<CPL, VEC>(wrow, a.x, a.x_ld, ta, c0, C, active);
   FwdSeq cs;
   cs.sd = seq_of_row<MODE>(a.seq, ta, dend, tb);
   const int64_t dist = ta - cs.sd.s < 3 ? ta - cs.sd.s : 3;  // window rows from the same sequence
   float h[3][CPL];
-  Pk<CPL> wrow[3];
-  load_window<CPL, VEC>(wrow, a.x, a.x_ld, ta, dist, c0, C, active);
   if (dist == 0) {
     fwd_enter<CPL, VEC, MODE>(a, cs, c0, active, h);
   } else {
