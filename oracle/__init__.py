@@ -47,16 +47,23 @@ def _taps(w, C, name, shape):
     raise OracleError(f"{name}: dtype must be float32 or uint16 (bf16 bits)")
 
 
+def _width(w, C):
+    """Taps [C, W] with W in 2..4 (the width of the depthwise filter)."""
+    if w is None or w.ndim != 2 or w.shape[0] != C or not 2 <= w.shape[1] <= 4:
+        raise OracleError("weight: need taps of shape [C, W] with 2 <= W <= 4")
+    return int(w.shape[1])
+
+
 class Oracle:
     def __init__(self, path=DEFAULT_LIB):
         if not os.path.exists(path):
             raise FileNotFoundError(f"{path} missing: run `python oracle/build.py`")
         lib = ctypes.CDLL(path)
-        lib.oracle_fwd.argtypes = [_p, _i64, _i64, _i64, _p, _int, _p, _int, _p, _i64, _p, _i64,
+        lib.oracle_fwd.argtypes = [_p, _i64, _i64, _i64, _p, _int, _int, _p, _int, _p, _i64, _p, _i64,
                                    _p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _int, _p,
                                    _i64, _int]
         lib.oracle_fwd.restype = _int
-        lib.oracle_bwd.argtypes = [_p, _p, _i64, _i64, _i64, _i64, _p, _int, _p, _int, _p, _i64,
+        lib.oracle_bwd.argtypes = [_p, _p, _i64, _i64, _i64, _i64, _p, _int, _int, _p, _int, _p, _i64,
                                    _p, _i64, _p, _p, _int, _p, _i64, _p, _p, _p, _int]
         lib.oracle_bwd.restype = _int
         lib.oracle_state_update.argtypes = [_p, _i64, _i64, _i64, _p, _int, _p, _int, _p, _i64,
@@ -109,19 +116,20 @@ class Oracle:
         x = np.asarray(x)
         rows, C = x.shape
         x_ld = _row_major_2d(x, "x")
-        w, wf = _taps(w, C, "weight", (C, 4))
+        W = _width(np.asarray(w), C)
+        w, wf = _taps(w, C, "weight", (C, W))
         b, bf = _taps(b, C, "bias", (C,))
         cu, si, nseq, seqlen = self._seq(rows, cu_seqlens, seq_idx, seqlen)
         pl, slots, L, ss, sc, sp = self._pool(pool, C)
         ci = None if cache_indices is None else np.ascontiguousarray(cache_indices, dtype=np.int32)
         hi = None if has_initial_state is None else np.ascontiguousarray(has_initial_state, dtype=np.uint8)
         hh = None if has_history is None else np.ascontiguousarray(has_history, dtype=np.uint8)
-        if hist is not None and (hist.dtype != np.uint16 or not hist.flags.c_contiguous or hist.shape[1:] != (3, C)):
-            raise OracleError("hist: need contiguous uint16 [nseq, 3, C]")
+        if hist is not None and (hist.dtype != np.uint16 or not hist.flags.c_contiguous or hist.shape[1:] != (W - 1, C)):
+            raise OracleError("hist: need contiguous uint16 [nseq, W - 1, C]")
         if y is None:
             y = np.full((rows, C), fill, dtype=np.uint16)
         y_ld = _row_major_2d(y, "y")
-        rc = self.lib.oracle_fwd(_ptr(x), rows, C, x_ld, _ptr(w), wf, _ptr(b), bf, _ptr(cu), nseq,
+        rc = self.lib.oracle_fwd(_ptr(x), rows, C, x_ld, _ptr(w), wf, W, _ptr(b), bf, _ptr(cu), nseq,
                                  _ptr(si), seqlen, _ptr(pl), slots, L, ss, sc, sp, _ptr(ci),
                                  _ptr(hi), _ptr(hist), _ptr(hh), {"none": 0, "silu": 1}[act],
                                  _ptr(y), y_ld, int(nthreads))
@@ -190,13 +198,16 @@ class Oracle:
     # ------------------------------------------------------------------ backward
     def bwd(self, x, dy, w, b=None, *, cu_seqlens=None, seq_idx=None, seqlen=None, hist=None,
             has_history=None, act="silu", want_db=None, want_dhist=None, fill=0x7FC1, nthreads=0):
-        """(dx bits, dw float32 [C,4], db float32 [C] or None, dhist bits or None)."""
+        """(dx bits, dw float32 [C, W], db float32 [C] or None, dhist bits or None)."""
         x = np.asarray(x)
         dy = np.asarray(dy)
         rows, C = x.shape
         x_ld = _row_major_2d(x, "x")
         dy_ld = _row_major_2d(dy, "dy")
-        w, wf = _taps(w, C, "weight", (C, 4))
+        W = _width(np.asarray(w), C)
+        w, wf = _taps(w, C, "weight", (C, W))
+        if hist is not None and (hist.dtype != np.uint16 or not hist.flags.c_contiguous or hist.shape[1:] != (W - 1, C)):
+            raise OracleError("hist: need contiguous uint16 [nseq, W - 1, C]")
         b, bf = _taps(b, C, "bias", (C,))
         cu, si, nseq, seqlen = self._seq(rows, cu_seqlens, seq_idx, seqlen)
         hh = None if has_history is None else np.ascontiguousarray(has_history, dtype=np.uint8)
@@ -205,10 +216,10 @@ class Oracle:
         if want_dhist is None:
             want_dhist = hist is not None
         dx = np.full((rows, C), fill, dtype=np.uint16)
-        dw = np.zeros((C, 4), dtype=np.float32)
+        dw = np.zeros((C, W), dtype=np.float32)
         db = np.zeros((C,), dtype=np.float32) if want_db else None
         dhist = np.full(hist.shape, fill, dtype=np.uint16) if (want_dhist and hist is not None) else None
-        rc = self.lib.oracle_bwd(_ptr(x), _ptr(dy), rows, C, x_ld, dy_ld, _ptr(w), wf, _ptr(b), bf,
+        rc = self.lib.oracle_bwd(_ptr(x), _ptr(dy), rows, C, x_ld, dy_ld, _ptr(w), wf, W, _ptr(b), bf,
                                  _ptr(cu), nseq, _ptr(si), seqlen, _ptr(hist), _ptr(hh),
                                  {"none": 0, "silu": 1}[act], _ptr(dx), C, _ptr(dw), _ptr(db),
                                  _ptr(dhist), int(nthreads))

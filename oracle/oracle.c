@@ -151,9 +151,10 @@ typedef struct {
   int64_t slots, len, s_slot, s_chan, s_pos;
   const int32_t* cache_indices;
   const uint8_t* has_init;
-  /* caller history rows: element (i, j, c) at hist[(i*3 + j)*C + c] */
+  /* caller history rows: element (i, j, c) at hist[(i*H + j)*C + c], H = width - 1 */
   const uint16_t* hist;
   const uint8_t* has_hist;
+  int64_t H;
 } ctx_t;
 
 /* raw bits of history position j of sequence i, channel c (0 when the sequence starts from zero) */
@@ -164,7 +165,7 @@ static uint16_t history_bits(const ctx_t* k, int64_t i, int64_t c, int64_t C, in
       return k->pool[slot * k->s_slot + c * k->s_chan + j * k->s_pos];
     return 0;
   }
-  if (k->hist && (!k->has_hist || k->has_hist[i])) return k->hist[(i * 3 + j) * C + c];
+  if (k->hist && (!k->has_hist || k->has_hist[i])) return k->hist[(i * k->H + j) * C + c];
   return 0;
 }
 
@@ -204,11 +205,20 @@ static float stencil_f32(float b, float w0, float w1, float w2, float w3, float 
   return z;
 }
 
+/* the same for W taps: z = b, then tap k on u[k] (tap W-1 on the current value), k = 0..W-1 */
+static float stencil_w(float b, const float* wt, const float* u, int W) {
+  float z = b;
+  for (int kk = 0; kk < W; ++kk) z = fmaf(wt[kk], u[kk], z);
+  return z;
+}
+
 /* ================================================================ forward
    y[t][c] for every row of every segment; pool positions 0:3 of live nonempty sequences.
-   act: 0 = identity, 1 = SiLU.  Returns OR_OK / OR_INVALID / OR_NOMEM. */
+   width W (2..4): taps [C, W], W - 1 history values (caller history rows [nseq, W-1, C]); the
+   pool form is width four only.  act: 0 = identity, 1 = SiLU.  Returns OR_OK / OR_INVALID /
+   OR_NOMEM. */
 int oracle_fwd(const uint16_t* x, int64_t rows, int64_t C, int64_t x_ld, const void* w, int w_f32,
-               const void* b, int b_f32, const int32_t* cu_seqlens, int64_t nseq,
+               int width, const void* b, int b_f32, const int32_t* cu_seqlens, int64_t nseq,
                const int32_t* seq_idx, int64_t seqlen, uint16_t* pool, int64_t slots, int64_t len,
                int64_t s_slot, int64_t s_chan, int64_t s_pos, const int32_t* cache_indices,
                const uint8_t* has_init, const uint16_t* hist, const uint8_t* has_hist, int act,
@@ -216,12 +226,14 @@ int oracle_fwd(const uint16_t* x, int64_t rows, int64_t C, int64_t x_ld, const v
   if (!x && rows > 0) return OR_INVALID;
   if (!w || !y || C < 1 || x_ld < C || y_ld < C || rows < 0 || (act != 0 && act != 1))
     return OR_INVALID;
+  if (width < 2 || width > 4 || (pool && width != 4)) return OR_INVALID;
   if (pool && hist) return OR_INVALID;
   if ((pool || hist) && !cu_seqlens && seq_idx) return OR_INVALID;
+  const int W = width, H = width - 1;
   seg_t* segs = NULL;
   int64_t ns = build_segments(rows, cu_seqlens, nseq, seq_idx, seqlen, &segs);
   if (ns < 0) return OR_INVALID;
-  ctx_t k = {pool, slots, len, s_slot, s_chan, s_pos, cache_indices, has_init, hist, has_hist};
+  ctx_t k = {pool, slots, len, s_slot, s_chan, s_pos, cache_indices, has_init, hist, has_hist, H};
   if (validate_pool(&k, ns, C) != OR_OK) { free(segs); return OR_INVALID; }
   int64_t maxlen = 0;
   for (int64_t q = 0; q < ns; ++q)
@@ -239,8 +251,8 @@ int oracle_fwd(const uint16_t* x, int64_t rows, int64_t C, int64_t x_ld, const v
 #pragma omp for schedule(static)
       for (int64_t cb = 0; cb < (C + 63) / 64; ++cb) {
         for (int64_t c = cb * 64; c < C && c < cb * 64 + 64; ++c) {
-          float w0 = load_tap(w, w_f32, c * 4 + 0), w1 = load_tap(w, w_f32, c * 4 + 1);
-          float w2 = load_tap(w, w_f32, c * 4 + 2), w3 = load_tap(w, w_f32, c * 4 + 3);
+          float wt[4];
+          for (int kk = 0; kk < W; ++kk) wt[kk] = load_tap(w, w_f32, c * W + kk);
           float bias = b ? load_tap(b, b_f32, c) : 0.0f;
           for (int64_t q = 0; q < ns; ++q) {
             int64_t s = segs[q].s, n = segs[q].e - segs[q].s, i = segs[q].i;
@@ -248,12 +260,12 @@ int oracle_fwd(const uint16_t* x, int64_t rows, int64_t C, int64_t x_ld, const v
               for (int64_t t = 0; t < n; ++t) y[(s + t) * y_ld + c] = 0;
               continue;
             }
-            /* extended sequence: u[0..2] = history, u[3+t] = x[s+t] */
-            for (int j = 0; j < 3; ++j) ubits[j] = history_bits(&k, i, c, C, j);
-            for (int64_t t = 0; t < n; ++t) ubits[3 + t] = x[(s + t) * x_ld + c];
-            for (int64_t t = 0; t < n + 3; ++t) u[t] = bf16_bits_to_float(ubits[t]);
+            /* extended sequence: u[0..H-1] = history, u[H+t] = x[s+t] */
+            for (int j = 0; j < H; ++j) ubits[j] = history_bits(&k, i, c, C, j);
+            for (int64_t t = 0; t < n; ++t) ubits[H + t] = x[(s + t) * x_ld + c];
+            for (int64_t t = 0; t < n + H; ++t) u[t] = bf16_bits_to_float(ubits[t]);
             for (int64_t t = 0; t < n; ++t) {
-              float z = stencil_f32(bias, w0, w1, w2, w3, u[t], u[t + 1], u[t + 2], u[t + 3]);
+              float z = stencil_w(bias, wt, u + t, W);
               uint16_t out;
               if (act == 1) {
                 double zd = (double)z;
@@ -290,7 +302,7 @@ int oracle_state_update(const uint16_t* x, int64_t nseq, int64_t C, int64_t x_ld
                         const int32_t* cache_indices, int act, uint16_t* y, int64_t y_ld) {
   if (!w || !pool || !cache_indices || C < 1 || x_ld < C || y_ld < C || nseq < 0) return OR_INVALID;
   if (nseq > 0 && (!x || !y)) return OR_INVALID;
-  ctx_t k = {pool, slots, len, s_slot, s_chan, s_pos, cache_indices, NULL, NULL, NULL};
+  ctx_t k = {pool, slots, len, s_slot, s_chan, s_pos, cache_indices, NULL, NULL, NULL, 3};
   if (validate_pool(&k, nseq, C) != OR_OK) return OR_INVALID;
   for (int64_t i = 0; i < nseq; ++i) {
     int32_t slot = cache_indices[i];
@@ -339,7 +351,7 @@ int oracle_spec_update(const uint16_t* x, int64_t nseq, int64_t K, int64_t C, in
     return OR_INVALID;
   if (nseq > 0 && (!x || !y)) return OR_INVALID;
   if (len < K + 2) return OR_INVALID;
-  ctx_t k = {pool, slots, len, s_slot, s_chan, s_pos, cache_indices, NULL, NULL, NULL};
+  ctx_t k = {pool, slots, len, s_slot, s_chan, s_pos, cache_indices, NULL, NULL, NULL, 3};
   if (validate_pool(&k, nseq, C) != OR_OK) return OR_INVALID;
   for (int64_t i = 0; i < nseq; ++i) {
     int32_t a = accepted ? accepted[i] : 1;
@@ -381,15 +393,16 @@ int oracle_spec_update(const uint16_t* x, int64_t nseq, int64_t K, int64_t C, in
 /* ================================================================ backward
    Given dy = dL/dy, produce dx = dL/dx (bf16), dw[c][k] = dL/dw (float), db[c] = dL/db (float,
    when db != NULL) and, for sequences that read caller history rows, dhist[i][j][c] = dL/dh_j
-   (bf16).  The FP32 z of the forward is recomputed exactly; everything after it is double.
+   (bf16).  The FP32 z of the forward is recomputed exactly; everything after it is double.  With
+   W taps and H = W - 1 history values:
      dz[t]  = dy[t] * act'(z[t])           silu'(z) = s(z) * (1 + z * (1 - s(z)))
-     dx[t]  = sum_{k : t+3-k inside the segment} w_k * dz[t+3-k]
-     dw_k   = sum over segments and t of dz[t] * u[t-3+k]
+     dx[t]  = sum_{k : t+H-k inside the segment} w_k * dz[t+H-k]
+     dw_k   = sum over segments and t of dz[t] * u[t+k]      (u[H+t] = x[s+t])
      db     = sum of dz
      dh_j   = sum_{tau = 0 .. min(j, n-1)} w_{j-tau} * dz[tau]
    Rows outside every segment are not written. */
 int oracle_bwd(const uint16_t* x, const uint16_t* dy, int64_t rows, int64_t C, int64_t x_ld,
-               int64_t dy_ld, const void* w, int w_f32, const void* b, int b_f32,
+               int64_t dy_ld, const void* w, int w_f32, int width, const void* b, int b_f32,
                const int32_t* cu_seqlens, int64_t nseq, const int32_t* seq_idx, int64_t seqlen,
                const uint16_t* hist, const uint8_t* has_hist, int act, uint16_t* dx, int64_t dx_ld,
                float* dw, float* db, uint16_t* dhist, int nthreads) {
@@ -397,12 +410,14 @@ int oracle_bwd(const uint16_t* x, const uint16_t* dy, int64_t rows, int64_t C, i
   if (!w || !dw || C < 1 || x_ld < C || dy_ld < C || dx_ld < C || rows < 0 ||
       (act != 0 && act != 1))
     return OR_INVALID;
+  if (width < 2 || width > 4) return OR_INVALID;
   if (hist && !cu_seqlens && seq_idx) return OR_INVALID;
   if (dhist && !hist) return OR_INVALID;
+  const int W = width, H = width - 1;
   seg_t* segs = NULL;
   int64_t ns = build_segments(rows, cu_seqlens, nseq, seq_idx, seqlen, &segs);
   if (ns < 0) return OR_INVALID;
-  ctx_t k = {NULL, 0, 0, 0, 0, 0, NULL, NULL, hist, has_hist};
+  ctx_t k = {NULL, 0, 0, 0, 0, 0, NULL, NULL, hist, has_hist, H};
   int64_t maxlen = 0;
   for (int64_t q = 0; q < ns; ++q)
     if (segs[q].e - segs[q].s > maxlen) maxlen = segs[q].e - segs[q].s;
@@ -411,8 +426,9 @@ int oracle_bwd(const uint16_t* x, const uint16_t* dy, int64_t rows, int64_t C, i
 #pragma omp parallel
   {
     double* u = (double*)malloc(sizeof(double) * (size_t)(maxlen + 3));
+    float* uf = (float*)malloc(sizeof(float) * (size_t)(maxlen + 3));
     double* dz = (double*)malloc(sizeof(double) * (size_t)(maxlen + 1));
-    if (!u || !dz) {
+    if (!u || !uf || !dz) {
 #pragma omp atomic write
       err = 1;
     } else {
@@ -420,16 +436,16 @@ int oracle_bwd(const uint16_t* x, const uint16_t* dy, int64_t rows, int64_t C, i
       for (int64_t cb = 0; cb < (C + 63) / 64; ++cb) {
         for (int64_t c = cb * 64; c < C && c < cb * 64 + 64; ++c) {
           float wf[4];
-          for (int q = 0; q < 4; ++q) wf[q] = load_tap(w, w_f32, c * 4 + q);
+          for (int q = 0; q < W; ++q) wf[q] = load_tap(w, w_f32, c * W + q);
           float bias = b ? load_tap(b, b_f32, c) : 0.0f;
           double dw_acc[4] = {0, 0, 0, 0}, db_acc = 0;
           for (int64_t q = 0; q < ns; ++q) {
             int64_t s = segs[q].s, n = segs[q].e - segs[q].s, i = segs[q].i;
-            for (int j = 0; j < 3; ++j) u[j] = bf16_bits_to_float(history_bits(&k, i, c, C, j));
-            for (int64_t t = 0; t < n; ++t) u[3 + t] = bf16_bits_to_float(x[(s + t) * x_ld + c]);
+            for (int j = 0; j < H; ++j) u[j] = bf16_bits_to_float(history_bits(&k, i, c, C, j));
+            for (int64_t t = 0; t < n; ++t) u[H + t] = bf16_bits_to_float(x[(s + t) * x_ld + c]);
+            for (int64_t t = 0; t < n + H; ++t) uf[t] = (float)u[t];
             for (int64_t t = 0; t < n; ++t) {
-              float z = stencil_f32(bias, wf[0], wf[1], wf[2], wf[3], (float)u[t], (float)u[t + 1],
-                                    (float)u[t + 2], (float)u[t + 3]);
+              float z = stencil_w(bias, wf, uf + t, W);
               double g = bf16_bits_to_float(dy[(s + t) * dy_ld + c]);
               if (act == 1) {
                 double zd = (double)z, sg = sigmoid_d(zd);
@@ -439,37 +455,37 @@ int oracle_bwd(const uint16_t* x, const uint16_t* dy, int64_t rows, int64_t C, i
             }
             for (int64_t t = 0; t < n; ++t) {
               double acc = 0;
-              for (int kk = 0; kk < 4; ++kk) {
-                int64_t tau = t + 3 - kk;
+              for (int kk = 0; kk < W; ++kk) {
+                int64_t tau = t + H - kk;
                 if (tau < n) acc += (double)wf[kk] * dz[tau];
               }
               dx[(s + t) * dx_ld + c] = double_to_bf16_rne(acc);
             }
             for (int64_t t = 0; t < n; ++t) {
-              for (int kk = 0; kk < 4; ++kk) dw_acc[kk] += dz[t] * u[t + kk];
+              for (int kk = 0; kk < W; ++kk) dw_acc[kk] += dz[t] * u[t + kk];
               db_acc += dz[t];
             }
             if (dhist && (!has_hist || has_hist[i])) {
-              for (int j = 0; j < 3; ++j) {
+              for (int j = 0; j < H; ++j) {
                 double acc = 0;
                 for (int64_t tau = 0; tau <= j && tau < n; ++tau) acc += (double)wf[j - tau] * dz[tau];
-                dhist[(i * 3 + j) * C + c] = double_to_bf16_rne(acc);
+                dhist[(i * H + j) * C + c] = double_to_bf16_rne(acc);
               }
             }
           }
-          for (int kk = 0; kk < 4; ++kk) dw[c * 4 + kk] = (float)dw_acc[kk];
+          for (int kk = 0; kk < W; ++kk) dw[c * W + kk] = (float)dw_acc[kk];
           if (db) db[c] = (float)db_acc;
         }
       }
     }
     free(u);
+    free(uf);
     free(dz);
   }
   free(segs);
   return err ? OR_NOMEM : OR_OK;
 }
 
-/* exposed so the tests can pin the rounding helpers against closed-form cases */
 uint16_t oracle_round_double_to_bf16(double d) { return double_to_bf16_rne(d); }
 uint16_t oracle_round_float_to_bf16(float f) { return float_to_bf16_rne(f); }
 int oracle_max_threads(void) { return set_threads(0); }

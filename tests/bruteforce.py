@@ -39,10 +39,14 @@ def segments(case):
     return out
 
 
+def width(case):
+    return int(case["w"].shape[1])
+
+
 def history_rows(case, nseq):
-    """float64 [nseq, 3, C]: the three raw history values each sequence starts from."""
+    """float64 [nseq, W-1, C]: the W-1 raw history values each sequence starts from."""
     C = case["x"].shape[1]
-    H = np.zeros((nseq, 3, C))
+    H = np.zeros((nseq, width(case) - 1, C))
     pool = case.get("pool")
     if pool is not None:
         ci = case["cache_indices"]
@@ -58,13 +62,16 @@ def history_rows(case, nseq):
     return H
 
 
-def selectors(rows, segs, nseq):
-    S = np.zeros((4, rows, rows + 3 * nseq))
+def selectors(rows, segs, nseq, W=4):
+    """S[k, t, col] = 1 where tap k of output row t reads V[col]: the input row t-(W-1)+k when it
+    lies in t's segment, else the matching history row of t's sequence."""
+    h = W - 1
+    S = np.zeros((W, rows, rows + h * nseq))
     for s, e, i in segs:
         for t in range(s, e):
-            for k in range(4):
-                src = t - 3 + k
-                col = src if src >= s else rows + 3 * i + (src - s + 3)
+            for k in range(W):
+                src = t - h + k
+                col = src if src >= s else rows + h * i + (src - s + h)
                 S[k, t, col] = 1.0
     return S
 
@@ -82,9 +89,10 @@ def forward_f64(case, w=None, b=None, x=None, H=None, requires_grad=False):
         w = torch.tensor(taps_f64(case["w"]))
     if b is None:
         b = torch.tensor(taps_f64(case["b"])) if case.get("b") is not None else torch.zeros(C, dtype=torch.float64)
-    V = torch.cat([x, H.reshape(nseq * 3, C)], dim=0)
-    S = torch.tensor(selectors(rows, segs, nseq))
-    z = b[None, :] + sum(w[None, :, k] * (S[k] @ V) for k in range(4))
+    W = width(case)
+    V = torch.cat([x, H.reshape(nseq * (W - 1), C)], dim=0)
+    S = torch.tensor(selectors(rows, segs, nseq, W))
+    z = b[None, :] + sum(w[None, :, k] * (S[k] @ V) for k in range(W))
     y = z * torch.sigmoid(z) if case.get("act", "silu") == "silu" else z
     covered = np.zeros(rows, dtype=bool)
     sent = np.zeros(rows, dtype=bool)

@@ -461,17 +461,18 @@ def pin_channels_first_conv1d(o, seed=24):
     three zeros of left padding in float64, then SiLU; backward = its autograd."""
     import torch.nn.functional as F
     rng = np.random.default_rng(seed)
-    for B, D, T, act, w_bf16, bias in ((2, 5, 9, "silu", False, True), (3, 4, 1, "silu", True, False),
-                                       (1, 7, 13, "none", False, True), (2, 3, 2, "silu", False, False),
-                                       (2, 6, 40, "silu", True, True)):
+    for B, D, T, act, w_bf16, bias, W in ((2, 5, 9, "silu", False, True, 4), (3, 4, 1, "silu", True, False, 4),
+                                          (1, 7, 13, "none", False, True, 4), (2, 3, 2, "silu", False, False, 4),
+                                          (2, 6, 40, "silu", True, True, 4), (2, 5, 11, "silu", False, True, 2),
+                                          (3, 4, 17, "none", True, True, 3)):
         x = wl.normal_bf16(rng, (B, D, T))
         dy = wl.normal_bf16(rng, (B, D, T))
-        w = wl.to_bf16_bits(wl.uniform_f32(rng, (D, 4))) if w_bf16 else wl.uniform_f32(rng, (D, 4))
+        w = wl.to_bf16_bits(wl.uniform_f32(rng, (D, W))) if w_bf16 else wl.uniform_f32(rng, (D, W))
         b = (rng.standard_normal(D) * 0.1).astype(np.float32) if bias else None
         xt = torch.tensor(bf.f64(x), requires_grad=True)
         wt = torch.tensor(bf.taps_f64(w), requires_grad=True)
         bt = torch.tensor(b.astype(np.float64) if bias else np.zeros(D), requires_grad=True)
-        z = F.conv1d(F.pad(xt, (3, 0)), wt[:, None, :], bias=bt, groups=D)
+        z = F.conv1d(F.pad(xt, (W - 1, 0)), wt[:, None, :], bias=bt, groups=D)
         yt = z * torch.sigmoid(z) if act == "silu" else z
         y = o.fwd_cf(x, w, b, act=act)
         _close(bf.f64(y), yt.detach().numpy(), 2.0 ** -8, 1e-5, "channels-first y vs grouped conv1d")
@@ -484,11 +485,76 @@ def pin_channels_first_conv1d(o, seed=24):
         _close(db, gb, 1e-5, 1e-5 * (1.0 + np.abs(gb).max()), "channels-first db vs autograd")
 
 
+def _narrow(case, W, rng):
+    """The same packed problem with W taps and W-1 history rows (no pool: the pool form is width four)."""
+    C = case["x"].shape[1]
+    out = dict(case)
+    for key in ("pool", "cache_indices", "has_initial_state"):
+        out.pop(key, None)
+    w = wl.uniform_f32(rng, (C, W))
+    out["w"] = w if case["w"].dtype == np.float32 else wl.to_bf16_bits(w)
+    if case.get("hist") is not None:
+        out["hist"] = wl.normal_bf16(rng, (case["hist"].shape[0], W - 1, C))
+    return out
+
+
+def pin_width_bruteforce(o, seed=25):
+    """Widths 2 and 3 (Megatron-Core causal_conv1d_cp, Parameters weight [D, W]): forward against the
+    dense Toeplitz form with W taps and W-1 history rows, backward against its autograd."""
+    rng = np.random.default_rng(seed)
+    for W in (2, 3):
+        for q in range(8):
+            mode = "idx" if q % 4 == 3 else "cu"
+            base = wl.random_case(rng, mode=mode, with_hist=(mode == "cu" and q % 2 == 0), w_f32=bool(q % 3),
+                                  act="silu" if q % 5 else "none", force_empty=bool(q % 2))
+            case = _narrow(base, W, rng)
+            _, yref, covered, _ = bf.forward_f64(case)
+            y = _fwd(o, case)
+            _close(bf.f64(y)[covered], yref.numpy()[covered], 2.0 ** -8, 1e-5, f"W={W} y vs dense Toeplitz")
+            assert (y[~covered] == FILL).all(), "rows past the last offset untouched"
+            dx, dw, db, dh = _bwd(o, case)
+            gx, gw, gb, gH, covered = bf.grads_f64(case)
+            assert dw.shape == (case["x"].shape[1], W)
+            _close(bf.f64(dx[covered]), gx[covered], 2.0 ** -8, 1e-5, f"W={W} dx vs autograd")
+            _close(dw, gw, 1e-5, 1e-5 * (1.0 + np.abs(gw).max()), f"W={W} dw vs autograd")
+            if case.get("b") is not None:
+                _close(db, gb, 1e-5, 1e-5 * (1 + np.abs(gb).max()), f"W={W} db vs autograd")
+            if dh is not None:
+                hh = case.get("has_history")
+                for i in range(dh.shape[0]):
+                    if hh is None or hh[i]:
+                        _close(bf.f64(dh[i]), gH[i], 2.0 ** -8, 1e-5, f"W={W} dhist vs autograd")
+
+
+def pin_width_closed_forms(o, seed=26):
+    """Width 2 with taps (0, 1) passes the current value through (z = b + x); with taps (1, 0) it
+    reads the previous value, which at a sequence start is the last history row."""
+    rng = np.random.default_rng(seed)
+    C, n = 5, 7
+    x = wl.normal_bf16(rng, (n, C))
+    hist = wl.normal_bf16(rng, (1, 1, C))
+    cu = np.array([0, n], np.int32)
+    ident = np.tile(np.array([0.0, 1.0], np.float32), (C, 1))
+    y = o.fwd(x, ident, None, cu_seqlens=cu, hist=hist, act="none")
+    assert np.array_equal(y, x), "width-2 identity tap"
+    prev = np.tile(np.array([1.0, 0.0], np.float32), (C, 1))
+    y = o.fwd(x, prev, None, cu_seqlens=cu, hist=hist, act="none")
+    assert np.array_equal(y[0], hist[0, 0]) and np.array_equal(y[1:], x[:-1]), "width-2 previous-value tap"
+    with_pool_rejected = False
+    try:
+        o.fwd(x, ident, None, cu_seqlens=cu, pool=np.zeros((2, C, 4), np.uint16),
+              cache_indices=np.array([0], np.int32), act="none")
+    except Exception:
+        with_pool_rejected = True
+    assert with_pool_rejected, "the pool form is width four only"
+
+
 ALL_PINS = [pin_rounding, pin_forward_bruteforce, pin_forward_conv1d_library, pin_forward_closed_forms,
             pin_segment_invariants, pin_pool_invariants, pin_decode_equals_unit_prefill,
             pin_cp_fragments_forward, pin_backward_autograd, pin_backward_finite_differences,
             pin_backward_linear_closed_form, pin_cp_fragments_backward, pin_spec_update_bruteforce,
-            pin_spec_protocol_equals_prefill, pin_channels_first_conv1d]
+            pin_spec_protocol_equals_prefill, pin_channels_first_conv1d,
+            pin_width_bruteforce, pin_width_closed_forms]
 
 
 def golden_dyadic():

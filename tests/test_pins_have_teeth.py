@@ -14,16 +14,17 @@ from oracle import Oracle, OracleError
 from oracle.build import SRC, build
 
 MUTATIONS = {
-    "taps_reversed": ("stencil_f32(bias, w0, w1, w2, w3, u[t]", "stencil_f32(bias, w3, w2, w1, w0, u[t]"),
-    "history_order_reversed": ("ubits[j] = history_bits(&k, i, c, C, j);", "ubits[j] = history_bits(&k, i, c, C, 2 - j);"),
+    "taps_reversed": ("for (int kk = 0; kk < W; ++kk) z = fmaf(wt[kk], u[kk], z);",
+                      "for (int kk = 0; kk < W; ++kk) z = fmaf(wt[W - 1 - kk], u[kk], z);"),
+    "history_order_reversed": ("ubits[j] = history_bits(&k, i, c, C, j);", "ubits[j] = history_bits(&k, i, c, C, H - 1 - j);"),
     "bias_dropped": ("float bias = b ? load_tap(b, b_f32, c) : 0.0f;\n          for (int64_t q = 0; q < ns; ++q) {\n            int64_t s = segs[q].s, n = segs[q].e - segs[q].s, i = segs[q].i;\n            if (pool",
                      "float bias = 0.0f; (void)b_f32;\n          for (int64_t q = 0; q < ns; ++q) {\n            int64_t s = segs[q].s, n = segs[q].e - segs[q].s, i = segs[q].i;\n            if (pool"),
     "sentinel_not_zero": ("for (int64_t t = 0; t < n; ++t) y[(s + t) * y_ld + c] = 0;", "for (int64_t t = 0; t < n; ++t) y[(s + t) * y_ld + c] = 0x3F80;"),
     "writeback_off_by_one": ("= ubits[n + j];", "= ubits[n + j - 1];"),
     "silu_sign": ("out = double_to_bf16_rne(zd * sigmoid_d(zd));", "out = double_to_bf16_rne(zd * sigmoid_d(-zd));"),
     "silu_grad_sign": ("g *= sg * (1.0 + zd * (1.0 - sg));", "g *= sg * (1.0 - zd * (1.0 - sg));"),
-    "dx_index": ("int64_t tau = t + 3 - kk;", "int64_t tau = t + kk;"),
-    "dw_offset": ("dw_acc[kk] += dz[t] * u[t + kk];", "dw_acc[kk] += dz[t] * u[t + 3 - kk];"),
+    "dx_index": ("int64_t tau = t + H - kk;", "int64_t tau = t + kk;"),
+    "dw_offset": ("dw_acc[kk] += dz[t] * u[t + kk];", "dw_acc[kk] += dz[t] * u[t + H - kk];"),
     "dhist_tap": ("acc += (double)wf[j - tau] * dz[tau];", "acc += (double)wf[tau] * dz[tau];"),
     "has_init_ignored": ("if (slot >= 0 && k->has_init && k->has_init[i])", "if (slot >= 0)"),
     "seq_idx_no_reset": ("boundary = (seq_idx[t] != seq_idx[t - 1]);", "boundary = 0;"),
