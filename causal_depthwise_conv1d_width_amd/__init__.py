@@ -107,11 +107,18 @@ def _pool(conv_state, cache_indices, has_initial_state, C):
     return p
 
 
-def _hist(history, has_history, C):
+def _width(weight, C):
+    """Filter width W from taps [C, W], W in 2..4."""
+    if weight is None or weight.dim() != 2 or weight.shape[0] != C or not 2 <= weight.shape[1] <= 4:
+        raise ValueError(f"weight: need taps of shape [{C}, W] with 2 <= W <= 4")
+    return int(weight.shape[1])
+
+
+def _hist(history, has_history, C, W=4):
     if history is None:
         return None
-    if history.dim() != 3 or tuple(history.shape[1:]) != (3, C) or not history.is_contiguous() or not _bits_ok(history):
-        raise ValueError("history: need a contiguous bf16 [nseq, 3, C] tensor")
+    if history.dim() != 3 or tuple(history.shape[1:]) != (W - 1, C) or not history.is_contiguous() or not _bits_ok(history):
+        raise ValueError(f"history: need a contiguous bf16 [nseq, {W - 1}, C] tensor")
     h = _lib.Hist()
     h.ptr = history.data_ptr()
     h.has_history = _u8(has_history, "has_history")
@@ -145,11 +152,12 @@ def conv1d_fwd(x, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqlen=No
     lib = _lib.load()
     rows, C = x.shape
     xp, x_ld = _rows2d(x, "x")
-    wp, wd = _taps(weight, C, (C, 4), "weight")
+    W = _width(weight, C)
+    wp, wd = _taps(weight, C, (C, W), "weight")
     bp, bd = _taps(bias, C, (C,), "bias")
     seq, nseq = _seq(rows, cu_seqlens, seq_idx, seqlen)
     pool = _pool(conv_state, cache_indices, has_initial_state, C)
-    hist = _hist(history, has_history, C)
+    hist = _hist(history, has_history, C, W)
     if out is None:
         out = torch.empty((rows, C), dtype=torch.bfloat16, device=x.device)
     yp, y_ld = _rows2d(out, "out", C)
@@ -157,7 +165,7 @@ def conv1d_fwd(x, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqlen=No
         raise ValueError("out: must have as many rows as x")
     ws = workspace.data_ptr() if workspace is not None else None
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.conv1d_fwd(xp, rows, C, x_ld, wp, wd, bp, bd, ctypes.byref(seq), _ref(pool), _ref(hist),
+    st = lib.conv1d_fwd(xp, rows, C, x_ld, wp, wd, W, bp, bd, ctypes.byref(seq), _ref(pool), _ref(hist),
                         _lib.ACT[activation], yp, y_ld, ws, wsb, _stream(stream))
     _lib.check(lib, st, "conv1d_fwd")
     return out
@@ -226,22 +234,23 @@ def conv1d_state_update_spec(x, weight, bias=None, *, conv_state, cache_indices,
 def conv1d_bwd(x, dy, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqlen=None, history=None,
                has_history=None, activation="silu", dx=None, dweight=None, want_dbias=None, dbias=None,
                want_dhistory=None, dhistory=None, workspace=None, stream=None):
-    """Returns (dx, dweight [C,4] fp32, dbias [C] fp32 or None, dhistory [nseq,3,C] or None)."""
+    """Returns (dx, dweight [C, W] fp32, dbias [C] fp32 or None, dhistory [nseq, W-1, C] or None)."""
     torch = _torch()
     lib = _lib.load()
     rows, C = x.shape
     xp, x_ld = _rows2d(x, "x")
     dyp, dy_ld = _rows2d(dy, "dy", C)
-    wp, wd = _taps(weight, C, (C, 4), "weight")
+    W = _width(weight, C)
+    wp, wd = _taps(weight, C, (C, W), "weight")
     bp, bd = _taps(bias, C, (C,), "bias")
     seq, nseq = _seq(rows, cu_seqlens, seq_idx, seqlen)
-    hist = _hist(history, has_history, C)
+    hist = _hist(history, has_history, C, W)
     dev = x.device
     if dx is None:
         dx = torch.empty((rows, C), dtype=torch.bfloat16, device=dev)
     dxp, dx_ld = _rows2d(dx, "dx", C)
     if dweight is None:
-        dweight = torch.empty((C, 4), dtype=torch.float32, device=dev)
+        dweight = torch.empty((C, W), dtype=torch.float32, device=dev)
     if want_dbias is None:
         want_dbias = bias is not None or dbias is not None
     if want_dbias and dbias is None:
@@ -249,7 +258,7 @@ def conv1d_bwd(x, dy, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqle
     if want_dhistory is None:
         want_dhistory = history is not None or dhistory is not None
     if want_dhistory and dhistory is None:
-        dhistory = torch.empty((max(nseq, 0), 3, C), dtype=torch.bfloat16, device=dev)
+        dhistory = torch.empty((max(nseq, 0), W - 1, C), dtype=torch.bfloat16, device=dev)
     for t, name, dt in ((dweight, "dweight", torch.float32), (dbias, "dbias", torch.float32)):
         if t is not None and (t.dtype != dt or not t.is_contiguous()):
             raise ValueError(f"{name}: need a contiguous float32 tensor")
@@ -257,7 +266,7 @@ def conv1d_bwd(x, dy, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqle
         need = lib.conv1d_bwd_workspace_bytes(rows, C)
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     wsb = workspace.numel() * workspace.element_size()
-    st = lib.conv1d_bwd(xp, dyp, rows, C, x_ld, dy_ld, wp, wd, bp, bd, ctypes.byref(seq), _ref(hist),
+    st = lib.conv1d_bwd(xp, dyp, rows, C, x_ld, dy_ld, wp, wd, W, bp, bd, ctypes.byref(seq), _ref(hist),
                         _lib.ACT[activation], dxp, dx_ld, dweight.data_ptr(),
                         None if dbias is None else dbias.data_ptr(),
                         None if dhistory is None else dhistory.data_ptr(), workspace.data_ptr(), wsb,
@@ -287,12 +296,13 @@ def conv1d_fwd_cf(x, weight, bias=None, *, activation="silu", out=None, stream=N
     lib = _lib.load()
     B, D, T = x.shape
     xp, xsb, xsd = _cf3d(x, "x")
-    wp, wd = _taps(weight, D, (D, 4), "weight")
+    W = _width(weight, D)
+    wp, wd = _taps(weight, D, (D, W), "weight")
     bp, bd = _taps(bias, D, (D,), "bias")
     if out is None:
         out = torch.empty((B, D, T), dtype=torch.bfloat16, device=x.device)
     yp, ysb, ysd = _cf3d(out, "out", (B, D, T))
-    st = lib.conv1d_fwd_cf(xp, B, D, T, xsb, xsd, wp, wd, bp, bd, _lib.ACT[activation], yp, ysb, ysd,
+    st = lib.conv1d_fwd_cf(xp, B, D, T, xsb, xsd, wp, wd, W, bp, bd, _lib.ACT[activation], yp, ysb, ysd,
                            _stream(stream))
     _lib.check(lib, st, "conv1d_fwd_cf")
     return out
@@ -306,14 +316,15 @@ def conv1d_bwd_cf(x, dy, weight, bias=None, *, activation="silu", dx=None, dweig
     B, D, T = x.shape
     xp, xsb, xsd = _cf3d(x, "x")
     dyp, dysb, dysd = _cf3d(dy, "dy", (B, D, T))
-    wp, wd = _taps(weight, D, (D, 4), "weight")
+    W = _width(weight, D)
+    wp, wd = _taps(weight, D, (D, W), "weight")
     bp, bd = _taps(bias, D, (D,), "bias")
     dev = x.device
     if dx is None:
         dx = torch.empty((B, D, T), dtype=torch.bfloat16, device=dev)
     dxp, dxsb, dxsd = _cf3d(dx, "dx", (B, D, T))
     if dweight is None:
-        dweight = torch.empty((D, 4), dtype=torch.float32, device=dev)
+        dweight = torch.empty((D, W), dtype=torch.float32, device=dev)
     if want_dbias is None:
         want_dbias = bias is not None
     if want_dbias and dbias is None:
@@ -321,7 +332,7 @@ def conv1d_bwd_cf(x, dy, weight, bias=None, *, activation="silu", dx=None, dweig
     need = lib.conv1d_bwd_cf_workspace_bytes(B, D)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-    st = lib.conv1d_bwd_cf(xp, dyp, B, D, T, xsb, xsd, dysb, dysd, wp, wd, bp, bd, _lib.ACT[activation], dxp,
+    st = lib.conv1d_bwd_cf(xp, dyp, B, D, T, xsb, xsd, dysb, dysd, wp, wd, W, bp, bd, _lib.ACT[activation], dxp,
                            dxsb, dxsd, dweight.data_ptr(), dbias.data_ptr() if want_dbias else None,
                            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
     _lib.check(lib, st, "conv1d_bwd_cf")

@@ -30,17 +30,17 @@ class Hist(ctypes.Structure):
 
 # name -> (restype, argtypes); must match include/conv1d.h
 SIGNATURES = {
-    "conv1d_fwd": (c_int, [c_p, c_i64, c_i64, c_i64, c_p, c_int, c_p, c_int, ctypes.POINTER(Seq),
+    "conv1d_fwd": (c_int, [c_p, c_i64, c_i64, c_i64, c_p, c_int, c_int, c_p, c_int, ctypes.POINTER(Seq),
                            ctypes.POINTER(Pool), ctypes.POINTER(Hist), c_int, c_p, c_i64, c_p, c_size, c_p]),
     "conv1d_state_update": (c_int, [c_p, c_i64, c_i64, c_i64, c_p, c_int, c_p, c_int, ctypes.POINTER(Pool),
                                     c_int, c_p, c_i64, c_p]),
     "conv1d_state_update_spec": (c_int, [c_p, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_p, c_int,
                                          ctypes.POINTER(Pool), c_p, c_int, c_p, c_i64, c_p]),
-    "conv1d_bwd": (c_int, [c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_p, c_int, ctypes.POINTER(Seq),
+    "conv1d_bwd": (c_int, [c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_int, c_p, c_int, ctypes.POINTER(Seq),
                            ctypes.POINTER(Hist), c_int, c_p, c_i64, c_p, c_p, c_p, c_p, c_size, c_p]),
-    "conv1d_fwd_cf": (c_int, [c_p, c_i64, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_p, c_int, c_int, c_p, c_i64,
+    "conv1d_fwd_cf": (c_int, [c_p, c_i64, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_int, c_p, c_int, c_int, c_p, c_i64,
                               c_i64, c_p]),
-    "conv1d_bwd_cf": (c_int, [c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_p, c_int,
+    "conv1d_bwd_cf": (c_int, [c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_int, c_p, c_int,
                               c_int, c_p, c_i64, c_i64, c_p, c_p, c_p, c_size, c_p]),
     "conv1d_bwd_cf_workspace_bytes": (c_size, [c_i64, c_i64]),
     "conv1d_fwd_workspace_bytes": (c_size, [c_i64, c_i64, c_i64]),

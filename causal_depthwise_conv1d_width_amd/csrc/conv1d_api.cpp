@@ -136,13 +136,14 @@ const char* conv1d_status_str(int status) {
   }
 }
 
-int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void* w, int w_dtype,
+int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void* w, int w_dtype, int width,
                const void* b, int b_dtype, const conv1d_seq* seq, const conv1d_pool* pool,
                const conv1d_hist* hist, int act, void* y, int64_t y_ld, void* ws, size_t ws_bytes,
                hipStream_t stream) {
   (void)ws;
   (void)ws_bytes;
   if (rows < 0 || C < 1 || x_ld < C || y_ld < C || !w || !dtype_ok(w_dtype)) return CONV1D_EINVAL;
+  if (width < 2 || width > 4) return CONV1D_EINVAL;
   if (b && !dtype_ok(b_dtype)) return CONV1D_EINVAL;
   if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
   if (rows > 0 && (!x || !y)) return CONV1D_EINVAL;
@@ -153,12 +154,13 @@ int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void*
   const bool use_hist = hist && hist->ptr;
   if (use_pool && use_hist) return CONV1D_EINVAL;
   if ((use_pool || use_hist) && mode == MODE_IDX) return CONV1D_EINVAL;
+  if (use_pool && width != 4) return CONV1D_EINVAL;  // the pool form is width four
 
   const Span sx = span_rows(x, rows, C, x_ld, 2), sy = span_rows(y, rows, C, y_ld, 2);
-  const Span sw = span_bytes(w, 4 * C * dsize(w_dtype)), sb = span_bytes(b, C * dsize(b_dtype));
+  const Span sw = span_bytes(w, width * C * dsize(w_dtype)), sb = span_bytes(b, C * dsize(b_dtype));
   Span sp, sh;
   if (use_pool && check_pool(pool, C, nseq, &sp) != CONV1D_OK) return CONV1D_EINVAL;
-  if (use_hist) sh = span_bytes(hist->ptr, nseq * 3 * C * 2);
+  if (use_hist) sh = span_bytes(hist->ptr, nseq * (width - 1) * C * 2);
   // out must not share storage with any operand; the pool must not alias the other operands
   const Span sm = span_seq(seq, rows);
   const Span sci = use_pool ? span_bytes(pool->cache_indices, nseq * 4) : Span{};
@@ -187,6 +189,7 @@ int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void*
   a.b = b;
   a.w_f32 = w_dtype == CONV1D_F32;
   a.b_f32 = b_dtype == CONV1D_F32;
+  a.width = width;
   a.seq = SeqArgs{seq->cu_seqlens, mode == MODE_BATCH ? nseq : seq->nseq, seq->seq_idx, seq->seqlen};
   if (use_pool)
     a.pool = PoolArgs{static_cast<uint16_t*>(pool->ptr), pool->slots, pool->len, pool->s_slot, pool->s_chan, pool->s_pos,
@@ -255,11 +258,12 @@ int conv1d_state_update_spec(const void* x, int64_t nseq, int64_t K, int64_t C, 
 }
 
 int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x_ld, int64_t dy_ld,
-               const void* w, int w_dtype, const void* b, int b_dtype, const conv1d_seq* seq,
+               const void* w, int w_dtype, int width, const void* b, int b_dtype, const conv1d_seq* seq,
                const conv1d_hist* hist, int act, void* dx, int64_t dx_ld, float* dw, float* db,
                void* dhist, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (rows < 0 || C < 1 || x_ld < C || dy_ld < C || dx_ld < C || !w || !dtype_ok(w_dtype) || !dw)
     return CONV1D_EINVAL;
+  if (width < 2 || width > 4) return CONV1D_EINVAL;
   if (b && !dtype_ok(b_dtype)) return CONV1D_EINVAL;
   if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
   if (rows > 0 && (!x || !dy || !dx)) return CONV1D_EINVAL;
@@ -275,10 +279,10 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
 
   const Span sx = span_rows(x, rows, C, x_ld, 2), sdy = span_rows(dy, rows, C, dy_ld, 2);
   const Span sdx = span_rows(dx, rows, C, dx_ld, 2);
-  const Span sw = span_bytes(w, 4 * C * dsize(w_dtype)), sb = span_bytes(b, C * dsize(b_dtype));
-  const Span sdw = span_bytes(dw, 4 * C * 4), sdb = span_bytes(db, C * 4);
-  const Span sh = use_hist ? span_bytes(hist->ptr, nseq * 3 * C * 2) : Span{};
-  const Span sdh = dhist ? span_bytes(dhist, nseq * 3 * C * 2) : Span{};
+  const Span sw = span_bytes(w, width * C * dsize(w_dtype)), sb = span_bytes(b, C * dsize(b_dtype));
+  const Span sdw = span_bytes(dw, width * C * 4), sdb = span_bytes(db, C * 4);
+  const Span sh = use_hist ? span_bytes(hist->ptr, nseq * (width - 1) * C * 2) : Span{};
+  const Span sdh = dhist ? span_bytes(dhist, nseq * (width - 1) * C * 2) : Span{};
   const Span sws = span_bytes(ws, (int64_t)need);
   const Span sm = span_seq(seq, rows);
   const Span shh = use_hist ? span_bytes(hist->has_history, nseq) : Span{};
@@ -312,6 +316,7 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
   a.b = b;
   a.w_f32 = w_dtype == CONV1D_F32;
   a.b_f32 = b_dtype == CONV1D_F32;
+  a.width = width;
   a.seq = SeqArgs{seq->cu_seqlens, mode == MODE_BATCH ? nseq : seq->nseq, seq->seq_idx, seq->seqlen};
   if (use_hist) a.hist = HistArgs{static_cast<const uint16_t*>(hist->ptr), hist->has_history};
   a.dhist = static_cast<uint16_t*>(dhist);
@@ -325,15 +330,15 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
 }
 
 int conv1d_fwd_cf(const void* x, int64_t B, int64_t D, int64_t T, int64_t x_sb, int64_t x_sd, const void* w,
-                  int w_dtype, const void* b, int b_dtype, int act, void* y, int64_t y_sb, int64_t y_sd,
+                  int w_dtype, int width, const void* b, int b_dtype, int act, void* y, int64_t y_sb, int64_t y_sd,
                   hipStream_t stream) {
-  if (B < 0 || D < 1 || T < 0 || !w || !dtype_ok(w_dtype)) return CONV1D_EINVAL;
+  if (B < 0 || D < 1 || T < 0 || !w || !dtype_ok(w_dtype) || width < 2 || width > 4) return CONV1D_EINVAL;
   if (b && !dtype_ok(b_dtype)) return CONV1D_EINVAL;
   if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
   if (!cf_layout_ok(B, D, T, x_sb, x_sd) || !cf_layout_ok(B, D, T, y_sb, y_sd)) return CONV1D_EINVAL;
   if (B * T > 0 && (!x || !y)) return CONV1D_EINVAL;
   const Span sx = span_cf(x, B, D, T, x_sb, x_sd), sy = span_cf(y, B, D, T, y_sb, y_sd);
-  const Span sw = span_bytes(w, 4 * D * dsize(w_dtype)), sb = span_bytes(b, D * dsize(b_dtype));
+  const Span sw = span_bytes(w, width * D * dsize(w_dtype)), sb = span_bytes(b, D * dsize(b_dtype));
   if (overlap(sy, sx) || overlap(sy, sw) || overlap(sy, sb)) return CONV1D_EINVAL;
   if (B * T == 0) return CONV1D_OK;
   if ((uint64_t)(B * D + 3) / 4 > 0x7fffffffull) return CONV1D_EINVAL;
@@ -353,14 +358,15 @@ int conv1d_fwd_cf(const void* x, int64_t B, int64_t D, int64_t T, int64_t x_sb, 
   a.b = b;
   a.w_f32 = w_dtype == CONV1D_F32;
   a.b_f32 = b_dtype == CONV1D_F32;
+  a.width = width;
   return launch_fwd_cf(a, vec, act == CONV1D_ACT_SILU, stream) == hipSuccess ? CONV1D_OK : CONV1D_EHIP;
 }
 
 int conv1d_bwd_cf(const void* x, const void* dy, int64_t B, int64_t D, int64_t T, int64_t x_sb, int64_t x_sd,
-                  int64_t dy_sb, int64_t dy_sd, const void* w, int w_dtype, const void* b, int b_dtype, int act,
-                  void* dx, int64_t dx_sb, int64_t dx_sd, float* dw, float* db, void* ws, size_t ws_bytes,
+                  int64_t dy_sb, int64_t dy_sd, const void* w, int w_dtype, int width, const void* b, int b_dtype,
+                  int act, void* dx, int64_t dx_sb, int64_t dx_sd, float* dw, float* db, void* ws, size_t ws_bytes,
                   hipStream_t stream) {
-  if (B < 0 || D < 1 || T < 0 || !w || !dtype_ok(w_dtype) || !dw) return CONV1D_EINVAL;
+  if (B < 0 || D < 1 || T < 0 || !w || !dtype_ok(w_dtype) || !dw || width < 2 || width > 4) return CONV1D_EINVAL;
   if (b && !dtype_ok(b_dtype)) return CONV1D_EINVAL;
   if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
   if (!cf_layout_ok(B, D, T, x_sb, x_sd) || !cf_layout_ok(B, D, T, dy_sb, dy_sd) ||
@@ -372,8 +378,8 @@ int conv1d_bwd_cf(const void* x, const void* dy, int64_t B, int64_t D, int64_t T
   if (ws && !aligned(ws, 16)) return CONV1D_EINVAL;
   const Span sx = span_cf(x, B, D, T, x_sb, x_sd), sdy = span_cf(dy, B, D, T, dy_sb, dy_sd);
   const Span sdx = span_cf(dx, B, D, T, dx_sb, dx_sd);
-  const Span sw = span_bytes(w, 4 * D * dsize(w_dtype)), sb = span_bytes(b, D * dsize(b_dtype));
-  const Span sdw = span_bytes(dw, 4 * D * 4), sdb = span_bytes(db, D * 4), sws = span_bytes(ws, (int64_t)need);
+  const Span sw = span_bytes(w, width * D * dsize(w_dtype)), sb = span_bytes(b, D * dsize(b_dtype));
+  const Span sdw = span_bytes(dw, width * D * 4), sdb = span_bytes(db, D * 4), sws = span_bytes(ws, (int64_t)need);
   const Span outs[4] = {sdx, sdw, sdb, sws};
   const Span ins[4] = {sx, sdy, sw, sb};
   for (int i = 0; i < 4; ++i) {
@@ -402,10 +408,12 @@ int conv1d_bwd_cf(const void* x, const void* dy, int64_t B, int64_t D, int64_t T
   a.b = b;
   a.w_f32 = w_dtype == CONV1D_F32;
   a.b_f32 = b_dtype == CONV1D_F32;
+  a.width = width;
   a.part = static_cast<float*>(ws);
   if (launch_bwd_cf(a, vec, act == CONV1D_ACT_SILU, stream) != hipSuccess) return CONV1D_EHIP;
   BwdArgs r{};
   r.C = D;
+  r.width = width;
   r.part = a.part;
   r.dw = dw;
   r.db = db;

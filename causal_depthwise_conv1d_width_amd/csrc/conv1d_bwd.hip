@@ -27,7 +27,8 @@
 
 namespace cconv {
 
-template <int CPL, bool VEC>
+// Width W: W-1 history rows fill the last W-1 window slots (j >= 4-W), the rest stay zero.
+template <int CPL, bool VEC, int W>
 __device__ __forceinline__ void load_hist_rows(const HistArgs& hist, int64_t idx, int64_t c0, int64_t C,
                                                bool active, float (&h)[3][CPL]) {
 #pragma unroll
@@ -36,7 +37,8 @@ __device__ __forceinline__ void load_hist_rows(const HistArgs& hist, int64_t idx
     for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
   if (idx >= 0 && hist.ptr && active && (!hist.has_hist || hist.has_hist[idx])) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j) unpack(load_row<CPL, VEC>(hist.ptr + (idx * 3 + j) * C, c0, C), h[j]);
+    for (int j = 4 - W; j < 3; ++j)
+      unpack(load_row<CPL, VEC>(hist.ptr + (idx * (W - 1) + j - (4 - W)) * C, c0, C), h[j]);
   }
 }
 
@@ -57,7 +59,8 @@ struct BwdState {
 };
 
 // One real row q (ring slot r): recompute z, dz = dy * act'(z); dweight/dbias sums when `own`.
-template <int CPL, bool SILU>
+// Tap k (k = 4-W .. 3) reads ring slot (r+1+k) % 4: rows q-3 .. q.
+template <int CPL, bool SILU, int W>
 __device__ __forceinline__ void bwd_row(BwdState<CPL>& st, const Pk<CPL>& xr, const Pk<CPL>& gr, int r, bool own) {
   unpack(xr, st.u[r % 4]);
   float dyv[CPL];
@@ -65,10 +68,8 @@ __device__ __forceinline__ void bwd_row(BwdState<CPL>& st, const Pk<CPL>& xr, co
 #pragma unroll
   for (int ch = 0; ch < CPL; ++ch) {
     float z = st.bias[ch];
-    z = __builtin_fmaf(st.wk[0][ch], st.u[(r + 1) % 4][ch], z);
-    z = __builtin_fmaf(st.wk[1][ch], st.u[(r + 2) % 4][ch], z);
-    z = __builtin_fmaf(st.wk[2][ch], st.u[(r + 3) % 4][ch], z);
-    z = __builtin_fmaf(st.wk[3][ch], st.u[r % 4][ch], z);
+#pragma unroll
+    for (int k = 4 - W; k < 4; ++k) z = __builtin_fmaf(st.wk[k][ch], st.u[(r + 1 + k) % 4][ch], z);
     float dz = dyv[ch];
     if (SILU) {
       const float sg = sigmoid_f32(z);
@@ -79,26 +80,25 @@ __device__ __forceinline__ void bwd_row(BwdState<CPL>& st, const Pk<CPL>& xr, co
   if (own) {
 #pragma unroll
     for (int ch = 0; ch < CPL; ++ch) {
-      st.acc[0][ch] = __builtin_fmaf(st.g[r % 4][ch], st.u[(r + 1) % 4][ch], st.acc[0][ch]);
-      st.acc[1][ch] = __builtin_fmaf(st.g[r % 4][ch], st.u[(r + 2) % 4][ch], st.acc[1][ch]);
-      st.acc[2][ch] = __builtin_fmaf(st.g[r % 4][ch], st.u[(r + 3) % 4][ch], st.acc[2][ch]);
-      st.acc[3][ch] = __builtin_fmaf(st.g[r % 4][ch], st.u[r % 4][ch], st.acc[3][ch]);
+#pragma unroll
+      for (int k = 4 - W; k < 4; ++k)
+        st.acc[k][ch] = __builtin_fmaf(st.g[r % 4][ch], st.u[(r + 1 + k) % 4][ch], st.acc[k][ch]);
       st.acc[4][ch] += st.g[r % 4][ch];
     }
   }
 }
 
 // The value of row p = q - 3 at step q (ring slot r of row q): w3 dz[p] + w2 dz[p+1] + w1 dz[p+2]
-// + w0 dz[p+3].  Ring slots of rows before a sequence's start hold dz = 0, so for the three rows
-// before a sequence this is the gradient of its history rows.
-template <int CPL>
+// + w0 dz[p+3], taps below 4-W left out (tap k reads ring slot (r+4-k) % 4).  Ring slots of rows
+// before a sequence's start hold dz = 0, so for the rows before a sequence this is the gradient
+// of its history rows.
+template <int CPL, int W>
 __device__ __forceinline__ void bwd_back(const BwdState<CPL>& st, int r, float (&d)[CPL]) {
 #pragma unroll
   for (int ch = 0; ch < CPL; ++ch) {
     float v = st.wk[3][ch] * st.g[(r + 1) % 4][ch];
-    v = __builtin_fmaf(st.wk[2][ch], st.g[(r + 2) % 4][ch], v);
-    v = __builtin_fmaf(st.wk[1][ch], st.g[(r + 3) % 4][ch], v);
-    v = __builtin_fmaf(st.wk[0][ch], st.g[r % 4][ch], v);
+#pragma unroll
+    for (int k = 2; k >= 4 - W; --k) v = __builtin_fmaf(st.wk[k][ch], st.g[(r + 4 - k) % 4][ch], v);
     d[ch] = v;
   }
 }
@@ -111,34 +111,37 @@ struct BwdSeq {
 };
 
 // Where the value of row p goes: dx when p is a row of the current sequence inside the wave's own
-// range [ta, tb); d(history) row p - s + 3 when p is one of the three history rows of a sequence
-// whose head this wave streams; nowhere otherwise (rows of the neighbouring ranges).
-template <int CPL, bool VEC>
+// range [ta, tb); d(history) row p - s + W - 1 when p is one of the W-1 history rows of a
+// sequence whose head this wave streams; nowhere otherwise (rows of the neighbouring ranges, and
+// for W < 4 the rows before the history).
+template <int CPL, bool VEC, int W>
 __device__ __forceinline__ void bwd_route(const BwdArgs& a, const BwdSeq& cs, int64_t p, int64_t ta, int64_t tb,
                                           const float (&v)[CPL], int64_t c0, bool active) {
   if (p >= cs.sd.s) {
     if (p >= ta && p < tb && active) store_row<CPL, VEC, true>(a.dx + p * a.dx_ld, c0, a.C, pack(v));
-  } else if (cs.dh && active) {
-    store_row<CPL, VEC>(a.dhist + (cs.sd.idx * 3 + (p - cs.sd.s + 3)) * a.C, c0, a.C, pack(v));
+  } else if (cs.dh && active && p - cs.sd.s + W - 1 >= 0) {
+    store_row<CPL, VEC>(a.dhist + (cs.sd.idx * (W - 1) + (p - cs.sd.s + W - 1)) * a.C, c0, a.C, pack(v));
   }
 }
 
 // The current sequence ends right before row e (ring slot r): the values of its last three rows
-// e-3, e-2, e-1 only take dz of rows before e.
-template <int CPL, bool VEC>
+// e-3, e-2, e-1 only take dz of rows before e (taps below 4-W left out).
+template <int CPL, bool VEC, int W>
 __device__ __forceinline__ void bwd_flush(const BwdArgs& a, const BwdState<CPL>& st, const BwdSeq& cs, int r, int64_t e,
                                           int64_t ta, int64_t tb, int64_t c0, bool active) {
   float v3[CPL], v2[CPL], v1[CPL];
 #pragma unroll
   for (int ch = 0; ch < CPL; ++ch) {
     const float g3 = st.g[(r + 1) % 4][ch], g2 = st.g[(r + 2) % 4][ch], g1 = st.g[(r + 3) % 4][ch];
-    v3[ch] = __builtin_fmaf(st.wk[1][ch], g1, __builtin_fmaf(st.wk[2][ch], g2, st.wk[3][ch] * g3));
+    float t3 = __builtin_fmaf(st.wk[2][ch], g2, st.wk[3][ch] * g3);
+    if (W >= 3) t3 = __builtin_fmaf(st.wk[1][ch], g1, t3);
+    v3[ch] = t3;
     v2[ch] = __builtin_fmaf(st.wk[2][ch], g1, st.wk[3][ch] * g2);
     v1[ch] = st.wk[3][ch] * g1;
   }
-  bwd_route<CPL, VEC>(a, cs, e - 3, ta, tb, v3, c0, active);
-  bwd_route<CPL, VEC>(a, cs, e - 2, ta, tb, v2, c0, active);
-  bwd_route<CPL, VEC>(a, cs, e - 1, ta, tb, v1, c0, active);
+  bwd_route<CPL, VEC, W>(a, cs, e - 3, ta, tb, v3, c0, active);
+  bwd_route<CPL, VEC, W>(a, cs, e - 2, ta, tb, v2, c0, active);
+  bwd_route<CPL, VEC, W>(a, cs, e - 1, ta, tb, v1, c0, active);
 }
 
 template <int MODE>
@@ -152,12 +155,12 @@ __device__ __forceinline__ bool bwd_wants_dh(const BwdArgs& a, const SeqDesc& sd
 
 // Row q = cs.sd.s (ring slot r), the first row of a sequence, is next: the three window slots
 // take its history and dz = 0.
-template <int CPL, bool VEC, int MODE>
+template <int CPL, bool VEC, int MODE, int W>
 __device__ __forceinline__ void bwd_enter(const BwdArgs& a, BwdState<CPL>& st, BwdSeq& cs, int r, int64_t c0,
                                           bool active) {
   float h[3][CPL];
   if constexpr (MODE != MODE_IDX) {
-    load_hist_rows<CPL, VEC>(a.hist, cs.sd.idx, c0, a.C, active, h);
+    load_hist_rows<CPL, VEC, W>(a.hist, cs.sd.idx, c0, a.C, active, h);
   } else {
 #pragma unroll
     for (int j = 0; j < 3; ++j)
@@ -179,16 +182,16 @@ __device__ __forceinline__ void bwd_enter(const BwdArgs& a, BwdState<CPL>& st, B
 // finish the last dx rows; it ends (done) at that sequence's end or at tb + 3.  A chunk of own
 // rows of one sequence, at least three rows past both its start and the range start, is a
 // straight recompute-and-dx; any other chunk takes the row-by-row path.
-template <int CPL, bool VEC, int MODE, int CH, bool SILU, bool FULL>
+template <int CPL, bool VEC, int MODE, int CH, bool SILU, bool FULL, int W>
 __device__ __forceinline__ void bwd_chunk(const BwdArgs& a, BwdState<CPL>& st, BwdSeq& cs, const Pk<CPL> (&X)[CH],
                                           const Pk<CPL> (&G)[CH], int64_t q0, int64_t ta, int64_t tb, int64_t dend,
                                           int64_t lim, int64_t c0, bool active, bool& done) {
   if (q0 + CH <= tb && cs.sd.e >= q0 + CH && q0 >= cs.sd.s + 3 && q0 >= ta + 3) {
 #pragma unroll
     for (int r = 0; r < CH; ++r) {
-      bwd_row<CPL, SILU>(st, X[r], G[r], r, true);
+      bwd_row<CPL, SILU, W>(st, X[r], G[r], r, true);
       float d[CPL];
-      bwd_back<CPL>(st, r, d);
+      bwd_back<CPL, W>(st, r, d);
       if (FULL || active) store_row<CPL, VEC, true>(a.dx + (q0 + r - 3) * a.dx_ld, c0, a.C, pack(d));
     }
     return;
@@ -197,20 +200,20 @@ __device__ __forceinline__ void bwd_chunk(const BwdArgs& a, BwdState<CPL>& st, B
   for (int r = 0; r < CH; ++r) {
     const int64_t q = q0 + r;
     if (!done && q == cs.sd.e) {
-      bwd_flush<CPL, VEC>(a, st, cs, r, q, ta, tb, c0, active);
+      bwd_flush<CPL, VEC, W>(a, st, cs, r, q, ta, tb, c0, active);
       if (q >= tb) {
         done = true;
       } else {
         cs.sd = next_seq<MODE>(a.seq, cs.sd, dend, lim);
-        bwd_enter<CPL, VEC, MODE>(a, st, cs, r, c0, active);
+        bwd_enter<CPL, VEC, MODE, W>(a, st, cs, r, c0, active);
       }
     }
     if (!done && q >= tb + 3) done = true;
     if (!done) {
-      bwd_row<CPL, SILU>(st, X[r], G[r], r, q < tb);
+      bwd_row<CPL, SILU, W>(st, X[r], G[r], r, q < tb);
       float d[CPL];
-      bwd_back<CPL>(st, r, d);
-      bwd_route<CPL, VEC>(a, cs, q - 3, ta, tb, d, c0, active);
+      bwd_back<CPL, W>(st, r, d);
+      bwd_route<CPL, VEC, W>(a, cs, q - 3, ta, tb, d, c0, active);
     }
   }
 }
@@ -226,8 +229,10 @@ __device__ __forceinline__ void bwd_load(Pk<CPL> (&X)[CH], Pk<CPL> (&G)[CH], con
   }
 }
 
+// Occupancy floor: a launch is sized for 4 waves per SIMD (one round of ~1024 blocks), so the
+// per-token-ID variant, which would otherwise take 131 VGPRs (3 waves), is held to 128.
 #ifndef CCONV_BWD_WAVES_PER_EU
-#define CCONV_BWD_WAVES_PER_EU 0
+#define CCONV_BWD_WAVES_PER_EU 4
 #endif
 #if CCONV_BWD_WAVES_PER_EU > 0
 #define CCONV_BWD_OCCUPANCY __attribute__((amdgpu_waves_per_eu(CCONV_BWD_WAVES_PER_EU)))
@@ -235,7 +240,7 @@ __device__ __forceinline__ void bwd_load(Pk<CPL> (&X)[CH], Pk<CPL> (&G)[CH], con
 #define CCONV_BWD_OCCUPANCY
 #endif
 
-template <int CPL, bool VEC, int MODE, bool SILU>
+template <int CPL, bool VEC, int MODE, bool SILU, int W>
 __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_kernel(const BwdArgs a) {
   constexpr int CH = CCONV_BWD_CHUNK;  // rows per unrolled chunk (a multiple of the 4-slot rings)
   static_assert(CH % 4 == 0, "chunks must keep the ring slot of a row fixed");
@@ -264,7 +269,7 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
     for (int ch = 0; ch < CPL; ++ch) st.acc[k][ch] = 0.f;
 
   if (ta < tb) {
-    load_taps<CPL>(a.w, a.w_f32, a.b, a.b_f32, c0, C, st.wk, st.bias);
+    load_taps<CPL, W>(a.w, a.w_f32, a.b, a.b_f32, c0, C, st.wk, st.bias);
     const int64_t lim = (tb + 3 < dend) ? tb + 3 : dend;  // sequence ends matter up to tb + 3
 
     // full chunks of own rows, software-pipelined with two register buffers (see the forward)
@@ -283,7 +288,7 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
     float h[3][CPL];
     cs.dh = false;
     if constexpr (MODE != MODE_IDX) {
-      load_hist_rows<CPL, VEC>(a.hist, dist < 3 ? cs.sd.idx : -1, c0, C, active, h);
+      load_hist_rows<CPL, VEC, W>(a.hist, dist < 3 ? cs.sd.idx : -1, c0, C, active, h);
       if (dist == 0) cs.dh = bwd_wants_dh<MODE>(a, cs.sd);
     } else {
 #pragma unroll
@@ -309,13 +314,13 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
       // past the last full chunk re-read its last row): see the forward kernel
       for (int j = 0;; j += 2, q0 += 2 * CH) {
         bwd_load<CPL, VEC, CH>(XB, GB, a, q0 + CH, qlast, c0);
-        bwd_chunk<CPL, VEC, MODE, CH, SILU, true>(a, st, cs, XA, GA, q0, ta, tb, dend, lim, c0, active, done);
+        bwd_chunk<CPL, VEC, MODE, CH, SILU, true, W>(a, st, cs, XA, GA, q0, ta, tb, dend, lim, c0, active, done);
         if (j + 1 >= nfull) {
           q0 += CH;
           break;
         }
         bwd_load<CPL, VEC, CH>(XA, GA, a, q0 + 2 * CH, qlast, c0);
-        bwd_chunk<CPL, VEC, MODE, CH, SILU, true>(a, st, cs, XB, GB, q0 + CH, ta, tb, dend, lim, c0, active, done);
+        bwd_chunk<CPL, VEC, MODE, CH, SILU, true, W>(a, st, cs, XB, GB, q0 + CH, ta, tb, dend, lim, c0, active, done);
         if (j + 2 >= nfull) {
           q0 += 2 * CH;
           break;
@@ -340,7 +345,7 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
           }
         }
       }
-      bwd_chunk<CPL, VEC, MODE, CH, SILU, false>(a, st, cs, XA, GA, q0, ta, tb, dend, lim, c0, active, done);
+      bwd_chunk<CPL, VEC, MODE, CH, SILU, false, W>(a, st, cs, XA, GA, q0, ta, tb, dend, lim, c0, active, done);
     }
   }
 
@@ -400,7 +405,9 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_reduce_kernel(const 
     s += __shfl_xor(s, 32);  // (s0+s1) + (s2+s3) on every lane
     if (ok && lane < 16) {
       const int64_t k = o / C, c = o - k * C;
-      if (k < 4) a.dw[c * 4 + k] = s;
+      if (k < 4) {  // tap slot k holds filter tap k - (4 - width); lower slots are padding
+        if (k >= 4 - a.width) a.dw[c * a.width + k - (4 - a.width)] = s;
+      }
       else if (a.db) a.db[c] = s;
     }
     return;
@@ -411,18 +418,18 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_reduce_kernel(const 
   if (a.hist.has_hist && !a.hist.has_hist[i]) return;
   if (a.seq.cu[i + 1] != a.seq.cu[i]) return;  // nonempty: written by the tile kernel
 #pragma unroll
-  for (int j = 0; j < 3; ++j) a.dhist[(i * 3 + j) * C + c] = 0;
+  for (int j = 0; j < a.width - 1; ++j) a.dhist[(i * (a.width - 1) + j) * C + c] = 0;
 }
 
 // ------------------------------------------------------------------ launchers
 constexpr int kCpl = kChannelsPerLane;
 
-template <int MODE, bool VEC, bool SILU>
+template <int MODE, bool VEC, bool SILU, int W>
 static hipError_t bwd_go(const BwdArgs& a, hipStream_t s) {
   const uint32_t blocks = a.n_strips * a.n_rowblocks;
   if (blocks) {
     void* args[] = {const_cast<BwdArgs*>(&a)};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&conv1d_bwd_kernel<kCpl, VEC, MODE, SILU>),
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&conv1d_bwd_kernel<kCpl, VEC, MODE, SILU, W>),
                                    dim3(blocks), dim3(kBlockThreads), args, 0, s);
     if (e != hipSuccess) return e;
   }
@@ -437,10 +444,19 @@ static hipError_t bwd_go(const BwdArgs& a, hipStream_t s) {
                          rargs, 0, s);
 }
 
-template <int MODE>
+template <int MODE, int W>
 static hipError_t bwd_mode(const BwdArgs& a, bool vec, bool silu, hipStream_t s) {
-  if (vec) return silu ? bwd_go<MODE, true, true>(a, s) : bwd_go<MODE, true, false>(a, s);
-  return silu ? bwd_go<MODE, false, true>(a, s) : bwd_go<MODE, false, false>(a, s);
+  if (vec) return silu ? bwd_go<MODE, true, true, W>(a, s) : bwd_go<MODE, true, false, W>(a, s);
+  return silu ? bwd_go<MODE, false, true, W>(a, s) : bwd_go<MODE, false, false, W>(a, s);
+}
+
+template <int W>
+static hipError_t bwd_width(const BwdArgs& a, int mode, bool vec, bool silu, hipStream_t s) {
+  switch (mode) {
+    case MODE_CU: return bwd_mode<MODE_CU, W>(a, vec, silu, s);
+    case MODE_IDX: return bwd_mode<MODE_IDX, W>(a, vec, silu, s);
+    default: return bwd_mode<MODE_BATCH, W>(a, vec, silu, s);
+  }
 }
 
 hipError_t launch_reduce(const BwdArgs& a, hipStream_t s) {
@@ -454,10 +470,10 @@ hipError_t launch_reduce(const BwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int mode, bool vec, bool silu, hipStream_t s) {
-  switch (mode) {
-    case MODE_CU: return bwd_mode<MODE_CU>(a, vec, silu, s);
-    case MODE_IDX: return bwd_mode<MODE_IDX>(a, vec, silu, s);
-    default: return bwd_mode<MODE_BATCH>(a, vec, silu, s);
+  switch (a.width) {
+    case 2: return bwd_width<2>(a, mode, vec, silu, s);
+    case 3: return bwd_width<3>(a, mode, vec, silu, s);
+    default: return bwd_width<4>(a, mode, vec, silu, s);
   }
 }
 

@@ -88,18 +88,24 @@ __device__ __forceinline__ void cf_window(float (&e)[11], const uint32_t (&v)[4]
   }
 }
 
+// Taps [D, W] in the last W of four slots (slot 3 on the current step); leading slots are zero
+// and never used (every tap loop starts at 4 - W).
+template <int W>
 __device__ __forceinline__ void cf_taps(const CfArgs& a, int64_t d, float (&wk)[4], float& bias) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    wk[k] = a.w_f32 ? static_cast<const float*>(a.w)[d * 4 + k]
-                    : __uint_as_float((uint32_t)static_cast<const uint16_t*>(a.w)[d * 4 + k] << 16);
+  for (int k = 0; k < 4; ++k) {
+    const int64_t i = d * W + (k - (4 - W));
+    wk[k] = k < 4 - W ? 0.f
+                      : (a.w_f32 ? static_cast<const float*>(a.w)[i]
+                                 : __uint_as_float((uint32_t)static_cast<const uint16_t*>(a.w)[i] << 16));
+  }
   bias = 0.f;
   if (a.b) bias = a.b_f32 ? static_cast<const float*>(a.b)[d]
                           : __uint_as_float((uint32_t)static_cast<const uint16_t*>(a.b)[d] << 16);
 }
 
 // ------------------------------------------------------------------ forward
-template <bool VEC, bool SILU>
+template <bool VEC, bool SILU, int W>
 __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_cf_kernel(const CfArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = (int64_t)blockIdx.x * kCfRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -108,7 +114,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_cf_kernel(const CfAr
   const uint16_t* x = a.x + bi * a.x_sb + d * a.x_sd;
   uint16_t* y = a.out + bi * a.o_sb + d * a.o_sd;
   float wk[4], bias;
-  cf_taps(a, d, wk, bias);
+  cf_taps<W>(a, d, wk, bias);
   uint32_t c2 = 0u, c3 = 0u;  // steps before the row: zero history
   for (int64_t t0 = 0; t0 < T; t0 += (int64_t)kCfUnroll * kCfBlock) {
     uint32_t v[kCfUnroll][4];
@@ -123,10 +129,8 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_cf_kernel(const CfAr
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float z = bias;
-        z = __builtin_fmaf(wk[0], e[j], z);
-        z = __builtin_fmaf(wk[1], e[j + 1], z);
-        z = __builtin_fmaf(wk[2], e[j + 2], z);
-        z = __builtin_fmaf(wk[3], e[j + 3], z);
+#pragma unroll
+        for (int k = 4 - W; k < 4; ++k) z = __builtin_fmaf(wk[k], e[j + k], z);
         out[j] = SILU ? z * sigmoid_f32(z) : z;
       }
       cf_store<VEC>(y, tb + lane * kCfSteps, T, out);
@@ -137,7 +141,9 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_cf_kernel(const CfAr
 }
 
 // ------------------------------------------------------------------ backward
-// dx of the eight steps of a lane from their dz and the dz of the next three steps (n0..n2).
+// dx of the eight steps of a lane from their dz and the dz of the next three steps (n0..n2);
+// tap k multiplies the dz 3 - k steps later, taps below 4 - W are left out.
+template <int W>
 __device__ __forceinline__ void cf_dx(float (&dx)[8], const float (&dz)[8], float n0, float n1, float n2,
                                       const float (&wk)[4]) {
   float g[11];
@@ -149,14 +155,13 @@ __device__ __forceinline__ void cf_dx(float (&dx)[8], const float (&dz)[8], floa
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     float s = wk[3] * g[j];
-    s = __builtin_fmaf(wk[2], g[j + 1], s);
-    s = __builtin_fmaf(wk[1], g[j + 2], s);
-    s = __builtin_fmaf(wk[0], g[j + 3], s);
+#pragma unroll
+    for (int k = 2; k >= 4 - W; --k) s = __builtin_fmaf(wk[k], g[j + 3 - k], s);
     dx[j] = s;
   }
 }
 
-template <bool VEC, bool SILU>
+template <bool VEC, bool SILU, int W>
 __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_cf_kernel(const CfArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = (int64_t)blockIdx.x * kCfRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -166,7 +171,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_cf_kernel(const CfAr
   const uint16_t* dy = a.dy + bi * a.dy_sb + d * a.dy_sd;
   uint16_t* dx = a.out + bi * a.o_sb + d * a.o_sd;
   float wk[4], bias;
-  cf_taps(a, d, wk, bias);
+  cf_taps<W>(a, d, wk, bias);
   float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
   float pdz[8];              // dz of the previous block (its dx is still to be written)
   int64_t ptb = -1;          // start of that block, -1 = none
@@ -189,10 +194,8 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_cf_kernel(const CfAr
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float z = bias;
-        z = __builtin_fmaf(wk[0], e[j], z);
-        z = __builtin_fmaf(wk[1], e[j + 1], z);
-        z = __builtin_fmaf(wk[2], e[j + 2], z);
-        z = __builtin_fmaf(wk[3], e[j + 3], z);
+#pragma unroll
+        for (int k = 4 - W; k < 4; ++k) z = __builtin_fmaf(wk[k], e[j + k], z);
         float g = (j & 1) ? bf16_hi(gv[u][j >> 1]) : bf16_lo(gv[u][j >> 1]);
         if (SILU) {
           const float sg = sigmoid_f32(z);
@@ -202,10 +205,8 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_cf_kernel(const CfAr
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        acc[0] = __builtin_fmaf(dz[j], e[j], acc[0]);
-        acc[1] = __builtin_fmaf(dz[j], e[j + 1], acc[1]);
-        acc[2] = __builtin_fmaf(dz[j], e[j + 2], acc[2]);
-        acc[3] = __builtin_fmaf(dz[j], e[j + 3], acc[3]);
+#pragma unroll
+        for (int k = 4 - W; k < 4; ++k) acc[k] = __builtin_fmaf(dz[j], e[j + k], acc[k]);
         acc[4] += dz[j];
       }
       if (ptb >= 0) {  // the previous block's dx: lane 63 takes this block's first three dz
@@ -219,7 +220,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_cf_kernel(const CfAr
           n2 = h2;
         }
         float o[8];
-        cf_dx(o, pdz, n0, n1, n2, wk);
+        cf_dx<W>(o, pdz, n0, n1, n2, wk);
         cf_store<VEC>(dx, ptb + lane * kCfSteps, T, o);
       }
 #pragma unroll
@@ -233,7 +234,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_cf_kernel(const CfAr
     float n0 = __shfl_down(pdz[0], 1), n1 = __shfl_down(pdz[1], 1), n2 = __shfl_down(pdz[2], 1);
     if (lane == kWave - 1) n0 = n1 = n2 = 0.f;
     float o[8];
-    cf_dx(o, pdz, n0, n1, n2, wk);
+    cf_dx<W>(o, pdz, n0, n1, n2, wk);
     cf_store<VEC>(dx, ptb + lane * kCfSteps, T, o);
   }
   // the row's partial: a fixed butterfly over the 64 lanes, lane 0 writes
@@ -251,20 +252,29 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_cf_kernel(const CfAr
 }
 
 // ------------------------------------------------------------------ launchers
-template <bool VEC, bool SILU>
+template <bool VEC, bool SILU, int W>
 static hipError_t cf_go(const CfArgs& a, bool bwd, hipStream_t s) {
   const int64_t rows = a.B * a.D;
   const uint32_t blocks = (uint32_t)((rows + kCfRowsPerBlock - 1) / kCfRowsPerBlock);
   void* args[] = {const_cast<CfArgs*>(&a)};
-  const void* fn = bwd ? reinterpret_cast<const void*>(&conv1d_bwd_cf_kernel<VEC, SILU>)
-                       : reinterpret_cast<const void*>(&conv1d_fwd_cf_kernel<VEC, SILU>);
+  const void* fn = bwd ? reinterpret_cast<const void*>(&conv1d_bwd_cf_kernel<VEC, SILU, W>)
+                       : reinterpret_cast<const void*>(&conv1d_fwd_cf_kernel<VEC, SILU, W>);
   return hipLaunchKernel(fn, dim3(blocks), dim3(kBlockThreads), args, 0, s);
+}
+
+template <int W>
+static hipError_t cf_width(const CfArgs& a, bool vec, bool silu, bool bwd, hipStream_t s) {
+  if (vec) return silu ? cf_go<true, true, W>(a, bwd, s) : cf_go<true, false, W>(a, bwd, s);
+  return silu ? cf_go<false, true, W>(a, bwd, s) : cf_go<false, false, W>(a, bwd, s);
 }
 
 static hipError_t cf_dispatch(const CfArgs& a, bool vec, bool silu, bool bwd, hipStream_t s) {
   if (a.B * a.D == 0) return hipSuccess;
-  if (vec) return silu ? cf_go<true, true>(a, bwd, s) : cf_go<true, false>(a, bwd, s);
-  return silu ? cf_go<false, true>(a, bwd, s) : cf_go<false, false>(a, bwd, s);
+  switch (a.width) {
+    case 2: return cf_width<2>(a, vec, silu, bwd, s);
+    case 3: return cf_width<3>(a, vec, silu, bwd, s);
+    default: return cf_width<4>(a, vec, silu, bwd, s);
+  }
 }
 
 hipError_t launch_fwd_cf(const CfArgs& a, bool vec, bool silu, hipStream_t s) {

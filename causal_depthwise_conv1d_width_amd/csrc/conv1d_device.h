@@ -132,9 +132,13 @@ __device__ __forceinline__ void store_row(uint16_t* __restrict__ row, int64_t c0
 }
 
 // ------------------------------------------------------------------ taps
-template <int CPL>
+// Filter width W (2..4): the taps are [C, W] and sit in the last W of four slots, wk[4-W .. 3]
+// (slot 3 on the current row); the leading 4-W slots hold zeros and every loop over taps
+// starts at 4-W, so they are never multiplied.
+template <int CPL, int W = 4>
 __device__ __forceinline__ void load_taps(const void* w, int w_f32, const void* b, int b_f32, int64_t c0,
                                           int64_t C, float (&wk)[4][CPL], float (&bias)[CPL]) {
+  static_assert(W >= 2 && W <= 4, "filter widths 2..4");
 #pragma unroll
   for (int ch = 0; ch < CPL; ++ch) {
     const int64_t c = c0 + ch;
@@ -142,8 +146,10 @@ __device__ __forceinline__ void load_taps(const void* w, int w_f32, const void* 
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       float v = 0.f;
-      if (ok) v = w_f32 ? static_cast<const float*>(w)[c * 4 + k]
-                        : __uint_as_float((uint32_t)static_cast<const uint16_t*>(w)[c * 4 + k] << 16);
+      if (ok && k >= 4 - W) {
+        const int64_t i = c * W + (k - (4 - W));
+        v = w_f32 ? static_cast<const float*>(w)[i] : __uint_as_float((uint32_t)static_cast<const uint16_t*>(w)[i] << 16);
+      }
       wk[k][ch] = v;
     }
     float bv = 0.f;

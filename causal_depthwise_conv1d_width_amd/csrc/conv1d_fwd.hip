@@ -32,8 +32,9 @@
 namespace cconv {
 
 // ------------------------------------------------------------------ sequence history
-// h[j][ch] = history position j (oldest first) of sequence idx, channel c0 + ch.
-template <int CPL, bool VEC>
+// h[j][ch] = history position j (oldest first) of sequence idx, channel c0 + ch.  Width W has
+// W-1 history values; they fill the last W-1 window slots (j >= 4-W), the rest stay zero.
+template <int CPL, bool VEC, int W>
 __device__ __forceinline__ void load_history(const PoolArgs& pool, const HistArgs& hist, int64_t idx,
                                              int32_t slot, bool live, int64_t c0, int64_t C, bool active,
                                              float (&h)[3][CPL]) {
@@ -42,7 +43,7 @@ __device__ __forceinline__ void load_history(const PoolArgs& pool, const HistArg
 #pragma unroll
     for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
   if (idx < 0) return;  // history not needed
-  if (pool.ptr) {
+  if (W == 4 && pool.ptr) {  // the pool form is width four
     const bool init = live && pool.has_init && pool.has_init[idx];
     if (init && active) {
       const uint16_t* base = pool.ptr + (int64_t)slot * pool.s_slot;
@@ -57,8 +58,8 @@ __device__ __forceinline__ void load_history(const PoolArgs& pool, const HistArg
     const bool has = !hist.has_hist || hist.has_hist[idx];
     if (has && active) {
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        Pk<CPL> p = load_row<CPL, VEC>(hist.ptr + (idx * 3 + j) * C, c0, C);
+      for (int j = 4 - W; j < 3; ++j) {
+        Pk<CPL> p = load_row<CPL, VEC>(hist.ptr + (idx * (W - 1) + j - (4 - W)) * C, c0, C);
         unpack(p, h[j]);
       }
     }
@@ -118,23 +119,21 @@ __device__ __forceinline__ void load_chunk(Pk<CPL> (&buf)[CH], const uint16_t* _
   }
 }
 
-template <int CPL, bool SILU>
+template <int CPL, bool SILU, int W>
 __device__ __forceinline__ Pk<CPL> stencil_row(const float (&wk)[4][CPL], const float (&bias)[CPL],
                                                const float (&u)[4][CPL], int r);
 
 // One output row from the ring: u[(r+1)%4], u[(r+2)%4], u[(r+3)%4] are rows t-3, t-2, t-1 and
-// u[r%4] the current row.  z = b, then the four taps in order (FMA), FP32; y = act(z) in bf16.
-template <int CPL, bool SILU>
+// u[r%4] the current row.  z = b, then the W taps in order (FMA), FP32; y = act(z) in bf16.
+template <int CPL, bool SILU, int W>
 __device__ __forceinline__ Pk<CPL> stencil_row(const float (&wk)[4][CPL], const float (&bias)[CPL],
                                                const float (&u)[4][CPL], int r) {
   float out[CPL];
 #pragma unroll
   for (int ch = 0; ch < CPL; ++ch) {
     float z = bias[ch];
-    z = __builtin_fmaf(wk[0][ch], u[(r + 1) % 4][ch], z);
-    z = __builtin_fmaf(wk[1][ch], u[(r + 2) % 4][ch], z);
-    z = __builtin_fmaf(wk[2][ch], u[(r + 3) % 4][ch], z);
-    z = __builtin_fmaf(wk[3][ch], u[r % 4][ch], z);
+#pragma unroll
+    for (int k = 4 - W; k < 4; ++k) z = __builtin_fmaf(wk[k][ch], u[(r + 1 + k) % 4][ch], z);
     out[ch] = SILU ? z * sigmoid_f32(z) : z;
   }
   return pack(out);
@@ -170,7 +169,7 @@ __device__ __forceinline__ void fwd_slot(const FwdArgs& a, FwdSeq& cs) {
 
 // Row q = cs.sd.s, the first row of a sequence, is next: h <- its history, and with a pool the
 // head writes the sequence's final state (the head wave is the only one that touches the slot).
-template <int CPL, bool VEC, int MODE>
+template <int CPL, bool VEC, int MODE, int W>
 __device__ __forceinline__ void fwd_enter(const FwdArgs& a, FwdSeq& cs, int64_t c0, bool active, float (&h)[3][CPL]) {
   fwd_slot<MODE>(a, cs);
 #pragma unroll
@@ -179,8 +178,10 @@ __device__ __forceinline__ void fwd_enter(const FwdArgs& a, FwdSeq& cs, int64_t 
     for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
   if constexpr (MODE != MODE_IDX) {
     if (!cs.zero) {
-      load_history<CPL, VEC>(a.pool, a.hist, cs.sd.idx, cs.slot, true, c0, a.C, active, h);
-      if (a.pool.ptr && cs.sd.e > cs.sd.s) pool_writeback<CPL, VEC>(a, cs.slot, cs.sd, h, c0, active);
+      load_history<CPL, VEC, W>(a.pool, a.hist, cs.sd.idx, cs.slot, true, c0, a.C, active, h);
+      if constexpr (W == 4) {
+        if (a.pool.ptr && cs.sd.e > cs.sd.s) pool_writeback<CPL, VEC>(a, cs.slot, cs.sd, h, c0, active);
+      }
     }
   }
 }
@@ -189,7 +190,7 @@ __device__ __forceinline__ void fwd_enter(const FwdArgs& a, FwdSeq& cs, int64_t 
 // mod 4 = r mod 4, as q0 - range start is a multiple of CH.  A chunk inside one sequence is a
 // straight stencil; a chunk where sequences start re-seeds the three window slots from the new
 // sequence's history right before its first row.
-template <int CPL, bool VEC, int MODE, int CH, bool SILU, bool FULL>
+template <int CPL, bool VEC, int MODE, int CH, bool SILU, bool FULL, int W>
 __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)[CH], int n, int64_t q0, int64_t tb,
                                           int64_t dend, FwdSeq& cs, int64_t c0, bool active,
                                           const float (&wk)[4][CPL], const float (&bias)[CPL], float (&u)[4][CPL]) {
@@ -203,7 +204,7 @@ __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)
 #pragma unroll
       for (int r = 0; r < CH; ++r) {
         unpack(buf[r], u[r % 4]);
-        const Pk<CPL> out = stencil_row<CPL, SILU>(wk, bias, u, r);
+        const Pk<CPL> out = stencil_row<CPL, SILU, W>(wk, bias, u, r);
         if (FULL || active) store_row<CPL, VEC, true>(a.y + (q0 + r) * a.y_ld, c0, a.C, out);
       }
     }
@@ -216,7 +217,7 @@ __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)
       if (q == cs.sd.e) {  // a new sequence starts at row q (empty ones are skipped)
         cs.sd = next_seq<MODE>(a.seq, cs.sd, dend, tb);
         float h[3][CPL];
-        fwd_enter<CPL, VEC, MODE>(a, cs, c0, active, h);
+        fwd_enter<CPL, VEC, MODE, W>(a, cs, c0, active, h);
 #pragma unroll
         for (int j = 0; j < 3; ++j)
 #pragma unroll
@@ -224,13 +225,13 @@ __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)
       }
       unpack(buf[r], u[r % 4]);
       Pk<CPL> out = zero_pk<CPL>();
-      if (!cs.zero) out = stencil_row<CPL, SILU>(wk, bias, u, r);
+      if (!cs.zero) out = stencil_row<CPL, SILU, W>(wk, bias, u, r);
       if (FULL || active) store_row<CPL, VEC, true>(a.y + q * a.y_ld, c0, a.C, out);
     }
   }
 }
 
-template <int CPL, bool VEC, int MODE, bool SILU>
+template <int CPL, bool VEC, int MODE, bool SILU, int W>
 __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs a) {
   constexpr int CH = CCONV_FWD_CHUNK;  // rows per unrolled chunk; a multiple of the 4-slot ring
   static_assert(CH % 4 == 0, "chunks must keep the ring slot of a row fixed");
@@ -259,7 +260,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
   if (ta >= tb) return;
 
   float wk[4][CPL], bias[CPL];
-  load_taps<CPL>(a.w, a.w_f32, a.b, a.b_f32, c0, C, wk, bias);
+  load_taps<CPL, W>(a.w, a.w_f32, a.b, a.b_f32, c0, C, wk, bias);
 
   // full chunks are software-pipelined over the whole range; lanes past the last channel only
   // occur in the last wave of a strip, which takes the predicated path for everything
@@ -277,7 +278,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
   const int64_t dist = ta - cs.sd.s < 3 ? ta - cs.sd.s : 3;  // window rows from the same sequence
   float h[3][CPL];
   if (dist == 0) {
-    fwd_enter<CPL, VEC, MODE>(a, cs, c0, active, h);
+    fwd_enter<CPL, VEC, MODE, W>(a, cs, c0, active, h);
   } else {
     // mid-sequence start: with a pool, range boundaries never fall on a sequence's rows 1 and 2,
     // so dist == 3 and the slot is not touched (only its -1 status matters)
@@ -287,7 +288,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
 #pragma unroll
       for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
     if constexpr (MODE != MODE_IDX) {
-      if (!cs.zero && dist < 3) load_history<CPL, VEC>(a.pool, a.hist, cs.sd.idx, cs.slot, true, c0, C, active, h);
+      if (!cs.zero && dist < 3) load_history<CPL, VEC, W>(a.pool, a.hist, cs.sd.idx, cs.slot, true, c0, C, active, h);
     }
   }
   // window rows ta-3, ta-2, ta-1 -> ring slots 1, 2, 3: the history, then the last `dist` input
@@ -308,13 +309,13 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
     // loop head carries the same outstanding loads and the compiler's wait counts stay exact.
     for (int j = 0;; j += 2, q0 += 2 * CH) {
       load_chunk<CPL, VEC, CH>(B, a.x, a.x_ld, q0 + CH, qlast, c0, C);
-      fwd_chunk<CPL, VEC, MODE, CH, SILU, true>(a, A, CH, q0, tb, dend, cs, c0, active, wk, bias, u);
+      fwd_chunk<CPL, VEC, MODE, CH, SILU, true, W>(a, A, CH, q0, tb, dend, cs, c0, active, wk, bias, u);
       if (j + 1 >= nfull) {
         q0 += CH;
         break;
       }
       load_chunk<CPL, VEC, CH>(A, a.x, a.x_ld, q0 + 2 * CH, qlast, c0, C);
-      fwd_chunk<CPL, VEC, MODE, CH, SILU, true>(a, B, CH, q0 + CH, tb, dend, cs, c0, active, wk, bias, u);
+      fwd_chunk<CPL, VEC, MODE, CH, SILU, true, W>(a, B, CH, q0 + CH, tb, dend, cs, c0, active, wk, bias, u);
       if (j + 2 >= nfull) {
         q0 += 2 * CH;
         break;
@@ -329,7 +330,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
       A[r] = zero_pk<CPL>();
       if (r < n && active) A[r] = load_row<CPL, VEC, true>(a.x + (q0 + r) * a.x_ld, c0, C);
     }
-    fwd_chunk<CPL, VEC, MODE, CH, SILU, false>(a, A, n, q0, tb, dend, cs, c0, active, wk, bias, u);
+    fwd_chunk<CPL, VEC, MODE, CH, SILU, false, W>(a, A, n, q0, tb, dend, cs, c0, active, wk, bias, u);
   }
 }
 
@@ -418,26 +419,35 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_decode_kernel(const Deco
 // ------------------------------------------------------------------ launchers
 constexpr int kCpl = kChannelsPerLane;
 
-template <int MODE, bool VEC, bool SILU>
+template <int MODE, bool VEC, bool SILU, int W>
 static hipError_t fwd_go(const FwdArgs& a, hipStream_t s) {
   const uint32_t blocks = a.n_strips * a.n_rowblocks;
   void* args[] = {const_cast<FwdArgs*>(&a)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&conv1d_fwd_kernel<kCpl, VEC, MODE, SILU>), dim3(blocks),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&conv1d_fwd_kernel<kCpl, VEC, MODE, SILU, W>), dim3(blocks),
                          dim3(kBlockThreads), args, 0, s);
 }
 
-template <int MODE>
+template <int MODE, int W>
 static hipError_t fwd_mode(const FwdArgs& a, bool vec, bool silu, hipStream_t s) {
-  if (vec) return silu ? fwd_go<MODE, true, true>(a, s) : fwd_go<MODE, true, false>(a, s);
-  return silu ? fwd_go<MODE, false, true>(a, s) : fwd_go<MODE, false, false>(a, s);
+  if (vec) return silu ? fwd_go<MODE, true, true, W>(a, s) : fwd_go<MODE, true, false, W>(a, s);
+  return silu ? fwd_go<MODE, false, true, W>(a, s) : fwd_go<MODE, false, false, W>(a, s);
+}
+
+template <int W>
+static hipError_t fwd_width(const FwdArgs& a, int mode, bool vec, bool silu, hipStream_t s) {
+  switch (mode) {
+    case MODE_CU: return fwd_mode<MODE_CU, W>(a, vec, silu, s);
+    case MODE_IDX: return fwd_mode<MODE_IDX, W>(a, vec, silu, s);
+    default: return fwd_mode<MODE_BATCH, W>(a, vec, silu, s);
+  }
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int mode, bool vec, bool silu, hipStream_t s) {
   if ((uint64_t)a.n_strips * a.n_rowblocks == 0) return hipSuccess;
-  switch (mode) {
-    case MODE_CU: return fwd_mode<MODE_CU>(a, vec, silu, s);
-    case MODE_IDX: return fwd_mode<MODE_IDX>(a, vec, silu, s);
-    default: return fwd_mode<MODE_BATCH>(a, vec, silu, s);
+  switch (a.width) {
+    case 2: return fwd_width<2>(a, mode, vec, silu, s);
+    case 3: return fwd_width<3>(a, mode, vec, silu, s);
+    default: return fwd_width<4>(a, mode, vec, silu, s);
   }
 }
 

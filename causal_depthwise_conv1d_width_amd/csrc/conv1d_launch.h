@@ -73,7 +73,7 @@ struct PoolArgs {
 };
 
 struct HistArgs {
-  const uint16_t* ptr;  // nullptr: no history rows; else contiguous [nseq, 3, C]
+  const uint16_t* ptr;  // nullptr: no history rows; else contiguous [nseq, W-1, C]
   const uint8_t* has_hist;
 };
 
@@ -81,11 +81,11 @@ struct FwdArgs {
   const uint16_t* x;
   uint16_t* y;
   int64_t x_ld, y_ld, rows, C;
-  const void* w;
+  const void* w;  // [C, width]
   const void* b;
-  int w_f32, b_f32;
+  int w_f32, b_f32, width;
   SeqArgs seq;
-  PoolArgs pool;
+  PoolArgs pool;  // width 4 only
   HistArgs hist;
   int64_t range_rows;  // rows per row range
   uint32_t n_strips, n_rowblocks;
@@ -107,14 +107,14 @@ struct BwdArgs {
   const uint16_t* dy;
   uint16_t* dx;
   int64_t x_ld, dy_ld, dx_ld, rows, C;
-  const void* w;
+  const void* w;  // [C, width]
   const void* b;
-  int w_f32, b_f32;
+  int w_f32, b_f32, width;
   SeqArgs seq;
   HistArgs hist;
   uint16_t* dhist;  // nullptr: not requested
   float* part;      // workspace: [n_rowblocks, 5, C] FP32 per-block partials
-  float* dw;        // [C, 4]
+  float* dw;        // [C, width]
   float* db;        // [C] or nullptr
   int64_t range_rows;  // rows per row range
   uint32_t n_strips, n_rowblocks;
@@ -129,9 +129,9 @@ struct CfArgs {
   uint16_t* out;       // forward: y; backward: dx
   int64_t B, D, T;
   int64_t x_sb, x_sd, dy_sb, dy_sd, o_sb, o_sd;
-  const void* w;
+  const void* w;  // [D, width]
   const void* b;
-  int w_f32, b_f32;
+  int w_f32, b_f32, width;
   float* part;  // backward only
 };
 

@@ -1,5 +1,6 @@
 /*
- * conv1d.h -- C ABI of the MI355X (gfx950) packed width-4 depthwise causal Conv1d (+ SiLU).
+ * conv1d.h -- C ABI of the MI355X (gfx950) packed depthwise causal Conv1d (+ SiLU), filter
+ * width 4 (widths 2 and 3 for the non-pool forms).
  *
  * The operation (FlashInfer docs, flashinfer.mamba.causal_conv1d_fn, Parameters and Notes):
  * for every packed sequence with rows [s, e) and channel c, with the extended sequence
@@ -20,8 +21,12 @@
  *     (causal_conv1d_fn, Notes).
  *   - bf16 tensors are 16-bit bf16 bit patterns.  x, y, dy, dx are row-major [rows, C] with a
  *     row stride (`*_ld`, in elements, >= C) and contiguous channels.
- *   - Taps w are a contiguous [C, 4] array of FP32 or bf16 (`w_dtype`); the optional bias is a
- *     contiguous [C] array of FP32 or bf16 (`b_dtype`), NULL for none
+ *   - Taps w are a contiguous [C, W] array of FP32 or bf16 (`w_dtype`) with filter width
+ *     W = `width` in 2..4 (causal_conv1d_fn has W = 4; causal_conv1d_cp, Parameters weight,
+ *     takes [D, W]).  For W < 4 read the formula above with the first 4 - W taps absent: tap
+ *     W - 1 multiplies the current token and the history is W - 1 values (u[-(W-1)] .. u[-1]).
+ *     The slot-pool forms (conv1d_fwd with a pool, conv1d_state_update*) are width four only.
+ *     The optional bias is a contiguous [C] array of FP32 or bf16 (`b_dtype`), NULL for none
  *     (causal_conv1d_fn, Parameters weight and bias).
  *   - Host-checkable preconditions are validated before anything is enqueued; a violation
  *     returns CONV1D_EINVAL (or CONV1D_EWORKSPACE) and launches nothing.  Device-side values
@@ -94,8 +99,8 @@ typedef struct {
 /* Caller-supplied history rows for the context-parallel share of one GPU
    (flashinfer.cake_causal_conv1d_train.cake_causal_conv1d_kcp, summary: a fragment that
    continues a document reads the preceding fragment's rows instead of zeros).  ptr: contiguous
-   bf16 [nseq, 3, C]; row j of entry i is the raw input 3 - j rows before sequence i's first
-   row.  has_history: uint8 [nseq], NULL = every sequence reads its rows; sequences with 0 start
+   bf16 [nseq, W - 1, C]; row j of entry i is the raw input W - 1 - j rows before sequence i's
+   first row.  has_history: uint8 [nseq], NULL = every sequence reads its rows; sequences with 0 start
    from zeros.  Needs the cu_seqlens or the batch-row form. */
 typedef struct {
   const void* ptr;
@@ -107,7 +112,7 @@ typedef struct {
    (NULL), not both.  act: conv1d_act.  y must not overlap x, w, b, the pool or hist; rows of y
    outside every sequence are not written.  ws/ws_bytes: unused (0 bytes needed; may be NULL).
    Returns a conv1d_status. */
-int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void* w, int w_dtype,
+int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void* w, int w_dtype, int width,
                const void* b, int b_dtype, const conv1d_seq* seq, const conv1d_pool* pool,
                const conv1d_hist* hist, int act, void* y, int64_t y_ld, void* ws, size_t ws_bytes,
                hipStream_t stream);
@@ -144,28 +149,28 @@ int conv1d_state_update_spec(const void* x, int64_t nseq, int64_t K, int64_t C, 
    causal_conv1d_cp).  Given dy = dL/dy (bf16 [rows, C], stride dy_ld), recomputes the forward
    z and writes
      dx   bf16 [rows, C] (stride dx_ld): dL/dx, rows outside every sequence untouched;
-     dw   FP32 [C, 4]: dL/dw, contiguous (required);
+     dw   FP32 [C, W]: dL/dw, contiguous (required);
      db   FP32 [C]: dL/db (NULL to skip; computed whether or not b is given);
-     dhist bf16 [nseq, 3, C]: dL/d(history rows) for sequences that read history rows
+     dhist bf16 [nseq, W - 1, C]: dL/d(history rows) for sequences that read history rows
           (requires hist; NULL to skip; rows of other sequences untouched).
    dw and db are sums of per-tile FP32 partials combined in a fixed order by a second kernel
    (no atomics), so they are bitwise identical from run to run and independent of the
    workspace address.  ws: device scratch of at least conv1d_bwd_workspace_bytes(rows, C)
    bytes, 16-byte aligned, not overlapping any operand.  No pool. */
 int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x_ld, int64_t dy_ld,
-               const void* w, int w_dtype, const void* b, int b_dtype, const conv1d_seq* seq,
+               const void* w, int w_dtype, int width, const void* b, int b_dtype, const conv1d_seq* seq,
                const conv1d_hist* hist, int act, void* dx, int64_t dx_ld, float* dw, float* db,
                void* dhist, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Channels-first layout [B, D, T], T contiguous (core.ssm.causal_conv1d,
    assert_causal_conv1d_deterministic names it: there a dweight element takes one contribution
    per batch row instead of batch * ceil(seqlen / 128)).  Every (b, d) row is one sequence with
-   zero history; the operation is the same width-4 stencil (z = b, taps 0..3, tap 3 on the current
-   step, FP32, then act).  Strides are in elements: row (b, d) starts at b * sb + d * sd; rows
+   zero history; the operation is the same stencil (z = b, taps 0..W-1, tap W-1 on the current
+   step, FP32, then act; taps [D, W], dw [D, W]).  Strides are in elements: row (b, d) starts at b * sb + d * sd; rows
    must not overlap (sd >= T, sb >= (D - 1) * sd + T).  x, y, dy, dx: bf16.  y / dx must not
    overlap any input.  Returns a conv1d_status. */
 int conv1d_fwd_cf(const void* x, int64_t B, int64_t D, int64_t T, int64_t x_sb, int64_t x_sd, const void* w,
-                  int w_dtype, const void* b, int b_dtype, int act, void* y, int64_t y_sb, int64_t y_sd,
+                  int w_dtype, int width, const void* b, int b_dtype, int act, void* y, int64_t y_sb, int64_t y_sd,
                   hipStream_t stream);
 
 /* Channels-first backward: dx [B, D, T] bf16, dw FP32 [D, 4] (required), db FP32 [D] (NULL to
@@ -173,8 +178,8 @@ int conv1d_fwd_cf(const void* x, int64_t B, int64_t D, int64_t T, int64_t x_sb, 
    partials of each channel in a fixed order, so dw and db are bitwise reproducible.  ws: at least
    conv1d_bwd_cf_workspace_bytes(B, D) bytes, 16-byte aligned, not overlapping any operand. */
 int conv1d_bwd_cf(const void* x, const void* dy, int64_t B, int64_t D, int64_t T, int64_t x_sb, int64_t x_sd,
-                  int64_t dy_sb, int64_t dy_sd, const void* w, int w_dtype, const void* b, int b_dtype, int act,
-                  void* dx, int64_t dx_sb, int64_t dx_sd, float* dw, float* db, void* ws, size_t ws_bytes,
+                  int64_t dy_sb, int64_t dy_sd, const void* w, int w_dtype, int width, const void* b, int b_dtype,
+                  int act, void* dx, int64_t dx_sb, int64_t dx_sd, float* dw, float* db, void* ws, size_t ws_bytes,
                   hipStream_t stream);
 
 /* Workspace sizes in bytes (host-only, pure functions of the capacities). */

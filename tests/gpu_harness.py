@@ -77,7 +77,7 @@ def gpu_bwd(case, workspace=None):
     hist = dev_bits(case["hist"]) if case.get("hist") is not None else None
     nseq = case["hist"].shape[0] if case.get("hist") is not None else 0
     dx = dev_bits(np.full((rows, C), wl.OUT_FILL, np.uint16))
-    dh = dev_bits(np.full((nseq, 3, C), wl.OUT_FILL, np.uint16)) if hist is not None else None
+    dh = dev_bits(np.full(case["hist"].shape, wl.OUT_FILL, np.uint16)) if hist is not None else None
     dx, dw, db, dh = cc.conv1d_bwd(x, dy, dev_taps(case["w"]), dev_taps(case.get("b")),
                                    cu_seqlens=dev_i32(case.get("cu_seqlens")), seq_idx=dev_i32(case.get("seq_idx")),
                                    seqlen=case.get("seqlen"), history=hist, has_history=dev_u8(case.get("has_history")),

@@ -99,7 +99,7 @@ def pool_hist_layout(fake, slots, C, L):
 
 
 def fwd(lib, fake, rows=64, C=64, x_ld=None, y_ld=None, w_dtype=1, act=1, seq="cu", pool=None, hist=None,
-        x=True, y=True, w=True, b=None, b_dtype=1):
+        x=True, y=True, w=True, b=None, b_dtype=1, width=4):
     x_ld = C if x_ld is None else x_ld
     y_ld = C if y_ld is None else y_ld
     xp = fake(rows * x_ld * 2) if x is True else x
@@ -107,7 +107,7 @@ def fwd(lib, fake, rows=64, C=64, x_ld=None, y_ld=None, w_dtype=1, act=1, seq="c
     wp = fake(C * 16) if w else None
     if seq == "cu":
         seq = seq_cu(fake, 4)
-    return lib.conv1d_fwd(xp, rows, C, x_ld, wp, w_dtype, b, b_dtype, None if seq is None else ctypes.byref(seq),
+    return lib.conv1d_fwd(xp, rows, C, x_ld, wp, w_dtype, width, b, b_dtype, None if seq is None else ctypes.byref(seq),
                           None if pool is None else ctypes.byref(pool), None if hist is None else ctypes.byref(hist),
                           act, yp, y_ld, None, 0, None)
 
@@ -125,6 +125,15 @@ def test_fwd_rejects_bad_arguments(lib):
     assert fwd(lib, f, seq=None) == EINVAL
     assert fwd(lib, f, b=f(256), b_dtype=9) == EINVAL
     assert fwd(lib, f, rows=-1) == EINVAL
+
+
+def test_width_checks(lib):
+    f = Fake()
+    assert fwd(lib, f, width=1) == EINVAL
+    assert fwd(lib, f, width=5) == EINVAL
+    C = 64
+    p = pool_hist_layout(f, 8, C, 4)
+    assert fwd(lib, f, pool=p, width=3) == EINVAL  # the pool form is width four
 
 
 def test_fwd_rejects_bad_sequence_forms(lib):
@@ -190,7 +199,7 @@ def bwd(lib, f, rows=256, C=64, ws_bytes=None, ws=True, dw=True, dhist=None, his
         seq = seq_cu(f, 4)
     need = lib.conv1d_bwd_workspace_bytes(rows, C)
     ws_bytes = need if ws_bytes is None else ws_bytes
-    return lib.conv1d_bwd(f(rows * C * 2), f(rows * C * 2) if dy is None else dy, rows, C, C, C, f(C * 16), 1,
+    return lib.conv1d_bwd(f(rows * C * 2), f(rows * C * 2) if dy is None else dy, rows, C, C, C, f(C * 16), 1, 4,
                           None, 1, ctypes.byref(seq), None if hist is None else ctypes.byref(hist), 1,
                           f(rows * C * 2) if dx is None else dx, C, f(C * 16) if dw else None, None, dhist,
                           f(need) if ws is True else ws, ws_bytes, None)
@@ -251,7 +260,7 @@ def test_channels_first_rejects_bad_arguments(lib):
     def fwd_cf(x=None, y=None, xs=(D * T, T), ys=(D * T, T), w=True, act=1, B=B, D=D, T=T):
         xp = f(B * D * T * 2) if x is None else x
         yp = f(B * D * T * 2) if y is None else y
-        return lib.conv1d_fwd_cf(xp, B, D, T, xs[0], xs[1], f(D * 16) if w else None, 1, None, 1, act, yp,
+        return lib.conv1d_fwd_cf(xp, B, D, T, xs[0], xs[1], f(D * 16) if w else None, 1, 4, None, 1, act, yp,
                                  ys[0], ys[1], None)
     assert fwd_cf(w=False) == EINVAL
     assert fwd_cf(act=5) == EINVAL
@@ -267,7 +276,7 @@ def test_channels_first_rejects_bad_arguments(lib):
         dyp = f(B * D * T * 2) if dy is None else dy
         dxp = f(B * D * T * 2) if dx is None else dx
         nb = need if ws_bytes is None else ws_bytes
-        return lib.conv1d_bwd_cf(f(B * D * T * 2), dyp, B, D, T, D * T, T, D * T, T, f(D * 16), 1, None, 1, 1, dxp,
+        return lib.conv1d_bwd_cf(f(B * D * T * 2), dyp, B, D, T, D * T, T, D * T, T, f(D * 16), 1, 4, None, 1, 1, dxp,
                                  D * T, T, f(D * 16) if dw else None, None, f(need) if ws is True else ws, nb, None)
     assert bwd_cf(ws_bytes=need - 1) == EWORKSPACE
     assert bwd_cf(ws=None) == EWORKSPACE
