@@ -297,6 +297,40 @@ def _cpu_model():
 
 
 # ------------------------------------------------------------------ main
+def layout_counters():
+    """28 back-to-back calls of each kind over 4 buffer sets, one kind after another, so that a
+    counter run can compare the channel-last kernels (the context-parallel share, x [16384, 5632])
+    with the channels-first ones (x [4, 4096, 4096]) and a contiguous copy of the same size."""
+    from causal_depthwise_conv1d_width_amd import workloads as wl
+    g = Gpu()
+    torch = g.torch
+    c5 = wl.config_5()
+    cl = [g.prepare(c5) for _ in range(4)]
+    rng = np.random.default_rng(5)
+    B, D, T = 4, 4096, 4096
+    w = g.taps(wl.uniform_f32(rng, (D, 4)))
+    cf = []
+    for _ in range(4):
+        x = g.bits(wl.normal_bf16(rng, (B, D, T)))
+        cf.append(dict(x=x, dy=g.bits(wl.normal_bf16(rng, (B, D, T))), y=torch.empty_like(x), dx=torch.empty_like(x),
+                       dw=torch.empty((D, 4), dtype=torch.float32, device=g.dev),
+                       ws=torch.empty((g.cc.conv1d_bwd_cf_workspace_bytes(B, D),), dtype=torch.uint8, device=g.dev)))
+    cp = [(d["x"], torch.empty_like(d["x"])) for d in cl]
+    calls = {
+        "channel-last forward": [lambda d=d: g.fwd(d) for d in cl],
+        "channels-first forward": [lambda d=d: g.cc.conv1d_fwd_cf(d["x"], w, out=d["y"]) for d in cf],
+        "channel-last backward": [lambda d=d: g.bwd(d) for d in cl],
+        "channels-first backward": [lambda d=d: g.cc.conv1d_bwd_cf(d["x"], d["dy"], w, dx=d["dx"], dweight=d["dw"],
+                                                                    workspace=d["ws"]) for d in cf],
+        "copy": [lambda a=a: a[1].copy_(a[0]) for a in cp],
+    }
+    for name, cs in calls.items():
+        for i in range(28):
+            cs[i % 4]()
+        torch.cuda.synchronize()
+        print(json.dumps({"done": name, "calls": 28}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,7 +340,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times (counter calibration)")
+    ap.add_argument("--layout-counters", action="store_true",
+                    help="only run 28 calls each of the channel-last and channels-first forward and backward "
+                         "and of a plain copy, one kind after another (for counter collection)")
     args = ap.parse_args()
+    if args.layout_counters:
+        layout_counters()
+        return
     if args.copy_only_mib:
         import torch
         a = torch.empty(args.copy_only_mib << 19, dtype=torch.bfloat16, device="cuda").normal_()

@@ -146,6 +146,9 @@ __device__ __forceinline__ Pk<CPL> stencil_row(const float (&wk)[4][CPL], const 
 #ifndef CCONV_FWD_PIPELINE
 #define CCONV_FWD_PIPELINE 1
 #endif
+#ifndef CCONV_FWD_DEPTH
+#define CCONV_FWD_DEPTH 2
+#endif
 
 // The sequence a wave is streaming: its rows, its pool slot, and whether its output is forced to
 // zero (a -1 slot).
@@ -267,8 +270,13 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
   const int nfull = (full && CCONV_FWD_PIPELINE) ? (int)((tb - ta) / CH) : 0;
   const int64_t qlast = ta + (int64_t)nfull * CH - 1;
   int64_t q0 = ta;
-  Pk<CPL> A[CH], B[CH];
-  if (nfull > 0) load_chunk<CPL, VEC, CH>(A, a.x, a.x_ld, q0, qlast, c0, C);  // in flight during the set-up
+  constexpr int NB = CCONV_FWD_DEPTH;  // register buffers: chunk j + NB - 1 is loading while j computes
+  static_assert(NB >= 2, "at least two buffers");
+  Pk<CPL> buf[NB][CH];
+  if (nfull > 0) {  // in flight during the set-up
+#pragma unroll
+    for (int b = 0; b + 1 < NB; ++b) load_chunk<CPL, VEC, CH>(buf[b], a.x, a.x_ld, q0 + b * CH, qlast, c0, C);
+  }
 
   // the window rows ta-3 .. ta-1 and the sequence holding row ta
   Pk<CPL> wrow[3];
@@ -302,23 +310,21 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
     for (int ch = 0; ch < CPL; ++ch) u[j + 1][ch] = h[j][ch];
 
   if (nfull > 0) {
-    // Two register buffers, unrolled by two chunks: chunk j+1's loads are issued before chunk j's
+    // NB register buffers, unrolled by NB chunks: chunk j+NB-1's loads are issued before chunk j's
     // stores, so waiting for a chunk's data never waits for the stores issued before it (the
-    // vector memory counter is in order).  The next chunk's loads are issued unconditionally;
-    // past the last full chunk they re-read the last row (a cache hit), so every path back to the
-    // loop head carries the same outstanding loads and the compiler's wait counts stay exact.
-    for (int j = 0;; j += 2, q0 += 2 * CH) {
-      load_chunk<CPL, VEC, CH>(B, a.x, a.x_ld, q0 + CH, qlast, c0, C);
-      fwd_chunk<CPL, VEC, MODE, CH, SILU, true, W>(a, A, CH, q0, tb, dend, cs, c0, active, wk, bias, u);
-      if (j + 1 >= nfull) {
-        q0 += CH;
-        break;
-      }
-      load_chunk<CPL, VEC, CH>(A, a.x, a.x_ld, q0 + 2 * CH, qlast, c0, C);
-      fwd_chunk<CPL, VEC, MODE, CH, SILU, true, W>(a, B, CH, q0 + CH, tb, dend, cs, c0, active, wk, bias, u);
-      if (j + 2 >= nfull) {
-        q0 += 2 * CH;
-        break;
+    // vector memory counter is in order).  Look-ahead loads are issued unconditionally; past the
+    // last full chunk they re-read the last row (a cache hit), so every path back to the loop
+    // head carries the same outstanding loads and the compiler's wait counts stay exact.
+    bool more = true;
+    for (int j = 0; more; j += NB) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (more) {
+          load_chunk<CPL, VEC, CH>(buf[(b + NB - 1) % NB], a.x, a.x_ld, q0 + (NB - 1) * CH, qlast, c0, C);
+          fwd_chunk<CPL, VEC, MODE, CH, SILU, true, W>(a, buf[b], CH, q0, tb, dend, cs, c0, active, wk, bias, u);
+          q0 += CH;
+          more = j + b + 1 < nfull;
+        }
       }
     }
   }
@@ -327,10 +333,10 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
     const int n = (int)(tb - q0 < CH ? tb - q0 : CH);
 #pragma unroll
     for (int r = 0; r < CH; ++r) {
-      A[r] = zero_pk<CPL>();
-      if (r < n && active) A[r] = load_row<CPL, VEC, true>(a.x + (q0 + r) * a.x_ld, c0, C);
+      buf[0][r] = zero_pk<CPL>();
+      if (r < n && active) buf[0][r] = load_row<CPL, VEC, true>(a.x + (q0 + r) * a.x_ld, c0, C);
     }
-    fwd_chunk<CPL, VEC, MODE, CH, SILU, false, W>(a, A, n, q0, tb, dend, cs, c0, active, wk, bias, u);
+    fwd_chunk<CPL, VEC, MODE, CH, SILU, false, W>(a, buf[0], n, q0, tb, dend, cs, c0, active, wk, bias, u);
   }
 }
 
