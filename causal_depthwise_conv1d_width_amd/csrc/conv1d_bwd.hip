@@ -230,7 +230,9 @@ __device__ __forceinline__ void bwd_load(Pk<CPL> (&X)[CH], Pk<CPL> (&G)[CH], con
 }
 
 // Occupancy floor: a launch is sized for 4 waves per SIMD (one round of ~1024 blocks), so the
-// per-token-ID variant, which would otherwise take 131 VGPRs (3 waves), is held to 128.
+// per-token-ID variant, which would otherwise take 131 VGPRs (3 waves), is held to 128.  At width
+// four that spills two 64-bit values that live from the set-up to the epilogue: they are stored
+// once before the row loop and reloaded after it, so the loop itself never touches scratch.
 #ifndef CCONV_BWD_WAVES_PER_EU
 #define CCONV_BWD_WAVES_PER_EU 4
 #endif
