@@ -48,6 +48,9 @@ __device__ __forceinline__ void load_hist_rows(const HistArgs& hist, int64_t idx
 #ifndef CCONV_BWD_PIPELINE
 #define CCONV_BWD_PIPELINE 1
 #endif
+#ifndef CCONV_BWD_DEPTH
+#define CCONV_BWD_DEPTH 2
+#endif
 
 // Per-lane state of the backward stream (CPL channels).
 template <int CPL>
@@ -274,12 +277,17 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
     load_taps<CPL, W>(a.w, a.w_f32, a.b, a.b_f32, c0, C, st.wk, st.bias);
     const int64_t lim = (tb + 3 < dend) ? tb + 3 : dend;  // sequence ends matter up to tb + 3
 
-    // full chunks of own rows, software-pipelined with two register buffers (see the forward)
+    // full chunks of own rows, software-pipelined with NB register buffers (see the forward)
     const int nfull = (full && CCONV_BWD_PIPELINE) ? (int)((tb - ta) / CH) : 0;
     const int64_t qlast = ta + (int64_t)nfull * CH - 1;
     int64_t q0 = ta;
-    Pk<CPL> XA[CH], GA[CH], XB[CH], GB[CH];
-    if (nfull > 0) bwd_load<CPL, VEC, CH>(XA, GA, a, q0, qlast, c0);  // in flight during the set-up
+    constexpr int NB = CCONV_BWD_DEPTH;
+    static_assert(NB >= 2, "at least two buffers");
+    Pk<CPL> X[NB][CH], G[NB][CH];
+    if (nfull > 0) {  // in flight during the set-up
+#pragma unroll
+      for (int b = 0; b + 1 < NB; ++b) bwd_load<CPL, VEC, CH>(X[b], G[b], a, q0 + b * CH, qlast, c0);
+    }
 
     // the window rows ta-3 .. ta-1 and the sequence holding row ta
     Pk<CPL> wrow[3];
@@ -312,20 +320,19 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
 
     bool done = false;
     if (nfull > 0) {
-      // two register buffers, unrolled by two chunks, next chunk's loads always issued (rows
-      // past the last full chunk re-read its last row): see the forward kernel
-      for (int j = 0;; j += 2, q0 += 2 * CH) {
-        bwd_load<CPL, VEC, CH>(XB, GB, a, q0 + CH, qlast, c0);
-        bwd_chunk<CPL, VEC, MODE, CH, SILU, true, W>(a, st, cs, XA, GA, q0, ta, tb, dend, lim, c0, active, done);
-        if (j + 1 >= nfull) {
-          q0 += CH;
-          break;
-        }
-        bwd_load<CPL, VEC, CH>(XA, GA, a, q0 + 2 * CH, qlast, c0);
-        bwd_chunk<CPL, VEC, MODE, CH, SILU, true, W>(a, st, cs, XB, GB, q0 + CH, ta, tb, dend, lim, c0, active, done);
-        if (j + 2 >= nfull) {
-          q0 += 2 * CH;
-          break;
+      // NB register buffers, unrolled by NB chunks, look-ahead loads always issued (rows past the
+      // last full chunk re-read its last row): see the forward kernel
+      bool more = true;
+      for (int j = 0; more; j += NB) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (more) {
+            bwd_load<CPL, VEC, CH>(X[(b + NB - 1) % NB], G[(b + NB - 1) % NB], a, q0 + (NB - 1) * CH, qlast, c0);
+            bwd_chunk<CPL, VEC, MODE, CH, SILU, true, W>(a, st, cs, X[b], G[b], q0, ta, tb, dend, lim, c0, active,
+                                                         done);
+            q0 += CH;
+            more = j + b + 1 < nfull;
+          }
         }
       }
     }
@@ -335,19 +342,19 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
 #pragma unroll
       for (int r = 0; r < CH; ++r) {
         const int64_t q = q0 + r;
-        XA[r] = zero_pk<CPL>();
-        GA[r] = zero_pk<CPL>();
+        X[0][r] = zero_pk<CPL>();
+        G[0][r] = zero_pk<CPL>();
         if (active && q < lim) {
           if (q < tb) {
-            XA[r] = load_row<CPL, VEC, true>(a.x + q * a.x_ld, c0, C);
-            GA[r] = load_row<CPL, VEC, true>(a.dy + q * a.dy_ld, c0, C);
+            X[0][r] = load_row<CPL, VEC, true>(a.x + q * a.x_ld, c0, C);
+            G[0][r] = load_row<CPL, VEC, true>(a.dy + q * a.dy_ld, c0, C);
           } else {
-            XA[r] = load_row<CPL, VEC>(a.x + q * a.x_ld, c0, C);
-            GA[r] = load_row<CPL, VEC>(a.dy + q * a.dy_ld, c0, C);
+            X[0][r] = load_row<CPL, VEC>(a.x + q * a.x_ld, c0, C);
+            G[0][r] = load_row<CPL, VEC>(a.dy + q * a.dy_ld, c0, C);
           }
         }
       }
-      bwd_chunk<CPL, VEC, MODE, CH, SILU, false, W>(a, st, cs, XA, GA, q0, ta, tb, dend, lim, c0, active, done);
+      bwd_chunk<CPL, VEC, MODE, CH, SILU, false, W>(a, st, cs, X[0], G[0], q0, ta, tb, dend, lim, c0, active, done);
     }
   }
 
