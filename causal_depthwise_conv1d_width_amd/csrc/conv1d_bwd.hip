@@ -382,7 +382,7 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
 // Ordered reduce of the per-range partials: out[o] = sum over row ranges p of part[p][o], for
 // the flattened o = k*C + c (k = 0..3 dweight taps, 4 = dbias).  A wave owns 16 consecutive o;
 // lane l sums the ranges p = l/16, l/16 + 4, l/16 + 8, ... in ascending order (each load of
-// the wave reads four 64-byte runs), then a fixed two-level butterfly across lanes l, l^16,
+// the wave reads four 64-byte runs; 16 loads are in flight per step), then a fixed two-level butterfly across lanes l, l^16,
 // l^32, l^48 adds the four interleaved subsets:  (s0 + s1) + (s2 + s3).  The order is fixed, so
 // dweight/dbias are bitwise reproducible; no atomics.  The remaining threads write zero
 // d(history) rows of empty continuing fragments.
@@ -399,16 +399,17 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_reduce_kernel(const 
     const int64_t n = a.n_rowblocks;
     float s = 0.f;
     if (ok) {
+      // 16 partials of the subset per step, all loads issued before the first add: a call waits
+      // for ceil(n / 64) memory round trips, not one per four partials
       const float* p = a.part + o;
-      int64_t i = sub;
-      for (; i + 12 < n; i += 16) {
-        const float v0 = p[i * nout], v1 = p[(i + 4) * nout], v2 = p[(i + 8) * nout], v3 = p[(i + 12) * nout];
-        s += v0;
-        s += v1;
-        s += v2;
-        s += v3;
+      for (int64_t i0 = sub; i0 < n; i0 += 64) {
+        float v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = i0 + 4 * k < n ? p[(i0 + 4 * k) * nout] : 0.f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if (i0 + 4 * k < n) s += v[k];
       }
-      for (; i < n; i += 4) s += p[i * nout];
     }
     s += __shfl_xor(s, 16);  // s0+s1 (lanes 0-31), s2+s3 (lanes 32-63); fp add commutes exactly
     s += __shfl_xor(s, 32);  // (s0+s1) + (s2+s3) on every lane
