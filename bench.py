@@ -55,9 +55,10 @@ def _segments(case):
 
 
 def fwd_bytes(case):
-    """2C per row read (live sequences) + 2C per row written + 6C per history read / state write
-    + taps + bias + metadata."""
+    """2C per row read (live sequences) + 2C per row written + 2(W-1)C per history read / state
+    write (W taps) + taps + bias + metadata."""
     rows, C = case["x"].shape
+    H = case["w"].shape[1] - 1  # history rows
     segs, r_out, nseq = _segments(case)
     r_read, n_state = r_out, 0
     meta = 0
@@ -74,14 +75,15 @@ def fwd_bytes(case):
             n_state = sum(1 for s, e, i in segs if e > s and (hh is None or hh[i]))
     if case.get("seq_idx") is not None:
         meta += rows * 4
-    return (2 * C * r_read + 2 * C * r_out + 6 * C * n_state + _tap_bytes(case["w"]) + _tap_bytes(case.get("b"))
+    return (2 * C * r_read + 2 * C * r_out + 2 * H * C * n_state + _tap_bytes(case["w"]) + _tap_bytes(case.get("b"))
             + meta)
 
 
 def bwd_bytes(case):
-    """6C per row (x, dy read; dx written) + 6C per history row set read and its gradient written
-    + taps + bias + dweight (+ dbias) + metadata."""
+    """6C per row (x, dy read; dx written) + 2(W-1)C per history row set read and as much for its
+    gradient written + taps + bias + dweight (+ dbias) + metadata."""
     rows, C = case["x"].shape
+    W = case["w"].shape[1]
     segs, r, nseq = _segments(case)
     n_hist, meta = 0, 0
     if segs is not None:
@@ -93,7 +95,7 @@ def bwd_bytes(case):
     if case.get("seq_idx") is not None:
         meta += rows * 4
     has_b = case.get("b") is not None
-    return (6 * C * r + 12 * C * n_hist + _tap_bytes(case["w"]) + _tap_bytes(case.get("b")) + 16 * C
+    return (6 * C * r + 4 * (W - 1) * C * n_hist + _tap_bytes(case["w"]) + _tap_bytes(case.get("b")) + 4 * W * C
             + (4 * C if has_b else 0) + meta)
 
 
@@ -178,7 +180,7 @@ class Gpu:
         if case.get("dy") is not None:
             d["dy"] = self.bits(case["dy"])
             d["dx"] = t.empty((rows, C), dtype=t.bfloat16, device=self.dev)
-            d["dw"] = t.empty((C, 4), dtype=t.float32, device=self.dev)
+            d["dw"] = t.empty((C, case["w"].shape[1]), dtype=t.float32, device=self.dev)
             d["db"] = t.empty((C,), dtype=t.float32, device=self.dev) if case.get("b") is not None else None
             need = self.cc.conv1d_bwd_workspace_bytes(rows, C)
             d["ws"] = t.empty((max(need, 1),), dtype=t.uint8, device=self.dev)
@@ -452,6 +454,19 @@ def main():
                 nbs = 2 * 64 * K * C * 2 + 64 * C * 2 * (3 + K + 2) + 4 * C * 4 + C * 4 + 2 * 64 * 4
                 extras["spec_update_N64_K4_C5632"] = {"GBps": round(gbps(nbs, mss), 1), "us": round(1e3 * mss, 2),
                                                       "bytes": nbs}
+        # filter width 3 on the step workload: taps [C, 3], two history rows per fragment
+        rng = np.random.default_rng(1008)
+        c3 = dict(case)
+        c3["w"] = wl.uniform_f32(rng, (case["x"].shape[1], 3))
+        c3["hist"] = wl.normal_bf16(rng, (case["hist"].shape[0], 2, case["x"].shape[1]))
+        d3 = [g.prepare(c3) for _ in range(4)]
+        nf3, nb3 = fwd_bytes(c3), bwd_bytes(c3)
+        msf3 = g.ring([lambda d=d: g.fwd(d) for d in d3], 40, 0, warm_ms=40)
+        msb3 = g.ring([lambda d=d: g.bwd(d) for d in d3], 40, 0, warm_ms=40)
+        extras["width3_" + case["name"]] = {"fwd_GBps": round(gbps(nf3, msf3), 1), "fwd_us": round(1e3 * msf3, 2),
+                                            "fwd_bytes": nf3, "bwd_GBps": round(gbps(nb3, msb3), 1),
+                                            "bwd_us": round(1e3 * msb3, 2), "bwd_bytes": nb3}
+        del d3
         # channels-first [B, D, T]: the per-token-ID training shape (4 x 4096 x 4096), one sequence per row
         rng = np.random.default_rng(1007)
         B, D, T = 4, 4096, 4096

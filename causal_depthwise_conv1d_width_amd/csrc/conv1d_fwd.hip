@@ -143,6 +143,11 @@ __device__ __forceinline__ Pk<CPL> stencil_row(const float (&wk)[4][CPL], const 
 #ifndef CCONV_FWD_CHUNK
 #define CCONV_FWD_CHUNK 4
 #endif
+// The per-token-ID form streams 8-row chunks: about 5% faster there, while the cu_seqlens form,
+// whose chunks more often hold a sequence start and take the row-by-row path, is faster with 4.
+#ifndef CCONV_FWD_CHUNK_IDX
+#define CCONV_FWD_CHUNK_IDX 8
+#endif
 #ifndef CCONV_FWD_PIPELINE
 #define CCONV_FWD_PIPELINE 1
 #endif
@@ -236,7 +241,7 @@ __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)
 
 template <int CPL, bool VEC, int MODE, bool SILU, int W>
 __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs a) {
-  constexpr int CH = CCONV_FWD_CHUNK;  // rows per unrolled chunk; a multiple of the 4-slot ring
+  constexpr int CH = MODE == MODE_IDX ? CCONV_FWD_CHUNK_IDX : CCONV_FWD_CHUNK;  // rows per unrolled chunk
   static_assert(CH % 4 == 0, "chunks must keep the ring slot of a row fixed");
 
   const int lane = threadIdx.x & (kWave - 1);
