@@ -47,6 +47,13 @@ Span span_seq(const conv1d_seq* s, int64_t rows) {
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+// Byte extents and element counts are computed in int64.  Sizes and strides whose products could
+// overflow it are rejected up front (no allocation comes near 2^56 elements).
+constexpr int64_t kMaxElems = (int64_t)1 << 56;
+bool mul_ok(int64_t a, int64_t b) {
+  return a >= 0 && b >= 0 && a <= kMaxElems && b <= kMaxElems && (b == 0 || a <= kMaxElems / b);
+}
+
 int mode_of(const conv1d_seq* s) {
   if (s->cu_seqlens) return MODE_CU;
   return s->seq_idx ? MODE_IDX : MODE_BATCH;
@@ -72,6 +79,7 @@ int64_t dsize(int d) { return d == CONV1D_F32 ? 4 : 2; }
 // inside a slot and no overlap between slots (causal_conv1d_fn, Parameters conv_state).
 int check_pool(const conv1d_pool* p, int64_t C, int64_t nseq, Span* out) {
   if (p->len < 3 || p->slots < 1 || p->s_slot < 1 || p->s_chan < 1 || p->s_pos < 1) return CONV1D_EINVAL;
+  if (!mul_ok(p->slots, p->s_slot) || !mul_ok(C, p->s_chan) || !mul_ok(p->len, p->s_pos)) return CONV1D_EINVAL;
   if (p->s_chan != 1 && p->s_pos != 1) return CONV1D_EINVAL;
   if (p->s_pos == 1 && C > 1 && p->s_chan < p->len) return CONV1D_EINVAL;  // (c, j) must not alias
   if (p->s_chan == 1 && p->s_pos != 1 && p->s_pos < C) return CONV1D_EINVAL;
@@ -85,6 +93,7 @@ int check_pool(const conv1d_pool* p, int64_t C, int64_t nseq, Span* out) {
 
 // Channels-first array [B, D, T]: rows (b, d) at b * sb + d * sd, T contiguous, no two rows overlapping.
 bool cf_layout_ok(int64_t B, int64_t D, int64_t T, int64_t sb, int64_t sd) {
+  if (!mul_ok(B, sb) || !mul_ok(D, sd) || !mul_ok(T, 2) || B > 0x7fffffff) return false;
   if (D > 1 && sd < T) return false;
   if (B > 1 && sb < (D - 1) * sd + T) return false;
   return sb >= 0 && sd >= 0;
@@ -112,7 +121,7 @@ size_t conv1d_fwd_workspace_bytes(int64_t rows, int64_t C, int64_t nseq) {
 }
 
 size_t conv1d_bwd_workspace_bytes(int64_t rows, int64_t C) {
-  if (rows <= 0 || C <= 0) return 0;
+  if (rows <= 0 || C <= 0 || !mul_ok(rows, C)) return 0;  // out-of-range sizes fail in the call itself
   const int64_t rr = range_rows_for(rows, ceil_div(C, kBlockChannels), kBwdBlocks, kBwdFixedRows);
   const size_t nrb = (size_t)((rows + rr - 1) / rr);
   const size_t bytes = nrb * 5u * (size_t)C * sizeof(float);
@@ -120,7 +129,7 @@ size_t conv1d_bwd_workspace_bytes(int64_t rows, int64_t C) {
 }
 
 size_t conv1d_bwd_cf_workspace_bytes(int64_t B, int64_t D) {
-  if (B <= 0 || D <= 0) return 0;
+  if (B <= 0 || D <= 0 || !mul_ok(B, D)) return 0;  // out-of-range sizes fail in the call itself
   const size_t bytes = (size_t)B * 5u * (size_t)D * sizeof(float);
   return (bytes + kWsAlign - 1) / kWsAlign * kWsAlign;
 }
@@ -147,8 +156,10 @@ int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void*
   if (b && !dtype_ok(b_dtype)) return CONV1D_EINVAL;
   if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
   if (rows > 0 && (!x || !y)) return CONV1D_EINVAL;
+  if (!mul_ok(rows, x_ld) || !mul_ok(rows, y_ld) || !mul_ok(C, 16)) return CONV1D_EINVAL;
   int64_t nseq = 0;
   if (check_seq(seq, rows, &nseq) != CONV1D_OK) return CONV1D_EINVAL;
+  if (!mul_ok(nseq > 0 ? nseq : 0, 8 * C)) return CONV1D_EINVAL;
   const int mode = mode_of(seq);
   const bool use_pool = pool && pool->ptr;
   const bool use_hist = hist && hist->ptr;
@@ -211,7 +222,7 @@ static int state_update_common(const void* x, int64_t nseq, int64_t K, int64_t C
   if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
   if (!pool || !pool->ptr) return CONV1D_EINVAL;
   if (nseq > 0 && (!x || !y)) return CONV1D_EINVAL;
-  if (nseq > INT64_MAX / K) return CONV1D_EINVAL;
+  if (!mul_ok(nseq, K) || !mul_ok(nseq * K, x_ld) || !mul_ok(nseq * K, y_ld) || !mul_ok(C, 16)) return CONV1D_EINVAL;
   Span sp;
   if (check_pool(pool, C, nseq, &sp) != CONV1D_OK) return CONV1D_EINVAL;
   if (pool->len < K + 2) return CONV1D_EINVAL;
@@ -267,8 +278,10 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
   if (b && !dtype_ok(b_dtype)) return CONV1D_EINVAL;
   if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
   if (rows > 0 && (!x || !dy || !dx)) return CONV1D_EINVAL;
+  if (!mul_ok(rows, x_ld) || !mul_ok(rows, dy_ld) || !mul_ok(rows, dx_ld) || !mul_ok(C, 16)) return CONV1D_EINVAL;
   int64_t nseq = 0;
   if (check_seq(seq, rows, &nseq) != CONV1D_OK) return CONV1D_EINVAL;
+  if (!mul_ok(nseq > 0 ? nseq : 0, 8 * C)) return CONV1D_EINVAL;
   const int mode = mode_of(seq);
   const bool use_hist = hist && hist->ptr;
   if (use_hist && mode == MODE_IDX) return CONV1D_EINVAL;

@@ -33,7 +33,11 @@
  *     (offsets, sequence IDs, slot numbers) are the caller's constraint and are not checked:
  *     offsets must start at 0, be nondecreasing and end at most at `rows`; live slots must be
  *     unique and in [0, slots); sequence IDs must be non-negative (causal_conv1d_fn, Notes;
- *     causal_conv1d_cp, Parameters global_seq_idx).  Violating them is undefined behaviour.
+ *     causal_conv1d_cp, Parameters global_seq_idx).  Violating them gives unspecified results,
+ *     but no access outside the buffers the host-side sizes describe: offsets are clamped to
+ *     [0, rows], a slot outside [0, slots) acts as -1, accepted counts are clamped to the pool.
+ *   - Sizes and strides whose products could exceed 2^56 elements (so that byte extents would
+ *     overflow 64-bit arithmetic) are rejected with CONV1D_EINVAL.
  *   - Any C >= 1 and any row stride are accepted.  When C, the strides and the pointers allow
  *     16-byte vectors a vectorized kernel runs, otherwise an element-wise one; results are
  *     identical.

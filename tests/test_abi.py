@@ -284,3 +284,31 @@ def test_channels_first_rejects_bad_arguments(lib):
     assert bwd_cf(ws=ctypes.c_void_p(f(need + 64).value + 4)) == EINVAL  # misaligned workspace
     dy = f(B * D * T * 2)
     assert bwd_cf(dy=dy, dx=ctypes.c_void_p(dy.value + 32)) == EINVAL  # dx overlaps dy
+
+
+def test_sizes_whose_byte_extents_overflow_are_rejected(lib):
+    """Sizes and strides whose products would overflow the int64 byte arithmetic fail validation
+    (fake pointers: nothing is dereferenced and nothing is launched)."""
+    f = Fake()
+    big_rows, big_ld = 1 << 40, 1 << 20
+    x, y, w = f(4096), f(4096), f(4096)
+    seq = seq_cu(f, 4)
+    assert lib.conv1d_fwd(x, big_rows, 64, big_ld, w, 1, 4, None, 1, ctypes.byref(seq), None, None, 1, y, 64,
+                          None, 0, None) == EINVAL
+    assert lib.conv1d_fwd(x, 4, 1 << 60, 1 << 60, w, 1, 4, None, 1, ctypes.byref(seq), None, None, 1, y, 1 << 60,
+                          None, 0, None) == EINVAL
+    assert lib.conv1d_bwd_workspace_bytes(big_rows, big_ld) == 0
+    assert lib.conv1d_bwd(x, f(4096), big_rows, 64, big_ld, 64, w, 1, 4, None, 1, ctypes.byref(seq), None, 1,
+                          f(4096), 64, f(4096), None, None, f(4096), 4096, None) == EINVAL
+    p = pool_hist_layout(f, 8, 64, 4)
+    p.s_slot = 1 << 60  # slots far apart: the pool's extent overflows
+    assert lib.conv1d_state_update(f(4096), 8, 64, 64, w, 1, None, 1, ctypes.byref(p), 1, f(4096), 64,
+                                   None) == EINVAL
+    p = pool_hist_layout(f, 8, 64, 6)
+    assert lib.conv1d_state_update_spec(f(4096), 1 << 40, 1 << 20, 64, 64, w, 1, None, 1, ctypes.byref(p), None, 1,
+                                        f(4096), 64, None) == EINVAL
+    T = 64
+    assert lib.conv1d_fwd_cf(f(4096), 1 << 31, 1, T, T, T, w, 1, 4, None, 1, 1, f(4096), T, T, None) == EINVAL
+    assert lib.conv1d_fwd_cf(f(4096), 2, 1 << 40, T, (1 << 40) * (1 << 20), 1 << 20, w, 1, 4, None, 1, 1, f(4096),
+                             T, T, None) == EINVAL
+    assert lib.conv1d_bwd_cf_workspace_bytes(1 << 40, 1 << 20) == 0
