@@ -185,7 +185,7 @@ int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void*
 
   const bool vec = (C % 8 == 0) && (x_ld % 8 == 0) && (y_ld % 8 == 0) && aligned(x, 16) && aligned(y, 16) &&
                    (!use_hist || aligned(hist->ptr, 16));
-  const int64_t rr = range_rows_for(rows, ceil_div(C, kBlockChannels), kFwdBlocks, kFwdFixedRows);
+  const int64_t rr = fwd_range_rows(rows, ceil_div(C, kBlockChannels));
   const uint64_t nblk = (uint64_t)ceil_div(C, kBlockChannels) * ceil_div(rows, rr);
   if (nblk > 0x7fffffffull) return CONV1D_EINVAL;
 

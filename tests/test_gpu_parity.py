@@ -184,3 +184,30 @@ def test_batch_rows_form(oracle):
                 act="silu")
     gh.check_fwd(oracle, case)
     gh.check_bwd(oracle, case)
+
+
+@pytest.mark.parametrize("form", ["idx", "batch", "cu"])
+def test_forward_short_ranges_at_large_row_counts(oracle, form):
+    """Past 256 rows per one-round range the forward switches to 40-row ranges (several rounds of
+    blocks): 24584 x 5632 crosses that point.  Sequences of every length, including 1..3 rows,
+    straddle the 40-row range boundaries."""
+    rng = np.random.default_rng(31)
+    C, B = 5632, 4
+    rows = B * 6146  # batch rows of 6146 rows: not a multiple of 40
+    x = wl.normal_bf16(rng, (rows, C))
+    case = dict(name=f"short-ranges-{form}", x=x, w=wl.uniform_f32(rng, (C, 4)),
+                b=(rng.standard_normal(C) * 0.1).astype(np.float32), act="silu")
+    lengths, total = [], 0
+    while total < rows:
+        n = min(int(rng.choice([1, 2, 3, 4, 39, 40, 41, 97, 1000])), rows - total)
+        lengths.append(n)
+        total += n
+    if form == "cu":
+        case["cu_seqlens"] = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    elif form == "idx":
+        case["seqlen"] = rows // B
+        case["seq_idx"] = np.repeat(np.arange(len(lengths)), lengths).astype(np.int32)
+    else:
+        case["seqlen"] = rows // B
+    _print_case(case["name"], rows=rows, C=C, seqs=len(lengths))
+    gh.check_fwd(oracle, case)
