@@ -221,14 +221,17 @@ __device__ __forceinline__ void bwd_chunk(const BwdArgs& a, BwdState<CPL>& st, B
   }
 }
 
+// CH rows of x and dy from q0; past the last full chunk (last row qlast) it re-reads that chunk
 template <int CPL, bool VEC, int CH>
 __device__ __forceinline__ void bwd_load(Pk<CPL> (&X)[CH], Pk<CPL> (&G)[CH], const BwdArgs& a, int64_t q0, int64_t qlast,
                                          int64_t c0) {
+  const int64_t qs = q0 + CH - 1 <= qlast ? q0 : qlast - (CH - 1);
+  const uint16_t* xr = a.x + qs * a.x_ld;
+  const uint16_t* gr = a.dy + qs * a.dy_ld;
 #pragma unroll
   for (int r = 0; r < CH; ++r) {
-    const int64_t q = q0 + r < qlast ? q0 + r : qlast;
-    X[r] = load_row<CPL, VEC, true>(a.x + q * a.x_ld, c0, a.C);
-    G[r] = load_row<CPL, VEC, true>(a.dy + q * a.dy_ld, c0, a.C);
+    X[r] = load_row<CPL, VEC, true>(xr + r * a.x_ld, c0, a.C);
+    G[r] = load_row<CPL, VEC, true>(gr + r * a.dy_ld, c0, a.C);
   }
 }
 

@@ -107,16 +107,16 @@ __device__ __forceinline__ int64_t owner_boundary(const SeqArgs& q, int64_t r, i
   }
 }
 
-// CH consecutive rows starting at q0 (rows past qlast re-read row qlast), every lane active,
-// streamed (non-temporal).
+// CH consecutive rows starting at q0, every lane active, streamed (non-temporal).  A chunk past
+// the last full one (qlast is that chunk's last row) re-reads the last full chunk: the clamp is
+// one compare per chunk.
 template <int CPL, bool VEC, int CH>
 __device__ __forceinline__ void load_chunk(Pk<CPL> (&buf)[CH], const uint16_t* __restrict__ x, int64_t ld, int64_t q0,
                                            int64_t qlast, int64_t c0, int64_t C) {
+  const int64_t qs = q0 + CH - 1 <= qlast ? q0 : qlast - (CH - 1);
+  const uint16_t* row = x + qs * ld;
 #pragma unroll
-  for (int r = 0; r < CH; ++r) {
-    const int64_t q = q0 + r < qlast ? q0 + r : qlast;
-    buf[r] = load_row<CPL, VEC, true>(x + q * ld, c0, C);
-  }
+  for (int r = 0; r < CH; ++r) buf[r] = load_row<CPL, VEC, true>(row + r * ld, c0, C);
 }
 
 template <int CPL, bool SILU, int W>
