@@ -125,11 +125,32 @@ def _hist(history, has_history, C, W=4):
     return h
 
 
-def _stream(stream):
+def _stream(stream, dev):
     torch = _torch()
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(dev)
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _on_gpu(dev, **tensors):
+    """Every tensor argument must live on x's GPU: the kernels dereference the raw pointers."""
+    if dev.type != "cuda":
+        raise ValueError(f"x: must be a GPU tensor (got device {dev})")
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name}: must be on {dev}, the device of x (got {t.device})")
+
+
+def _at_least(t, n, name):
+    """A per-sequence (or per-row) array the kernels read n entries of."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{name}: needs at least {n} entries, has {t.numel()}")
+
+
+def _f32(t, shape, name):
+    torch = _torch()
+    if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous()):
+        raise ValueError(f"{name}: need a contiguous float32 tensor of shape {tuple(shape)}")
 
 
 def _ref(s):
@@ -158,6 +179,15 @@ def conv1d_fwd(x, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqlen=No
     seq, nseq = _seq(rows, cu_seqlens, seq_idx, seqlen)
     pool = _pool(conv_state, cache_indices, has_initial_state, C)
     hist = _hist(history, has_history, C, W)
+    _on_gpu(x.device, weight=weight, bias=bias, cu_seqlens=cu_seqlens, seq_idx=seq_idx, conv_state=conv_state,
+            cache_indices=cache_indices, has_initial_state=has_initial_state, history=history,
+            has_history=has_history, out=out, workspace=workspace)
+    _at_least(seq_idx, rows, "seq_idx")
+    for t, name in ((cache_indices, "cache_indices"), (has_initial_state, "has_initial_state"),
+                    (has_history, "has_history")):
+        _at_least(t, max(nseq, 0), name)
+    if history is not None and history.shape[0] < max(nseq, 0):
+        raise ValueError(f"history: needs a row set for each of the {nseq} sequences")
     if out is None:
         out = torch.empty((rows, C), dtype=torch.bfloat16, device=x.device)
     yp, y_ld = _rows2d(out, "out", C)
@@ -166,7 +196,7 @@ def conv1d_fwd(x, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqlen=No
     ws = workspace.data_ptr() if workspace is not None else None
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib.conv1d_fwd(xp, rows, C, x_ld, wp, wd, W, bp, bd, ctypes.byref(seq), _ref(pool), _ref(hist),
-                        _lib.ACT[activation], yp, y_ld, ws, wsb, _stream(stream))
+                        _lib.ACT[activation], yp, y_ld, ws, wsb, _stream(stream, x.device))
     _lib.check(lib, st, "conv1d_fwd")
     return out
 
@@ -183,11 +213,15 @@ def conv1d_state_update(x, weight, bias=None, *, conv_state, cache_indices, acti
     pool = _pool(conv_state, cache_indices, None, C)
     if pool is None:
         raise ValueError("conv_state is required")
+    _on_gpu(x.device, weight=weight, bias=bias, conv_state=conv_state, cache_indices=cache_indices, out=out)
+    _at_least(cache_indices, nseq, "cache_indices")
     if out is None:
         out = torch.empty((nseq, C), dtype=torch.bfloat16, device=x.device)
     yp, y_ld = _rows2d(out, "out", C)
+    if out.shape[0] != nseq:
+        raise ValueError("out: must have one row per sequence")
     st = lib.conv1d_state_update(xp, nseq, C, x_ld, wp, wd, bp, bd, ctypes.byref(pool), _lib.ACT[activation],
-                                 yp, y_ld, _stream(stream))
+                                 yp, y_ld, _stream(stream, x.device))
     _lib.check(lib, st, "conv1d_state_update")
     return out
 
@@ -221,12 +255,18 @@ def conv1d_state_update_spec(x, weight, bias=None, *, conv_state, cache_indices,
     pool = _pool(conv_state, cache_indices, None, C)
     if pool is None:
         raise ValueError("conv_state is required")
+    _on_gpu(x.device, weight=weight, bias=bias, conv_state=conv_state, cache_indices=cache_indices,
+            num_accepted=num_accepted, out=out)
+    _at_least(cache_indices, nseq, "cache_indices")
+    _at_least(num_accepted, nseq, "num_accepted")
     if out is None:
         out = torch.empty((nseq, K, C), dtype=torch.bfloat16, device=x.device)
     yp, y_ld = _tokens3d(out, "out", C)
+    if tuple(out.shape[:2]) != (nseq, K):
+        raise ValueError("out: must have the shape of x")
     acc = _i32(num_accepted, "num_accepted")
     st = lib.conv1d_state_update_spec(xp, nseq, K, C, x_ld, wp, wd, bp, bd, ctypes.byref(pool), acc,
-                                      _lib.ACT[activation], yp, y_ld, _stream(stream))
+                                      _lib.ACT[activation], yp, y_ld, _stream(stream, x.device))
     _lib.check(lib, st, "conv1d_state_update_spec")
     return out
 
@@ -246,9 +286,24 @@ def conv1d_bwd(x, dy, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqle
     seq, nseq = _seq(rows, cu_seqlens, seq_idx, seqlen)
     hist = _hist(history, has_history, C, W)
     dev = x.device
+    _on_gpu(dev, dy=dy, weight=weight, bias=bias, cu_seqlens=cu_seqlens, seq_idx=seq_idx, history=history,
+            has_history=has_history, dx=dx, dweight=dweight, dbias=dbias, dhistory=dhistory, workspace=workspace)
+    if dy.shape[0] != rows:
+        raise ValueError("dy: must have as many rows as x")
+    _at_least(seq_idx, rows, "seq_idx")
+    _at_least(has_history, max(nseq, 0), "has_history")
+    if history is not None and history.shape[0] < max(nseq, 0):
+        raise ValueError(f"history: needs a row set for each of the {nseq} sequences")
+    _f32(dweight, (C, W), "dweight")
+    _f32(dbias, (C,), "dbias")
+    if dhistory is not None and (tuple(dhistory.shape) != (max(nseq, 0), W - 1, C) or not dhistory.is_contiguous()
+                                 or not _bits_ok(dhistory)):
+        raise ValueError(f"dhistory: need a contiguous bf16 tensor of shape {(max(nseq, 0), W - 1, C)}")
     if dx is None:
         dx = torch.empty((rows, C), dtype=torch.bfloat16, device=dev)
     dxp, dx_ld = _rows2d(dx, "dx", C)
+    if dx.shape[0] != rows:
+        raise ValueError("dx: must have as many rows as x")
     if dweight is None:
         dweight = torch.empty((C, W), dtype=torch.float32, device=dev)
     if want_dbias is None:
@@ -259,9 +314,6 @@ def conv1d_bwd(x, dy, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqle
         want_dhistory = history is not None or dhistory is not None
     if want_dhistory and dhistory is None:
         dhistory = torch.empty((max(nseq, 0), W - 1, C), dtype=torch.bfloat16, device=dev)
-    for t, name, dt in ((dweight, "dweight", torch.float32), (dbias, "dbias", torch.float32)):
-        if t is not None and (t.dtype != dt or not t.is_contiguous()):
-            raise ValueError(f"{name}: need a contiguous float32 tensor")
     if workspace is None:
         need = lib.conv1d_bwd_workspace_bytes(rows, C)
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
@@ -270,7 +322,7 @@ def conv1d_bwd(x, dy, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqle
                         _lib.ACT[activation], dxp, dx_ld, dweight.data_ptr(),
                         None if dbias is None else dbias.data_ptr(),
                         None if dhistory is None else dhistory.data_ptr(), workspace.data_ptr(), wsb,
-                        _stream(stream))
+                        _stream(stream, dev))
     _lib.check(lib, st, "conv1d_bwd")
     return dx, dweight, (dbias if want_dbias else None), (dhistory if want_dhistory else None)
 
@@ -299,11 +351,12 @@ def conv1d_fwd_cf(x, weight, bias=None, *, activation="silu", out=None, stream=N
     W = _width(weight, D)
     wp, wd = _taps(weight, D, (D, W), "weight")
     bp, bd = _taps(bias, D, (D,), "bias")
+    _on_gpu(x.device, weight=weight, bias=bias, out=out)
     if out is None:
         out = torch.empty((B, D, T), dtype=torch.bfloat16, device=x.device)
     yp, ysb, ysd = _cf3d(out, "out", (B, D, T))
     st = lib.conv1d_fwd_cf(xp, B, D, T, xsb, xsd, wp, wd, W, bp, bd, _lib.ACT[activation], yp, ysb, ysd,
-                           _stream(stream))
+                           _stream(stream, x.device))
     _lib.check(lib, st, "conv1d_fwd_cf")
     return out
 
@@ -320,6 +373,9 @@ def conv1d_bwd_cf(x, dy, weight, bias=None, *, activation="silu", dx=None, dweig
     wp, wd = _taps(weight, D, (D, W), "weight")
     bp, bd = _taps(bias, D, (D,), "bias")
     dev = x.device
+    _on_gpu(dev, dy=dy, weight=weight, bias=bias, dx=dx, dweight=dweight, dbias=dbias, workspace=workspace)
+    _f32(dweight, (D, W), "dweight")
+    _f32(dbias, (D,), "dbias")
     if dx is None:
         dx = torch.empty((B, D, T), dtype=torch.bfloat16, device=dev)
     dxp, dxsb, dxsd = _cf3d(dx, "dx", (B, D, T))
@@ -334,6 +390,6 @@ def conv1d_bwd_cf(x, dy, weight, bias=None, *, activation="silu", dx=None, dweig
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     st = lib.conv1d_bwd_cf(xp, dyp, B, D, T, xsb, xsd, dysb, dysd, wp, wd, W, bp, bd, _lib.ACT[activation], dxp,
                            dxsb, dxsd, dweight.data_ptr(), dbias.data_ptr() if want_dbias else None,
-                           workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream, dev))
     _lib.check(lib, st, "conv1d_bwd_cf")
     return dx, dweight, (dbias if want_dbias else None)
