@@ -314,7 +314,7 @@ def layout_counters():
     from causal_depthwise_conv1d_width_amd import workloads as wl
     g = Gpu()
     torch = g.torch
-    c5 = wl.config_5()
+    c5 = wl.cp_share()
     cl = [g.prepare(c5) for _ in range(4)]
     rng = np.random.default_rng(5)
     B, D, T = 4, 4096, 4096
@@ -376,7 +376,7 @@ def main():
     g = Gpu()
     torch = g.torch
 
-    case = wl.config_5()
+    case = wl.cp_share()
     sets = [g.prepare(case) for _ in range(4)]
     fb, bb = fwd_bytes(case), bwd_bytes(case)
     # step k: forward on set k % 4, backward on set (k + 2) % 4 -> consecutive calls never share data
@@ -413,8 +413,8 @@ def main():
 
     if not args.no_extras:
         extras = {"copy_ceiling_GBps": round(g.copy_ceiling(), 1)}
-        for k in (1, 2, 3, 4):
-            c = wl.CONFIGS[k]()
+        for make in (wl.single_sequence, wl.varlen_pool, wl.prefill_pool, wl.train_seq_ids):
+            c = make()
             nb = fwd_bytes(c)
             nsets = int(min(8, max(2, -(-(1 << 30) // nb))))
             dd = [g.prepare(c) for _ in range(nsets)]
@@ -429,7 +429,7 @@ def main():
                 r.update({"bwd_GBps": round(gbps(nbb, msb), 1), "bwd_us": round(1e3 * msb, 2), "bwd_bytes": nbb})
             extras[c["name"]] = r
             del dd
-            if k == 3:  # decode step: one token for each of the 64 live slots of the prefill pool
+            if make is wl.prefill_pool:  # decode step: one token for each of the 64 live slots of the prefill pool
                 C = c["x"].shape[1]
                 x1 = g.bits(c["x"][:64])
                 pool = g.pool(c["pool"])

@@ -5,18 +5,20 @@ arithmetic.  Both the GPU tests / benchmark and the CPU oracle consume exactly t
 produces.  bf16 tensors are numpy ``uint16`` arrays of bit patterns (round-to-nearest-even of a
 float32 draw); FP32 taps and biases are ``float32``.
 
-Each ``config_N`` uses ``numpy.random.default_rng(1000 + N)`` (PCG64) and draws in the order the
-code reads.  The shapes follow the workload list of the packed causal conv1d pages:
-  1  one sequence, T = 64, C = 64, FP32 taps + bias, zero history, SiLU;
-  2  eight packed sequences (lengths uniform in 0..512, one forced empty), C = 2048, bf16 taps,
-     no bias, slot pool [16, C, 4] with one -1 sentinel and random has_initial_state;
-  3  32768 rows (last 256 padding), 64 lognormal-length sequences (median 256) summing to 32512,
-     C = 5632 (the GDP channel count 2048*2 + 4*128*2 + 4*128), FP32 taps + bias, pool [128, C, 4],
-     every sequence with initial state;
-  4  training: 4 x 4096 rows, C = 4096, 1-8 documents per batch row marked by per-token IDs, FP32
-     taps + bias, dy ~ N(0, 1);
-  5  context-parallel share: 16384 rows, C = 5632, 12 fragments at random cut points, 8 of which
-     read 3 caller history rows, FP32 taps, no bias, dy ~ N(0, 1).
+Every workload draws from its own ``numpy.random.default_rng`` seed (PCG64) in the order the code
+reads.  The shapes follow the workload list of the packed causal conv1d pages:
+  single_sequence   one sequence, T = 64, C = 64, FP32 taps + bias, zero history, SiLU (seed 1001);
+  varlen_pool       eight packed sequences (lengths uniform in 0..512, one forced empty), C = 2048,
+                    bf16 taps, no bias, slot pool [16, C, 4] with one -1 sentinel and random
+                    has_initial_state (seed 1002);
+  prefill_pool      32768 rows (last 256 padding), 64 lognormal-length sequences (median 256)
+                    summing to 32512, C = 5632 (the GDP channel count 2048*2 + 4*128*2 + 4*128),
+                    FP32 taps + bias, pool [128, C, 4], every sequence with initial state (seed 1003);
+  train_seq_ids     training: 4 x 4096 rows, C = 4096, 1-8 documents per batch row marked by
+                    per-token IDs, FP32 taps + bias, dy ~ N(0, 1) (seed 1004);
+  cp_share          context-parallel share: 16384 rows, C = 5632, 12 fragments at random cut
+                    points, 8 of which read 3 caller history rows, FP32 taps, no bias, dy ~ N(0, 1)
+                    (seed 1005).
 """
 import numpy as np
 
@@ -57,17 +59,17 @@ def pool_layout(values, layout):
     raise ValueError(layout)
 
 
-def config_1():
+def single_sequence():
     rng = np.random.default_rng(1001)
     T, C = 64, 64
     x = normal_bf16(rng, (T, C))
     w = uniform_f32(rng, (C, 4))
     b = (rng.standard_normal(C) * 0.1).astype(np.float32)
-    return dict(name="config1_single_seq_T64_C64", x=x, w=w, b=b,
+    return dict(name="single_seq_T64_C64", x=x, w=w, b=b,
                 cu_seqlens=np.array([0, T], dtype=np.int32), act="silu")
 
 
-def config_2(layout="hist"):
+def varlen_pool(layout="hist"):
     rng = np.random.default_rng(1002)
     N, C, slots, L = 8, 2048, 16, 4
     lengths = rng.integers(0, 513, size=N)
@@ -88,7 +90,7 @@ def config_2(layout="hist"):
         hi = rng.random(N) < 0.5
         if len({bool(hi[i]) for i in live_nonempty}) == 2:
             break
-    return dict(name=f"config2_varlen_N8_C2048_pool16_{layout}", x=x, w=w, b=None, cu_seqlens=cu,
+    return dict(name=f"varlen_N8_C2048_pool16_{layout}", x=x, w=w, b=None, cu_seqlens=cu,
                 pool=pool, cache_indices=ci, has_initial_state=hi.astype(np.uint8), act="silu",
                 empty=empty, sentinel=sentinel)
 
@@ -101,7 +103,7 @@ def lognormal_lengths(rng, n, total, median=256.0, sigma=1.17):
     return lengths
 
 
-def config_3():
+def prefill_pool():
     rng = np.random.default_rng(1003)
     N, rows, valid, C, slots, L = 64, 32768, 32512, GDP_CHANNELS, 128, 4
     lengths = lognormal_lengths(rng, N, valid)
@@ -113,7 +115,7 @@ def config_3():
     pool = normal_bf16(rng, (slots, C, L))
     ci = rng.permutation(slots)[:N].astype(np.int32)
     hi = np.ones(N, dtype=np.uint8)
-    return dict(name="config3_prefill_rows32768_N64_C5632_pool128", x=x, w=w, b=b, cu_seqlens=cu,
+    return dict(name="prefill_rows32768_N64_C5632_pool128", x=x, w=w, b=b, cu_seqlens=cu,
                 pool=pool, cache_indices=ci, has_initial_state=hi, act="silu")
 
 
@@ -132,7 +134,7 @@ def docs_seq_idx(rng, B, T, max_docs=8):
     return ids
 
 
-def config_4():
+def train_seq_ids():
     rng = np.random.default_rng(1004)
     B, T, C = 4, 4096, 4096
     seq_idx = docs_seq_idx(rng, B, T)
@@ -140,11 +142,11 @@ def config_4():
     w = uniform_f32(rng, (C, 4))
     b = (rng.standard_normal(C) * 0.1).astype(np.float32)
     dy = normal_bf16(rng, (B * T, C))
-    return dict(name="config4_train_B4_T4096_C4096_seqidx", x=x, w=w, b=b, seq_idx=seq_idx,
+    return dict(name="train_B4_T4096_C4096_seqidx", x=x, w=w, b=b, seq_idx=seq_idx,
                 seqlen=T, dy=dy, act="silu")
 
 
-def config_5():
+def cp_share():
     rng = np.random.default_rng(1005)
     S, C, nfrag, nhist = 16384, GDP_CHANNELS, 12, 8
     cuts = np.sort(rng.choice(np.arange(1, S), size=nfrag - 1, replace=False))
@@ -155,11 +157,12 @@ def config_5():
     x = normal_bf16(rng, (S, C))
     w = uniform_f32(rng, (C, 4))
     dy = normal_bf16(rng, (S, C))
-    return dict(name="config5_cp_share_S16384_C5632_12frag", x=x, w=w, b=None, cu_seqlens=cu,
+    return dict(name="cp_share_S16384_C5632_12frag", x=x, w=w, b=None, cu_seqlens=cu,
                 hist=hist, has_history=has_hist, dy=dy, act="silu")
 
 
-CONFIGS = {1: config_1, 2: config_2, 3: config_3, 4: config_4, 5: config_5}
+# every workload, in the order of the list above
+WORKLOADS = (single_sequence, varlen_pool, prefill_pool, train_seq_ids, cp_share)
 
 
 def random_case(rng, *, C=None, nseq=None, max_len=10, mode="cu", pool_layout_name=None,

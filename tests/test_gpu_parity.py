@@ -23,15 +23,15 @@ def _print_case(name, **kw):
 
 
 # ------------------------------------------------------------------ the five workloads
-def test_config1_forward(oracle):
-    case = wl.config_1()
+def test_single_sequence_forward(oracle):
+    case = wl.single_sequence()
     _print_case(case["name"])
     gh.check_fwd(oracle, case)
 
 
 @pytest.mark.parametrize("layout", ["hist", "chan"])
-def test_config2_forward_pool(oracle, layout):
-    case = wl.config_2(layout)
+def test_varlen_forward_pool(oracle, layout):
+    case = wl.varlen_pool(layout)
     _print_case(case["name"])
     y, pool = gh.check_fwd(oracle, case)
     # the empty sequence keeps its slot untouched; the sentinel's slot too
@@ -39,22 +39,22 @@ def test_config2_forward_pool(oracle, layout):
     assert np.array_equal(pool[ci[case["empty"]]], case["pool"][ci[case["empty"]]])
 
 
-def test_config3_forward_pool_padding(oracle):
-    case = wl.config_3()
+def test_prefill_forward_pool_padding(oracle):
+    case = wl.prefill_pool()
     _print_case(case["name"])
     y, _ = gh.check_fwd(oracle, case)
     assert (y[32512:] == wl.OUT_FILL).all(), "padding rows after the last offset must stay untouched"
 
 
-def test_config4_forward_backward(oracle):
-    case = wl.config_4()
+def test_train_seq_ids_forward_backward(oracle):
+    case = wl.train_seq_ids()
     _print_case(case["name"])
     gh.check_fwd(oracle, case)
     gh.check_bwd(oracle, case)
 
 
-def test_config5_forward_backward(oracle):
-    case = wl.config_5()
+def test_cp_share_forward_backward(oracle):
+    case = wl.cp_share()
     _print_case(case["name"])
     gh.check_fwd(oracle, case)
     gh.check_bwd(oracle, case)

@@ -21,8 +21,8 @@ def say(msg):
 
 def test_dweight_bitwise_reproducible():
     """Ten backward runs, fresh and garbage-filled workspaces, another stream: identical dw/db bits."""
-    say("determinism config4/config5")
-    for case in (wl.config_4(), wl.config_5()):
+    say("determinism: per-token-ID training and context-parallel share")
+    for case in (wl.train_seq_ids(), wl.cp_share()):
         x, dy = gh.dev_bits(case["x"]), gh.dev_bits(case["dy"])
         w, b = gh.dev_taps(case["w"]), gh.dev_taps(case.get("b"))
         kw = dict(cu_seqlens=gh.dev_i32(case.get("cu_seqlens")), seq_idx=gh.dev_i32(case.get("seq_idx")),
@@ -48,7 +48,7 @@ def test_dweight_bitwise_reproducible():
 
 def test_forward_recompute_bitwise_identical():
     say("forward recompute")
-    case = wl.config_5()
+    case = wl.cp_share()
     y1, _ = gh.gpu_fwd(case)
     y2, _ = gh.gpu_fwd(case)
     assert np.array_equal(y1, y2)

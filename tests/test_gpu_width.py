@@ -68,8 +68,8 @@ def test_width_short_sequences_across_ranges(oracle, W):
 
 def test_width3_context_parallel_full_size(oracle):
     rng = np.random.default_rng(75)
-    case = _narrow(wl.config_5(), 3, rng)
-    case["name"] = "width3-config5"
+    case = _narrow(wl.cp_share(), 3, rng)
+    case["name"] = "width3-cp-share"
     say(case["name"])
     gh.check_fwd(oracle, case)
     gh.check_bwd(oracle, case)
