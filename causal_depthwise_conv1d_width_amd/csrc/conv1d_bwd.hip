@@ -295,6 +295,18 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
     // the window rows ta-3 .. ta-1 and the sequence holding row ta
     Pk<CPL> wrow[3];
     load_window<CPL, VEC>(wrow, a.x, a.x_ld, ta, c0, C, active);
+    // the look-ahead rows tb .. lim-1 (at most three, the next range's first rows), loaded with
+    // the set-up: the end of the range then never waits on a memory round trip
+    Pk<CPL> LX[3], LG[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      LX[j] = zero_pk<CPL>();
+      LG[j] = zero_pk<CPL>();
+      if (active && tb + j < lim) {
+        LX[j] = load_row<CPL, VEC>(a.x + (tb + j) * a.x_ld, c0, C);
+        LG[j] = load_row<CPL, VEC>(a.dy + (tb + j) * a.dy_ld, c0, C);
+      }
+    }
     BwdSeq cs;
     cs.sd = seq_of_row<MODE>(a.seq, ta, dend, lim);
     const int64_t dist = ta - cs.sd.s < 3 ? ta - cs.sd.s : 3;
@@ -339,8 +351,8 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
         }
       }
     }
-    // the rest: remaining own rows (and partially active waves), then the look-ahead rows, which
-    // the next row range streams at the same time (cached loads)
+    // the rest: remaining own rows (and partially active waves), then the look-ahead rows
+    // fetched with the set-up (q - tb is 0, 1 or 2 there)
     for (; !done; q0 += CH) {
 #pragma unroll
       for (int r = 0; r < CH; ++r) {
@@ -352,8 +364,8 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
             X[0][r] = load_row<CPL, VEC, true>(a.x + q * a.x_ld, c0, C);
             G[0][r] = load_row<CPL, VEC, true>(a.dy + q * a.dy_ld, c0, C);
           } else {
-            X[0][r] = load_row<CPL, VEC>(a.x + q * a.x_ld, c0, C);
-            G[0][r] = load_row<CPL, VEC>(a.dy + q * a.dy_ld, c0, C);
+            X[0][r] = q == tb ? LX[0] : (q == tb + 1 ? LX[1] : LX[2]);
+            G[0][r] = q == tb ? LG[0] : (q == tb + 1 ? LG[1] : LG[2]);
           }
         }
       }
@@ -385,7 +397,8 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
 // Ordered reduce of the per-range partials: out[o] = sum over row ranges p of part[p][o], for
 // the flattened o = k*C + c (k = 0..3 dweight taps, 4 = dbias).  A wave owns 16 consecutive o;
 // lane l sums the ranges p = l/16, l/16 + 4, l/16 + 8, ... in ascending order (each load of
-// the wave reads four 64-byte runs; 16 loads are in flight per step), then a fixed two-level butterfly across lanes l, l^16,
+// the wave reads four 64-byte runs; 32 loads are in flight per step, so up to 128 ranges take
+// one memory round trip), then a fixed two-level butterfly across lanes l, l^16,
 // l^32, l^48 adds the four interleaved subsets:  (s0 + s1) + (s2 + s3).  The order is fixed, so
 // dweight/dbias are bitwise reproducible; no atomics.  The remaining threads write zero
 // d(history) rows of empty continuing fragments.
@@ -402,15 +415,15 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_reduce_kernel(const 
     const int64_t n = a.n_rowblocks;
     float s = 0.f;
     if (ok) {
-      // 16 partials of the subset per step, all loads issued before the first add: a call waits
-      // for ceil(n / 64) memory round trips, not one per four partials
+      // 32 partials of the subset per step, all loads issued before the first add: a call waits
+      // for ceil(n / 128) memory round trips, not one per four partials
       const float* p = a.part + o;
-      for (int64_t i0 = sub; i0 < n; i0 += 64) {
-        float v[16];
+      for (int64_t i0 = sub; i0 < n; i0 += 128) {
+        float v[32];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) v[k] = i0 + 4 * k < n ? p[(i0 + 4 * k) * nout] : 0.f;
+        for (int k = 0; k < 32; ++k) v[k] = i0 + 4 * k < n ? p[(i0 + 4 * k) * nout] : 0.f;
 #pragma unroll
-        for (int k = 0; k < 16; ++k)
+        for (int k = 0; k < 32; ++k)
           if (i0 + 4 * k < n) s += v[k];
       }
     }
@@ -430,7 +443,6 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_reduce_kernel(const 
   const int64_t i = hid / C, c = hid - i * C;
   if (a.hist.has_hist && !a.hist.has_hist[i]) return;
   if (a.seq.cu[i + 1] != a.seq.cu[i]) return;  // nonempty: written by the tile kernel
-#pragma unroll
   for (int j = 0; j < a.width - 1; ++j) a.dhist[(i * (a.width - 1) + j) * C + c] = 0;
 }
 

@@ -43,17 +43,27 @@ constexpr int64_t kFwdBlocks = CCONV_FWD_BLOCKS;
 constexpr int64_t kBwdBlocks = CCONV_BWD_BLOCKS;
 constexpr int64_t kFwdFixedRows = CCONV_FWD_FIXED_ROWS;
 constexpr int64_t kBwdFixedRows = CCONV_BWD_FIXED_ROWS;
-constexpr int64_t kRangeAlign = 8;  // range lengths are multiples of 8 rows
+#ifndef CCONV_RANGE_ALIGN
+#define CCONV_RANGE_ALIGN 8
+#endif
+constexpr int64_t kRangeAlign = CCONV_RANGE_ALIGN;  // range lengths are multiples of this
+constexpr int64_t kMinRangeRows = 8;                 // and at least this many rows
 
 // Rows per range for `rows` rows of `n_strips` channel strips and a target block count.  A
 // positive `fixed` length overrides the target (a build-time tuning knob).
+//
+// The dispatcher deals a one-round launch to the CUs in turn (blocks b, b + 256, b + 512, ...
+// share a CU), and blocks on a CU that holds fewer of them stream faster.  Yet neither an
+// exactly even split (16384 rows x 11 strips: 93 ranges of 177 rows) nor any fixed length from
+// 48 to 232 rows beat floor(target / n_strips) ranges per strip rounded up to 8 rows (90 ranges
+// of 184 rows there): the memory system as a whole, not the most loaded CU, sets the rate.
 inline int64_t range_rows_for(int64_t rows, int64_t n_strips, int64_t target_blocks, int64_t fixed = 0) {
   if (fixed > 0) return fixed;
   int64_t per_strip = target_blocks / (n_strips > 0 ? n_strips : 1);
   if (per_strip < 1) per_strip = 1;
   int64_t r = (rows + per_strip - 1) / per_strip;
   r = (r + kRangeAlign - 1) / kRangeAlign * kRangeAlign;
-  return r > 0 ? r : kRangeAlign;
+  return r > kMinRangeRows ? r : kMinRangeRows;
 }
 
 // The forward's range length.  Up to kFwdLongRows rows per range it is one round of ~kFwdBlocks
@@ -70,7 +80,6 @@ inline int64_t range_rows_for(int64_t rows, int64_t n_strips, int64_t target_blo
 #endif
 constexpr int64_t kFwdLongRows = CCONV_FWD_LONG_ROWS;
 constexpr int64_t kFwdShortRows = CCONV_FWD_SHORT_ROWS;
-static_assert(kFwdShortRows % kRangeAlign == 0, "range lengths are multiples of kRangeAlign");
 
 inline int64_t fwd_range_rows(int64_t rows, int64_t n_strips) {
   const int64_t r = range_rows_for(rows, n_strips, kFwdBlocks, kFwdFixedRows);
