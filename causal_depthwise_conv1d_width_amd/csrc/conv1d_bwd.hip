@@ -296,16 +296,22 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
     Pk<CPL> wrow[3];
     load_window<CPL, VEC>(wrow, a.x, a.x_ld, ta, c0, C, active);
     // the look-ahead rows tb .. lim-1 (at most three, the next range's first rows), loaded with
-    // the set-up: the end of the range then never waits on a memory round trip
-    Pk<CPL> LX[3], LG[3];
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      LX[j] = zero_pk<CPL>();
-      LG[j] = zero_pk<CPL>();
-      if (active && tb + j < lim) {
-        LX[j] = load_row<CPL, VEC>(a.x + (tb + j) * a.x_ld, c0, C);
-        LG[j] = load_row<CPL, VEC>(a.dy + (tb + j) * a.dy_ld, c0, C);
-      }
+    // the set-up: the end of the range then never waits on a memory round trip.  Named values,
+    // not an array: the row select below would otherwise become a runtime index, and the
+    // compiler then moved the array to LDS (the backward ran 10% slower).
+    Pk<CPL> lx0 = zero_pk<CPL>(), lx1 = zero_pk<CPL>(), lx2 = zero_pk<CPL>();
+    Pk<CPL> lg0 = zero_pk<CPL>(), lg1 = zero_pk<CPL>(), lg2 = zero_pk<CPL>();
+    if (active && tb < lim) {
+      lx0 = load_row<CPL, VEC>(a.x + tb * a.x_ld, c0, C);
+      lg0 = load_row<CPL, VEC>(a.dy + tb * a.dy_ld, c0, C);
+    }
+    if (active && tb + 1 < lim) {
+      lx1 = load_row<CPL, VEC>(a.x + (tb + 1) * a.x_ld, c0, C);
+      lg1 = load_row<CPL, VEC>(a.dy + (tb + 1) * a.dy_ld, c0, C);
+    }
+    if (active && tb + 2 < lim) {
+      lx2 = load_row<CPL, VEC>(a.x + (tb + 2) * a.x_ld, c0, C);
+      lg2 = load_row<CPL, VEC>(a.dy + (tb + 2) * a.dy_ld, c0, C);
     }
     BwdSeq cs;
     cs.sd = seq_of_row<MODE>(a.seq, ta, dend, lim);
@@ -364,8 +370,8 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
             X[0][r] = load_row<CPL, VEC, true>(a.x + q * a.x_ld, c0, C);
             G[0][r] = load_row<CPL, VEC, true>(a.dy + q * a.dy_ld, c0, C);
           } else {
-            X[0][r] = q == tb ? LX[0] : (q == tb + 1 ? LX[1] : LX[2]);
-            G[0][r] = q == tb ? LG[0] : (q == tb + 1 ? LG[1] : LG[2]);
+            X[0][r] = q == tb ? lx0 : (q == tb + 1 ? lx1 : lx2);
+            G[0][r] = q == tb ? lg0 : (q == tb + 1 ? lg1 : lg2);
           }
         }
       }
