@@ -48,9 +48,9 @@ def _taps(w, C, name, shape):
 
 
 def _width(w, C):
-    """Taps [C, W] with W in 2..4 (the width of the depthwise filter)."""
-    if w is None or w.ndim != 2 or w.shape[0] != C or not 2 <= w.shape[1] <= 4:
-        raise OracleError("weight: need taps of shape [C, W] with 2 <= W <= 4")
+    """Taps [C, W] with W in 2..8 (the width of the depthwise filter)."""
+    if w is None or w.ndim != 2 or w.shape[0] != C or not 2 <= w.shape[1] <= 8:
+        raise OracleError("weight: need taps of shape [C, W] with 2 <= W <= 8")
     return int(w.shape[1])
 
 

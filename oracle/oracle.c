@@ -214,7 +214,7 @@ static float stencil_w(float b, const float* wt, const float* u, int W) {
 
 /* ================================================================ forward
    y[t][c] for every row of every segment; pool positions 0:3 of live nonempty sequences.
-   width W (2..4): taps [C, W], W - 1 history values (caller history rows [nseq, W-1, C]); the
+   width W (2..8): taps [C, W], W - 1 history values (caller history rows [nseq, W-1, C]); the
    pool form is width four only.  act: 0 = identity, 1 = SiLU.  Returns OR_OK / OR_INVALID /
    OR_NOMEM. */
 int oracle_fwd(const uint16_t* x, int64_t rows, int64_t C, int64_t x_ld, const void* w, int w_f32,
@@ -226,7 +226,7 @@ int oracle_fwd(const uint16_t* x, int64_t rows, int64_t C, int64_t x_ld, const v
   if (!x && rows > 0) return OR_INVALID;
   if (!w || !y || C < 1 || x_ld < C || y_ld < C || rows < 0 || (act != 0 && act != 1))
     return OR_INVALID;
-  if (width < 2 || width > 4 || (pool && width != 4)) return OR_INVALID;
+  if (width < 2 || width > 8 || (pool && width != 4)) return OR_INVALID;
   if (pool && hist) return OR_INVALID;
   if ((pool || hist) && !cu_seqlens && seq_idx) return OR_INVALID;
   const int W = width, H = width - 1;
@@ -242,8 +242,8 @@ int oracle_fwd(const uint16_t* x, int64_t rows, int64_t C, int64_t x_ld, const v
   int err = 0;
 #pragma omp parallel
   {
-    uint16_t* ubits = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(maxlen + 3));
-    float* u = (float*)malloc(sizeof(float) * (size_t)(maxlen + 3));
+    uint16_t* ubits = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(maxlen + H));
+    float* u = (float*)malloc(sizeof(float) * (size_t)(maxlen + H));
     if (!ubits || !u) {
 #pragma omp atomic write
       err = 1;
@@ -251,7 +251,7 @@ int oracle_fwd(const uint16_t* x, int64_t rows, int64_t C, int64_t x_ld, const v
 #pragma omp for schedule(static)
       for (int64_t cb = 0; cb < (C + 63) / 64; ++cb) {
         for (int64_t c = cb * 64; c < C && c < cb * 64 + 64; ++c) {
-          float wt[4];
+          float wt[8];
           for (int kk = 0; kk < W; ++kk) wt[kk] = load_tap(w, w_f32, c * W + kk);
           float bias = b ? load_tap(b, b_f32, c) : 0.0f;
           for (int64_t q = 0; q < ns; ++q) {
@@ -410,7 +410,7 @@ int oracle_bwd(const uint16_t* x, const uint16_t* dy, int64_t rows, int64_t C, i
   if (!w || !dw || C < 1 || x_ld < C || dy_ld < C || dx_ld < C || rows < 0 ||
       (act != 0 && act != 1))
     return OR_INVALID;
-  if (width < 2 || width > 4) return OR_INVALID;
+  if (width < 2 || width > 8) return OR_INVALID;
   if (hist && !cu_seqlens && seq_idx) return OR_INVALID;
   if (dhist && !hist) return OR_INVALID;
   const int W = width, H = width - 1;
@@ -425,8 +425,8 @@ int oracle_bwd(const uint16_t* x, const uint16_t* dy, int64_t rows, int64_t C, i
   int err = 0;
 #pragma omp parallel
   {
-    double* u = (double*)malloc(sizeof(double) * (size_t)(maxlen + 3));
-    float* uf = (float*)malloc(sizeof(float) * (size_t)(maxlen + 3));
+    double* u = (double*)malloc(sizeof(double) * (size_t)(maxlen + H));
+    float* uf = (float*)malloc(sizeof(float) * (size_t)(maxlen + H));
     double* dz = (double*)malloc(sizeof(double) * (size_t)(maxlen + 1));
     if (!u || !uf || !dz) {
 #pragma omp atomic write
@@ -435,10 +435,10 @@ int oracle_bwd(const uint16_t* x, const uint16_t* dy, int64_t rows, int64_t C, i
 #pragma omp for schedule(static)
       for (int64_t cb = 0; cb < (C + 63) / 64; ++cb) {
         for (int64_t c = cb * 64; c < C && c < cb * 64 + 64; ++c) {
-          float wf[4];
+          float wf[8];
           for (int q = 0; q < W; ++q) wf[q] = load_tap(w, w_f32, c * W + q);
           float bias = b ? load_tap(b, b_f32, c) : 0.0f;
-          double dw_acc[4] = {0, 0, 0, 0}, db_acc = 0;
+          double dw_acc[8] = {0, 0, 0, 0, 0, 0, 0, 0}, db_acc = 0;
           for (int64_t q = 0; q < ns; ++q) {
             int64_t s = segs[q].s, n = segs[q].e - segs[q].s, i = segs[q].i;
             for (int j = 0; j < H; ++j) u[j] = bf16_bits_to_float(history_bits(&k, i, c, C, j));

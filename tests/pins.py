@@ -499,11 +499,12 @@ def _narrow(case, W, rng):
 
 
 def pin_width_bruteforce(o, seed=25):
-    """Widths 2 and 3 (Megatron-Core causal_conv1d_cp, Parameters weight [D, W]): forward against the
-    dense Toeplitz form with W taps and W-1 history rows, backward against its autograd."""
+    """Widths 2, 3 and 5..8 (Megatron-Core causal_conv1d_cp, Parameters weight [D, W]): forward
+    against the dense Toeplitz form with W taps and W-1 history rows, backward against its
+    autograd."""
     rng = np.random.default_rng(seed)
-    for W in (2, 3):
-        for q in range(8):
+    for W in (2, 3, 5, 6, 7, 8):
+        for q in range(8 if W < 4 else 5):
             mode = "idx" if q % 4 == 3 else "cu"
             base = wl.random_case(rng, mode=mode, with_hist=(mode == "cu" and q % 2 == 0), w_f32=bool(q % 3),
                                   act="silu" if q % 5 else "none", force_empty=bool(q % 2))
@@ -549,12 +550,44 @@ def pin_width_closed_forms(o, seed=26):
     assert with_pool_rejected, "the pool form is width four only"
 
 
+def pin_wide_closed_forms(o, seed=27):
+    """Width 8: unit taps e_k read the extended sequence k - 7 rows back, bit for bit, so every tap
+    and all seven history rows land where the order (oldest history row first, tap W-1 on the
+    current row) says; with tap k = 1 only, a sequence of n rows reads history rows k .. 6 then
+    its own first rows.  Per-token IDs reset to zero history at every boundary."""
+    rng = np.random.default_rng(seed)
+    C, n, W = 3, 11, 8
+    x = wl.normal_bf16(rng, (n, C))
+    hist = wl.normal_bf16(rng, (1, W - 1, C))
+    cu = np.array([0, n], np.int32)
+    u = np.concatenate([hist[0], x], axis=0)  # extended sequence, oldest first
+    for k in range(W):
+        e = np.zeros((C, W), np.float32)
+        e[:, k] = 1.0
+        y = o.fwd(x, e, None, cu_seqlens=cu, hist=hist, act="none")
+        assert np.array_equal(y, u[k:k + n]), f"width-8 unit tap {k}"
+    # per-token IDs: two documents, zero history at each start
+    ids = np.array([0] * 5 + [1] * 6, np.int32)
+    e = np.zeros((C, W), np.float32)
+    e[:, 2] = 1.0  # reads five rows back
+    y = o.fwd(x, e, None, seq_idx=ids, seqlen=n, act="none")
+    want = np.zeros_like(x)
+    want[5 + 5:] = x[5:6]
+    assert np.array_equal(y, want), "width-8 tap reading five rows back, reset at a document start"
+    rejected = False
+    try:
+        o.fwd(x, np.zeros((C, 9), np.float32), None, cu_seqlens=cu, act="none")
+    except Exception:
+        rejected = True
+    assert rejected, "widths above 8 are rejected"
+
+
 ALL_PINS = [pin_rounding, pin_forward_bruteforce, pin_forward_conv1d_library, pin_forward_closed_forms,
             pin_segment_invariants, pin_pool_invariants, pin_decode_equals_unit_prefill,
             pin_cp_fragments_forward, pin_backward_autograd, pin_backward_finite_differences,
             pin_backward_linear_closed_form, pin_cp_fragments_backward, pin_spec_update_bruteforce,
             pin_spec_protocol_equals_prefill, pin_channels_first_conv1d,
-            pin_width_bruteforce, pin_width_closed_forms]
+            pin_width_bruteforce, pin_width_closed_forms, pin_wide_closed_forms]
 
 
 def golden_dyadic():
