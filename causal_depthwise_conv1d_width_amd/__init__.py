@@ -107,10 +107,11 @@ def _pool(conv_state, cache_indices, has_initial_state, C):
     return p
 
 
-def _width(weight, C):
-    """Filter width W from taps [C, W], W in 2..4."""
-    if weight is None or weight.dim() != 2 or weight.shape[0] != C or not 2 <= weight.shape[1] <= 4:
-        raise ValueError(f"weight: need taps of shape [{C}, W] with 2 <= W <= 4")
+def _width(weight, C, max_width=8):
+    """Filter width W from taps [C, W], W in 2..max_width (8 for the channel-last calls, 4 for the
+    channels-first ones)."""
+    if weight is None or weight.dim() != 2 or weight.shape[0] != C or not 2 <= weight.shape[1] <= max_width:
+        raise ValueError(f"weight: need taps of shape [{C}, W] with 2 <= W <= {max_width}")
     return int(weight.shape[1])
 
 
@@ -348,7 +349,7 @@ def conv1d_fwd_cf(x, weight, bias=None, *, activation="silu", out=None, stream=N
     lib = _lib.load()
     B, D, T = x.shape
     xp, xsb, xsd = _cf3d(x, "x")
-    W = _width(weight, D)
+    W = _width(weight, D, max_width=4)
     wp, wd = _taps(weight, D, (D, W), "weight")
     bp, bd = _taps(bias, D, (D,), "bias")
     _on_gpu(x.device, weight=weight, bias=bias, out=out)
@@ -369,7 +370,7 @@ def conv1d_bwd_cf(x, dy, weight, bias=None, *, activation="silu", dx=None, dweig
     B, D, T = x.shape
     xp, xsb, xsd = _cf3d(x, "x")
     dyp, dysb, dysd = _cf3d(dy, "dy", (B, D, T))
-    W = _width(weight, D)
+    W = _width(weight, D, max_width=4)
     wp, wd = _taps(weight, D, (D, W), "weight")
     bp, bd = _taps(bias, D, (D,), "bias")
     dev = x.device

@@ -124,7 +124,8 @@ size_t conv1d_bwd_workspace_bytes(int64_t rows, int64_t C) {
   if (rows <= 0 || C <= 0 || !mul_ok(rows, C)) return 0;  // out-of-range sizes fail in the call itself
   const int64_t rr = range_rows_for(rows, ceil_div(C, kBlockChannels), kBwdBlocks, kBwdFixedRows);
   const size_t nrb = (size_t)((rows + rr - 1) / rr);
-  const size_t bytes = nrb * 5u * (size_t)C * sizeof(float);
+  // room for any filter width (partial_rows(width) <= partial_rows(kMaxWidth))
+  const size_t bytes = nrb * (size_t)partial_rows(kMaxWidth) * (size_t)C * sizeof(float);
   return (bytes + kWsAlign - 1) / kWsAlign * kWsAlign;
 }
 
@@ -152,7 +153,7 @@ int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void*
   (void)ws;
   (void)ws_bytes;
   if (rows < 0 || C < 1 || x_ld < C || y_ld < C || !w || !dtype_ok(w_dtype)) return CONV1D_EINVAL;
-  if (width < 2 || width > 4) return CONV1D_EINVAL;
+  if (width < 2 || width > kMaxWidth) return CONV1D_EINVAL;
   if (b && !dtype_ok(b_dtype)) return CONV1D_EINVAL;
   if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
   if (rows > 0 && (!x || !y)) return CONV1D_EINVAL;
@@ -274,7 +275,7 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
                void* dhist, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (rows < 0 || C < 1 || x_ld < C || dy_ld < C || dx_ld < C || !w || !dtype_ok(w_dtype) || !dw)
     return CONV1D_EINVAL;
-  if (width < 2 || width > 4) return CONV1D_EINVAL;
+  if (width < 2 || width > kMaxWidth) return CONV1D_EINVAL;
   if (b && !dtype_ok(b_dtype)) return CONV1D_EINVAL;
   if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
   if (rows > 0 && (!x || !dy || !dx)) return CONV1D_EINVAL;
@@ -313,7 +314,7 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
                    (!dhist || aligned(dhist, 16));
   const int64_t rr = range_rows_for(rows, ceil_div(C, kBlockChannels), kBwdBlocks, kBwdFixedRows);
   const uint64_t nblk = (uint64_t)ceil_div(C, kBlockChannels) * ceil_div(rows, rr);
-  if (nblk > 0x7fffffffull || (uint64_t)((20 + (nseq > 0 ? nseq : 0)) * C) / 256 > 0x7fffffffull)
+  if (nblk > 0x7fffffffull || (uint64_t)((36 + (nseq > 0 ? nseq : 0)) * C) / 256 > 0x7fffffffull)
     return CONV1D_EINVAL;
 
   BwdArgs a{};

@@ -23,22 +23,25 @@
 // the partials of all row ranges in ascending range order.  No atomics anywhere, so the bits
 // depend only on the input values and the range length, never on scheduling or on the
 // workspace address.
+#include <type_traits>
+
 #include "conv1d_device.h"
 
 namespace cconv {
 
-// Width W: W-1 history rows fill the last W-1 window slots (j >= 4-W), the rest stay zero.
-template <int CPL, bool VEC, int W>
+// Width W: W-1 history rows fill the last W-1 of the H window slots (j >= R-W), the rest stay zero.
+template <int CPL, bool VEC, int W, int H = Win<W>::H>
 __device__ __forceinline__ void load_hist_rows(const HistArgs& hist, int64_t idx, int64_t c0, int64_t C,
-                                               bool active, float (&h)[3][CPL]) {
+                                               bool active, float (&h)[H][CPL]) {
+  constexpr int R = Win<W>::R;
 #pragma unroll
-  for (int j = 0; j < 3; ++j)
+  for (int j = 0; j < H; ++j)
 #pragma unroll
     for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
   if (idx >= 0 && hist.ptr && active && (!hist.has_hist || hist.has_hist[idx])) {
 #pragma unroll
-    for (int j = 4 - W; j < 3; ++j)
-      unpack(load_row<CPL, VEC>(hist.ptr + (idx * (W - 1) + j - (4 - W)) * C, c0, C), h[j]);
+    for (int j = R - W; j < H; ++j)
+      unpack(load_row<CPL, VEC>(hist.ptr + (idx * (W - 1) + j - (R - W)) * C, c0, C), h[j]);
   }
 }
 
@@ -52,56 +55,56 @@ __device__ __forceinline__ void load_hist_rows(const HistArgs& hist, int64_t idx
 #define CCONV_BWD_DEPTH 2
 #endif
 
-// Per-lane state of the backward stream (CPL channels).
-template <int CPL>
+// Per-lane state of the backward stream (CPL channels) with a ring of R slots.
+template <int CPL, int R>
 struct BwdState {
-  float wk[4][CPL], bias[CPL];
-  float u[4][CPL];    // extended-sequence ring, slot = (row - run start) mod 4
-  float g[4][CPL];    // dz ring, same slots
-  float acc[5][CPL];  // dw_0..3, db partial sums over the wave's rows
+  float wk[R][CPL], bias[CPL];
+  float u[R][CPL];        // extended-sequence ring, slot = (row - run start) mod R
+  float g[R][CPL];        // dz ring, same slots
+  float acc[R + 1][CPL];  // dw per tap slot, then db: partial sums over the wave's rows
 };
 
 // One real row q (ring slot r): recompute z, dz = dy * act'(z); dweight/dbias sums when `own`.
-// Tap k (k = 4-W .. 3) reads ring slot (r+1+k) % 4: rows q-3 .. q.
-template <int CPL, bool SILU, int W>
-__device__ __forceinline__ void bwd_row(BwdState<CPL>& st, const Pk<CPL>& xr, const Pk<CPL>& gr, int r, bool own) {
-  unpack(xr, st.u[r % 4]);
+// Tap slot k (k = R-W .. R-1) reads ring slot (r+1+k) % R: rows q-(R-1) .. q.
+template <int CPL, bool SILU, int W, int R = Win<W>::R>
+__device__ __forceinline__ void bwd_row(BwdState<CPL, R>& st, const Pk<CPL>& xr, const Pk<CPL>& gr, int r, bool own) {
+  unpack(xr, st.u[r % R]);
   float dyv[CPL];
   unpack(gr, dyv);
 #pragma unroll
   for (int ch = 0; ch < CPL; ++ch) {
     float z = st.bias[ch];
 #pragma unroll
-    for (int k = 4 - W; k < 4; ++k) z = __builtin_fmaf(st.wk[k][ch], st.u[(r + 1 + k) % 4][ch], z);
+    for (int k = R - W; k < R; ++k) z = __builtin_fmaf(st.wk[k][ch], st.u[(r + 1 + k) % R][ch], z);
     float dz = dyv[ch];
     if (SILU) {
       const float sg = sigmoid_f32(z);
       dz = dz * (sg * __builtin_fmaf(z, 1.0f - sg, 1.0f));
     }
-    st.g[r % 4][ch] = dz;
+    st.g[r % R][ch] = dz;
   }
   if (own) {
 #pragma unroll
     for (int ch = 0; ch < CPL; ++ch) {
 #pragma unroll
-      for (int k = 4 - W; k < 4; ++k)
-        st.acc[k][ch] = __builtin_fmaf(st.g[r % 4][ch], st.u[(r + 1 + k) % 4][ch], st.acc[k][ch]);
-      st.acc[4][ch] += st.g[r % 4][ch];
+      for (int k = R - W; k < R; ++k)
+        st.acc[k][ch] = __builtin_fmaf(st.g[r % R][ch], st.u[(r + 1 + k) % R][ch], st.acc[k][ch]);
+      st.acc[R][ch] += st.g[r % R][ch];
     }
   }
 }
 
-// The value of row p = q - 3 at step q (ring slot r of row q): w3 dz[p] + w2 dz[p+1] + w1 dz[p+2]
-// + w0 dz[p+3], taps below 4-W left out (tap k reads ring slot (r+4-k) % 4).  Ring slots of rows
-// before a sequence's start hold dz = 0, so for the rows before a sequence this is the gradient
-// of its history rows.
-template <int CPL, int W>
-__device__ __forceinline__ void bwd_back(const BwdState<CPL>& st, int r, float (&d)[CPL]) {
+// The value of row p = q - (R-1) at step q (ring slot r of row q): sum over tap slots k of
+// w_k dz[p + R-1-k], i.e. the last tap on dz[p] and the first tap on dz[p + W-1]; tap slots below
+// R-W left out (slot k reads ring slot (r+R-k) % R).  Ring slots of rows before a sequence's
+// start hold dz = 0, so for the rows before a sequence this is the gradient of its history rows.
+template <int CPL, int W, int R = Win<W>::R>
+__device__ __forceinline__ void bwd_back(const BwdState<CPL, R>& st, int r, float (&d)[CPL]) {
 #pragma unroll
   for (int ch = 0; ch < CPL; ++ch) {
-    float v = st.wk[3][ch] * st.g[(r + 1) % 4][ch];
+    float v = st.wk[R - 1][ch] * st.g[(r + 1) % R][ch];
 #pragma unroll
-    for (int k = 2; k >= 4 - W; --k) v = __builtin_fmaf(st.wk[k][ch], st.g[(r + 4 - k) % 4][ch], v);
+    for (int k = R - 2; k >= R - W; --k) v = __builtin_fmaf(st.wk[k][ch], st.g[(r + R - k) % R][ch], v);
     d[ch] = v;
   }
 }
@@ -127,24 +130,28 @@ __device__ __forceinline__ void bwd_route(const BwdArgs& a, const BwdSeq& cs, in
   }
 }
 
-// The current sequence ends right before row e (ring slot r): the values of its last three rows
-// e-3, e-2, e-1 only take dz of rows before e (taps below 4-W left out).
-template <int CPL, bool VEC, int W>
-__device__ __forceinline__ void bwd_flush(const BwdArgs& a, const BwdState<CPL>& st, const BwdSeq& cs, int r, int64_t e,
-                                          int64_t ta, int64_t tb, int64_t c0, bool active) {
-  float v3[CPL], v2[CPL], v1[CPL];
+// The current sequence ends right before row e (ring slot r): the values of its last H rows
+// e-H .. e-1 only take dz of rows before e (tap slots below R-W left out), summed in the order of
+// bwd_back.
+template <int CPL, bool VEC, int W, int R = Win<W>::R>
+__device__ __forceinline__ void bwd_flush(const BwdArgs& a, const BwdState<CPL, R>& st, const BwdSeq& cs, int r,
+                                          int64_t e, int64_t ta, int64_t tb, int64_t c0, bool active) {
+  constexpr int H = R - 1;
+  float v[H][CPL];  // v[j-1]: row e - j
 #pragma unroll
-  for (int ch = 0; ch < CPL; ++ch) {
-    const float g3 = st.g[(r + 1) % 4][ch], g2 = st.g[(r + 2) % 4][ch], g1 = st.g[(r + 3) % 4][ch];
-    float t3 = __builtin_fmaf(st.wk[2][ch], g2, st.wk[3][ch] * g3);
-    if (W >= 3) t3 = __builtin_fmaf(st.wk[1][ch], g1, t3);
-    v3[ch] = t3;
-    v2[ch] = __builtin_fmaf(st.wk[2][ch], g1, st.wk[3][ch] * g2);
-    v1[ch] = st.wk[3][ch] * g1;
+  for (int j = H; j >= 1; --j) {
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch) {
+      // tap slot k of row e-j reads dz of row e-j+R-1-k, ring slot (r + 2R-1-j-k) % R
+      float t = st.wk[R - 1][ch] * st.g[(r + R - j) % R][ch];
+#pragma unroll
+      for (int k = R - 2; k >= (R - W > R - j ? R - W : R - j); --k)
+        t = __builtin_fmaf(st.wk[k][ch], st.g[(r + 2 * R - 1 - j - k) % R][ch], t);
+      v[j - 1][ch] = t;
+    }
   }
-  bwd_route<CPL, VEC, W>(a, cs, e - 3, ta, tb, v3, c0, active);
-  bwd_route<CPL, VEC, W>(a, cs, e - 2, ta, tb, v2, c0, active);
-  bwd_route<CPL, VEC, W>(a, cs, e - 1, ta, tb, v1, c0, active);
+#pragma unroll
+  for (int j = H; j >= 1; --j) bwd_route<CPL, VEC, W>(a, cs, e - j, ta, tb, v[j - 1], c0, active);
 }
 
 template <int MODE>
@@ -156,46 +163,48 @@ __device__ __forceinline__ bool bwd_wants_dh(const BwdArgs& a, const SeqDesc& sd
   }
 }
 
-// Row q = cs.sd.s (ring slot r), the first row of a sequence, is next: the three window slots
-// take its history and dz = 0.
-template <int CPL, bool VEC, int MODE, int W>
-__device__ __forceinline__ void bwd_enter(const BwdArgs& a, BwdState<CPL>& st, BwdSeq& cs, int r, int64_t c0,
+// Row q = cs.sd.s (ring slot r), the first row of a sequence, is next: the H window slots take
+// its history and dz = 0.
+template <int CPL, bool VEC, int MODE, int W, int R = Win<W>::R>
+__device__ __forceinline__ void bwd_enter(const BwdArgs& a, BwdState<CPL, R>& st, BwdSeq& cs, int r, int64_t c0,
                                           bool active) {
-  float h[3][CPL];
+  constexpr int H = R - 1;
+  float h[H][CPL];
   if constexpr (MODE != MODE_IDX) {
     load_hist_rows<CPL, VEC, W>(a.hist, cs.sd.idx, c0, a.C, active, h);
   } else {
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+    for (int j = 0; j < H; ++j)
 #pragma unroll
       for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
   }
   cs.dh = bwd_wants_dh<MODE>(a, cs.sd);
 #pragma unroll
-  for (int j = 0; j < 3; ++j)
+  for (int j = 0; j < H; ++j)
 #pragma unroll
     for (int ch = 0; ch < CPL; ++ch) {
-      st.u[(r + 1 + j) % 4][ch] = h[j][ch];
-      st.g[(r + 1 + j) % 4][ch] = 0.f;
+      st.u[(r + 1 + j) % R][ch] = h[j][ch];
+      st.g[(r + 1 + j) % R][ch] = 0.f;
     }
 }
 
-// CH rows starting at q0 (ring slot of row q0 + r is r mod 4).  The stream covers the own rows
-// [ta, tb) and then up to three look-ahead rows of the sequence that holds row tb - 1, which
-// finish the last dx rows; it ends (done) at that sequence's end or at tb + 3.  A chunk of own
-// rows of one sequence, at least three rows past both its start and the range start, is a
-// straight recompute-and-dx; any other chunk takes the row-by-row path.
-template <int CPL, bool VEC, int MODE, int CH, bool SILU, bool FULL, int W>
-__device__ __forceinline__ void bwd_chunk(const BwdArgs& a, BwdState<CPL>& st, BwdSeq& cs, const Pk<CPL> (&X)[CH],
+// CH rows starting at q0 (ring slot of row q0 + r is r mod R).  The stream covers the own rows
+// [ta, tb) and then up to H look-ahead rows of the sequence that holds row tb - 1, which finish
+// the last dx rows; it ends (done) at that sequence's end or at tb + H.  A chunk of own rows of
+// one sequence, at least H rows past both its start and the range start, is a straight
+// recompute-and-dx; any other chunk takes the row-by-row path.
+template <int CPL, bool VEC, int MODE, int CH, bool SILU, bool FULL, int W, int R = Win<W>::R>
+__device__ __forceinline__ void bwd_chunk(const BwdArgs& a, BwdState<CPL, R>& st, BwdSeq& cs, const Pk<CPL> (&X)[CH],
                                           const Pk<CPL> (&G)[CH], int64_t q0, int64_t ta, int64_t tb, int64_t dend,
                                           int64_t lim, int64_t c0, bool active, bool& done) {
-  if (q0 + CH <= tb && cs.sd.e >= q0 + CH && q0 >= cs.sd.s + 3 && q0 >= ta + 3) {
+  constexpr int H = R - 1;
+  if (q0 + CH <= tb && cs.sd.e >= q0 + CH && q0 >= cs.sd.s + H && q0 >= ta + H) {
 #pragma unroll
     for (int r = 0; r < CH; ++r) {
       bwd_row<CPL, SILU, W>(st, X[r], G[r], r, true);
       float d[CPL];
       bwd_back<CPL, W>(st, r, d);
-      if (FULL || active) store_row<CPL, VEC, true>(a.dx + (q0 + r - 3) * a.dx_ld, c0, a.C, pack(d));
+      if (FULL || active) store_row<CPL, VEC, true>(a.dx + (q0 + r - H) * a.dx_ld, c0, a.C, pack(d));
     }
     return;
   }
@@ -211,12 +220,12 @@ __device__ __forceinline__ void bwd_chunk(const BwdArgs& a, BwdState<CPL>& st, B
         bwd_enter<CPL, VEC, MODE, W>(a, st, cs, r, c0, active);
       }
     }
-    if (!done && q >= tb + 3) done = true;
+    if (!done && q >= tb + H) done = true;
     if (!done) {
       bwd_row<CPL, SILU, W>(st, X[r], G[r], r, q < tb);
       float d[CPL];
       bwd_back<CPL, W>(st, r, d);
-      bwd_route<CPL, VEC, W>(a, cs, q - 3, ta, tb, d, c0, active);
+      bwd_route<CPL, VEC, W>(a, cs, q - H, ta, tb, d, c0, active);
     }
   }
 }
@@ -235,6 +244,16 @@ __device__ __forceinline__ void bwd_load(Pk<CPL> (&X)[CH], Pk<CPL> (&G)[CH], con
   }
 }
 
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>): a loop whose index must stay
+// a compile-time constant (it picks a register buffer) however large the body is.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void unroll_steps(F& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    unroll_steps<N, I + 1>(f);
+  }
+}
+
 // Occupancy floor: a launch is sized for 4 waves per SIMD (one round of ~1024 blocks), so the
 // per-token-ID variant, which would otherwise take 131 VGPRs (3 waves), is held to 128.  At width
 // four that spills two 64-bit values that live from the set-up to the epilogue: they are stored
@@ -242,16 +261,19 @@ __device__ __forceinline__ void bwd_load(Pk<CPL> (&X)[CH], Pk<CPL> (&G)[CH], con
 #ifndef CCONV_BWD_WAVES_PER_EU
 #define CCONV_BWD_WAVES_PER_EU 4
 #endif
+// The floor holds for widths up to four; the eight-slot ring of wider filters needs more than
+// 128 VGPRs and would spill under it, so those run at the occupancy their registers allow.
 #if CCONV_BWD_WAVES_PER_EU > 0
-#define CCONV_BWD_OCCUPANCY __attribute__((amdgpu_waves_per_eu(CCONV_BWD_WAVES_PER_EU)))
+#define CCONV_BWD_OCCUPANCY __attribute__((amdgpu_waves_per_eu(W <= 4 ? CCONV_BWD_WAVES_PER_EU : 1)))
 #else
 #define CCONV_BWD_OCCUPANCY
 #endif
 
 template <int CPL, bool VEC, int MODE, bool SILU, int W>
 __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_kernel(const BwdArgs a) {
-  constexpr int CH = CCONV_BWD_CHUNK;  // rows per unrolled chunk (a multiple of the 4-slot rings)
-  static_assert(CH % 4 == 0, "chunks must keep the ring slot of a row fixed");
+  constexpr int R = Win<W>::R, H = Win<W>::H;  // ring slots, history values
+  constexpr int CH = CCONV_BWD_CHUNK % R == 0 ? CCONV_BWD_CHUNK : R;  // rows per unrolled chunk
+  static_assert(CH % R == 0, "chunks must keep the ring slot of a row fixed");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -270,15 +292,15 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
   ta = ta < dend ? ta : dend;
   tb = tb < dend ? tb : dend;
 
-  BwdState<CPL> st;
+  BwdState<CPL, R> st;
 #pragma unroll
-  for (int k = 0; k < 5; ++k)
+  for (int k = 0; k < R + 1; ++k)
 #pragma unroll
     for (int ch = 0; ch < CPL; ++ch) st.acc[k][ch] = 0.f;
 
   if (ta < tb) {
     load_taps<CPL, W>(a.w, a.w_f32, a.b, a.b_f32, c0, C, st.wk, st.bias);
-    const int64_t lim = (tb + 3 < dend) ? tb + 3 : dend;  // sequence ends matter up to tb + 3
+    const int64_t lim = (tb + H < dend) ? tb + H : dend;  // sequence ends matter up to tb + H
 
     // full chunks of own rows, software-pipelined with NB register buffers (see the forward)
     const int nfull = (full && CCONV_BWD_PIPELINE) ? (int)((tb - ta) / CH) : 0;
@@ -292,50 +314,51 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
       for (int b = 0; b + 1 < NB; ++b) bwd_load<CPL, VEC, CH>(X[b], G[b], a, q0 + b * CH, qlast, c0);
     }
 
-    // the window rows ta-3 .. ta-1 and the sequence holding row ta
-    Pk<CPL> wrow[3];
-    load_window<CPL, VEC>(wrow, a.x, a.x_ld, ta, c0, C, active);
-    // the look-ahead rows tb .. lim-1 (at most three, the next range's first rows), loaded with
-    // the set-up: the end of the range then never waits on a memory round trip.  Named values,
-    // not an array: the row select below would otherwise become a runtime index, and the
-    // compiler then moved the array to LDS (the backward ran 10% slower).
+    // the window rows ta-H .. ta-1 and the sequence holding row ta
+    Pk<CPL> wrow[H];
+    load_window<CPL, VEC, H>(wrow, a.x, a.x_ld, ta, c0, C, active);
+    // the look-ahead rows tb .. lim-1 (at most three at widths up to four: the next range's first
+    // rows), loaded with the set-up: the end of the range then never waits on a memory round
+    // trip.  Named values, not an array: the row select below would otherwise become a runtime
+    // index, and the compiler then moved the array to LDS (the backward ran 10% slower).  Wider
+    // filters load their look-ahead rows at the end of the range.
     Pk<CPL> lx0 = zero_pk<CPL>(), lx1 = zero_pk<CPL>(), lx2 = zero_pk<CPL>();
     Pk<CPL> lg0 = zero_pk<CPL>(), lg1 = zero_pk<CPL>(), lg2 = zero_pk<CPL>();
-    if (active && tb < lim) {
+    if (H == 3 && active && tb < lim) {
       lx0 = load_row<CPL, VEC>(a.x + tb * a.x_ld, c0, C);
       lg0 = load_row<CPL, VEC>(a.dy + tb * a.dy_ld, c0, C);
     }
-    if (active && tb + 1 < lim) {
+    if (H == 3 && active && tb + 1 < lim) {
       lx1 = load_row<CPL, VEC>(a.x + (tb + 1) * a.x_ld, c0, C);
       lg1 = load_row<CPL, VEC>(a.dy + (tb + 1) * a.dy_ld, c0, C);
     }
-    if (active && tb + 2 < lim) {
+    if (H == 3 && active && tb + 2 < lim) {
       lx2 = load_row<CPL, VEC>(a.x + (tb + 2) * a.x_ld, c0, C);
       lg2 = load_row<CPL, VEC>(a.dy + (tb + 2) * a.dy_ld, c0, C);
     }
     BwdSeq cs;
-    cs.sd = seq_of_row<MODE>(a.seq, ta, dend, lim);
-    const int64_t dist = ta - cs.sd.s < 3 ? ta - cs.sd.s : 3;
-    float h[3][CPL];
+    cs.sd = seq_of_row<MODE, H>(a.seq, ta, dend, lim);
+    const int64_t dist = ta - cs.sd.s < H ? ta - cs.sd.s : H;
+    float h[H][CPL];
     cs.dh = false;
     if constexpr (MODE != MODE_IDX) {
-      load_hist_rows<CPL, VEC, W>(a.hist, dist < 3 ? cs.sd.idx : -1, c0, C, active, h);
+      load_hist_rows<CPL, VEC, W>(a.hist, dist < H ? cs.sd.idx : -1, c0, C, active, h);
       if (dist == 0) cs.dh = bwd_wants_dh<MODE>(a, cs.sd);
     } else {
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
+      for (int j = 0; j < H; ++j)
 #pragma unroll
         for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
     }
-    // window rows ta-3..ta-1: the history, then the last `dist` rows of the same sequence (the
+    // window rows ta-H..ta-1: the history, then the last `dist` rows of the same sequence (the
     // previous row range streamed them moments earlier on this XCD: cached loads); dz = 0 there
-    shift_window<CPL>(h, wrow, dist);
+    shift_window<CPL, H>(h, wrow, dist);
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+    for (int j = 0; j < H; ++j)
 #pragma unroll
       for (int ch = 0; ch < CPL; ++ch) st.u[j + 1][ch] = h[j][ch];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < R; ++j)
 #pragma unroll
       for (int ch = 0; ch < CPL; ++ch) st.g[j][ch] = 0.f;
 
@@ -343,22 +366,25 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
     if (nfull > 0) {
       // NB register buffers, unrolled by NB chunks, look-ahead loads always issued (rows past the
       // last full chunk re-read its last row): see the forward kernel
+      // the buffer index is a template constant (step<b>), not a loop variable: at width eight
+      // the loop body is too large for the compiler to unroll, and a runtime buffer index moved
+      // the buffers to LDS
       bool more = true;
-      for (int j = 0; more; j += NB) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          if (more) {
-            bwd_load<CPL, VEC, CH>(X[(b + NB - 1) % NB], G[(b + NB - 1) % NB], a, q0 + (NB - 1) * CH, qlast, c0);
-            bwd_chunk<CPL, VEC, MODE, CH, SILU, true, W>(a, st, cs, X[b], G[b], q0, ta, tb, dend, lim, c0, active,
-                                                         done);
-            q0 += CH;
-            more = j + b + 1 < nfull;
-          }
+      int j = 0;
+      auto step = [&](auto bc) {
+        constexpr int b = decltype(bc)::value;
+        if (more) {
+          bwd_load<CPL, VEC, CH>(X[(b + NB - 1) % NB], G[(b + NB - 1) % NB], a, q0 + (NB - 1) * CH, qlast, c0);
+          bwd_chunk<CPL, VEC, MODE, CH, SILU, true, W>(a, st, cs, X[b], G[b], q0, ta, tb, dend, lim, c0, active,
+                                                       done);
+          q0 += CH;
+          more = j + b + 1 < nfull;
         }
-      }
+      };
+      for (; more; j += NB) unroll_steps<NB>(step);
     }
     // the rest: remaining own rows (and partially active waves), then the look-ahead rows
-    // fetched with the set-up (q - tb is 0, 1 or 2 there)
+    // (fetched with the set-up at widths up to four: q - tb is 0, 1 or 2 there)
     for (; !done; q0 += CH) {
 #pragma unroll
       for (int r = 0; r < CH; ++r) {
@@ -369,9 +395,12 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
           if (q < tb) {
             X[0][r] = load_row<CPL, VEC, true>(a.x + q * a.x_ld, c0, C);
             G[0][r] = load_row<CPL, VEC, true>(a.dy + q * a.dy_ld, c0, C);
-          } else {
+          } else if constexpr (H == 3) {
             X[0][r] = q == tb ? lx0 : (q == tb + 1 ? lx1 : lx2);
             G[0][r] = q == tb ? lg0 : (q == tb + 1 ? lg1 : lg2);
+          } else {
+            X[0][r] = load_row<CPL, VEC>(a.x + q * a.x_ld, c0, C);
+            G[0][r] = load_row<CPL, VEC>(a.dy + q * a.dy_ld, c0, C);
           }
         }
       }
@@ -383,8 +412,8 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
   // empty ranges write zeros, so the reduce can read all of them)
   if (active) {
 #pragma unroll
-    for (int k = 0; k < 5; ++k) {
-      float* dst = a.part + ((int64_t)rb * 5 + k) * C + c0;
+    for (int k = 0; k < R + 1; ++k) {
+      float* dst = a.part + ((int64_t)rb * (R + 1) + k) * C + c0;
       if constexpr (VEC && CPL >= 4) {
 #pragma unroll
         for (int q = 0; q < CPL; q += 4)
@@ -401,7 +430,8 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
 }
 
 // Ordered reduce of the per-range partials: out[o] = sum over row ranges p of part[p][o], for
-// the flattened o = k*C + c (k = 0..3 dweight taps, 4 = dbias).  A wave owns 16 consecutive o;
+// the flattened o = k*C + c (k = 0..R-1 dweight tap slots, R = dbias; R = 4 up to width four,
+// 8 up to width eight).  A wave owns 16 consecutive o;
 // lane l sums the ranges p = l/16, l/16 + 4, l/16 + 8, ... in ascending order (each load of
 // the wave reads four 64-byte runs; 32 loads are in flight per step, so up to 128 ranges take
 // one memory round trip), then a fixed two-level butterfly across lanes l, l^16,
@@ -413,7 +443,8 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_reduce_kernel(const 
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t gwave = ((int64_t)blockIdx.x * kBlockThreads + threadIdx.x) / kWave;
   const int64_t C = a.C;
-  const int64_t nout = 5 * C;
+  const int R = partial_rows(a.width) - 1;
+  const int64_t nout = (R + 1) * C;
   if (gwave < n_red_waves) {
     const int64_t o = gwave * 16 + (lane & 15);
     const int sub = lane >> 4;
@@ -437,8 +468,8 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_reduce_kernel(const 
     s += __shfl_xor(s, 32);  // (s0+s1) + (s2+s3) on every lane
     if (ok && lane < 16) {
       const int64_t k = o / C, c = o - k * C;
-      if (k < 4) {  // tap slot k holds filter tap k - (4 - width); lower slots are padding
-        if (k >= 4 - a.width) a.dw[c * a.width + k - (4 - a.width)] = s;
+      if (k < R) {  // tap slot k holds filter tap k - (R - width); lower slots are padding
+        if (k >= R - a.width) a.dw[c * a.width + k - (R - a.width)] = s;
       }
       else if (a.db) a.db[c] = s;
     }
@@ -466,7 +497,7 @@ static hipError_t bwd_go(const BwdArgs& a, hipStream_t s) {
   }
   // empty fragments that read history rows still get a (zero) d(history)
   const int64_t nz = (a.dhist && MODE == MODE_CU) ? a.seq.nseq : 0;
-  int64_t n_red_waves = (5 * a.C + 15) / 16;
+  int64_t n_red_waves = (partial_rows(a.width) * a.C + 15) / 16;
   const int64_t threads = n_red_waves * kWave + nz * a.C;
   const uint32_t rblocks = (uint32_t)((threads + kBlockThreads - 1) / kBlockThreads);
   int64_t nz_arg = nz;
@@ -491,7 +522,7 @@ static hipError_t bwd_width(const BwdArgs& a, int mode, bool vec, bool silu, hip
 }
 
 hipError_t launch_reduce(const BwdArgs& a, hipStream_t s) {
-  int64_t n_red_waves = (5 * a.C + 15) / 16;
+  int64_t n_red_waves = (partial_rows(a.width) * a.C + 15) / 16;
   const int64_t threads = n_red_waves * kWave;
   const uint32_t rblocks = (uint32_t)((threads + kBlockThreads - 1) / kBlockThreads);
   int64_t nz_arg = 0;
@@ -504,6 +535,10 @@ hipError_t launch_bwd(const BwdArgs& a, int mode, bool vec, bool silu, hipStream
   switch (a.width) {
     case 2: return bwd_width<2>(a, mode, vec, silu, s);
     case 3: return bwd_width<3>(a, mode, vec, silu, s);
+    case 5: return bwd_width<5>(a, mode, vec, silu, s);
+    case 6: return bwd_width<6>(a, mode, vec, silu, s);
+    case 7: return bwd_width<7>(a, mode, vec, silu, s);
+    case 8: return bwd_width<8>(a, mode, vec, silu, s);
     default: return bwd_width<4>(a, mode, vec, silu, s);
   }
 }

@@ -132,22 +132,30 @@ __device__ __forceinline__ void store_row(uint16_t* __restrict__ row, int64_t c0
 }
 
 // ------------------------------------------------------------------ taps
-// Filter width W (2..4): the taps are [C, W] and sit in the last W of four slots, wk[4-W .. 3]
-// (slot 3 on the current row); the leading 4-W slots hold zeros and every loop over taps
-// starts at 4-W, so they are never multiplied.
-template <int CPL, int W = 4>
+// Window geometry of filter width W: a ring of R register slots (R = 4 up to W = 4, R = 8 up to
+// W = 8) and H = R - 1 history values.  The taps [C, W] sit in the last W of R slots,
+// wk[R-W .. R-1] (slot R-1 on the current row); the leading R-W slots hold zeros and every loop
+// over taps starts at R-W, so they are never multiplied.  Widths up to four keep the four-slot
+// ring, so their code does not change with the wider form.
+template <int W>
+struct Win {
+  static_assert(W >= 2 && W <= 8, "filter widths 2..8");
+  static constexpr int R = W <= 4 ? 4 : 8;
+  static constexpr int H = R - 1;
+};
+
+template <int CPL, int W = 4, int R = Win<W>::R>
 __device__ __forceinline__ void load_taps(const void* w, int w_f32, const void* b, int b_f32, int64_t c0,
-                                          int64_t C, float (&wk)[4][CPL], float (&bias)[CPL]) {
-  static_assert(W >= 2 && W <= 4, "filter widths 2..4");
+                                          int64_t C, float (&wk)[R][CPL], float (&bias)[CPL]) {
 #pragma unroll
   for (int ch = 0; ch < CPL; ++ch) {
     const int64_t c = c0 + ch;
     const bool ok = c < C;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < R; ++k) {
       float v = 0.f;
-      if (ok && k >= 4 - W) {
-        const int64_t i = c * W + (k - (4 - W));
+      if (ok && k >= R - W) {
+        const int64_t i = c * W + (k - (R - W));
         v = w_f32 ? static_cast<const float*>(w)[i] : __uint_as_float((uint32_t)static_cast<const uint16_t*>(w)[i] << 16);
       }
       wk[k][ch] = v;
@@ -159,39 +167,39 @@ __device__ __forceinline__ void load_taps(const void* w, int w_f32, const void* 
   }
 }
 
-// Three-row window w = [oldest, middle, newest]: drop the oldest, append row p.  Windows are
-// built by shifting rows into the sequence history (never by a runtime register index).
-template <int CPL>
-__device__ __forceinline__ void shift_in(float (&w)[3][CPL], const Pk<CPL>& p) {
+// H-row window w = [oldest, ..., newest]: drop the oldest, append row p.  Windows are built by
+// shifting rows into the sequence history (never by a runtime register index).
+template <int CPL, int H = 3>
+__device__ __forceinline__ void shift_in(float (&w)[H][CPL], const Pk<CPL>& p) {
   float f[CPL];
   unpack(p, f);
 #pragma unroll
   for (int ch = 0; ch < CPL; ++ch) {
-    w[0][ch] = w[1][ch];
-    w[1][ch] = w[2][ch];
-    w[2][ch] = f[ch];
+#pragma unroll
+    for (int j = 0; j + 1 < H; ++j) w[j][ch] = w[j + 1][ch];
+    w[H - 1][ch] = f[ch];
   }
 }
 
-// Rows t-3 .. t-1 (those >= 0), loaded before the sequence lookup says how many of them belong
+// Rows t-H .. t-1 (those >= 0), loaded before the sequence lookup says how many of them belong
 // to t's sequence, so the lookup, these loads and the first chunk share one memory round trip;
 // shift_window keeps only the last `dist` of them.
-template <int CPL, bool VEC>
-__device__ __forceinline__ void load_window(Pk<CPL> (&p)[3], const uint16_t* __restrict__ x, int64_t ld, int64_t t,
+template <int CPL, bool VEC, int H = 3>
+__device__ __forceinline__ void load_window(Pk<CPL> (&p)[H], const uint16_t* __restrict__ x, int64_t ld, int64_t t,
                                             int64_t c0, int64_t C, bool active) {
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
+  for (int j = 0; j < H; ++j) {
     p[j] = zero_pk<CPL>();
-    if (active && t - 3 + j >= 0) p[j] = load_row<CPL, VEC>(x + (t - 3 + j) * ld, c0, C);
+    if (active && t - H + j >= 0) p[j] = load_row<CPL, VEC>(x + (t - H + j) * ld, c0, C);
   }
 }
 
-// h = the sequence's history positions 0..2; shift in the window rows load_window fetched.
-template <int CPL>
-__device__ __forceinline__ void shift_window(float (&h)[3][CPL], const Pk<CPL> (&p)[3], int64_t dist) {
+// h = the sequence's history positions 0..H-1; shift in the window rows load_window fetched.
+template <int CPL, int H = 3>
+__device__ __forceinline__ void shift_window(float (&h)[H][CPL], const Pk<CPL> (&p)[H], int64_t dist) {
 #pragma unroll
-  for (int j = 0; j < 3; ++j)
-    if (j >= 3 - dist) shift_in<CPL>(h, p[j]);
+  for (int j = 0; j < H; ++j)
+    if (j >= H - dist) shift_in<CPL, H>(h, p[j]);
 }
 
 // ------------------------------------------------------------------ activation
@@ -259,7 +267,7 @@ __device__ __forceinline__ int64_t idx_next_start(const SeqArgs& q, int64_t t, i
 }
 
 // The sequence containing row t (t < dend).  `limit` bounds the IDX-mode forward scan.
-template <int MODE>
+template <int MODE, int HB = 3>
 __device__ __forceinline__ SeqDesc seq_of_row(const SeqArgs& q, int64_t t, int64_t dend, int64_t limit) {
   SeqDesc d;
   const int lane = threadIdx.x & (kWave - 1);
@@ -292,19 +300,20 @@ __device__ __forceinline__ SeqDesc seq_of_row(const SeqArgs& q, int64_t t, int64
     d.e = d.s + q.seqlen;
     if (d.e > dend) d.e = dend;
   } else {
-    // only the distance to the sequence start up to 3 matters (d.s = t - min(dist, 3)), and the
-    // next start below `limit`: lane l tests row t - 3 + l, one pass covers rows t-3 .. t+60
-    const int64_t r = t - 3 + lane;
+    // only the distance to the sequence start up to HB (the history length) matters
+    // (d.s = t - min(dist, HB)), and the next start below `limit`: lane l tests row t - HB + l,
+    // one pass covers rows t-HB .. t+63-HB
+    const int64_t r = t - HB + lane;
     bool st = false;
-    if (r >= 0 && (lane <= 3 || r < limit)) st = idx_is_start(q, r);
+    if (r >= 0 && (lane <= HB || r < limit)) st = idx_is_start(q, r);
     const uint64_t m = __ballot(st);
-    const uint64_t back = m & 0xEull;  // rows t-2, t-1, t
-    const int64_t dist = back ? 3 - (63 - __builtin_clzll(back)) : 3;
+    const uint64_t back = m & (((1ull << HB) - 1) << 1);  // rows t-HB+1 .. t
+    const int64_t dist = back ? HB - (63 - __builtin_clzll(back)) : HB;
     d.s = t - dist;
     d.idx = -1;
-    const uint64_t ahead = m >> 4;  // rows t+1 ..
+    const uint64_t ahead = m >> (HB + 1);  // rows t+1 ..
     if (ahead) d.e = t + 1 + (int64_t)__builtin_ctzll(ahead);
-    else d.e = t + 61 < limit ? idx_next_start(q, t + 60, limit) : limit;
+    else d.e = t + 64 - HB < limit ? idx_next_start(q, t + 63 - HB, limit) : limit;
   }
   return d;
 }

@@ -21,7 +21,8 @@
 //            0..2, caller history rows, or zeros) right before its first row.
 //   halo   = at the range start, the three rows before it: raw inputs of the same sequence
 //            (cached loads), or the sequence's history at its first row.
-//   taps   = FP32 in registers; z = b, then four FMAs in tap order 0..3 (tap 3 = current row).
+//   taps   = FP32 in registers; z = b, then W FMAs in tap order 0..W-1 (tap W-1 = current row).
+//   width  = W taps and W-1 history values in a ring of R = 4 register slots (W <= 4) or 8 (W <= 8).
 //   pool   = the wave that holds a sequence's first row is the only one that reads or writes
 //            its slot (for its channels).  With a pool, row-range boundaries that fall on the
 //            first three rows of a sequence move to that sequence's fourth row (or its end), so
@@ -33,13 +34,14 @@ namespace cconv {
 
 // ------------------------------------------------------------------ sequence history
 // h[j][ch] = history position j (oldest first) of sequence idx, channel c0 + ch.  Width W has
-// W-1 history values; they fill the last W-1 window slots (j >= 4-W), the rest stay zero.
-template <int CPL, bool VEC, int W>
+// W-1 history values; they fill the last W-1 of the H window slots (j >= R-W), the rest stay zero.
+template <int CPL, bool VEC, int W, int H = Win<W>::H>
 __device__ __forceinline__ void load_history(const PoolArgs& pool, const HistArgs& hist, int64_t idx,
                                              int32_t slot, bool live, int64_t c0, int64_t C, bool active,
-                                             float (&h)[3][CPL]) {
+                                             float (&h)[H][CPL]) {
+  constexpr int R = Win<W>::R;
 #pragma unroll
-  for (int j = 0; j < 3; ++j)
+  for (int j = 0; j < H; ++j)
 #pragma unroll
     for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
   if (idx < 0) return;  // history not needed
@@ -58,8 +60,8 @@ __device__ __forceinline__ void load_history(const PoolArgs& pool, const HistArg
     const bool has = !hist.has_hist || hist.has_hist[idx];
     if (has && active) {
 #pragma unroll
-      for (int j = 4 - W; j < 3; ++j) {
-        Pk<CPL> p = load_row<CPL, VEC>(hist.ptr + (idx * (W - 1) + j - (4 - W)) * C, c0, C);
+      for (int j = R - W; j < H; ++j) {
+        Pk<CPL> p = load_row<CPL, VEC>(hist.ptr + (idx * (W - 1) + j - (R - W)) * C, c0, C);
         unpack(p, h[j]);
       }
     }
@@ -119,21 +121,17 @@ __device__ __forceinline__ void load_chunk(Pk<CPL> (&buf)[CH], const uint16_t* _
   for (int r = 0; r < CH; ++r) buf[r] = load_row<CPL, VEC, true>(row + r * ld, c0, C);
 }
 
-template <int CPL, bool SILU, int W>
-__device__ __forceinline__ Pk<CPL> stencil_row(const float (&wk)[4][CPL], const float (&bias)[CPL],
-                                               const float (&u)[4][CPL], int r);
-
-// One output row from the ring: u[(r+1)%4], u[(r+2)%4], u[(r+3)%4] are rows t-3, t-2, t-1 and
-// u[r%4] the current row.  z = b, then the W taps in order (FMA), FP32; y = act(z) in bf16.
-template <int CPL, bool SILU, int W>
-__device__ __forceinline__ Pk<CPL> stencil_row(const float (&wk)[4][CPL], const float (&bias)[CPL],
-                                               const float (&u)[4][CPL], int r) {
+// One output row from the ring of R slots: u[(r+1+k)%R] is row t-(R-1)+k and u[r%R] the current
+// row.  z = b, then the W taps in order (FMA), FP32; y = act(z) in bf16.
+template <int CPL, bool SILU, int W, int R = Win<W>::R>
+__device__ __forceinline__ Pk<CPL> stencil_row(const float (&wk)[R][CPL], const float (&bias)[CPL],
+                                               const float (&u)[R][CPL], int r) {
   float out[CPL];
 #pragma unroll
   for (int ch = 0; ch < CPL; ++ch) {
     float z = bias[ch];
 #pragma unroll
-    for (int k = 4 - W; k < 4; ++k) z = __builtin_fmaf(wk[k][ch], u[(r + 1 + k) % 4][ch], z);
+    for (int k = R - W; k < R; ++k) z = __builtin_fmaf(wk[k][ch], u[(r + 1 + k) % R][ch], z);
     out[ch] = SILU ? z * sigmoid_f32(z) : z;
   }
   return pack(out);
@@ -177,11 +175,11 @@ __device__ __forceinline__ void fwd_slot(const FwdArgs& a, FwdSeq& cs) {
 
 // Row q = cs.sd.s, the first row of a sequence, is next: h <- its history, and with a pool the
 // head writes the sequence's final state (the head wave is the only one that touches the slot).
-template <int CPL, bool VEC, int MODE, int W>
-__device__ __forceinline__ void fwd_enter(const FwdArgs& a, FwdSeq& cs, int64_t c0, bool active, float (&h)[3][CPL]) {
+template <int CPL, bool VEC, int MODE, int W, int H = Win<W>::H>
+__device__ __forceinline__ void fwd_enter(const FwdArgs& a, FwdSeq& cs, int64_t c0, bool active, float (&h)[H][CPL]) {
   fwd_slot<MODE>(a, cs);
 #pragma unroll
-  for (int j = 0; j < 3; ++j)
+  for (int j = 0; j < H; ++j)
 #pragma unroll
     for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
   if constexpr (MODE != MODE_IDX) {
@@ -198,10 +196,11 @@ __device__ __forceinline__ void fwd_enter(const FwdArgs& a, FwdSeq& cs, int64_t 
 // mod 4 = r mod 4, as q0 - range start is a multiple of CH.  A chunk inside one sequence is a
 // straight stencil; a chunk where sequences start re-seeds the three window slots from the new
 // sequence's history right before its first row.
-template <int CPL, bool VEC, int MODE, int CH, bool SILU, bool FULL, int W>
+template <int CPL, bool VEC, int MODE, int CH, bool SILU, bool FULL, int W, int R = Win<W>::R>
 __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)[CH], int n, int64_t q0, int64_t tb,
                                           int64_t dend, FwdSeq& cs, int64_t c0, bool active,
-                                          const float (&wk)[4][CPL], const float (&bias)[CPL], float (&u)[4][CPL]) {
+                                          const float (&wk)[R][CPL], const float (&bias)[CPL], float (&u)[R][CPL]) {
+  constexpr int H = R - 1;
   if (n == CH && cs.sd.e >= q0 + CH) {
     if (cs.zero) {
       if (FULL || active) {
@@ -211,7 +210,7 @@ __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)
     } else {
 #pragma unroll
       for (int r = 0; r < CH; ++r) {
-        unpack(buf[r], u[r % 4]);
+        unpack(buf[r], u[r % R]);
         const Pk<CPL> out = stencil_row<CPL, SILU, W>(wk, bias, u, r);
         if (FULL || active) store_row<CPL, VEC, true>(a.y + (q0 + r) * a.y_ld, c0, a.C, out);
       }
@@ -224,14 +223,14 @@ __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)
       const int64_t q = q0 + r;
       if (q == cs.sd.e) {  // a new sequence starts at row q (empty ones are skipped)
         cs.sd = next_seq<MODE>(a.seq, cs.sd, dend, tb);
-        float h[3][CPL];
+        float h[H][CPL];
         fwd_enter<CPL, VEC, MODE, W>(a, cs, c0, active, h);
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
+        for (int j = 0; j < H; ++j)
 #pragma unroll
-          for (int ch = 0; ch < CPL; ++ch) u[(r + 1 + j) % 4][ch] = h[j][ch];
+          for (int ch = 0; ch < CPL; ++ch) u[(r + 1 + j) % R][ch] = h[j][ch];
       }
-      unpack(buf[r], u[r % 4]);
+      unpack(buf[r], u[r % R]);
       Pk<CPL> out = zero_pk<CPL>();
       if (!cs.zero) out = stencil_row<CPL, SILU, W>(wk, bias, u, r);
       if (FULL || active) store_row<CPL, VEC, true>(a.y + q * a.y_ld, c0, a.C, out);
@@ -241,8 +240,10 @@ __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)
 
 template <int CPL, bool VEC, int MODE, bool SILU, int W>
 __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs a) {
-  constexpr int CH = MODE == MODE_IDX ? CCONV_FWD_CHUNK_IDX : CCONV_FWD_CHUNK;  // rows per unrolled chunk
-  static_assert(CH % 4 == 0, "chunks must keep the ring slot of a row fixed");
+  constexpr int R = Win<W>::R, H = Win<W>::H;  // ring slots, history values
+  constexpr int CH0 = MODE == MODE_IDX ? CCONV_FWD_CHUNK_IDX : CCONV_FWD_CHUNK;
+  constexpr int CH = CH0 % R == 0 ? CH0 : R;  // rows per unrolled chunk
+  static_assert(CH % R == 0, "chunks must keep the ring slot of a row fixed");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -267,7 +268,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
   tb = tb < dend ? tb : dend;
   if (ta >= tb) return;
 
-  float wk[4][CPL], bias[CPL];
+  float wk[R][CPL], bias[CPL];
   load_taps<CPL, W>(a.w, a.w_f32, a.b, a.b_f32, c0, C, wk, bias);
 
   // full chunks are software-pipelined over the whole range; lanes past the last channel only
@@ -283,13 +284,13 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
     for (int b = 0; b + 1 < NB; ++b) load_chunk<CPL, VEC, CH>(buf[b], a.x, a.x_ld, q0 + b * CH, qlast, c0, C);
   }
 
-  // the window rows ta-3 .. ta-1 and the sequence holding row ta
-  Pk<CPL> wrow[3];
-  load_window<CPL, VEC>(wrow, a.x, a.x_ld, ta, c0, C, active);
+  // the window rows ta-H .. ta-1 and the sequence holding row ta
+  Pk<CPL> wrow[H];
+  load_window<CPL, VEC, H>(wrow, a.x, a.x_ld, ta, c0, C, active);
   FwdSeq cs;
-  cs.sd = seq_of_row<MODE>(a.seq, ta, dend, tb);
-  const int64_t dist = ta - cs.sd.s < 3 ? ta - cs.sd.s : 3;  // window rows from the same sequence
-  float h[3][CPL];
+  cs.sd = seq_of_row<MODE, H>(a.seq, ta, dend, tb);
+  const int64_t dist = ta - cs.sd.s < H ? ta - cs.sd.s : H;  // window rows from the same sequence
+  float h[H][CPL];
   if (dist == 0) {
     fwd_enter<CPL, VEC, MODE, W>(a, cs, c0, active, h);
   } else {
@@ -297,20 +298,20 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
     // so dist == 3 and the slot is not touched (only its -1 status matters)
     fwd_slot<MODE>(a, cs);
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+    for (int j = 0; j < H; ++j)
 #pragma unroll
       for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
     if constexpr (MODE != MODE_IDX) {
-      if (!cs.zero && dist < 3) load_history<CPL, VEC, W>(a.pool, a.hist, cs.sd.idx, cs.slot, true, c0, C, active, h);
+      if (!cs.zero && dist < H) load_history<CPL, VEC, W>(a.pool, a.hist, cs.sd.idx, cs.slot, true, c0, C, active, h);
     }
   }
-  // window rows ta-3, ta-2, ta-1 -> ring slots 1, 2, 3: the history, then the last `dist` input
-  // rows of the same sequence (the neighbouring range streamed them moments earlier on this XCD,
-  // so they come from L2)
-  shift_window<CPL>(h, wrow, dist);
-  float u[4][CPL];
+  // window rows ta-H .. ta-1 -> ring slots 1 .. H: the history, then the last `dist` input rows
+  // of the same sequence (the neighbouring range streamed them moments earlier on this XCD, so
+  // they come from L2)
+  shift_window<CPL, H>(h, wrow, dist);
+  float u[R][CPL];
 #pragma unroll
-  for (int j = 0; j < 3; ++j)
+  for (int j = 0; j < H; ++j)
 #pragma unroll
     for (int ch = 0; ch < CPL; ++ch) u[j + 1][ch] = h[j][ch];
 
@@ -458,6 +459,10 @@ hipError_t launch_fwd(const FwdArgs& a, int mode, bool vec, bool silu, hipStream
   switch (a.width) {
     case 2: return fwd_width<2>(a, mode, vec, silu, s);
     case 3: return fwd_width<3>(a, mode, vec, silu, s);
+    case 5: return fwd_width<5>(a, mode, vec, silu, s);
+    case 6: return fwd_width<6>(a, mode, vec, silu, s);
+    case 7: return fwd_width<7>(a, mode, vec, silu, s);
+    case 8: return fwd_width<8>(a, mode, vec, silu, s);
     default: return fwd_width<4>(a, mode, vec, silu, s);
   }
 }

@@ -86,6 +86,11 @@ inline int64_t fwd_range_rows(int64_t rows, int64_t n_strips) {
   return (kFwdFixedRows == 0 && r > kFwdLongRows) ? kFwdShortRows : r;
 }
 
+// Rows of one range's dweight/dbias partial: a tap slot per register-ring slot (4 up to filter
+// width four, 8 up to width eight; the first R - W are padding), then dbias.
+constexpr int kMaxWidth = 8;
+__host__ __device__ inline int partial_rows(int width) { return width <= 4 ? 5 : 9; }
+
 // How rows split into sequences: cu_seqlens offsets, per-token sequence IDs, or batch rows.
 enum { MODE_CU = 0, MODE_IDX = 1, MODE_BATCH = 2 };
 
@@ -144,7 +149,7 @@ struct BwdArgs {
   SeqArgs seq;
   HistArgs hist;
   uint16_t* dhist;  // nullptr: not requested
-  float* part;      // workspace: [n_rowblocks, 5, C] FP32 per-block partials
+  float* part;      // workspace: [n_rowblocks, partial_rows(width), C] FP32 per-block partials
   float* dw;        // [C, width]
   float* db;        // [C] or nullptr
   int64_t range_rows;  // rows per row range

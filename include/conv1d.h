@@ -1,6 +1,6 @@
 /*
  * conv1d.h -- C ABI of the MI355X (gfx950) packed depthwise causal Conv1d (+ SiLU), filter
- * width 4 (widths 2 and 3 for the non-pool forms).
+ * width 4 (widths 2..8 for the channel-last non-pool forms, 2..4 channels-first).
  *
  * The operation (FlashInfer docs, flashinfer.mamba.causal_conv1d_fn, Parameters and Notes):
  * for every packed sequence with rows [s, e) and channel c, with the extended sequence
@@ -22,10 +22,11 @@
  *   - bf16 tensors are 16-bit bf16 bit patterns.  x, y, dy, dx are row-major [rows, C] with a
  *     row stride (`*_ld`, in elements, >= C) and contiguous channels.
  *   - Taps w are a contiguous [C, W] array of FP32 or bf16 (`w_dtype`) with filter width
- *     W = `width` in 2..4 (causal_conv1d_fn has W = 4; causal_conv1d_cp, Parameters weight,
- *     takes [D, W]).  For W < 4 read the formula above with the first 4 - W taps absent: tap
- *     W - 1 multiplies the current token and the history is W - 1 values (u[-(W-1)] .. u[-1]).
- *     The slot-pool forms (conv1d_fwd with a pool, conv1d_state_update*) are width four only.
+ *     W = `width` in 2..8 (causal_conv1d_fn has W = 4; causal_conv1d_cp, Parameters weight,
+ *     takes [D, W]).  Read the formula above with W taps in the same order: z = b + sum over
+ *     k of w[c][k]*u[t-(W-1)+k], tap W - 1 on the current token, and the history is W - 1
+ *     values (u[-(W-1)] .. u[-1], oldest first).  The slot-pool forms (conv1d_fwd with a pool,
+ *     conv1d_state_update*) are width four only; the channels-first calls take widths 2..4.
  *     The optional bias is a contiguous [C] array of FP32 or bf16 (`b_dtype`), NULL for none
  *     (causal_conv1d_fn, Parameters weight and bias).
  *   - Host-checkable preconditions are validated before anything is enqueued; a violation
@@ -160,7 +161,8 @@ int conv1d_state_update_spec(const void* x, int64_t nseq, int64_t K, int64_t C, 
    dw and db are sums of per-tile FP32 partials combined in a fixed order by a second kernel
    (no atomics), so they are bitwise identical from run to run and independent of the
    workspace address.  ws: device scratch of at least conv1d_bwd_workspace_bytes(rows, C)
-   bytes, 16-byte aligned, not overlapping any operand.  No pool. */
+   bytes (room for any width: one FP32 partial of up to 9 x C values per row range), 16-byte
+   aligned, not overlapping any operand.  No pool. */
 int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x_ld, int64_t dy_ld,
                const void* w, int w_dtype, int width, const void* b, int b_dtype, const conv1d_seq* seq,
                const conv1d_hist* hist, int act, void* dx, int64_t dx_ld, float* dw, float* db,

@@ -1,6 +1,7 @@
-"""Filter widths 2 and 3 (taps [C, W], W-1 history rows) on the GPU against the oracle: random
-packed sweeps in both sequence forms, sequences of length 1..4 across range boundaries, the
-context-parallel workload at full size, and the channels-first layout."""
+"""Filter widths 2, 3 and 5..8 (taps [C, W], W-1 history rows) on the GPU against the oracle:
+random packed sweeps in both sequence forms, sequences shorter than the history across range
+boundaries, the context-parallel workload at full size (widths 3 and 8), and the channels-first
+layout (widths 2 and 3)."""
 import numpy as np
 import pytest
 
@@ -30,11 +31,11 @@ def _narrow(case, W, rng):
     return out
 
 
-@pytest.mark.parametrize("W", [2, 3])
+@pytest.mark.parametrize("W", [2, 3, 5, 6, 7, 8])
 @pytest.mark.parametrize("mode", ["cu", "idx"])
 def test_width_sweep(oracle, W, mode):
     rng = np.random.default_rng(60 + W * 10 + (mode == "idx"))
-    for q in range(24):
+    for q in range(24 if W < 4 else 12):
         C = int(rng.choice([1, 3, 13, 64, 520, 1024]))
         base = wl.random_case(rng, C=C, nseq=int(rng.integers(0, 9)), max_len=int(rng.choice([3, 40, 300])), mode=mode,
                               with_hist=(mode == "cu" and q % 2 == 0), w_f32=bool(q % 2),
@@ -46,13 +47,13 @@ def test_width_sweep(oracle, W, mode):
         gh.check_bwd(oracle, case)
 
 
-@pytest.mark.parametrize("W", [2, 3])
+@pytest.mark.parametrize("W", [2, 3, 5, 8])
 def test_width_short_sequences_across_ranges(oracle, W):
-    """Many sequences of length 1..4 (shorter than the history) with history rows, over enough rows
-    that row-range boundaries fall inside and at the heads of them."""
+    """Many sequences of length 1..W (down to shorter than the history) with history rows, over
+    enough rows that row-range boundaries fall inside and at the heads of them."""
     rng = np.random.default_rng(70 + W)
     C = 1024
-    lengths = np.concatenate([rng.integers(1, 5, size=400), rng.integers(150, 260, size=6)])
+    lengths = np.concatenate([rng.integers(1, max(5, W + 1), size=400), rng.integers(150, 260, size=6)])
     rng.shuffle(lengths)
     cu = np.zeros(len(lengths) + 1, np.int32)
     cu[1:] = np.cumsum(lengths)
@@ -66,10 +67,11 @@ def test_width_short_sequences_across_ranges(oracle, W):
     gh.check_bwd(oracle, case)
 
 
-def test_width3_context_parallel_full_size(oracle):
-    rng = np.random.default_rng(75)
-    case = _narrow(wl.cp_share(), 3, rng)
-    case["name"] = "width3-cp-share"
+@pytest.mark.parametrize("W", [3, 8])
+def test_width_context_parallel_full_size(oracle, W):
+    rng = np.random.default_rng(75 + W)
+    case = _narrow(wl.cp_share(), W, rng)
+    case["name"] = f"width{W}-cp-share"
     say(case["name"])
     gh.check_fwd(oracle, case)
     gh.check_bwd(oracle, case)
