@@ -454,19 +454,21 @@ def main():
                 nbs = 2 * 64 * K * C * 2 + 64 * C * 2 * (3 + K + 2) + 4 * C * 4 + C * 4 + 2 * 64 * 4
                 extras["spec_update_N64_K4_C5632"] = {"GBps": round(gbps(nbs, mss), 1), "us": round(1e3 * mss, 2),
                                                       "bytes": nbs}
-        # filter width 3 on the step workload: taps [C, 3], two history rows per fragment
-        rng = np.random.default_rng(1008)
-        c3 = dict(case)
-        c3["w"] = wl.uniform_f32(rng, (case["x"].shape[1], 3))
-        c3["hist"] = wl.normal_bf16(rng, (case["hist"].shape[0], 2, case["x"].shape[1]))
-        d3 = [g.prepare(c3) for _ in range(4)]
-        nf3, nb3 = fwd_bytes(c3), bwd_bytes(c3)
-        msf3 = g.ring([lambda d=d: g.fwd(d) for d in d3], 40, 0, warm_ms=40)
-        msb3 = g.ring([lambda d=d: g.bwd(d) for d in d3], 40, 0, warm_ms=40)
-        extras["width3_" + case["name"]] = {"fwd_GBps": round(gbps(nf3, msf3), 1), "fwd_us": round(1e3 * msf3, 2),
-                                            "fwd_bytes": nf3, "bwd_GBps": round(gbps(nb3, msb3), 1),
-                                            "bwd_us": round(1e3 * msb3, 2), "bwd_bytes": nb3}
-        del d3
+        # filter widths 3 and 8 on the step workload: taps [C, W], W - 1 history rows per fragment
+        for Wx, seed in ((3, 1008), (8, 1009)):
+            rng = np.random.default_rng(seed)
+            cw = dict(case)
+            cw["w"] = wl.uniform_f32(rng, (case["x"].shape[1], Wx))
+            cw["hist"] = wl.normal_bf16(rng, (case["hist"].shape[0], Wx - 1, case["x"].shape[1]))
+            dw_sets = [g.prepare(cw) for _ in range(4)]
+            nfw, nbw = fwd_bytes(cw), bwd_bytes(cw)
+            msfw = g.ring([lambda d=d: g.fwd(d) for d in dw_sets], 40, 0, warm_ms=40)
+            msbw = g.ring([lambda d=d: g.bwd(d) for d in dw_sets], 40, 0, warm_ms=40)
+            extras[f"width{Wx}_" + case["name"]] = {"fwd_GBps": round(gbps(nfw, msfw), 1),
+                                                   "fwd_us": round(1e3 * msfw, 2), "fwd_bytes": nfw,
+                                                   "bwd_GBps": round(gbps(nbw, msbw), 1),
+                                                   "bwd_us": round(1e3 * msbw, 2), "bwd_bytes": nbw}
+            del dw_sets
         # channels-first [B, D, T]: the per-token-ID training shape (4 x 4096 x 4096), one sequence per row
         rng = np.random.default_rng(1007)
         B, D, T = 4, 4096, 4096
