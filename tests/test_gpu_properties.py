@@ -19,10 +19,22 @@ def say(msg):
     print(f"[gpu] {msg}", flush=True)
 
 
+def _width8(case, seed):
+    """The same workload with taps [C, 8] and seven history rows per fragment."""
+    rng = np.random.default_rng(seed)
+    out = dict(case)
+    C = case["x"].shape[1]
+    out["w"] = wl.uniform_f32(rng, (C, 8))
+    if case.get("hist") is not None:
+        out["hist"] = wl.normal_bf16(rng, (case["hist"].shape[0], 7, C))
+    return out
+
+
 def test_dweight_bitwise_reproducible():
-    """Ten backward runs, fresh and garbage-filled workspaces, another stream: identical dw/db bits."""
-    say("determinism: per-token-ID training and context-parallel share")
-    for case in (wl.train_seq_ids(), wl.cp_share()):
+    """Ten backward runs, fresh and garbage-filled workspaces, another stream: identical dw/db bits
+    (filter width 4, and width 8 with its nine-row partials)."""
+    say("determinism: per-token-ID training and context-parallel share, widths 4 and 8")
+    for case in (wl.train_seq_ids(), wl.cp_share(), _width8(wl.train_seq_ids(), 90), _width8(wl.cp_share(), 91)):
         x, dy = gh.dev_bits(case["x"]), gh.dev_bits(case["dy"])
         w, b = gh.dev_taps(case["w"]), gh.dev_taps(case.get("b"))
         kw = dict(cu_seqlens=gh.dev_i32(case.get("cu_seqlens")), seq_idx=gh.dev_i32(case.get("seq_idx")),
