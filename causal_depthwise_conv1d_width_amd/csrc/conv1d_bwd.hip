@@ -1,26 +1,29 @@
-// conv1d_bwd.hip -- training backward of the packed width-4 causal depthwise Conv1d.
+// conv1d_bwd.hip -- training backward of the packed depthwise causal Conv1d (filter width 4;
+// widths 2..8 as well).
 //
 // Operation: the gradients of the forward in conv1d_fwd.hip for the training path of FlashInfer
 // cake_causal_conv1d_kcp (Returns: dx, a deterministic FP32 dweight, and the gradient of the
 // history rows that the preceding fragment supplied) and Megatron-Core causal_conv1d_cp.  With
-// z[t] = b + sum_k w_k u[t-3+k] and dz[t] = dy[t] * act'(z[t]):
-//     dx[t]  = sum_k w_k dz[t+3-k]           (terms inside t's sequence only)
-//     dw_k   = sum_t dz[t] u[t-3+k],  db = sum_t dz[t]
+// W taps, z[t] = b + sum_k w_k u[t-(W-1)+k] and dz[t] = dy[t] * act'(z[t]):
+//     dx[t]  = sum_k w_k dz[t+(W-1)-k]       (terms inside t's sequence only)
+//     dw_k   = sum_t dz[t] u[t-(W-1)+k],  db = sum_t dz[t]
 //     dh_j   = sum_{tau <= j} w_{j-tau} dz[s+tau]   (history row j of a continuing fragment)
 //
 // Tiling: as the forward (waves side by side in channels, lane = CPL channels, one launch of
-// about kBwdBlocks equal row ranges).  A wave streams x and dy over its own rows [ta, tb) and up
-// to three look-ahead rows of the sequence that holds row tb - 1; the three look-behind and the
-// look-ahead rows belong to the neighbouring ranges (cached loads).  The step at row q produces
-// the value w3 dz[q-3] + w2 dz[q-2] + w1 dz[q-1] + w0 dz[q] of row q - 3: dx when q - 3 is a row
-// of q's sequence, d(history) row j when q - 3 is the sequence's history row j (the dz ring holds
-// zeros before a sequence's start).  Where a sequence ends, the values of its last three rows
-// are flushed with the dz of later rows left out, and the stream goes straight on.
+// about kBwdBlocks equal row ranges).  The window is a ring of R register slots (R = 4 up to
+// width four, 8 up to width eight) with H = R - 1 history rows.  A wave streams x and dy over its
+// own rows [ta, tb) and up to H look-ahead rows of the sequence that holds row tb - 1; the H
+// look-behind and the look-ahead rows belong to the neighbouring ranges (cached loads).  The step
+// at row q produces the value of row q - H (at width four: w3 dz[q-3] + w2 dz[q-2] + w1 dz[q-1]
+// + w0 dz[q]): dx when q - H is a row of q's sequence, d(history) row j when it is the
+// sequence's history row j (the dz ring holds zeros before a sequence's start).  Where a
+// sequence ends, the values of its last H rows are flushed with the dz of later rows left out,
+// and the stream goes straight on.
 //
 // dweight/dbias are deterministic by construction: each lane accumulates its channels over its
 // rows in row order (FP32) and owns those channels for the whole row range, so the range's
-// [5, C] partial is written straight from registers to the workspace, and a second kernel adds
-// the partials of all row ranges in ascending range order.  No atomics anywhere, so the bits
+// [R + 1, C] partial is written straight from registers to the workspace, and a second kernel
+// adds the partials of all row ranges in ascending range order.  No atomics anywhere, so the bits
 // depend only on the input values and the range length, never on scheduling or on the
 // workspace address.
 #include <type_traits>

@@ -1,4 +1,5 @@
-// conv1d_fwd.hip -- forward and decode kernels of the packed width-4 causal depthwise Conv1d.
+// conv1d_fwd.hip -- forward and decode kernels of the packed depthwise causal Conv1d (filter width 4;
+// widths 2..8 for the forward without a pool).
 //
 // Operation: FlashInfer causal_conv1d_fn (Parameters x, weight, conv_state, cu_seqlens,
 // cache_indices, has_initial_state, bias, out) with the optional activation and per-token
