@@ -108,8 +108,7 @@ def _pool(conv_state, cache_indices, has_initial_state, C):
 
 
 def _width(weight, C, max_width=8):
-    """Filter width W from taps [C, W], W in 2..max_width (8 for the channel-last calls, 4 for the
-    channels-first ones)."""
+    """Filter width W from taps [C, W], W in 2..max_width."""
     if weight is None or weight.dim() != 2 or weight.shape[0] != C or not 2 <= weight.shape[1] <= max_width:
         raise ValueError(f"weight: need taps of shape [{C}, W] with 2 <= W <= {max_width}")
     return int(weight.shape[1])
@@ -344,12 +343,12 @@ def conv1d_bwd_cf_workspace_bytes(B, D):
 
 
 def conv1d_fwd_cf(x, weight, bias=None, *, activation="silu", out=None, stream=None):
-    """y = act(causal width-4 conv along T) for x [B, D, T]; every (b, d) row is one sequence."""
+    """y = act(causal width-W conv along T) for x [B, D, T]; every (b, d) row is one sequence."""
     torch = _torch()
     lib = _lib.load()
     B, D, T = x.shape
     xp, xsb, xsd = _cf3d(x, "x")
-    W = _width(weight, D, max_width=4)
+    W = _width(weight, D)
     wp, wd = _taps(weight, D, (D, W), "weight")
     bp, bd = _taps(bias, D, (D,), "bias")
     _on_gpu(x.device, weight=weight, bias=bias, out=out)
@@ -364,13 +363,13 @@ def conv1d_fwd_cf(x, weight, bias=None, *, activation="silu", out=None, stream=N
 
 def conv1d_bwd_cf(x, dy, weight, bias=None, *, activation="silu", dx=None, dweight=None, want_dbias=None,
                   dbias=None, workspace=None, stream=None):
-    """(dx [B, D, T], dweight [D, 4] fp32, dbias [D] fp32 or None) for the channels-first layout."""
+    """(dx [B, D, T], dweight [D, W] fp32, dbias [D] fp32 or None) for the channels-first layout."""
     torch = _torch()
     lib = _lib.load()
     B, D, T = x.shape
     xp, xsb, xsd = _cf3d(x, "x")
     dyp, dysb, dysd = _cf3d(dy, "dy", (B, D, T))
-    W = _width(weight, D, max_width=4)
+    W = _width(weight, D)
     wp, wd = _taps(weight, D, (D, W), "weight")
     bp, bd = _taps(bias, D, (D,), "bias")
     dev = x.device

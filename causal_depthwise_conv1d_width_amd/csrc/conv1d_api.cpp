@@ -131,7 +131,7 @@ size_t conv1d_bwd_workspace_bytes(int64_t rows, int64_t C) {
 
 size_t conv1d_bwd_cf_workspace_bytes(int64_t B, int64_t D) {
   if (B <= 0 || D <= 0 || !mul_ok(B, D)) return 0;  // out-of-range sizes fail in the call itself
-  const size_t bytes = (size_t)B * 5u * (size_t)D * sizeof(float);
+  const size_t bytes = (size_t)B * (size_t)partial_rows(kMaxWidth) * (size_t)D * sizeof(float);  // any width
   return (bytes + kWsAlign - 1) / kWsAlign * kWsAlign;
 }
 
@@ -346,7 +346,7 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
 int conv1d_fwd_cf(const void* x, int64_t B, int64_t D, int64_t T, int64_t x_sb, int64_t x_sd, const void* w,
                   int w_dtype, int width, const void* b, int b_dtype, int act, void* y, int64_t y_sb, int64_t y_sd,
                   hipStream_t stream) {
-  if (B < 0 || D < 1 || T < 0 || !w || !dtype_ok(w_dtype) || width < 2 || width > 4) return CONV1D_EINVAL;
+  if (B < 0 || D < 1 || T < 0 || !w || !dtype_ok(w_dtype) || width < 2 || width > kMaxWidth) return CONV1D_EINVAL;
   if (b && !dtype_ok(b_dtype)) return CONV1D_EINVAL;
   if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
   if (!cf_layout_ok(B, D, T, x_sb, x_sd) || !cf_layout_ok(B, D, T, y_sb, y_sd)) return CONV1D_EINVAL;
@@ -380,7 +380,7 @@ int conv1d_bwd_cf(const void* x, const void* dy, int64_t B, int64_t D, int64_t T
                   int64_t dy_sb, int64_t dy_sd, const void* w, int w_dtype, int width, const void* b, int b_dtype,
                   int act, void* dx, int64_t dx_sb, int64_t dx_sd, float* dw, float* db, void* ws, size_t ws_bytes,
                   hipStream_t stream) {
-  if (B < 0 || D < 1 || T < 0 || !w || !dtype_ok(w_dtype) || !dw || width < 2 || width > 4) return CONV1D_EINVAL;
+  if (B < 0 || D < 1 || T < 0 || !w || !dtype_ok(w_dtype) || !dw || width < 2 || width > kMaxWidth) return CONV1D_EINVAL;
   if (b && !dtype_ok(b_dtype)) return CONV1D_EINVAL;
   if (act != CONV1D_ACT_NONE && act != CONV1D_ACT_SILU) return CONV1D_EINVAL;
   if (!cf_layout_ok(B, D, T, x_sb, x_sd) || !cf_layout_ok(B, D, T, dy_sb, dy_sd) ||
@@ -402,7 +402,7 @@ int conv1d_bwd_cf(const void* x, const void* dy, int64_t B, int64_t D, int64_t T
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outs[j])) return CONV1D_EINVAL;
   }
-  if ((uint64_t)(B * D + 3) / 4 > 0x7fffffffull || (uint64_t)(20 * D) / 256 > 0x7fffffffull) return CONV1D_EINVAL;
+  if ((uint64_t)(B * D + 3) / 4 > 0x7fffffffull || (uint64_t)(36 * D) / 256 > 0x7fffffffull) return CONV1D_EINVAL;
   const bool vec = T % 8 == 0 && x_sb % 8 == 0 && x_sd % 8 == 0 && dy_sb % 8 == 0 && dy_sd % 8 == 0 &&
                    dx_sb % 8 == 0 && dx_sd % 8 == 0 && aligned(x, 16) && aligned(dy, 16) && aligned(dx, 16);
   CfArgs a{};

@@ -74,32 +74,39 @@ __device__ __forceinline__ void cf_store(uint16_t* __restrict__ row, int64_t t, 
   }
 }
 
-// e[0..2] = the three steps before the lane's first, e[3..10] = its eight steps.  Lane 0 takes
-// the previous block's last three steps (c2 = the dword holding steps 4,5 of lane 63, c3 = 6,7).
-__device__ __forceinline__ void cf_window(float (&e)[11], const uint32_t (&v)[4], uint32_t c2, uint32_t c3, int lane) {
-  uint32_t p2 = __shfl_up(v[2], 1), p3 = __shfl_up(v[3], 1);
-  if (lane == 0) {
-    p2 = c2;
-    p3 = c3;
+// e[0..H-1] = the H steps before the lane's first, e[H..H+7] = its eight steps (H = 3 up to
+// width four, 7 up to width eight: at most one lane's eight steps back).  They come from lane
+// l-1; lane 0 takes the previous block's lane 63 (c[0..3], its four dwords).
+template <int H>
+__device__ __forceinline__ void cf_window(float (&e)[H + 8], const uint32_t (&v)[4], const uint32_t (&c)[4], int lane) {
+  static_assert(H >= 1 && H <= 7, "history of one lane at most");
+  constexpr int D0 = (8 - H) / 2;  // first dword of lane l-1 that holds a needed step
+  uint32_t p[4];
+#pragma unroll
+  for (int q = D0; q < 4; ++q) {
+    p[q] = __shfl_up(v[q], 1);
+    if (lane == 0) p[q] = c[q];
   }
-  e[0] = bf16_hi(p2);
-  e[1] = bf16_lo(p3);
-  e[2] = bf16_hi(p3);
+#pragma unroll
+  for (int i = 0; i < H; ++i) {  // step 8-H+i of lane l-1
+    const int st = 8 - H + i;
+    e[i] = (st & 1) ? bf16_hi(p[st >> 1]) : bf16_lo(p[st >> 1]);
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    e[3 + 2 * j] = bf16_lo(v[j]);
-    e[4 + 2 * j] = bf16_hi(v[j]);
+    e[H + 2 * j] = bf16_lo(v[j]);
+    e[H + 1 + 2 * j] = bf16_hi(v[j]);
   }
 }
 
-// Taps [D, W] in the last W of four slots (slot 3 on the current step); leading slots are zero
-// and never used (every tap loop starts at 4 - W).
-template <int W>
-__device__ __forceinline__ void cf_taps(const CfArgs& a, int64_t d, float (&wk)[4], float& bias) {
+// Taps [D, W] in the last W of R slots (slot R-1 on the current step; R = 4 up to width four, 8
+// up to width eight); leading slots are zero and never used (every tap loop starts at R - W).
+template <int W, int R = Win<W>::R>
+__device__ __forceinline__ void cf_taps(const CfArgs& a, int64_t d, float (&wk)[R], float& bias) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t i = d * W + (k - (4 - W));
-    wk[k] = k < 4 - W ? 0.f
+  for (int k = 0; k < R; ++k) {
+    const int64_t i = d * W + (k - (R - W));
+    wk[k] = k < R - W ? 0.f
                       : (a.w_f32 ? static_cast<const float*>(a.w)[i]
                                  : __uint_as_float((uint32_t)static_cast<const uint16_t*>(a.w)[i] << 16));
   }
@@ -117,9 +124,10 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_cf_kernel(const CfAr
   const int64_t bi = row / a.D, d = row - bi * a.D, T = a.T;
   const uint16_t* x = a.x + bi * a.x_sb + d * a.x_sd;
   uint16_t* y = a.out + bi * a.o_sb + d * a.o_sd;
-  float wk[4], bias;
+  constexpr int R = Win<W>::R, H = Win<W>::H;
+  float wk[R], bias;
   cf_taps<W>(a, d, wk, bias);
-  uint32_t c2 = 0u, c3 = 0u;  // steps before the row: zero history
+  uint32_t c[4] = {0u, 0u, 0u, 0u};  // steps before the row: zero history
   for (int64_t t0 = 0; t0 < T; t0 += (int64_t)kCfUnroll * kCfBlock) {
     uint32_t v[kCfUnroll][4];
 #pragma unroll
@@ -128,39 +136,38 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_cf_kernel(const CfAr
     for (int u = 0; u < kCfUnroll; ++u) {
       const int64_t tb = t0 + u * kCfBlock;
       if (tb >= T) break;
-      float e[11], out[8];
-      cf_window(e, v[u], c2, c3, lane);
+      float e[H + 8], out[8];
+      cf_window<H>(e, v[u], c, lane);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float z = bias;
 #pragma unroll
-        for (int k = 4 - W; k < 4; ++k) z = __builtin_fmaf(wk[k], e[j + k], z);
+        for (int k = R - W; k < R; ++k) z = __builtin_fmaf(wk[k], e[j + k], z);
         out[j] = SILU ? z * sigmoid_f32(z) : z;
       }
       cf_store<VEC>(y, tb + lane * kCfSteps, T, out);
-      c2 = __builtin_amdgcn_readlane(v[u][2], kWave - 1);
-      c3 = __builtin_amdgcn_readlane(v[u][3], kWave - 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) c[q] = __builtin_amdgcn_readlane(v[u][q], kWave - 1);
     }
   }
 }
 
 // ------------------------------------------------------------------ backward
-// dx of the eight steps of a lane from their dz and the dz of the next three steps (n0..n2);
-// tap k multiplies the dz 3 - k steps later, taps below 4 - W are left out.
-template <int W>
-__device__ __forceinline__ void cf_dx(float (&dx)[8], const float (&dz)[8], float n0, float n1, float n2,
-                                      const float (&wk)[4]) {
-  float g[11];
+// dx of the eight steps of a lane from their dz and the dz of the next H steps (n[0..H-1]);
+// tap slot k multiplies the dz R-1-k steps later, slots below R - W are left out.
+template <int W, int R = Win<W>::R>
+__device__ __forceinline__ void cf_dx(float (&dx)[8], const float (&dz)[8], const float (&n)[R - 1],
+                                      const float (&wk)[R]) {
+  float g[R + 7];
 #pragma unroll
   for (int j = 0; j < 8; ++j) g[j] = dz[j];
-  g[8] = n0;
-  g[9] = n1;
-  g[10] = n2;
+#pragma unroll
+  for (int i = 0; i < R - 1; ++i) g[8 + i] = n[i];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    float s = wk[3] * g[j];
+    float s = wk[R - 1] * g[j];
 #pragma unroll
-    for (int k = 2; k >= 4 - W; --k) s = __builtin_fmaf(wk[k], g[j + 3 - k], s);
+    for (int k = R - 2; k >= R - W; --k) s = __builtin_fmaf(wk[k], g[j + R - 1 - k], s);
     dx[j] = s;
   }
 }
@@ -174,12 +181,15 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_cf_kernel(const CfAr
   const uint16_t* x = a.x + bi * a.x_sb + d * a.x_sd;
   const uint16_t* dy = a.dy + bi * a.dy_sb + d * a.dy_sd;
   uint16_t* dx = a.out + bi * a.o_sb + d * a.o_sd;
-  float wk[4], bias;
+  constexpr int R = Win<W>::R, H = Win<W>::H;
+  float wk[R], bias;
   cf_taps<W>(a, d, wk, bias);
-  float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+  float acc[R + 1];  // tap slots, then db
+#pragma unroll
+  for (int k = 0; k <= R; ++k) acc[k] = 0.f;
   float pdz[8];              // dz of the previous block (its dx is still to be written)
   int64_t ptb = -1;          // start of that block, -1 = none
-  uint32_t c2 = 0u, c3 = 0u;
+  uint32_t c[4] = {0u, 0u, 0u, 0u};
   for (int64_t t0 = 0; t0 < T; t0 += (int64_t)kCfUnrollBwd * kCfBlock) {
     uint32_t v[kCfUnrollBwd][4], gv[kCfUnrollBwd][4];
 #pragma unroll
@@ -193,13 +203,13 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_cf_kernel(const CfAr
       const int64_t tb = t0 + u * kCfBlock;
       if (tb >= T) break;
       const int64_t t = tb + lane * kCfSteps;
-      float e[11], dz[8];
-      cf_window(e, v[u], c2, c3, lane);
+      float e[H + 8], dz[8];
+      cf_window<H>(e, v[u], c, lane);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float z = bias;
 #pragma unroll
-        for (int k = 4 - W; k < 4; ++k) z = __builtin_fmaf(wk[k], e[j + k], z);
+        for (int k = R - W; k < R; ++k) z = __builtin_fmaf(wk[k], e[j + k], z);
         float g = (j & 1) ? bf16_hi(gv[u][j >> 1]) : bf16_lo(gv[u][j >> 1]);
         if (SILU) {
           const float sg = sigmoid_f32(z);
@@ -215,40 +225,42 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_cf_kernel(const CfAr
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
 #pragma unroll
-        for (int k = 4 - W; k < 4; ++k) acc[k] = __builtin_fmaf(dz[j], e[j + k], acc[k]);
-        acc[4] += dz[j];
+        for (int k = R - W; k < R; ++k) acc[k] = __builtin_fmaf(dz[j], e[j + k], acc[k]);
+        acc[R] += dz[j];
       }
-      if (ptb >= 0) {  // the previous block's dx: lane 63 takes this block's first three dz
-        float n0 = __shfl_down(pdz[0], 1), n1 = __shfl_down(pdz[1], 1), n2 = __shfl_down(pdz[2], 1);
-        const float h0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(dz[0]), 0));
-        const float h1 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(dz[1]), 0));
-        const float h2 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(dz[2]), 0));
-        if (lane == kWave - 1) {
-          n0 = h0;
-          n1 = h1;
-          n2 = h2;
+      if (ptb >= 0) {  // the previous block's dx: lane 63 takes this block's first H dz
+        float n[H];
+#pragma unroll
+        for (int i = 0; i < H; ++i) {
+          n[i] = __shfl_down(pdz[i], 1);
+          const float h = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(dz[i]), 0));
+          if (lane == kWave - 1) n[i] = h;
         }
         float o[8];
-        cf_dx<W>(o, pdz, n0, n1, n2, wk);
+        cf_dx<W>(o, pdz, n, wk);
         cf_store<VEC>(dx, ptb + lane * kCfSteps, T, o);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) pdz[j] = dz[j];
       ptb = tb;
-      c2 = __builtin_amdgcn_readlane(v[u][2], kWave - 1);
-      c3 = __builtin_amdgcn_readlane(v[u][3], kWave - 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) c[q] = __builtin_amdgcn_readlane(v[u][q], kWave - 1);
     }
   }
   if (ptb >= 0) {  // the last block: no steps after it
-    float n0 = __shfl_down(pdz[0], 1), n1 = __shfl_down(pdz[1], 1), n2 = __shfl_down(pdz[2], 1);
-    if (lane == kWave - 1) n0 = n1 = n2 = 0.f;
+    float n[H];
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      n[i] = __shfl_down(pdz[i], 1);
+      if (lane == kWave - 1) n[i] = 0.f;
+    }
     float o[8];
-    cf_dx<W>(o, pdz, n0, n1, n2, wk);
+    cf_dx<W>(o, pdz, n, wk);
     cf_store<VEC>(dx, ptb + lane * kCfSteps, T, o);
   }
   // the row's partial: a fixed butterfly over the 64 lanes, lane 0 writes
 #pragma unroll
-  for (int k = 0; k < 5; ++k) {
+  for (int k = 0; k <= R; ++k) {
     float s = acc[k];
     s += __shfl_xor(s, 32);
     s += __shfl_xor(s, 16);
@@ -256,7 +268,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_cf_kernel(const CfAr
     s += __shfl_xor(s, 4);
     s += __shfl_xor(s, 2);
     s += __shfl_xor(s, 1);
-    if (lane == 0) a.part[(bi * 5 + k) * a.D + d] = s;
+    if (lane == 0) a.part[(bi * (R + 1) + k) * a.D + d] = s;
   }
 }
 
@@ -282,6 +294,10 @@ static hipError_t cf_dispatch(const CfArgs& a, bool vec, bool silu, bool bwd, hi
   switch (a.width) {
     case 2: return cf_width<2>(a, vec, silu, bwd, s);
     case 3: return cf_width<3>(a, vec, silu, bwd, s);
+    case 5: return cf_width<5>(a, vec, silu, bwd, s);
+    case 6: return cf_width<6>(a, vec, silu, bwd, s);
+    case 7: return cf_width<7>(a, vec, silu, bwd, s);
+    case 8: return cf_width<8>(a, vec, silu, bwd, s);
     default: return cf_width<4>(a, vec, silu, bwd, s);
   }
 }

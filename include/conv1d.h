@@ -1,6 +1,6 @@
 /*
  * conv1d.h -- C ABI of the MI355X (gfx950) packed depthwise causal Conv1d (+ SiLU), filter
- * width 4 (widths 2..8 for the channel-last non-pool forms, 2..4 channels-first).
+ * width 4 (widths 2..8 for every form without a slot pool).
  *
  * The operation (FlashInfer docs, flashinfer.mamba.causal_conv1d_fn, Parameters and Notes):
  * for every packed sequence with rows [s, e) and channel c, with the extended sequence
@@ -26,7 +26,7 @@
  *     takes [D, W]).  Read the formula above with W taps in the same order: z = b + sum over
  *     k of w[c][k]*u[t-(W-1)+k], tap W - 1 on the current token, and the history is W - 1
  *     values (u[-(W-1)] .. u[-1], oldest first).  The slot-pool forms (conv1d_fwd with a pool,
- *     conv1d_state_update*) are width four only; the channels-first calls take widths 2..4.
+ *     conv1d_state_update*) are width four only.
  *     The optional bias is a contiguous [C] array of FP32 or bf16 (`b_dtype`), NULL for none
  *     (causal_conv1d_fn, Parameters weight and bias).
  *   - Host-checkable preconditions are validated before anything is enqueued; a violation

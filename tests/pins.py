@@ -464,7 +464,8 @@ def pin_channels_first_conv1d(o, seed=24):
     for B, D, T, act, w_bf16, bias, W in ((2, 5, 9, "silu", False, True, 4), (3, 4, 1, "silu", True, False, 4),
                                           (1, 7, 13, "none", False, True, 4), (2, 3, 2, "silu", False, False, 4),
                                           (2, 6, 40, "silu", True, True, 4), (2, 5, 11, "silu", False, True, 2),
-                                          (3, 4, 17, "none", True, True, 3)):
+                                          (3, 4, 17, "none", True, True, 3), (2, 5, 23, "silu", False, True, 8),
+                                          (2, 3, 6, "silu", True, True, 6)):
         x = wl.normal_bf16(rng, (B, D, T))
         dy = wl.normal_bf16(rng, (B, D, T))
         w = wl.to_bf16_bits(wl.uniform_f32(rng, (D, W))) if w_bf16 else wl.uniform_f32(rng, (D, W))

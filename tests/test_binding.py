@@ -36,7 +36,7 @@ def test_shape_checks_come_first():
     x = torch.zeros((rows, C), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="weight"):
         cc.conv1d_fwd(x, torch.zeros((C, 9)), cu_seqlens=torch.tensor([0, rows], dtype=torch.int32))
-    with pytest.raises(ValueError, match="weight"):  # channels-first takes widths up to four
-        cc.conv1d_fwd_cf(torch.zeros((2, C, 32), dtype=torch.bfloat16), torch.zeros((C, 5)))
+    with pytest.raises(ValueError, match="weight"):
+        cc.conv1d_fwd_cf(torch.zeros((2, C, 32), dtype=torch.bfloat16), torch.zeros((C, 9)))
     with pytest.raises(ValueError, match="bf16"):
         cc.conv1d_fwd(x.float(), torch.zeros((C, 4)), cu_seqlens=torch.tensor([0, rows], dtype=torch.int32))

@@ -1,7 +1,7 @@
 """Filter widths 2, 3 and 5..8 (taps [C, W], W-1 history rows) on the GPU against the oracle:
 random packed sweeps in both sequence forms, sequences shorter than the history across range
 boundaries, the context-parallel workload at full size (widths 3 and 8), and the channels-first
-layout (widths 2 and 3)."""
+layout (widths 2, 3, 5 and 8)."""
 import numpy as np
 import pytest
 
@@ -77,7 +77,7 @@ def test_width_context_parallel_full_size(oracle, W):
     gh.check_bwd(oracle, case)
 
 
-@pytest.mark.parametrize("W", [2, 3])
+@pytest.mark.parametrize("W", [2, 3, 5, 8])
 def test_width_channels_first(oracle, W):
     rng = np.random.default_rng(80 + W)
     for B, D, T in ((2, 96, 1500), (3, 7, 517)):
