@@ -22,12 +22,7 @@ SOURCES = [s for s in build.SOURCES if s.endswith(".hip")]
 pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None, reason="needs hipcc")
 
 
-def _descriptors(src, tmp_path):
-    out = tmp_path / (src + ".s")
-    cmd = ["hipcc", *build.hipcc_flags(), "-x", "hip", "--cuda-device-only", "-S",
-           os.path.join(build.CSRC, src), "-o", str(out)]
-    subprocess.run(cmd, check=True, capture_output=True, text=True)
-    text = out.read_text()
+def _descriptors(text, src):
     kernels = re.findall(r"\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel", text, re.S)
     assert kernels, f"no kernels found in {src}"
     out = {}
@@ -38,8 +33,18 @@ def _descriptors(src, tmp_path):
     return out
 
 
-@pytest.mark.parametrize("src", SOURCES)
-def test_no_lds_and_no_scratch(src, tmp_path):
-    desc = _descriptors(src, tmp_path)
-    bad = {name: v for name, v in desc.items() if v != (0, 0)}
-    assert not bad, f"{src}: kernels with (LDS bytes, scratch bytes per lane) != (0, 0): {bad}"
+def test_no_lds_and_no_scratch(tmp_path):
+    procs = {}
+    for src in SOURCES:  # the sources compile concurrently
+        out = tmp_path / (src + ".s")
+        cmd = ["hipcc", *build.hipcc_flags(), "-x", "hip", "--cuda-device-only", "-S",
+               os.path.join(build.CSRC, src), "-o", str(out)]
+        procs[src] = (subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE, text=True), out)
+    bad = {}
+    for src, (proc, out) in procs.items():
+        _, err = proc.communicate()
+        assert proc.returncode == 0, f"{src}: hipcc failed\n{err}"
+        for name, v in _descriptors(out.read_text(), src).items():
+            if v != (0, 0):
+                bad[name] = v
+    assert not bad, f"kernels with (LDS bytes, scratch bytes per lane) != (0, 0): {bad}"
