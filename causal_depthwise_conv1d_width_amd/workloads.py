@@ -168,7 +168,10 @@ WORKLOADS = (single_sequence, varlen_pool, prefill_pool, train_seq_ids, cp_share
 def random_case(rng, *, C=None, nseq=None, max_len=10, mode="cu", pool_layout_name=None,
                 slots=None, L=3, with_hist=False, w_f32=True, bias=None, act="silu",
                 pad_rows=None, force_empty=False, sentinel=False):
-    """A small random packed problem for sweeps: returns the same dict layout as the configs."""
+    """A small random packed problem for sweeps: returns the same dict layout as the configs.
+
+    mode: "cu" (offsets), "idx" (per-token IDs inside batch rows) or "batch" (nseq batch rows of one
+    sequence each, no offsets or IDs); pools and history rows need "cu" or "batch"."""
     if C is None:
         C = int(rng.choice([1, 3, 8, 13, 64]))
     if nseq is None:
@@ -183,6 +186,11 @@ def random_case(rng, *, C=None, nseq=None, max_len=10, mode="cu", pool_layout_na
         pad = int(rng.integers(0, 3)) if pad_rows is None else pad_rows
         rows = int(cu[-1]) + pad
         d["cu_seqlens"] = cu
+    elif mode == "batch":  # neither offsets nor IDs: every batch row of T rows is one sequence
+        nseq = max(nseq, 1)
+        T = int(rng.integers(1, max_len + 1))
+        d["seqlen"] = T
+        rows = nseq * T
     else:  # "idx": per-token IDs inside batch rows
         B = int(rng.integers(1, 4))
         T = int(rng.integers(1, max_len + 1))
@@ -198,7 +206,7 @@ def random_case(rng, *, C=None, nseq=None, max_len=10, mode="cu", pool_layout_na
         d["b"] = bf if rng.integers(0, 2) else to_bf16_bits(bf)
     else:
         d["b"] = None
-    if mode == "cu" and pool_layout_name is not None:
+    if mode in ("cu", "batch") and pool_layout_name is not None:
         slots = slots if slots is not None else nseq + 2
         d["pool"] = pool_layout(normal_bf16(rng, (slots, C, L)), pool_layout_name)
         ci = rng.permutation(slots)[:nseq].astype(np.int32)
@@ -206,7 +214,7 @@ def random_case(rng, *, C=None, nseq=None, max_len=10, mode="cu", pool_layout_na
             ci[int(rng.integers(0, nseq))] = -1
         d["cache_indices"] = ci
         d["has_initial_state"] = (rng.random(nseq) < 0.5).astype(np.uint8)
-    if mode == "cu" and with_hist:
+    if mode in ("cu", "batch") and with_hist:
         d["hist"] = normal_bf16(rng, (nseq, 3, C))
         d["has_history"] = (rng.random(nseq) < 0.6).astype(np.uint8)
     d["dy"] = normal_bf16(rng, (rows, C))

@@ -64,7 +64,7 @@ class Oracle:
                                    _i64, _int]
         lib.oracle_fwd.restype = _int
         lib.oracle_bwd.argtypes = [_p, _p, _i64, _i64, _i64, _i64, _p, _int, _int, _p, _int, _p, _i64,
-                                   _p, _i64, _p, _p, _int, _p, _i64, _p, _p, _p, _int]
+                                   _p, _i64, _p, _p, _int, _p, _i64, _p, _p, _p, _p, _int]
         lib.oracle_bwd.restype = _int
         lib.oracle_state_update.argtypes = [_p, _i64, _i64, _i64, _p, _int, _p, _int, _p, _i64,
                                             _i64, _i64, _i64, _i64, _p, _int, _p, _i64]
@@ -72,6 +72,8 @@ class Oracle:
         lib.oracle_spec_update.argtypes = [_p, _i64, _i64, _i64, _i64, _p, _int, _p, _int, _p, _i64,
                                            _i64, _i64, _i64, _i64, _p, _p, _int, _p, _i64]
         lib.oracle_spec_update.restype = _int
+        lib.oracle_combine.argtypes = [_p, _i64, _i64, _p]
+        lib.oracle_combine.restype = _int
         lib.oracle_round_double_to_bf16.argtypes = [ctypes.c_double]
         lib.oracle_round_double_to_bf16.restype = ctypes.c_uint16
         lib.oracle_round_float_to_bf16.argtypes = [ctypes.c_float]
@@ -197,8 +199,11 @@ class Oracle:
 
     # ------------------------------------------------------------------ backward
     def bwd(self, x, dy, w, b=None, *, cu_seqlens=None, seq_idx=None, seqlen=None, hist=None,
-            has_history=None, act="silu", want_db=None, want_dhist=None, fill=0x7FC1, nthreads=0):
-        """(dx bits, dw float32 [C, W], db float32 [C] or None, dhist bits or None)."""
+            has_history=None, act="silu", want_db=None, want_dhist=None, dtail=None, fill=0x7FC1, nthreads=0):
+        """(dx bits, dw float32 [C, W], db float32 [C] or None, dhist bits or None).
+
+        dtail: bf16 bits [W - 1, C] or None, the next shard's gradient of the last W - 1 values of
+        the last sequence's extended sequence (see oracle_bwd)."""
         x = np.asarray(x)
         dy = np.asarray(dy)
         rows, C = x.shape
@@ -219,10 +224,29 @@ class Oracle:
         dw = np.zeros((C, W), dtype=np.float32)
         db = np.zeros((C,), dtype=np.float32) if want_db else None
         dhist = np.full(hist.shape, fill, dtype=np.uint16) if (want_dhist and hist is not None) else None
+        if dtail is not None:
+            dtail = np.asarray(dtail)
+            if dtail.dtype != np.uint16 or not dtail.flags.c_contiguous or dtail.shape != (W - 1, C):
+                raise OracleError("dtail: need contiguous uint16 [W - 1, C]")
         rc = self.lib.oracle_bwd(_ptr(x), _ptr(dy), rows, C, x_ld, dy_ld, _ptr(w), wf, W, _ptr(b), bf,
                                  _ptr(cu), nseq, _ptr(si), seqlen, _ptr(hist), _ptr(hh),
                                  {"none": 0, "silu": 1}[act], _ptr(dx), C, _ptr(dw), _ptr(db),
-                                 _ptr(dhist), int(nthreads))
+                                 _ptr(dhist), _ptr(dtail), int(nthreads))
         if rc != 0:
             raise OracleError(f"oracle_bwd rejected its input (code {rc})")
         return dx, dw, db, dhist
+
+    # ------------------------------------------------------------------ shard-ordered combine
+    def combine(self, parts):
+        """parts: float32 [nshards, ...]; returns the element-wise sum in ascending shard order
+        (one FP32 addition per shard, starting from shard 0's value), shaped like one shard."""
+        parts = np.ascontiguousarray(parts, dtype=np.float32)
+        if parts.ndim < 1:
+            raise OracleError("parts: need a leading shard axis")
+        nshards = parts.shape[0]
+        n = int(np.prod(parts.shape[1:], dtype=np.int64))
+        out = np.zeros(parts.shape[1:], dtype=np.float32)
+        rc = self.lib.oracle_combine(_ptr(parts), nshards, n, _ptr(out))
+        if rc != 0:
+            raise OracleError(f"oracle_combine rejected its input (code {rc})")
+        return out

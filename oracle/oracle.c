@@ -17,7 +17,10 @@
  *     with a state reset at every sequence boundary.
  *   - flashinfer.cake_causal_conv1d_train.cake_causal_conv1d_kcp (FlashInfer docs), summary and
  *     Returns: a fragment that continues a document reads history rows instead of zeros, and the
- *     backward produces dx, a deterministic FP32 dweight and the gradient of the history rows.
+ *     backward produces dx, a deterministic FP32 dweight and the gradient of the history rows;
+ *     the successor's history-row gradient comes back into the shard's last rows (d(tail)).
+ *   - core.ssm.causal_conv1d.assert_causal_conv1d_deterministic (Megatron-Core docs): dweight
+ *     contributions added in a fixed order, here per-shard partials in ascending shard order.
  *
  * Readings where the pages leave a step open (all listed in the design notes):
  *   - history position j (j = 0,1,2) holds the raw input 3-j rows before the segment's first
@@ -400,12 +403,17 @@ int oracle_spec_update(const uint16_t* x, int64_t nseq, int64_t K, int64_t C, in
      dw_k   = sum over segments and t of dz[t] * u[t+k]      (u[H+t] = x[s+t])
      db     = sum of dz
      dh_j   = sum_{tau = 0 .. min(j, n-1)} w_{j-tau} * dz[tau]
-   Rows outside every segment are not written. */
+   Rows outside every segment are not written.
+   dtail (bf16 [H, C], or NULL): the gradient that arrives from the next shard for the last H values
+   of the last segment's extended sequence u (cake_causal_conv1d_kcp, Returns: the successor's
+   history-row gradient flows back into this shard; core.ssm.causal_conv1d, _exchange_initial_states
+   is differentiable).  Tail value j is u[n+j] of the last segment: it adds to dx[s+n+j-H] when
+   n+j >= H, else to that segment's dh_{n+j}; the sum stays in double and is rounded once. */
 int oracle_bwd(const uint16_t* x, const uint16_t* dy, int64_t rows, int64_t C, int64_t x_ld,
                int64_t dy_ld, const void* w, int w_f32, int width, const void* b, int b_f32,
                const int32_t* cu_seqlens, int64_t nseq, const int32_t* seq_idx, int64_t seqlen,
                const uint16_t* hist, const uint8_t* has_hist, int act, uint16_t* dx, int64_t dx_ld,
-               float* dw, float* db, uint16_t* dhist, int nthreads) {
+               float* dw, float* db, uint16_t* dhist, const uint16_t* dtail, int nthreads) {
   if ((!x || !dy || !dx) && rows > 0) return OR_INVALID;
   if (!w || !dw || C < 1 || x_ld < C || dy_ld < C || dx_ld < C || rows < 0 ||
       (act != 0 && act != 1))
@@ -453,12 +461,14 @@ int oracle_bwd(const uint16_t* x, const uint16_t* dy, int64_t rows, int64_t C, i
               }
               dz[t] = g;
             }
+            const int tail = dtail && q == ns - 1; /* the last segment takes the next shard's gradient */
             for (int64_t t = 0; t < n; ++t) {
               double acc = 0;
               for (int kk = 0; kk < W; ++kk) {
                 int64_t tau = t + H - kk;
                 if (tau < n) acc += (double)wf[kk] * dz[tau];
               }
+              if (tail && t + H - n >= 0) acc += bf16_bits_to_float(dtail[(t + H - n) * C + c]);
               dx[(s + t) * dx_ld + c] = double_to_bf16_rne(acc);
             }
             for (int64_t t = 0; t < n; ++t) {
@@ -469,6 +479,7 @@ int oracle_bwd(const uint16_t* x, const uint16_t* dy, int64_t rows, int64_t C, i
               for (int j = 0; j < H; ++j) {
                 double acc = 0;
                 for (int64_t tau = 0; tau <= j && tau < n; ++tau) acc += (double)wf[j - tau] * dz[tau];
+                if (tail && j - n >= 0) acc += bf16_bits_to_float(dtail[(j - n) * C + c]);
                 dhist[(i * H + j) * C + c] = double_to_bf16_rne(acc);
               }
             }
@@ -484,6 +495,22 @@ int oracle_bwd(const uint16_t* x, const uint16_t* dy, int64_t rows, int64_t C, i
   }
   free(segs);
   return err ? OR_NOMEM : OR_OK;
+}
+
+/* ================================================================ shard-ordered combine
+   The deterministic mode of core.ssm.causal_conv1d (assert_causal_conv1d_deterministic): per-shard
+   FP32 dweight / dbias contributions are added in a fixed order instead of by atomics.  Reading:
+   out[e] = (((p_0[e] + p_1[e]) + p_2[e]) + ...) + p_{S-1}[e], one FP32 addition per shard in
+   ascending shard order, starting from shard 0's value (so one shard is returned bit for bit).
+   parts: [nshards, n] float, contiguous.  nshards = 0 gives zeros. */
+int oracle_combine(const float* parts, int64_t nshards, int64_t n, float* out) {
+  if (nshards < 0 || n < 0 || (n > 0 && (!out || (nshards > 0 && !parts)))) return OR_INVALID;
+  for (int64_t e = 0; e < n; ++e) {
+    float acc = nshards > 0 ? parts[e] : 0.0f;
+    for (int64_t sh = 1; sh < nshards; ++sh) acc = acc + parts[sh * n + e];
+    out[e] = acc;
+  }
+  return OR_OK;
 }
 
 uint16_t oracle_round_double_to_bf16(double d) { return double_to_bf16_rne(d); }

@@ -139,3 +139,24 @@ def loss_f64(case, w):
     _, y, covered, _ = forward_f64(case, w=torch.tensor(w))
     dy = torch.tensor(f64(case["dy"]) * covered[:, None])
     return float((y * dy).sum())
+
+
+def grads_f64_with_tail(case, dtail):
+    """Autograd of L = sum(dy * y) + sum_j <dtail[j], u_last[n + j]>, where u_last = [history rows,
+    x rows] of the last sequence and n its length: the gradient the next shard sends back for the
+    last W-1 values of that extended sequence.  Returns (dx, dH) in float64."""
+    rows, C = case["x"].shape
+    segs = segments(case)
+    W = width(case)
+    x = torch.tensor(f64(case["x"]), requires_grad=True)
+    H = torch.tensor(history_rows(case, len(segs)), requires_grad=True)
+    _, y, covered, _ = forward_f64(case, x=x, H=H)
+    dy = torch.tensor(f64(case["dy"]) * covered[:, None])
+    loss = (y * dy).sum()
+    if segs:
+        s, e, i = segs[-1]
+        ext = torch.cat([H[i], x[s:e]], dim=0)  # [W-1 + n, C], oldest first
+        loss = loss + (ext[-(W - 1):] * torch.tensor(f64(dtail))).sum()
+    loss.backward()
+    return x.grad.numpy(), H.grad.numpy(), covered
+

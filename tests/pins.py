@@ -583,12 +583,138 @@ def pin_wide_closed_forms(o, seed=27):
     assert rejected, "widths above 8 are rejected"
 
 
+def pin_batch_rows_bruteforce(o, seed=28):
+    """The batch-row form (no offsets, no IDs: every batch row of `seqlen` rows is one sequence)
+    with a slot pool in both layouts (with -1 sentinels and mixed has_initial_state) and with
+    caller history rows: forward against the dense Toeplitz form and the pool write-back rule,
+    backward against its autograd (causal_conv1d_cp, Parameters x [B, T, D]; causal_conv1d_fn,
+    Parameters conv_state and cache_indices)."""
+    rng = np.random.default_rng(seed)
+    for q in range(12):
+        layout = ["hist", "chan", None][q % 3]
+        case = wl.random_case(rng, mode="batch", nseq=int(rng.integers(1, 5)), max_len=int(rng.choice([1, 2, 3, 9])),
+                              pool_layout_name=layout, with_hist=(layout is None), L=int(rng.choice([3, 4, 6])),
+                              w_f32=bool(q % 2), act="silu" if q % 5 else "none", sentinel=(q % 2 == 0))
+        pool0 = case["pool"].copy() if case.get("pool") is not None else None
+        _, yref, covered, sent = bf.forward_f64(case)
+        y = _fwd(o, case)
+        live = covered & ~sent
+        _close(bf.f64(y)[live], yref.numpy()[live], 2.0 ** -8, 1e-5, "batch rows: y vs dense Toeplitz")
+        assert (y[sent] == 0).all(), "batch rows: sentinel rows must be +0"
+        if pool0 is not None:
+            assert np.array_equal(case["pool"], bf.pool_after(dict(case, pool=pool0))), "batch rows: pool write-back"
+        else:
+            dx, dw, db, dh = _bwd(o, case)
+            gx, gw, gb, gH, covered = bf.grads_f64(case)
+            _close(bf.f64(dx), gx, 2.0 ** -8, 1e-5, "batch rows: dx vs autograd")
+            _close(dw, gw, 1e-5, 1e-5 * (1.0 + np.abs(gw).max()), "batch rows: dw vs autograd")
+            hh = case.get("has_history")
+            for i in range(dh.shape[0]):
+                if hh[i]:
+                    _close(bf.f64(dh[i]), gH[i], 2.0 ** -8, 1e-5, "batch rows: dhist vs autograd")
+                else:
+                    assert (dh[i] == FILL).all(), "batch rows: dhist of sequences without history untouched"
+
+
+def pin_dtail_autograd(o, seed=29):
+    """The next shard's gradient for the last W-1 values of the last sequence's extended sequence
+    (cake_causal_conv1d_kcp, Returns; the history exchange of causal_conv1d_cp is differentiable):
+    dx and d(history) against autograd of sum(dy * y) + <dtail, those values>, for last sequences
+    longer and shorter than the history (the short ones pass part of dtail on to their own
+    history rows), empty last sequences, batch rows and per-token IDs, widths 2, 4 and 8."""
+    rng = np.random.default_rng(seed)
+    for q in range(18):
+        W = (4, 2, 8)[q % 3]
+        mode = ("cu", "batch", "idx")[(q // 3) % 3]
+        base = wl.random_case(rng, mode=mode, nseq=int(rng.integers(1, 5)), max_len=int(rng.choice([1, 2, 5, 12])),
+                              with_hist=(mode != "idx"), w_f32=bool(q % 2), act="silu" if q % 4 else "none")
+        if mode == "cu" and q % 2:  # a short or empty last fragment
+            cu = base["cu_seqlens"].copy()
+            cu[-1] = cu[-2] + min(int(rng.integers(0, 3)), int(cu[-1] - cu[-2]))
+            base["cu_seqlens"] = cu
+            base["x"] = base["x"][: cu[-1] + 1]
+            base["dy"] = base["dy"][: cu[-1] + 1]
+        case = _narrow(base, W, rng) if W != 4 else base
+        C = case["x"].shape[1]
+        dtail = wl.normal_bf16(rng, (W - 1, C))
+        dx, _, _, dh = o.bwd(case["x"], case["dy"], case["w"], case.get("b"), cu_seqlens=case.get("cu_seqlens"),
+                             seq_idx=case.get("seq_idx"), seqlen=case.get("seqlen"), hist=case.get("hist"),
+                             has_history=case.get("has_history"), act=case.get("act", "silu"), dtail=dtail)
+        gx, gH, covered = bf.grads_f64_with_tail(case, dtail)
+        _close(bf.f64(dx[covered]), gx[covered], 2.0 ** -8, 1e-5, f"W={W} {mode}: dx with d(tail) vs autograd")
+        assert (dx[~covered] == FILL).all(), "rows past the last offset untouched"
+        if dh is not None:
+            hh = case.get("has_history")
+            for i in range(dh.shape[0]):
+                if hh is None or hh[i]:
+                    _close(bf.f64(dh[i]), gH[i], 2.0 ** -8, 1e-5, f"W={W} {mode}: dhist with d(tail) vs autograd")
+
+
+def pin_dtail_shard_split(o, seed=30):
+    """Two shards of one packed batch on one host: shard B's d(history) for its first fragment,
+    passed back as shard A's d(tail), gives A's dx (and, when A's last fragment is shorter than the
+    history, A's own d(history)) equal to the unsplit dx up to one bf16 rounding of each part; the
+    dweight contributions of the shards add up to the unsplit one."""
+    rng = np.random.default_rng(seed)
+    C = 6
+    for cut_in_frag, S in ((7, 40), (1, 30), (2, 31), (0, 25)):
+        x, dy = wl.normal_bf16(rng, (S, C)), wl.normal_bf16(rng, (S, C))
+        w = wl.uniform_f32(rng, (C, 4))
+        doc_cu = np.array([0, 9, S], np.int32)      # two documents; the shard cut lies in the second
+        cut = 9 + cut_in_frag if cut_in_frag else 12
+        dx_u, dw_u, _, _ = o.bwd(x, dy, w, None, cu_seqlens=doc_cu)
+        # shard A: rows [0, cut) = fragments [0, 9), [9, cut); shard B: rows [cut, S), continuing
+        xa, dya = x[:cut], dy[:cut]
+        ha = np.zeros((2, 3, C), np.uint16)
+        dx_a0, _, _, _ = o.bwd(xa, dya, w, None, cu_seqlens=np.array([0, 9, cut], np.int32), hist=ha,
+                               has_history=np.array([0, 0], np.uint8))
+        hb = np.zeros((1, 3, C), np.uint16)
+        for j in range(3):
+            r = cut - 3 + j
+            hb[0, j] = x[r] if r >= 9 else 0
+        dx_b, dw_b, _, dh_b = o.bwd(x[cut:], dy[cut:], w, None, cu_seqlens=np.array([0, S - cut], np.int32), hist=hb,
+                                    has_history=np.array([1], np.uint8))
+        dx_a, dw_a, _, _ = o.bwd(xa, dya, w, None, cu_seqlens=np.array([0, 9, cut], np.int32), hist=ha,
+                                 has_history=np.array([0, 0], np.uint8), dtail=dh_b[0])
+        _close(bf.f64(dx_b), bf.f64(dx_u[cut:]), 0, 0, "shard B's dx equals the unsplit dx")
+        ref, part, tail = bf.f64(dx_u[:cut]), bf.f64(dx_a0), np.zeros((cut, C))
+        for j in range(3):
+            if cut - 3 + j >= 9:
+                tail[cut - 3 + j] = bf.f64(dh_b[0, j])
+        assert np.array_equal(dx_a[:cut - 3], dx_a0[:cut - 3]), "d(tail) reaches only the last three rows"
+        bad = np.abs(bf.f64(dx_a) - ref) > 2.0 ** -8 * (np.abs(part) + np.abs(tail) + np.abs(ref)) + 1e-30
+        assert not bad.any(), f"shard A's dx with d(tail) = unsplit dx (cut {cut})"
+        if tail.any():
+            assert not np.array_equal(dx_a, dx_a0), "d(tail) must change dx"
+        _close(o.combine(np.stack([dw_a, dw_b])), dw_u, 1e-5, 1e-5, "shard dweights add up")
+
+
+def pin_combine_closed_forms(o):
+    """Shard-ordered FP32 combine (assert_causal_conv1d_deterministic's fixed order): values whose
+    FP32 sum depends on the order pin ascending shard order; one shard comes back bit for bit (also
+    -0.0); zero shards give zeros; random sums lie within the FP32 bound of the exact sum."""
+    big = np.float32(1e8)
+    parts = np.array([[big, big, 1.0], [1.0, -big, big], [-big, 1.0, -big]], np.float32)[:, None, :]
+    out = o.combine(parts)
+    # (1e8 + 1) - 1e8 = 0 in FP32; (1e8 - 1e8) + 1 = 1; (1 + 1e8) - 1e8 = 0
+    assert np.array_equal(out[0], np.array([0.0, 1.0, 0.0], np.float32)), out
+    one = np.array([[[-0.0, 3.5e-40, -7.25]]], np.float32)
+    assert np.array_equal(o.combine(one).view(np.uint32), one[0].view(np.uint32)), "one shard is the identity"
+    assert np.array_equal(o.combine(np.zeros((0, 2, 3), np.float32)), np.zeros((2, 3), np.float32))
+    rng = np.random.default_rng(31)
+    p = rng.standard_normal((9, 5, 7)).astype(np.float32)
+    exact = p.astype(np.float64).sum(axis=0)
+    bound = 8 * 2.0 ** -24 * np.abs(p).astype(np.float64).sum(axis=0)
+    assert (np.abs(o.combine(p) - exact) <= bound).all(), "within the FP32 bound of the exact sum"
+
+
 ALL_PINS = [pin_rounding, pin_forward_bruteforce, pin_forward_conv1d_library, pin_forward_closed_forms,
             pin_segment_invariants, pin_pool_invariants, pin_decode_equals_unit_prefill,
             pin_cp_fragments_forward, pin_backward_autograd, pin_backward_finite_differences,
             pin_backward_linear_closed_form, pin_cp_fragments_backward, pin_spec_update_bruteforce,
             pin_spec_protocol_equals_prefill, pin_channels_first_conv1d,
-            pin_width_bruteforce, pin_width_closed_forms, pin_wide_closed_forms]
+            pin_width_bruteforce, pin_width_closed_forms, pin_wide_closed_forms, pin_batch_rows_bruteforce,
+            pin_dtail_autograd, pin_dtail_shard_split, pin_combine_closed_forms]
 
 
 def golden_dyadic():

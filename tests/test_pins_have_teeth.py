@@ -41,6 +41,13 @@ MUTATIONS = {
     "spec_writeback_short": ("for (int64_t j = 0; j < K + 2; ++j) h[j * s_pos] = u[j + 1];",
                              "for (int64_t j = 0; j < K + 1; ++j) h[j * s_pos] = u[j + 1];"),
     "spec_token_stride": ("u[3 + t] = x[(i * K + t) * x_ld + c];", "u[3 + t] = x[(i + t) * x_ld + c];"),
+    "dtail_reversed": ("acc += bf16_bits_to_float(dtail[(t + H - n) * C + c]);",
+                       "acc += bf16_bits_to_float(dtail[(n - 1 - t) * C + c]);"),
+    "dtail_dhist_dropped": ("if (tail && j - n >= 0) acc += bf16_bits_to_float(dtail[(j - n) * C + c]);", ""),
+    "dtail_first_segment": ("const int tail = dtail && q == ns - 1;", "const int tail = dtail && q == 0;"),
+    "combine_descending": ("for (int64_t sh = 1; sh < nshards; ++sh) acc = acc + parts[sh * n + e];",
+                           "for (int64_t sh = nshards - 1; sh >= 1; --sh) acc = acc + parts[sh * n + e];"),
+    "batch_rows_one_index": ("          v[n].i = n;\n", "          v[n].i = 0;\n"),
     "dx_mask_dropped_at_end": ("if (tau < n) acc += (double)wf[kk] * dz[tau];", "if (tau < n && tau + 1 < n) acc += (double)wf[kk] * dz[tau];"),
 }
 
