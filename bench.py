@@ -10,8 +10,9 @@ resident in HBM before the timed region.  Steady state, as inside a training or 
 the timed calls run back to back on one stream over a ring of independent buffer sets (4 for the
 step workload, about 3 GB), so no call finds its operands in the 256 MB Infinity Cache and every
 call's writes evict the previous calls' dirty lines, i.e. each written byte is paid for in HBM.
-W untimed warm-up steps come first (default 200, about 45 ms: after an idle gap the clocks need
-some 20 ms of sustained load to settle, and a shorter warm-up times the ramp).  HIP events on the
+W untimed warm-up steps come first (default 200), then whole untimed passes until 40 ms of
+load have gone by, before every timed ring: after an idle gap the clocks need some 20 ms of
+sustained load to settle, and a warm-up shorter than that times the ramp.  HIP events on the
 stream the library launches on bracket each batch of calls; `value` = algorithmic bytes of K
 steps / the batch time.  Effective bytes count what the method must move,
 each once (activations read and written, history rows, taps, gradients); halo re-reads and the
@@ -36,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
+WARM_MS = 40.0  # untimed load before every timed ring (clock ramp after idle gaps)
 METRIC = "effective GB/s (fwd, bwd) of packed causal conv1d+SiLU; % of HBM peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_conv1d_bwd_kernel_cp_share.md")
 KERNEL_SOURCES = ["conv1d_device.h", "conv1d_launch.h", "conv1d_fwd.hip", "conv1d_bwd.hip", "conv1d_cf.hip", "conv1d_api.cpp"]
@@ -262,7 +264,7 @@ class Gpu:
         t = self.torch
         bufs = [(t.empty(nbytes // 2, dtype=t.bfloat16, device=self.dev).normal_(),
                  t.empty(nbytes // 2, dtype=t.bfloat16, device=self.dev)) for _ in range(2)]
-        ms = self.ring([lambda a=a, b=b: b.copy_(a) for a, b in bufs], 40, 0, warm_ms=40)
+        ms = self.ring([lambda a=a, b=b: b.copy_(a) for a, b in bufs], 40, 0, warm_ms=WARM_MS)
         return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
@@ -385,10 +387,13 @@ def main():
         step_calls.append(lambda k=k: g.fwd(sets[k]))
         step_calls.append(lambda k=k: g.bwd(sets[(k + 2) % 4]))
     walls = []
-    mean_step = 2 * g.ring(step_calls, 2 * args.steps, 2 * args.warmup, wall=walls)
+    # every ring first runs `--warmup` calls and then whole passes until WARM_MS of load have gone
+    # by, all untimed: preparing the inputs leaves the GPU idle, and the clocks need some 20 ms of
+    # sustained load to settle, whatever count of warm-up steps the caller asked for
+    mean_step = 2 * g.ring(step_calls, 2 * args.steps, 2 * args.warmup, warm_ms=WARM_MS, wall=walls)
     wall = walls[0]
-    mean_f = g.ring([lambda k=k: g.fwd(sets[k]) for k in range(4)], args.steps, 20)
-    mean_b = g.ring([lambda k=k: g.bwd(sets[k]) for k in range(4)], args.steps, 20)
+    mean_f = g.ring([lambda k=k: g.fwd(sets[k]) for k in range(4)], args.steps, 20, warm_ms=WARM_MS)
+    mean_b = g.ring([lambda k=k: g.bwd(sets[k]) for k in range(4)], args.steps, 20, warm_ms=WARM_MS)
     value = gbps(fb + bb, mean_step)
 
     traffic = stored_traffic()
@@ -421,11 +426,11 @@ def main():
             if nb < (64 << 20):  # latency-bound: time replays of a captured graph (GPU time per call)
                 ms = g.graph_ms([lambda d=d: g.fwd(d) for d in dd])
             else:
-                ms = g.ring([lambda d=d: g.fwd(d) for d in dd], 40, 0, warm_ms=40)
+                ms = g.ring([lambda d=d: g.fwd(d) for d in dd], 40, 0, warm_ms=WARM_MS)
             r = {"fwd_GBps": round(gbps(nb, ms), 1), "fwd_us": round(1e3 * ms, 2), "fwd_bytes": nb}
             if c.get("dy") is not None:
                 nbb = bwd_bytes(c)
-                msb = g.ring([lambda d=d: g.bwd(d) for d in dd], 40, 0, warm_ms=40)
+                msb = g.ring([lambda d=d: g.bwd(d) for d in dd], 40, 0, warm_ms=WARM_MS)
                 r.update({"bwd_GBps": round(gbps(nbb, msb), 1), "bwd_us": round(1e3 * msb, 2), "bwd_bytes": nbb})
             extras[c["name"]] = r
             del dd
@@ -462,8 +467,8 @@ def main():
             cw["hist"] = wl.normal_bf16(rng, (case["hist"].shape[0], Wx - 1, case["x"].shape[1]))
             dw_sets = [g.prepare(cw) for _ in range(4)]
             nfw, nbw = fwd_bytes(cw), bwd_bytes(cw)
-            msfw = g.ring([lambda d=d: g.fwd(d) for d in dw_sets], 40, 0, warm_ms=40)
-            msbw = g.ring([lambda d=d: g.bwd(d) for d in dw_sets], 40, 0, warm_ms=40)
+            msfw = g.ring([lambda d=d: g.fwd(d) for d in dw_sets], 40, 0, warm_ms=WARM_MS)
+            msbw = g.ring([lambda d=d: g.bwd(d) for d in dw_sets], 40, 0, warm_ms=WARM_MS)
             extras[f"width{Wx}_" + case["name"]] = {"fwd_GBps": round(gbps(nfw, msfw), 1),
                                                    "fwd_us": round(1e3 * msfw, 2), "fwd_bytes": nfw,
                                                    "bwd_GBps": round(gbps(nbw, msbw), 1),
@@ -484,10 +489,10 @@ def main():
                                            device=g.dev)))
         nbf = B * D * T * 2 * 2 + D * 16 + D * 4
         nbb = B * D * T * 2 * 3 + D * 16 + D * 4 + D * 16 + D * 4
-        msf = g.ring([lambda d=d: g.cc.conv1d_fwd_cf(d["x"], wcf, bcf, out=d["y"]) for d in cfs], 40, 0, warm_ms=40)
+        msf = g.ring([lambda d=d: g.cc.conv1d_fwd_cf(d["x"], wcf, bcf, out=d["y"]) for d in cfs], 40, 0, warm_ms=WARM_MS)
         msb = g.ring([lambda d=d: g.cc.conv1d_bwd_cf(d["x"], d["dy"], wcf, bcf, dx=d["dx"], dweight=d["dw"],
                                                      dbias=d["db"], want_dbias=True, workspace=d["ws"])
-                      for d in cfs], 40, 0, warm_ms=40)
+                      for d in cfs], 40, 0, warm_ms=WARM_MS)
         extras["channels_first_B4_D4096_T4096"] = {"fwd_GBps": round(gbps(nbf, msf), 1), "fwd_us": round(1e3 * msf, 2),
                                                    "fwd_bytes": nbf, "bwd_GBps": round(gbps(nbb, msb), 1),
                                                    "bwd_us": round(1e3 * msb, 2), "bwd_bytes": nbb}

@@ -12,7 +12,9 @@ Entry points (same names as the C ABI):
                        or caller history rows (history, has_history)
   conv1d_state_update  one decode step per sequence against its slot
   conv1d_state_update_spec  K speculative tokens per sequence, history read at the accepted offset
-  conv1d_bwd           dx, deterministic FP32 dweight / dbias, and d(history)
+  conv1d_bwd           dx, deterministic FP32 dweight / dbias, and d(history); optionally takes the
+                       next shard's gradient of this shard's tail (dtail)
+  conv1d_bwd_combine   per-shard dweight / dbias contributions added in ascending shard order
   conv1d_fwd_cf / conv1d_bwd_cf  the channels-first layout [B, D, T] (T contiguous, one sequence
                        per (b, d) row, zero history)
 """
@@ -20,7 +22,8 @@ import ctypes
 
 from . import _lib
 
-__all__ = ["conv1d_fwd", "conv1d_state_update", "conv1d_state_update_spec", "conv1d_bwd", "conv1d_fwd_cf",
+__all__ = ["conv1d_fwd", "conv1d_state_update", "conv1d_state_update_spec", "conv1d_bwd", "conv1d_bwd_combine",
+           "conv1d_fwd_cf",
            "conv1d_bwd_cf", "conv1d_bwd_cf_workspace_bytes", "conv1d_fwd_workspace_bytes",
            "conv1d_bwd_workspace_bytes", "library_path"]
 
@@ -273,8 +276,12 @@ def conv1d_state_update_spec(x, weight, bias=None, *, conv_state, cache_indices,
 
 def conv1d_bwd(x, dy, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqlen=None, history=None,
                has_history=None, activation="silu", dx=None, dweight=None, want_dbias=None, dbias=None,
-               want_dhistory=None, dhistory=None, workspace=None, stream=None):
-    """Returns (dx, dweight [C, W] fp32, dbias [C] fp32 or None, dhistory [nseq, W-1, C] or None)."""
+               want_dhistory=None, dhistory=None, dtail=None, workspace=None, stream=None):
+    """Returns (dx, dweight [C, W] fp32, dbias [C] fp32 or None, dhistory [nseq, W-1, C] or None).
+
+    dtail: bf16 [W-1, C] or None, the next shard's gradient of the last W-1 values of the last
+    sequence's extended sequence (its d(history) output there), added into dx (or into that
+    sequence's dhistory) before the single rounding."""
     torch = _torch()
     lib = _lib.load()
     rows, C = x.shape
@@ -287,7 +294,10 @@ def conv1d_bwd(x, dy, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqle
     hist = _hist(history, has_history, C, W)
     dev = x.device
     _on_gpu(dev, dy=dy, weight=weight, bias=bias, cu_seqlens=cu_seqlens, seq_idx=seq_idx, history=history,
-            has_history=has_history, dx=dx, dweight=dweight, dbias=dbias, dhistory=dhistory, workspace=workspace)
+            has_history=has_history, dx=dx, dweight=dweight, dbias=dbias, dhistory=dhistory, dtail=dtail,
+            workspace=workspace)
+    if dtail is not None and (tuple(dtail.shape) != (W - 1, C) or not dtail.is_contiguous() or not _bits_ok(dtail)):
+        raise ValueError(f"dtail: need a contiguous bf16 tensor of shape {(W - 1, C)}")
     if dy.shape[0] != rows:
         raise ValueError("dy: must have as many rows as x")
     _at_least(seq_idx, rows, "seq_idx")
@@ -321,10 +331,37 @@ def conv1d_bwd(x, dy, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqle
     st = lib.conv1d_bwd(xp, dyp, rows, C, x_ld, dy_ld, wp, wd, W, bp, bd, ctypes.byref(seq), _ref(hist),
                         _lib.ACT[activation], dxp, dx_ld, dweight.data_ptr(),
                         None if dbias is None else dbias.data_ptr(),
-                        None if dhistory is None else dhistory.data_ptr(), workspace.data_ptr(), wsb,
-                        _stream(stream, dev))
+                        None if dhistory is None else dhistory.data_ptr(),
+                        None if dtail is None else dtail.data_ptr(), workspace.data_ptr(), wsb, _stream(stream, dev))
     _lib.check(lib, st, "conv1d_bwd")
     return dx, dweight, (dbias if want_dbias else None), (dhistory if want_dhistory else None)
+
+
+def conv1d_bwd_combine(dweight_parts, dbias_parts=None, *, dweight=None, dbias=None, stream=None):
+    """dweight_parts: fp32 [nshards, C, W] (each shard's dweight, stacked in shard order);
+    dbias_parts: fp32 [nshards, C] or None.  Returns (dweight [C, W], dbias [C] or None), each element
+    the FP32 sum of its shards in ascending shard order."""
+    torch = _torch()
+    lib = _lib.load()
+    if dweight_parts.dim() != 3 or dweight_parts.dtype != torch.float32 or not dweight_parts.is_contiguous():
+        raise ValueError("dweight_parts: need a contiguous float32 tensor [nshards, C, W]")
+    S, C, W = dweight_parts.shape
+    if dbias_parts is not None and (tuple(dbias_parts.shape) != (S, C) or dbias_parts.dtype != torch.float32
+                                    or not dbias_parts.is_contiguous()):
+        raise ValueError(f"dbias_parts: need a contiguous float32 tensor of shape {(S, C)}")
+    dev = dweight_parts.device
+    _on_gpu(dev, dbias_parts=dbias_parts, dweight=dweight, dbias=dbias)
+    _f32(dweight, (C, W), "dweight")
+    _f32(dbias, (C,), "dbias")
+    if dweight is None:
+        dweight = torch.empty((C, W), dtype=torch.float32, device=dev)
+    if dbias_parts is not None and dbias is None:
+        dbias = torch.empty((C,), dtype=torch.float32, device=dev)
+    st = lib.conv1d_bwd_combine(dweight_parts.data_ptr(), None if dbias_parts is None else dbias_parts.data_ptr(),
+                                S, C, W, dweight.data_ptr(), None if dbias_parts is None else dbias.data_ptr(),
+                                _stream(stream, dev))
+    _lib.check(lib, st, "conv1d_bwd_combine")
+    return dweight, (dbias if dbias_parts is not None else None)
 
 
 # ------------------------------------------------------------------ channels-first [B, D, T]

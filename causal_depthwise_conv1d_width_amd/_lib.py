@@ -37,7 +37,8 @@ SIGNATURES = {
     "conv1d_state_update_spec": (c_int, [c_p, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_p, c_int,
                                          ctypes.POINTER(Pool), c_p, c_int, c_p, c_i64, c_p]),
     "conv1d_bwd": (c_int, [c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_int, c_p, c_int, ctypes.POINTER(Seq),
-                           ctypes.POINTER(Hist), c_int, c_p, c_i64, c_p, c_p, c_p, c_p, c_size, c_p]),
+                           ctypes.POINTER(Hist), c_int, c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_size, c_p]),
+    "conv1d_bwd_combine": (c_int, [c_p, c_p, c_i64, c_i64, c_int, c_p, c_p, c_p]),
     "conv1d_fwd_cf": (c_int, [c_p, c_i64, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_int, c_p, c_int, c_int, c_p, c_i64,
                               c_i64, c_p]),
     "conv1d_bwd_cf": (c_int, [c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_int, c_p, c_int,

@@ -47,6 +47,15 @@ Span span_seq(const conv1d_seq* s, int64_t rows) {
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+// The channel-last kernels move a lane's kChannelsPerLane channels of a row as one vector when
+// the channel count, every row stride and every row base allow it; otherwise they take the
+// element-wise path (same results).
+constexpr int64_t kVecElems = kChannelsPerLane;
+constexpr uintptr_t kVecBytes = 2 * kChannelsPerLane;
+bool vec_rows(int64_t C, int64_t ld, const void* p) {
+  return C % kVecElems == 0 && ld % kVecElems == 0 && aligned(p, kVecBytes);
+}
+
 // Byte extents and element counts are computed in int64.  Sizes and strides whose products could
 // overflow it are rejected up front (no allocation comes near 2^56 elements).
 constexpr int64_t kMaxElems = (int64_t)1 << 56;
@@ -184,8 +193,7 @@ int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void*
   if (overlap(sy, sp)) return CONV1D_EINVAL;
   if (rows == 0) return CONV1D_OK;
 
-  const bool vec = (C % 8 == 0) && (x_ld % 8 == 0) && (y_ld % 8 == 0) && aligned(x, 16) && aligned(y, 16) &&
-                   (!use_hist || aligned(hist->ptr, 16));
+  const bool vec = vec_rows(C, x_ld, x) && vec_rows(C, y_ld, y) && (!use_hist || vec_rows(C, C, hist->ptr));
   const int64_t rr = fwd_range_rows(rows, ceil_div(C, kBlockChannels));
   const uint64_t nblk = (uint64_t)ceil_div(C, kBlockChannels) * ceil_div(rows, rr);
   if (nblk > 0x7fffffffull) return CONV1D_EINVAL;
@@ -238,7 +246,7 @@ static int state_update_common(const void* x, int64_t nseq, int64_t K, int64_t C
   if (overlap(sy, sp)) return CONV1D_EINVAL;
   if (nseq == 0) return CONV1D_OK;
   if ((uint64_t)nseq * ceil_div(C, kChannelsPerLane) / kBlockThreads > 0x7fffffffull) return CONV1D_EINVAL;
-  const bool vec = (C % 8 == 0) && (x_ld % 8 == 0) && (y_ld % 8 == 0) && aligned(x, 16) && aligned(y, 16);
+  const bool vec = vec_rows(C, x_ld, x) && vec_rows(C, y_ld, y);
   DecodeArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.y = static_cast<uint16_t*>(y);
@@ -269,10 +277,12 @@ int conv1d_state_update_spec(const void* x, int64_t nseq, int64_t K, int64_t C, 
   return state_update_common(x, nseq, K, C, x_ld, w, w_dtype, b, b_dtype, pool, num_accepted, act, y, y_ld, stream);
 }
 
-int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x_ld, int64_t dy_ld,
-               const void* w, int w_dtype, int width, const void* b, int b_dtype, const conv1d_seq* seq,
-               const conv1d_hist* hist, int act, void* dx, int64_t dx_ld, float* dw, float* db,
-               void* dhist, void* ws, size_t ws_bytes, hipStream_t stream) {
+// The backward behind conv1d_bwd: ws / ws_bytes is the caller's workspace (checked against the
+// size query) or, from conv1d_bwd_noalloc, the library's own scratch.
+static int bwd_common(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x_ld, int64_t dy_ld,
+                      const void* w, int w_dtype, int width, const void* b, int b_dtype, const conv1d_seq* seq,
+                      const conv1d_hist* hist, int act, void* dx, int64_t dx_ld, float* dw, float* db,
+                      void* dhist, const void* dtail, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (rows < 0 || C < 1 || x_ld < C || dy_ld < C || dx_ld < C || !w || !dtype_ok(w_dtype) || !dw)
     return CONV1D_EINVAL;
   if (width < 2 || width > kMaxWidth) return CONV1D_EINVAL;
@@ -297,21 +307,22 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
   const Span sdw = span_bytes(dw, width * C * 4), sdb = span_bytes(db, C * 4);
   const Span sh = use_hist ? span_bytes(hist->ptr, nseq * (width - 1) * C * 2) : Span{};
   const Span sdh = dhist ? span_bytes(dhist, nseq * (width - 1) * C * 2) : Span{};
+  const Span sdt = span_bytes(dtail, (width - 1) * C * 2);
   const Span sws = span_bytes(ws, (int64_t)need);
   const Span sm = span_seq(seq, rows);
   const Span shh = use_hist ? span_bytes(hist->has_history, nseq) : Span{};
   const Span outs[5] = {sdx, sdw, sdb, sdh, sws};
-  const Span ins[7] = {sx, sdy, sw, sb, sh, sm, shh};
+  const Span ins[8] = {sx, sdy, sw, sb, sh, sm, shh, sdt};
   for (int i = 0; i < 5; ++i) {
-    for (int j = 0; j < 7; ++j)
+    for (int j = 0; j < 8; ++j)
       if (overlap(outs[i], ins[j])) return CONV1D_EINVAL;
     for (int j = i + 1; j < 5; ++j)
       if (overlap(outs[i], outs[j])) return CONV1D_EINVAL;
   }
 
-  const bool vec = (C % 8 == 0) && (x_ld % 8 == 0) && (dy_ld % 8 == 0) && (dx_ld % 8 == 0) && aligned(x, 16) &&
-                   aligned(dy, 16) && aligned(dx, 16) && (!use_hist || aligned(hist->ptr, 16)) &&
-                   (!dhist || aligned(dhist, 16));
+  const bool vec = vec_rows(C, x_ld, x) && vec_rows(C, dy_ld, dy) && vec_rows(C, dx_ld, dx) &&
+                   (!use_hist || vec_rows(C, C, hist->ptr)) && (!dhist || vec_rows(C, C, dhist)) &&
+                   (!dtail || vec_rows(C, C, dtail));
   const int64_t rr = range_rows_for(rows, ceil_div(C, kBlockChannels), kBwdBlocks, kBwdFixedRows);
   const uint64_t nblk = (uint64_t)ceil_div(C, kBlockChannels) * ceil_div(rows, rr);
   if (nblk > 0x7fffffffull || (uint64_t)((36 + (nseq > 0 ? nseq : 0)) * C) / 256 > 0x7fffffffull)
@@ -334,6 +345,7 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
   a.seq = SeqArgs{seq->cu_seqlens, mode == MODE_BATCH ? nseq : seq->nseq, seq->seq_idx, seq->seqlen};
   if (use_hist) a.hist = HistArgs{static_cast<const uint16_t*>(hist->ptr), hist->has_history};
   a.dhist = static_cast<uint16_t*>(dhist);
+  a.dtail = static_cast<const uint16_t*>(dtail);
   a.part = static_cast<float*>(ws);
   a.dw = dw;
   a.db = db;
@@ -341,6 +353,36 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
   a.n_strips = ceil_div(C, kBlockChannels);
   a.n_rowblocks = ceil_div(rows, rr);
   return launch_bwd(a, mode, vec, act == CONV1D_ACT_SILU, stream) == hipSuccess ? CONV1D_OK : CONV1D_EHIP;
+}
+
+int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x_ld, int64_t dy_ld,
+               const void* w, int w_dtype, int width, const void* b, int b_dtype, const conv1d_seq* seq,
+               const conv1d_hist* hist, int act, void* dx, int64_t dx_ld, float* dw, float* db,
+               void* dhist, const void* dtail, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return bwd_common(x, dy, rows, C, x_ld, dy_ld, w, w_dtype, width, b, b_dtype, seq, hist, act, dx, dx_ld, dw, db,
+                    dhist, dtail, ws, ws_bytes, stream);
+}
+
+int conv1d_bwd_combine(const float* dw_parts, const float* db_parts, int64_t nshards, int64_t C, int width,
+                       float* dw, float* db, hipStream_t stream) {
+  if (nshards < 0 || C < 1 || width < 2 || width > kMaxWidth || !dw) return CONV1D_EINVAL;
+  if ((nshards > 0 && !dw_parts) || (db && nshards > 0 && !db_parts)) return CONV1D_EINVAL;
+  if (!mul_ok(nshards, C * kMaxWidth) || !mul_ok(C, 4 * kMaxWidth)) return CONV1D_EINVAL;
+  if ((uint64_t)((width + 1) * C) / kBlockThreads > 0x7fffffffull) return CONV1D_EINVAL;
+  const Span sp = span_bytes(dw_parts, nshards * C * width * 4);
+  const Span spb = db ? span_bytes(db_parts, nshards * C * 4) : Span{};
+  const Span sdw = span_bytes(dw, C * width * 4), sdb = span_bytes(db, C * 4);
+  if (overlap(sdw, sp) || overlap(sdw, spb) || overlap(sdb, sp) || overlap(sdb, spb) || overlap(sdw, sdb))
+    return CONV1D_EINVAL;
+  CombineArgs a{};
+  a.dw_parts = dw_parts;
+  a.db_parts = db ? db_parts : nullptr;
+  a.dw = dw;
+  a.db = db;
+  a.nshards = nshards;
+  a.C = C;
+  a.width = width;
+  return launch_combine(a, stream) == hipSuccess ? CONV1D_OK : CONV1D_EHIP;
 }
 
 int conv1d_fwd_cf(const void* x, int64_t B, int64_t D, int64_t T, int64_t x_sb, int64_t x_sd, const void* w,

@@ -133,10 +133,23 @@ __device__ __forceinline__ void bwd_route(const BwdArgs& a, const BwdSeq& cs, in
   }
 }
 
+// Is sd the last sequence of the call (the one whose tail continues into the next shard)?
+template <int MODE>
+__device__ __forceinline__ bool bwd_is_last(const BwdArgs& a, const SeqDesc& sd) {
+  if constexpr (MODE == MODE_IDX) {
+    return sd.e >= a.rows;  // no empty sequences in this form: the last one ends at the last row
+  } else {
+    return sd.idx == a.seq.nseq - 1;
+  }
+}
+
 // The current sequence ends right before row e (ring slot r): the values of its last H rows
 // e-H .. e-1 only take dz of rows before e (tap slots below R-W left out), summed in the order of
-// bwd_back.
-template <int CPL, bool VEC, int W, int R = Win<W>::R>
+// bwd_back.  For the last sequence of the call, the next shard's gradient of the last W-1 values
+// of its extended sequence (d(tail) row j: the value W-1-j rows before e) is added in FP32
+// before the single rounding; values before the sequence's first row go to its d(history) rows
+// like every other value there (cake_causal_conv1d_kcp, Returns).
+template <int CPL, bool VEC, int MODE, int W, int R = Win<W>::R>
 __device__ __forceinline__ void bwd_flush(const BwdArgs& a, const BwdState<CPL, R>& st, const BwdSeq& cs, int r,
                                           int64_t e, int64_t ta, int64_t tb, int64_t c0, bool active) {
   constexpr int H = R - 1;
@@ -151,6 +164,15 @@ __device__ __forceinline__ void bwd_flush(const BwdArgs& a, const BwdState<CPL, 
       for (int k = R - 2; k >= (R - W > R - j ? R - W : R - j); --k)
         t = __builtin_fmaf(st.wk[k][ch], st.g[(r + 2 * R - 1 - j - k) % R][ch], t);
       v[j - 1][ch] = t;
+    }
+  }
+  if (a.dtail && active && bwd_is_last<MODE>(a, cs.sd)) {
+#pragma unroll
+    for (int j = 1; j <= W - 1; ++j) {
+      float f[CPL];
+      unpack(load_row<CPL, VEC>(a.dtail + (int64_t)(W - 1 - j) * a.C, c0, a.C), f);
+#pragma unroll
+      for (int ch = 0; ch < CPL; ++ch) v[j - 1][ch] += f[ch];
     }
   }
 #pragma unroll
@@ -215,7 +237,7 @@ __device__ __forceinline__ void bwd_chunk(const BwdArgs& a, BwdState<CPL, R>& st
   for (int r = 0; r < CH; ++r) {
     const int64_t q = q0 + r;
     if (!done && q == cs.sd.e) {
-      bwd_flush<CPL, VEC, W>(a, st, cs, r, q, ta, tb, c0, active);
+      bwd_flush<CPL, VEC, MODE, W>(a, st, cs, r, q, ta, tb, c0, active);
       if (q >= tb) {
         done = true;
       } else {
@@ -257,10 +279,10 @@ __device__ __forceinline__ void unroll_steps(F& f) {
   }
 }
 
-// Occupancy floor: a launch is sized for 4 waves per SIMD (one round of ~1024 blocks), so the
-// per-token-ID variant, which would otherwise take 131 VGPRs (3 waves), is held to 128.  At width
-// four that spills two 64-bit values that live from the set-up to the epilogue: they are stored
-// once before the row loop and reloaded after it, so the loop itself never touches scratch.
+// Occupancy floor: a launch is sized for 4 waves per SIMD (one round of ~1024 blocks), so every
+// width-four variant is held to 128 VGPRs (an earlier form of the per-token-ID variant took 131
+// and fell to 3 waves).  They fit without spilling: the kernel-resource test checks that no
+// kernel uses scratch or LDS.
 #ifndef CCONV_BWD_WAVES_PER_EU
 #define CCONV_BWD_WAVES_PER_EU 4
 #endif
@@ -440,7 +462,8 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
 // one memory round trip), then a fixed two-level butterfly across lanes l, l^16,
 // l^32, l^48 adds the four interleaved subsets:  (s0 + s1) + (s2 + s3).  The order is fixed, so
 // dweight/dbias are bitwise reproducible; no atomics.  The remaining threads write zero
-// d(history) rows of empty continuing fragments.
+// d(history) rows of empty continuing fragments (zeros, or the d(tail) rows when the empty
+// fragment is the last sequence: its extended sequence is its history alone).
 __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_reduce_kernel(const BwdArgs a, int64_t nhist_zero,
                                                                            int64_t n_red_waves) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -483,7 +506,38 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_reduce_kernel(const 
   const int64_t i = hid / C, c = hid - i * C;
   if (a.hist.has_hist && !a.hist.has_hist[i]) return;
   if (a.seq.cu[i + 1] != a.seq.cu[i]) return;  // nonempty: written by the tile kernel
-  for (int j = 0; j < a.width - 1; ++j) a.dhist[(i * (a.width - 1) + j) * C + c] = 0;
+  const bool tail = a.dtail && i == a.seq.nseq - 1;
+  for (int j = 0; j < a.width - 1; ++j) a.dhist[(i * (a.width - 1) + j) * C + c] = tail ? a.dtail[j * C + c] : 0;
+}
+
+// Shard-ordered combine of per-shard dweight / dbias contributions: one thread per output element,
+// acc = p[0] then acc = acc + p[s] for s = 1 .. n-1 in ascending shard order (FP32, no
+// reassociation: the library is built without contraction or fast-math), so the result depends
+// only on the values and their order (core.ssm.causal_conv1d, assert_causal_conv1d_deterministic).
+// Eight shards' loads are issued ahead of their adds.
+__global__ void __launch_bounds__(kBlockThreads) conv1d_combine_kernel(const CombineArgs a) {
+  const int64_t e = (int64_t)blockIdx.x * kBlockThreads + threadIdx.x;
+  const int64_t ndw = a.C * a.width;
+  const float* p;
+  float* out;
+  int64_t n, idx;
+  if (e < ndw) {
+    p = a.dw_parts, out = a.dw, n = ndw, idx = e;
+  } else if (a.db && e < ndw + a.C) {
+    p = a.db_parts, out = a.db, n = a.C, idx = e - ndw;
+  } else {
+    return;
+  }
+  float acc = a.nshards > 0 ? p[idx] : 0.f;
+  for (int64_t s0 = 1; s0 < a.nshards; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = s0 + k < a.nshards ? p[(s0 + k) * n + idx] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (s0 + k < a.nshards) acc = acc + v[k];
+  }
+  out[idx] = acc;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -532,6 +586,15 @@ hipError_t launch_reduce(const BwdArgs& a, hipStream_t s) {
   void* rargs[] = {const_cast<BwdArgs*>(&a), &nz_arg, &n_red_waves};
   return hipLaunchKernel(reinterpret_cast<const void*>(&conv1d_bwd_reduce_kernel), dim3(rblocks), dim3(kBlockThreads),
                          rargs, 0, s);
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  const int64_t n = a.C * a.width + (a.db ? a.C : 0);
+  const uint32_t blocks = (uint32_t)((n + kBlockThreads - 1) / kBlockThreads);
+  if (blocks == 0) return hipSuccess;
+  void* args[] = {const_cast<CombineArgs*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&conv1d_combine_kernel), dim3(blocks), dim3(kBlockThreads),
+                         args, 0, s);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int mode, bool vec, bool silu, hipStream_t s) {

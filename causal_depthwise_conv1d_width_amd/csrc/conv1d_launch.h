@@ -149,6 +149,8 @@ struct BwdArgs {
   SeqArgs seq;
   HistArgs hist;
   uint16_t* dhist;  // nullptr: not requested
+  const uint16_t* dtail;  // nullptr, or bf16 [width-1, C]: the next shard's gradient of the last
+                          // width-1 values of the last sequence's extended sequence
   float* part;      // workspace: [n_rowblocks, partial_rows(width), C] FP32 per-block partials
   float* dw;        // [C, width]
   float* db;        // [C] or nullptr
@@ -171,6 +173,17 @@ struct CfArgs {
   float* part;  // backward only
 };
 
+// Shard-ordered combine: out[e] = ((p[0][e] + p[1][e]) + ...) + p[n-1][e] in FP32, for the
+// dweight [C, width] and dbias [C] contributions of n shards stacked shard-major.
+struct CombineArgs {
+  const float* dw_parts;  // [nshards, C * width]
+  const float* db_parts;  // [nshards, C] or nullptr
+  float* dw;              // [C * width]
+  float* db;              // [C] or nullptr
+  int64_t nshards, C;
+  int width;
+};
+
 // Launchers (return hipError_t of the launch).  mode: 0 = cu_seqlens, 1 = seq_idx, 2 = batch rows.
 hipError_t launch_fwd(const FwdArgs& a, int mode, bool vec, bool silu, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, bool vec, bool silu, hipStream_t stream);
@@ -179,5 +192,6 @@ hipError_t launch_bwd(const BwdArgs& a, int mode, bool vec, bool silu, hipStream
 hipError_t launch_reduce(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_cf(const CfArgs& a, bool vec, bool silu, hipStream_t stream);
 hipError_t launch_bwd_cf(const CfArgs& a, bool vec, bool silu, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 }  // namespace cconv

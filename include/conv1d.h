@@ -39,9 +39,10 @@
  *     [0, rows], a slot outside [0, slots) acts as -1, accepted counts are clamped to the pool.
  *   - Sizes and strides whose products could exceed 2^56 elements (so that byte extents would
  *     overflow 64-bit arithmetic) are rejected with CONV1D_EINVAL.
- *   - Any C >= 1 and any row stride are accepted.  When C, the strides and the pointers allow
- *     16-byte vectors a vectorized kernel runs, otherwise an element-wise one; results are
- *     identical.
+ *   - Any C >= 1 and any row stride are accepted.  When C and the row strides are even and the
+ *     row bases 4-byte aligned (the channels-first calls: T and the strides multiples of 8, bases
+ *     16-byte aligned), a lane's channels move as one vector; otherwise an element-wise path
+ *     runs.  Results are identical.
  *   - Two calls that run concurrently must not share live slots or workspaces.
  */
 #ifndef CONV1D_H
@@ -158,15 +159,37 @@ int conv1d_state_update_spec(const void* x, int64_t nseq, int64_t K, int64_t C, 
      db   FP32 [C]: dL/db (NULL to skip; computed whether or not b is given);
      dhist bf16 [nseq, W - 1, C]: dL/d(history rows) for sequences that read history rows
           (requires hist; NULL to skip; rows of other sequences untouched).
+   dtail: bf16 [W - 1, C] contiguous, or NULL.  The gradient the next shard sends back for the
+   last W - 1 values of the LAST sequence's extended sequence [history rows, x rows] (the
+   sequence that continues into the next shard: its d(history) output there; cake_causal_conv1d_kcp,
+   Returns, and the differentiable history exchange of core.ssm.causal_conv1d,
+   _exchange_initial_states).  Row j belongs to the value W - 1 - j positions before the end of
+   that extended sequence: it is added in FP32, before the single bf16 rounding, to dx of that
+   row, or to the sequence's d(history) row when the sequence is shorter than W - 1 rows (an
+   empty last sequence passes dtail to its d(history) whole).  The last sequence is sequence
+   nseq - 1 (cu_seqlens and batch-row forms) or the one holding row rows - 1 (per-token IDs).
    dw and db are sums of per-tile FP32 partials combined in a fixed order by a second kernel
    (no atomics), so they are bitwise identical from run to run and independent of the
    workspace address.  ws: device scratch of at least conv1d_bwd_workspace_bytes(rows, C)
-   bytes (room for any width: one FP32 partial of up to 9 x C values per row range), 16-byte
-   aligned, not overlapping any operand.  No pool. */
+   bytes, 16-byte aligned, not overlapping any operand.  The query does not take the filter
+   width: it reserves for width eight (one FP32 partial of 9 x C values per row range), which
+   is 1.8 times what widths up to four use (5 x C).  No pool. */
 int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x_ld, int64_t dy_ld,
                const void* w, int w_dtype, int width, const void* b, int b_dtype, const conv1d_seq* seq,
                const conv1d_hist* hist, int act, void* dx, int64_t dx_ld, float* dw, float* db,
-               void* dhist, void* ws, size_t ws_bytes, hipStream_t stream);
+               void* dhist, const void* dtail, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Shard-ordered combine of dweight / dbias contributions (core.ssm.causal_conv1d,
+   assert_causal_conv1d_deterministic: deterministic reductions instead of atomics; the one-GPU
+   share of gathering per-rank partials and adding them in rank order).  dw_parts: FP32
+   [nshards, C, W] contiguous (each shard's dw from conv1d_bwd, stacked in shard order);
+   db_parts: FP32 [nshards, C] or NULL.  Writes dw [C, W] and, when db is not NULL, db [C]:
+   element e is ((p[0][e] + p[1][e]) + p[2][e]) + ... + p[nshards-1][e], one FP32 addition per
+   shard in ascending shard order, so the bits depend only on the values and their order
+   (one shard is copied bit for bit; nshards = 0 gives zeros).  Outputs must not overlap the
+   inputs.  Returns a conv1d_status. */
+int conv1d_bwd_combine(const float* dw_parts, const float* db_parts, int64_t nshards, int64_t C, int width,
+                       float* dw, float* db, hipStream_t stream);
 
 /* Channels-first layout [B, D, T], T contiguous (core.ssm.causal_conv1d,
    assert_causal_conv1d_deterministic names it: there a dweight element takes one contribution
@@ -179,7 +202,7 @@ int conv1d_fwd_cf(const void* x, int64_t B, int64_t D, int64_t T, int64_t x_sb, 
                   int w_dtype, int width, const void* b, int b_dtype, int act, void* y, int64_t y_sb, int64_t y_sd,
                   hipStream_t stream);
 
-/* Channels-first backward: dx [B, D, T] bf16, dw FP32 [D, 4] (required), db FP32 [D] (NULL to
+/* Channels-first backward: dx [B, D, T] bf16, dw FP32 [D, W] (required), db FP32 [D] (NULL to
    skip).  One FP32 partial per (batch row, channel) goes to ws, and a second kernel adds the B
    partials of each channel in a fixed order, so dw and db are bitwise reproducible.  ws: at least
    conv1d_bwd_cf_workspace_bytes(B, D) bytes, 16-byte aligned, not overlapping any operand. */

@@ -70,7 +70,7 @@ def gpu_fwd(case, out_fill=wl.OUT_FILL, x_dev=None, out=None):
     return host_bits(y), (host_pool(pool) if pool is not None else None)
 
 
-def gpu_bwd(case, workspace=None):
+def gpu_bwd(case, workspace=None, dtail=None):
     x = dev_bits(case["x"])
     dy = dev_bits(case["dy"])
     rows, C = case["x"].shape
@@ -82,7 +82,8 @@ def gpu_bwd(case, workspace=None):
                                    cu_seqlens=dev_i32(case.get("cu_seqlens")), seq_idx=dev_i32(case.get("seq_idx")),
                                    seqlen=case.get("seqlen"), history=hist, has_history=dev_u8(case.get("has_history")),
                                    activation=case.get("act", "silu"), dx=dx, dhistory=dh,
-                                   want_dbias=case.get("b") is not None, workspace=workspace)
+                                   want_dbias=case.get("b") is not None, workspace=workspace,
+                                   dtail=None if dtail is None else dev_bits(dtail))
     torch.cuda.synchronize()
     return (host_bits(dx), dw.cpu().numpy(), None if db is None else db.cpu().numpy(),
             None if dh is None else host_bits(dh).reshape(dh.shape))
@@ -97,10 +98,10 @@ def oracle_fwd(o, case):
     return y, pool
 
 
-def oracle_bwd(o, case):
+def oracle_bwd(o, case, dtail=None):
     return o.bwd(case["x"], case["dy"], case["w"], case.get("b"), cu_seqlens=case.get("cu_seqlens"),
                  seq_idx=case.get("seq_idx"), seqlen=case.get("seqlen"), hist=case.get("hist"),
-                 has_history=case.get("has_history"), act=case.get("act", "silu"))
+                 has_history=case.get("has_history"), act=case.get("act", "silu"), dtail=dtail)
 
 
 def f32(bits):
@@ -146,9 +147,9 @@ def check_fwd(o, case, **kw):
     return y, pool
 
 
-def check_bwd(o, case, **kw):
-    dx, dw, db, dh = gpu_bwd(case, **kw)
-    dxr, dwr, dbr, dhr = oracle_bwd(o, case)
+def check_bwd(o, case, dtail=None, **kw):
+    dx, dw, db, dh = gpu_bwd(case, dtail=dtail, **kw)
+    dxr, dwr, dbr, dhr = oracle_bwd(o, case, dtail=dtail)
     assert_bf16_close(dx, dxr, f"{case.get('name')}: dx")
     assert_w_close(dw, dwr, f"{case.get('name')}: dweight")
     if dbr is not None:

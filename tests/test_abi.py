@@ -194,14 +194,14 @@ def test_fwd_rejects_aliasing(lib):
 
 
 def bwd(lib, f, rows=256, C=64, ws_bytes=None, ws=True, dw=True, dhist=None, hist=None, dx=None, dy=None,
-        seq="cu"):
+        seq="cu", dtail=None):
     if seq == "cu":
         seq = seq_cu(f, 4)
     need = lib.conv1d_bwd_workspace_bytes(rows, C)
     ws_bytes = need if ws_bytes is None else ws_bytes
     return lib.conv1d_bwd(f(rows * C * 2), f(rows * C * 2) if dy is None else dy, rows, C, C, C, f(C * 16), 1, 4,
                           None, 1, ctypes.byref(seq), None if hist is None else ctypes.byref(hist), 1,
-                          f(rows * C * 2) if dx is None else dx, C, f(C * 16) if dw else None, None, dhist,
+                          f(rows * C * 2) if dx is None else dx, C, f(C * 16) if dw else None, None, dhist, dtail,
                           f(need) if ws is True else ws, ws_bytes, None)
 
 
@@ -219,6 +219,25 @@ def test_bwd_rejects_bad_arguments(lib):
     h = _lib.Hist()
     h.ptr = f(4 * 3 * 64 * 2)
     assert bwd(lib, f, seq=s, hist=h) == EINVAL  # history rows need host-known nseq
+    dx = f(256 * 64 * 2)
+    assert bwd(lib, f, dx=dx, dtail=ctypes.c_void_p(dx.value + 256)) == EINVAL  # d(tail) overlaps dx
+
+
+def test_combine_rejects_bad_arguments(lib):
+    f = Fake()
+    C, W, S = 64, 4, 3
+    def call(parts=True, bparts=None, S=S, C=C, W=W, dw=True, db=None):
+        return lib.conv1d_bwd_combine(f(S * C * W * 4) if parts is True else parts, bparts, S, C, W,
+                                      f(C * W * 4) if dw is True else dw, db, None)
+    assert call(dw=None) == EINVAL
+    assert call(C=0) == EINVAL
+    assert call(W=1) == EINVAL and call(W=9) == EINVAL
+    assert call(S=-1) == EINVAL
+    assert call(parts=None) == EINVAL
+    assert call(db=f(C * 4)) == EINVAL  # dbias wanted without its parts
+    p = f(S * C * W * 4)
+    assert call(parts=p, dw=ctypes.c_void_p(p.value + 64)) == EINVAL  # output overlaps the parts
+    assert lib.conv1d_bwd_combine(f(4), None, 1 << 40, 1 << 20, 4, f(4), None, None) == EINVAL
 
 
 def test_state_update_rejects_bad_arguments(lib):
@@ -299,7 +318,7 @@ def test_sizes_whose_byte_extents_overflow_are_rejected(lib):
                           None, 0, None) == EINVAL
     assert lib.conv1d_bwd_workspace_bytes(big_rows, big_ld) == 0
     assert lib.conv1d_bwd(x, f(4096), big_rows, 64, big_ld, 64, w, 1, 4, None, 1, ctypes.byref(seq), None, 1,
-                          f(4096), 64, f(4096), None, None, f(4096), 4096, None) == EINVAL
+                          f(4096), 64, f(4096), None, None, None, f(4096), 4096, None) == EINVAL
     p = pool_hist_layout(f, 8, 64, 4)
     p.s_slot = 1 << 60  # slots far apart: the pool's extent overflows
     assert lib.conv1d_state_update(f(4096), 8, 64, 64, w, 1, None, 1, ctypes.byref(p), 1, f(4096), 64,

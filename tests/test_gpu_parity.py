@@ -186,6 +186,61 @@ def test_batch_rows_form(oracle):
     gh.check_bwd(oracle, case)
 
 
+def _batch_case(rng, B, T, C, kind, layout="hist", W=4):
+    """B batch rows of T rows (one sequence each, no offsets or IDs) with a slot pool (kind "pool":
+    a -1 sentinel when B > 1, mixed has_initial_state) or caller history rows (kind "hist")."""
+    rows = B * T
+    case = dict(name=f"batch-rows-{kind}-B{B}-T{T}-C{C}-{layout}-W{W}", x=wl.normal_bf16(rng, (rows, C)),
+                w=wl.uniform_f32(rng, (C, W)), b=(rng.standard_normal(C) * 0.1).astype(np.float32), seqlen=T,
+                dy=wl.normal_bf16(rng, (rows, C)), act="silu")
+    if kind == "pool":
+        slots = B + 3
+        case["pool"] = wl.pool_layout(wl.normal_bf16(rng, (slots, C, 4)), layout)
+        ci = rng.permutation(slots)[:B].astype(np.int32)
+        if B > 1:
+            ci[int(rng.integers(0, B))] = -1
+        case["cache_indices"] = ci
+        hi = (rng.random(B) < 0.5).astype(np.uint8)
+        hi[0], hi[-1] = 1, 0 if B > 1 else 1
+        case["has_initial_state"] = hi
+    else:
+        case["hist"] = wl.normal_bf16(rng, (B, W - 1, C))
+        hh = (rng.random(B) < 0.6).astype(np.uint8)
+        hh[0] = 1
+        case["has_history"] = hh
+    return case
+
+
+@pytest.mark.parametrize("layout", ["hist", "chan"])
+def test_batch_rows_with_pool(oracle, layout):
+    """The batch-row form with a slot pool: the sequence of a batch row is its index, so its slot
+    is cache_indices[row]; state read at the first row and written back after the last.  Batch
+    rows that are not a multiple of the range length, shorter than the history, and one shape at
+    full size (4 x 4096 rows of 5632 channels)."""
+    rng = np.random.default_rng(41)
+    shapes = [(5, 77, 64), (3, 1, 520), (4, 2, 13), (7, 3, 1024), (2, 333, 24), (6, 200, 5632), (4, 4096, 5632)]
+    for B, T, C in shapes:
+        case = _batch_case(rng, B, T, C, "pool", layout)
+        _print_case(case["name"])
+        y, pool = gh.check_fwd(oracle, case)
+        for i, slot in enumerate(case["cache_indices"]):
+            if slot == -1:
+                assert (y[i * T:(i + 1) * T] == 0).all(), "sentinel batch row must be +0"
+
+
+def test_batch_rows_with_history(oracle):
+    """The batch-row form with caller history rows: forward, and backward with dx, dweight, dbias
+    and d(history), at widths 4, 2 and 8, ragged batch rows, and 4 x 4096 x 5632."""
+    rng = np.random.default_rng(42)
+    shapes = [(5, 77, 64, 4), (3, 1, 520, 4), (4, 2, 13, 4), (7, 3, 1024, 4), (2, 333, 24, 4), (6, 200, 5632, 4),
+              (3, 50, 128, 2), (4, 9, 264, 8), (4, 4096, 5632, 4)]
+    for B, T, C, W in shapes:
+        case = _batch_case(rng, B, T, C, "hist", W=W)
+        _print_case(case["name"])
+        gh.check_fwd(oracle, case)
+        gh.check_bwd(oracle, case)
+
+
 @pytest.mark.parametrize("form", ["idx", "batch", "cu"])
 def test_forward_short_ranges_at_large_row_counts(oracle, form):
     """Past 256 rows per one-round range the forward switches to 40-row ranges (several rounds of
