@@ -15,6 +15,8 @@ Entry points (same names as the C ABI):
   conv1d_bwd           dx, deterministic FP32 dweight / dbias, and d(history); optionally takes the
                        next shard's gradient of this shard's tail (dtail)
   conv1d_bwd_combine   per-shard dweight / dbias contributions added in ascending shard order
+  conv1d_bwd_noalloc   conv1d_bwd without a workspace, for callers that cannot allocate: the
+                       partials use a scratch array the library holds on each GPU
   conv1d_fwd_cf / conv1d_bwd_cf  the channels-first layout [B, D, T] (T contiguous, one sequence
                        per (b, d) row, zero history)
 """
@@ -23,7 +25,7 @@ import ctypes
 from . import _lib
 
 __all__ = ["conv1d_fwd", "conv1d_state_update", "conv1d_state_update_spec", "conv1d_bwd", "conv1d_bwd_combine",
-           "conv1d_fwd_cf",
+           "conv1d_bwd_noalloc", "conv1d_fwd_cf",
            "conv1d_bwd_cf", "conv1d_bwd_cf_workspace_bytes", "conv1d_fwd_workspace_bytes",
            "conv1d_bwd_workspace_bytes", "library_path"]
 
@@ -335,6 +337,50 @@ def conv1d_bwd(x, dy, weight, bias=None, *, cu_seqlens=None, seq_idx=None, seqle
                         None if dtail is None else dtail.data_ptr(), workspace.data_ptr(), wsb, _stream(stream, dev))
     _lib.check(lib, st, "conv1d_bwd")
     return dx, dweight, (dbias if want_dbias else None), (dhistory if want_dhistory else None)
+
+
+def conv1d_bwd_noalloc(x, dy, weight, bias=None, *, dx, dweight, dbias=None, dhistory=None, cu_seqlens=None,
+                       seq_idx=None, seqlen=None, history=None, has_history=None, dtail=None, activation="silu",
+                       stream=None):
+    """conv1d_bwd into caller-given outputs with no allocation anywhere: dx bf16 [rows, C] and
+    dweight fp32 [C, W] are required; dbias fp32 [C] and dhistory bf16 [nseq, W-1, C] are written
+    when given.  The per-range partials use the library's own scratch on the GPU (calls that
+    overlap in time on one GPU race on it).  Returns (dx, dweight, dbias, dhistory)."""
+    lib = _lib.load()
+    rows, C = x.shape
+    xp, x_ld = _rows2d(x, "x")
+    dyp, dy_ld = _rows2d(dy, "dy", C)
+    W = _width(weight, C)
+    wp, wd = _taps(weight, C, (C, W), "weight")
+    bp, bd = _taps(bias, C, (C,), "bias")
+    seq, nseq = _seq(rows, cu_seqlens, seq_idx, seqlen)
+    hist = _hist(history, has_history, C, W)
+    dev = x.device
+    _on_gpu(dev, dy=dy, weight=weight, bias=bias, cu_seqlens=cu_seqlens, seq_idx=seq_idx, history=history,
+            has_history=has_history, dx=dx, dweight=dweight, dbias=dbias, dhistory=dhistory, dtail=dtail)
+    if dx is None or dweight is None:
+        raise ValueError("dx and dweight are required (this entry point allocates nothing)")
+    if dtail is not None and (tuple(dtail.shape) != (W - 1, C) or not dtail.is_contiguous() or not _bits_ok(dtail)):
+        raise ValueError(f"dtail: need a contiguous bf16 tensor of shape {(W - 1, C)}")
+    if dy.shape[0] != rows or dx.shape[0] != rows:
+        raise ValueError("dy, dx: must have as many rows as x")
+    _at_least(seq_idx, rows, "seq_idx")
+    _at_least(has_history, max(nseq, 0), "has_history")
+    if history is not None and history.shape[0] < max(nseq, 0):
+        raise ValueError(f"history: needs a row set for each of the {nseq} sequences")
+    _f32(dweight, (C, W), "dweight")
+    _f32(dbias, (C,), "dbias")
+    if dhistory is not None and (tuple(dhistory.shape) != (max(nseq, 0), W - 1, C) or not dhistory.is_contiguous()
+                                 or not _bits_ok(dhistory)):
+        raise ValueError(f"dhistory: need a contiguous bf16 tensor of shape {(max(nseq, 0), W - 1, C)}")
+    dxp, dx_ld = _rows2d(dx, "dx", C)
+    st = lib.conv1d_bwd_noalloc(xp, dyp, rows, C, x_ld, dy_ld, wp, wd, W, bp, bd, ctypes.byref(seq), _ref(hist),
+                                _lib.ACT[activation], dxp, dx_ld, dweight.data_ptr(),
+                                None if dbias is None else dbias.data_ptr(),
+                                None if dhistory is None else dhistory.data_ptr(),
+                                None if dtail is None else dtail.data_ptr(), _stream(stream, dev))
+    _lib.check(lib, st, "conv1d_bwd_noalloc")
+    return dx, dweight, dbias, dhistory
 
 
 def conv1d_bwd_combine(dweight_parts, dbias_parts=None, *, dweight=None, dbias=None, stream=None):

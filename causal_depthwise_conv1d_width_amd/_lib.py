@@ -10,7 +10,8 @@ c_i64 = ctypes.c_int64
 c_int = ctypes.c_int
 c_size = ctypes.c_size_t
 
-OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP = 0, 1, 2, 3, 4
+OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP, ETOOLARGE = 0, 1, 2, 3, 4, 5
+NOALLOC_SCRATCH_BYTES = 20 << 20  # CONV1D_NOALLOC_SCRATCH_BYTES
 BF16, F32 = 0, 1
 ACT = {"none": 0, None: 0, "silu": 1, "swish": 1}
 
@@ -39,6 +40,9 @@ SIGNATURES = {
     "conv1d_bwd": (c_int, [c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_int, c_p, c_int, ctypes.POINTER(Seq),
                            ctypes.POINTER(Hist), c_int, c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_size, c_p]),
     "conv1d_bwd_combine": (c_int, [c_p, c_p, c_i64, c_i64, c_int, c_p, c_p, c_p]),
+    "conv1d_bwd_noalloc": (c_int, [c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_int, c_p, c_int,
+                                   ctypes.POINTER(Seq), ctypes.POINTER(Hist), c_int, c_p, c_i64, c_p, c_p, c_p, c_p,
+                                   c_p]),
     "conv1d_fwd_cf": (c_int, [c_p, c_i64, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_int, c_p, c_int, c_int, c_p, c_i64,
                               c_i64, c_p]),
     "conv1d_bwd_cf": (c_int, [c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_p, c_int, c_int, c_p, c_int,

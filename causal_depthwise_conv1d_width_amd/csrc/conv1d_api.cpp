@@ -151,6 +151,7 @@ const char* conv1d_status_str(int status) {
     case CONV1D_EWORKSPACE: return "workspace missing or too small";
     case CONV1D_EUNSUPPORTED: return "unsupported configuration";
     case CONV1D_EHIP: return "HIP launch error";
+    case CONV1D_ETOOLARGE: return "problem too large for the library's scratch (CONV1D_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -277,12 +278,14 @@ int conv1d_state_update_spec(const void* x, int64_t nseq, int64_t K, int64_t C, 
   return state_update_common(x, nseq, K, C, x_ld, w, w_dtype, b, b_dtype, pool, num_accepted, act, y, y_ld, stream);
 }
 
-// The backward behind conv1d_bwd: ws / ws_bytes is the caller's workspace (checked against the
-// size query) or, from conv1d_bwd_noalloc, the library's own scratch.
+// The backward behind conv1d_bwd and conv1d_bwd_noalloc: with use_scratch, the partials go to the
+// library's own scratch (the problem must fit it) and ws / ws_bytes are ignored; otherwise ws is
+// the caller's workspace, checked against the size query.
 static int bwd_common(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x_ld, int64_t dy_ld,
                       const void* w, int w_dtype, int width, const void* b, int b_dtype, const conv1d_seq* seq,
                       const conv1d_hist* hist, int act, void* dx, int64_t dx_ld, float* dw, float* db,
-                      void* dhist, const void* dtail, void* ws, size_t ws_bytes, hipStream_t stream) {
+                      void* dhist, const void* dtail, void* ws, size_t ws_bytes, bool use_scratch,
+                      hipStream_t stream) {
   if (rows < 0 || C < 1 || x_ld < C || dy_ld < C || dx_ld < C || !w || !dtype_ok(w_dtype) || !dw)
     return CONV1D_EINVAL;
   if (width < 2 || width > kMaxWidth) return CONV1D_EINVAL;
@@ -297,7 +300,11 @@ static int bwd_common(const void* x, const void* dy, int64_t rows, int64_t C, in
   const bool use_hist = hist && hist->ptr;
   if (use_hist && mode == MODE_IDX) return CONV1D_EINVAL;
   if (dhist && !use_hist) return CONV1D_EINVAL;
-  const size_t need = conv1d_bwd_workspace_bytes(rows, C);
+  if (use_scratch) {
+    ws = nullptr;
+    ws_bytes = 0;
+  }
+  const size_t need = use_scratch ? 0 : conv1d_bwd_workspace_bytes(rows, C);
   if (ws_bytes < need || (need > 0 && !ws)) return CONV1D_EWORKSPACE;
   if (ws && !aligned(ws, 16)) return CONV1D_EINVAL;
 
@@ -327,6 +334,12 @@ static int bwd_common(const void* x, const void* dy, int64_t rows, int64_t C, in
   const uint64_t nblk = (uint64_t)ceil_div(C, kBlockChannels) * ceil_div(rows, rr);
   if (nblk > 0x7fffffffull || (uint64_t)((36 + (nseq > 0 ? nseq : 0)) * C) / 256 > 0x7fffffffull)
     return CONV1D_EINVAL;
+  if (use_scratch && rows > 0) {
+    // this width's partials: (ranges) x partial_rows(width) x C FP32
+    const uint64_t bytes = (uint64_t)ceil_div(rows, rr) * (uint64_t)partial_rows(width) * (uint64_t)C * 4;
+    if (bytes > kScratchBytes) return CONV1D_ETOOLARGE;
+    if (bwd_scratch(stream, &ws) != hipSuccess) return CONV1D_EHIP;
+  }
 
   BwdArgs a{};
   a.x = static_cast<const uint16_t*>(x);
@@ -360,7 +373,15 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
                const conv1d_hist* hist, int act, void* dx, int64_t dx_ld, float* dw, float* db,
                void* dhist, const void* dtail, void* ws, size_t ws_bytes, hipStream_t stream) {
   return bwd_common(x, dy, rows, C, x_ld, dy_ld, w, w_dtype, width, b, b_dtype, seq, hist, act, dx, dx_ld, dw, db,
-                    dhist, dtail, ws, ws_bytes, stream);
+                    dhist, dtail, ws, ws_bytes, false, stream);
+}
+
+int conv1d_bwd_noalloc(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x_ld, int64_t dy_ld,
+                       const void* w, int w_dtype, int width, const void* b, int b_dtype, const conv1d_seq* seq,
+                       const conv1d_hist* hist, int act, void* dx, int64_t dx_ld, float* dw, float* db,
+                       void* dhist, const void* dtail, hipStream_t stream) {
+  return bwd_common(x, dy, rows, C, x_ld, dy_ld, w, w_dtype, width, b, b_dtype, seq, hist, act, dx, dx_ld, dw, db,
+                    dhist, dtail, nullptr, 0, true, stream);
 }
 
 int conv1d_bwd_combine(const float* dw_parts, const float* db_parts, int64_t nshards, int64_t C, int width,

@@ -26,6 +26,7 @@
 // adds the partials of all row ranges in ascending range order.  No atomics anywhere, so the bits
 // depend only on the input values and the range length, never on scheduling or on the
 // workspace address.
+#include <mutex>
 #include <type_traits>
 
 #include "conv1d_device.h"
@@ -538,6 +539,48 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_combine_kernel(const Com
       if (s0 + k < a.nshards) acc = acc + v[k];
   }
   out[idx] = acc;
+}
+
+// ------------------------------------------------------------------ library-held scratch
+// conv1d_bwd_noalloc's partial workspace: a file-scope device array, one copy per GPU, held until
+// the process ends.  Host code never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol): the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and kept per device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (nullptr: not looked up)
+}  // namespace
+
+hipError_t bwd_scratch(hipStream_t stream, void** ptr) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t d = 0;
+    e = hipStreamGetDevice(stream, &d);
+    if (e != hipSuccess) return e;
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 // ------------------------------------------------------------------ launchers

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "conv1d.h"
+
 namespace cconv {
 
 // Tiling.  A block is kWavesPerBlock waves side by side in channels: lane = CPL channels, wave =
@@ -193,5 +195,10 @@ hipError_t launch_reduce(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_cf(const CfArgs& a, bool vec, bool silu, hipStream_t stream);
 hipError_t launch_bwd_cf(const CfArgs& a, bool vec, bool silu, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+// The library-held backward scratch of conv1d_bwd_noalloc (kScratchBytes on every GPU it runs
+// on): its device address on the GPU of `stream`, looked up once per device.
+constexpr size_t kScratchBytes = CONV1D_NOALLOC_SCRATCH_BYTES;
+hipError_t bwd_scratch(hipStream_t stream, void** ptr);
 
 }  // namespace cconv

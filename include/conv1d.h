@@ -62,8 +62,13 @@ typedef enum {
   CONV1D_EINVAL = 1,      /* a host-checkable precondition failed; nothing was launched     */
   CONV1D_EWORKSPACE = 2,  /* workspace missing or smaller than the *_workspace_bytes query  */
   CONV1D_EUNSUPPORTED = 3,/* reserved; not returned by this version                         */
-  CONV1D_EHIP = 4         /* the HIP runtime reported a launch error                        */
+  CONV1D_EHIP = 4,        /* the HIP runtime reported a launch error                        */
+  CONV1D_ETOOLARGE = 5    /* conv1d_bwd_noalloc: the problem needs more than the library's
+                             scratch (CONV1D_NOALLOC_SCRATCH_BYTES); nothing was launched     */
 } conv1d_status;
+
+/* Size of the device scratch conv1d_bwd_noalloc keeps on every GPU it runs on. */
+#define CONV1D_NOALLOC_SCRATCH_BYTES ((size_t)20 << 20)
 
 typedef enum { CONV1D_BF16 = 0, CONV1D_F32 = 1 } conv1d_dtype;
 typedef enum { CONV1D_ACT_NONE = 0, CONV1D_ACT_SILU = 1 } conv1d_act;
@@ -178,6 +183,24 @@ int conv1d_bwd(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x
                const void* w, int w_dtype, int width, const void* b, int b_dtype, const conv1d_seq* seq,
                const conv1d_hist* hist, int act, void* dx, int64_t dx_ld, float* dw, float* db,
                void* dhist, const void* dtail, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* conv1d_bwd without a workspace argument, for callers that cannot allocate device memory (code
+   under HIP graph capture, tight serving loops, harnesses that forbid allocation).  Same
+   arguments, checks, kernels and results (bit for bit) as conv1d_bwd; the per-range FP32
+   partials go to a scratch array the library holds on each GPU instead: a file-scope device
+   array of CONV1D_NOALLOC_SCRATCH_BYTES (20 MiB), kept until the process ends; its address is
+   looked up once per device, on the first call there.  The call itself allocates nothing.
+   Limit: (number of row ranges) * (5 for widths up to four, 9 above) * C * 4 bytes must fit in
+   the scratch; that holds for every C up to 524288 channels (and wider ones while the rows are
+   few); larger problems return CONV1D_ETOOLARGE with nothing launched.  Every call on one GPU
+   shares that GPU's scratch: calls that overlap in time on the same GPU (different streams,
+   threads or graphs) race on it and must be serialized by the caller.  The scratch keeps the
+   last call's partials; every call overwrites all the partials it reads, so nothing needs
+   clearing. */
+int conv1d_bwd_noalloc(const void* x, const void* dy, int64_t rows, int64_t C, int64_t x_ld, int64_t dy_ld,
+                       const void* w, int w_dtype, int width, const void* b, int b_dtype, const conv1d_seq* seq,
+                       const conv1d_hist* hist, int act, void* dx, int64_t dx_ld, float* dw, float* db,
+                       void* dhist, const void* dtail, hipStream_t stream);
 
 /* Shard-ordered combine of dweight / dbias contributions (core.ssm.causal_conv1d,
    assert_causal_conv1d_deterministic: deterministic reductions instead of atomics; the one-GPU

@@ -11,4 +11,5 @@ hipError_t launch_reduce(const BwdArgs&, hipStream_t) { return fail(); }
 hipError_t launch_fwd_cf(const CfArgs&, bool, bool, hipStream_t) { return fail(); }
 hipError_t launch_bwd_cf(const CfArgs&, bool, bool, hipStream_t) { return fail(); }
 hipError_t launch_combine(const CombineArgs&, hipStream_t) { return fail(); }
+hipError_t bwd_scratch(hipStream_t, void**) { return fail(); }
 }

@@ -15,7 +15,7 @@ from causal_depthwise_conv1d_width_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "conv1d.h")
 
-OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP = 0, 1, 2, 3, 4
+OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP, ETOOLARGE = 0, 1, 2, 3, 4, 5
 
 
 @pytest.fixture(scope="module")
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP):
+    for code in (OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP, ETOOLARGE):
         assert lib.conv1d_status_str(code)
     assert b"unknown" in lib.conv1d_status_str(99)
 
@@ -221,6 +221,24 @@ def test_bwd_rejects_bad_arguments(lib):
     assert bwd(lib, f, seq=s, hist=h) == EINVAL  # history rows need host-known nseq
     dx = f(256 * 64 * 2)
     assert bwd(lib, f, dx=dx, dtail=ctypes.c_void_p(dx.value + 256)) == EINVAL  # d(tail) overlaps dx
+
+
+def test_noalloc_rejects_bad_arguments_and_oversized_problems(lib):
+    """The allocation-free backward validates like conv1d_bwd and refuses, before any HIP call, a
+    problem whose partials exceed the library's scratch (20 MiB)."""
+    f = Fake()
+    def call(rows, C, width=4, dw=True, dhist=None, dx=None):
+        seq = seq_cu(f, 4)
+        return lib.conv1d_bwd_noalloc(f(rows * C * 2), f(rows * C * 2), rows, C, C, C, f(C * 32), 1, width, None, 1,
+                                      ctypes.byref(seq), None, 1, f(rows * C * 2) if dx is None else dx, C,
+                                      f(C * 32) if dw else None, None, dhist, None, None)
+    assert call(256, 64, dw=False) == EINVAL
+    assert call(256, 64, width=9) == EINVAL
+    assert call(256, 64, dhist=f(4 * 3 * 64 * 2)) == EINVAL  # d(history) needs history rows
+    # one row range of 600000 channels: 9 x 600000 x 4 bytes at width 8 (21.6 MB) > 20 MiB, while
+    # widths up to four need 5 x 600000 x 4 = 12 MB (that call would launch: not made here)
+    assert call(8, 600000, width=8) == ETOOLARGE
+    assert b"scratch" in lib.conv1d_status_str(ETOOLARGE)
 
 
 def test_combine_rejects_bad_arguments(lib):
