@@ -270,16 +270,6 @@ __device__ __forceinline__ void bwd_load(Pk<CPL> (&X)[CH], Pk<CPL> (&G)[CH], con
   }
 }
 
-// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>): a loop whose index must stay
-// a compile-time constant (it picks a register buffer) however large the body is.
-template <int N, int I = 0, class F>
-__device__ __forceinline__ void unroll_steps(F& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    unroll_steps<N, I + 1>(f);
-  }
-}
-
 // Occupancy floor: a launch is sized for 4 waves per SIMD (one round of ~1024 blocks), so every
 // width-four variant is held to 128 VGPRs (an earlier form of the per-token-ID variant took 131
 // and fell to 3 waves).  They fit without spilling: the kernel-resource test checks that no

@@ -1,19 +1,31 @@
 // conv1d_device.h -- device-side building blocks of the gfx950 kernels (library-internal).
 //
 // Data layout: activations are channel-last bf16 rows.  One lane owns CPL consecutive channels
-// of a row (CPL = 8: one 16-byte global_load_dwordx4 per row), a 64-lane wave covers 64*CPL
-// channels of the same row, and the waves of a block sit side by side, so one row access of a
-// block is one contiguous, fully coalesced segment of kBlockChannels*2 bytes.
+// of a row (CPL = 2: one 4-byte load per row), a 64-lane wave covers 64*CPL channels of the same
+// row, and the waves of a block sit side by side, so one row access of a block is one
+// contiguous, fully coalesced segment of kBlockChannels*2 bytes.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "conv1d_launch.h"
 
 namespace cconv {
 
 constexpr int kWave = 64;
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>): a loop whose index must stay
+// a compile-time constant (it picks a register buffer) however large the body is.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void unroll_steps(F& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    unroll_steps<N, I + 1>(f);
+  }
+}
 
 // ------------------------------------------------------------------ bf16 packing
 template <int CPL>
@@ -248,40 +260,87 @@ __device__ __forceinline__ int64_t cu_at(const SeqArgs& q, int64_t i, int64_t de
   return v < 0 ? 0 : (v > dend ? dend : v);
 }
 
-// IDX mode: does row t (0 <= t < rows) start a sequence?
-__device__ __forceinline__ bool idx_is_start(const SeqArgs& q, int64_t t) {
-  return (t % q.seqlen == 0) || (q.seq_idx[t] != q.seq_idx[t - 1]);  // t == 0 is caught first
-}
-
-// IDX mode: first sequence start in (t, limit), or limit.  64 rows per step, one row per lane.
+// IDX mode: first sequence start in (t, limit), or limit (t >= 0).  64 rows per step, one row per
+// lane; the batch-row position of each step's first row is kept as a scalar, so a lane tests the
+// batch-row start with an add and a compare.
 __device__ __forceinline__ int64_t idx_next_start(const SeqArgs& q, int64_t t, int64_t limit) {
   const int lane = threadIdx.x & (kWave - 1);
+  const int64_t L = q.seqlen;
+  int64_t m0 = (t + 1) % L;  // batch-row position of row t + 1
   for (int64_t base = t + 1; base < limit; base += kWave) {
     const int64_t r = base + lane;
     bool st = false;
-    if (r < limit) st = idx_is_start(q, r);
+    if (r < limit) {
+      const int64_t pos = m0 + lane;
+      const bool bstart = L >= kWave ? (pos == 0 || pos == L) : (pos % L == 0);
+      st = bstart || (q.seq_idx[r] != q.seq_idx[r - 1]);
+    }
     const uint64_t m = __ballot(st);
     if (m) return base + (int64_t)__builtin_ctzll(m);
+    m0 = (m0 + kWave) % L;
   }
   return limit;
 }
 
-// The sequence containing row t (t < dend).  `limit` bounds the IDX-mode forward scan.
+// The sequence containing row t (t < dend), in two phases so that a kernel can issue the lookup's
+// first loads before its row loads and use them after: seq_probe issues them (the first level of
+// the offset search, or the IDs around row t), seq_resolve finishes the lookup with their values.
+// `limit` bounds the IDX-mode forward scan.  seq_of_row does both at once.
+struct SeqProbe {
+  int32_t v, w;  // CU: raw offset of the first search level; IDX: IDs of rows r and r - 1
+};
+
 template <int MODE, int HB = 3>
-__device__ __forceinline__ SeqDesc seq_of_row(const SeqArgs& q, int64_t t, int64_t dend, int64_t limit) {
+__device__ __forceinline__ SeqProbe seq_probe(const SeqArgs& q, int64_t t, int64_t limit) {
+  SeqProbe p{0, 0};
+  const int lane = threadIdx.x & (kWave - 1);
+  if constexpr (MODE == MODE_CU) {
+    const int64_t n = q.nseq;
+    const int64_t stride = n < kWave ? 1 : (n + kWave - 2) / (kWave - 1);
+    const int64_t off = (int64_t)lane * stride;
+    if (off <= n) p.v = q.cu[off];
+  } else if constexpr (MODE == MODE_IDX) {
+    // lane l tests row r = t - HB + l: a start where r is a batch-row start or its ID differs.
+    // The batch-row position of lane 0's row is computed once per wave (scalar); a lane's row is a
+    // batch-row start where that position plus the lane is a multiple of seqlen.
+    const int64_t L = q.seqlen;
+    const int64_t r = t - HB + lane;
+    int64_t m0 = (t - HB) % L;
+    if (m0 < 0) m0 += L;
+    const int64_t pos = m0 + lane;
+    const bool bstart = L >= kWave ? (pos == 0 || pos == L) : (pos % L == 0);
+    if (r >= 0 && (lane <= HB || r < limit)) {
+      p.v = q.seq_idx[r];
+      p.w = bstart ? ~p.v : q.seq_idx[r - 1];
+    } else {
+      p.w = p.v;  // not a start
+    }
+  }
+  return p;
+}
+
+template <int MODE, int HB = 3>
+__device__ __forceinline__ SeqDesc seq_resolve(const SeqArgs& q, int64_t t, int64_t dend, int64_t limit,
+                                               const SeqProbe& p) {
   SeqDesc d;
   const int lane = threadIdx.x & (kWave - 1);
   if constexpr (MODE == MODE_CU) {
     // largest i in [0, nseq) with cu[i] <= t, by a 64-ary search: lane l reads cu[lo + l*stride]
-    // (one load per lane per level, a single level while nseq <= 63), the highest lane whose
-    // offset is <= t narrows the interval.  Lane 0 is taken as the floor without a test, as the
-    // offsets start at 0.  The last level also hands over cu[i + 1] from the next lane.
+    // (one load per lane per level, a single level while nseq <= 63; the first level's values
+    // come from the probe), the highest lane whose offset is <= t narrows the interval.  Lane 0 is
+    // taken as the floor without a test, as the offsets start at 0.  The last level also hands
+    // over cu[i + 1] from the next lane.
     int64_t lo = 0, n = q.nseq;  // the answer lies in [lo, lo + n)
+    bool first = true;
     while (true) {
       const int64_t stride = n < kWave ? 1 : (n + kWave - 2) / (kWave - 1);
       const int64_t off = (int64_t)lane * stride;
       int32_t v = 0;
-      if (off <= n) v = (int32_t)cu_at(q, lo + off, dend);  // lo + n <= nseq: in bounds
+      if (off <= n) {  // lo + n <= nseq: in bounds; offsets are clamped into [0, dend]
+        const int64_t raw = first ? (int64_t)p.v : (int64_t)q.cu[lo + off];
+        v = (int32_t)(raw < 0 ? 0 : (raw > dend ? dend : raw));
+      }
+      first = false;
       const uint64_t m = __ballot(lane == 0 || (off < n && v <= t));
       const int k = 63 - __builtin_clzll(m);
       if (stride == 1) {
@@ -303,10 +362,7 @@ __device__ __forceinline__ SeqDesc seq_of_row(const SeqArgs& q, int64_t t, int64
     // only the distance to the sequence start up to HB (the history length) matters
     // (d.s = t - min(dist, HB)), and the next start below `limit`: lane l tests row t - HB + l,
     // one pass covers rows t-HB .. t+63-HB
-    const int64_t r = t - HB + lane;
-    bool st = false;
-    if (r >= 0 && (lane <= HB || r < limit)) st = idx_is_start(q, r);
-    const uint64_t m = __ballot(st);
+    const uint64_t m = __ballot(p.v != p.w);
     const uint64_t back = m & (((1ull << HB) - 1) << 1);  // rows t-HB+1 .. t
     const int64_t dist = back ? HB - (63 - __builtin_clzll(back)) : HB;
     d.s = t - dist;
@@ -316,6 +372,11 @@ __device__ __forceinline__ SeqDesc seq_of_row(const SeqArgs& q, int64_t t, int64
     else d.e = t + 64 - HB < limit ? idx_next_start(q, t + 63 - HB, limit) : limit;
   }
   return d;
+}
+
+template <int MODE, int HB = 3>
+__device__ __forceinline__ SeqDesc seq_of_row(const SeqArgs& q, int64_t t, int64_t dend, int64_t limit) {
+  return seq_resolve<MODE, HB>(q, t, dend, limit, seq_probe<MODE, HB>(q, t, limit));
 }
 
 // The sequence that starts right where `cur` ended (cur.e < dend).  Empty sequences are skipped.

@@ -8,27 +8,26 @@
 //
 // Forward tiling (HBM-bound stencil, no MFMA):
 //   block  = kWavesPerBlock waves side by side; lane = CPL consecutive channels; a block covers
-//            kBlockChannels channels of one row range, so each row it touches is one contiguous
-//            segment.  The range length is set per launch so that one launch is about
-//            kFwdBlocks equal blocks, all resident at once.  Logical tiles run row-range major
-//            and each XCD gets one contiguous slice of them.
-//   stream = every wave walks its whole range top to bottom in unrolled chunks, software-
-//            pipelined with two register buffers (the next chunk's non-temporal loads are in
-//            flight while this chunk computes and stores), straight across sequence boundaries:
-//            the loads never depend on where sequences start, only the window does.
-//   window = a 4-slot register ring indexed by row mod 4 inside the unrolled chunk, so the
-//            sliding window costs no register moves.  Where a sequence starts inside a chunk,
-//            its three window slots are re-seeded from that sequence's history (pool positions
-//            0..2, caller history rows, or zeros) right before its first row.
-//   halo   = at the range start, the three rows before it: raw inputs of the same sequence
-//            (cached loads), or the sequence's history at its first row.
+//            kBlockChannels channels (a strip) of kFwdTileRows rows, so each row it touches is
+//            one contiguous segment.  A launch is many rounds of these short tiles, dispatched in
+//            row order (tile = row tile * strips + strip, each XCD one contiguous slice): the
+//            resident blocks sweep a compact band of rows, as a contiguous copy does, and the
+//            dispatcher balances the load to the end of the launch.
+//   loads  = one memory round trip per block: every row of the tile (non-temporal), the H window
+//            rows above it (the tile above read them moments ago on this XCD), the taps and the
+//            sequence offsets, all issued before any of them is used; row addresses never wait
+//            for the metadata.
+//   window = a ring of R register slots indexed by row mod R inside the unrolled tile, so the
+//            sliding window costs no register moves.  Where a sequence starts inside the tile,
+//            its window slots are re-seeded from that sequence's history (pool positions 0..2,
+//            caller history rows, or zeros) right before its first row.
 //   taps   = FP32 in registers; z = b, then W FMAs in tap order 0..W-1 (tap W-1 = current row).
 //   width  = W taps and W-1 history values in a ring of R = 4 register slots (W <= 4) or 8 (W <= 8).
-//   pool   = the wave that holds a sequence's first row is the only one that reads or writes
-//            its slot (for its channels).  With a pool, row-range boundaries that fall on the
-//            first three rows of a sequence move to that sequence's fourth row (or its end), so
-//            no other wave ever needs the slot's old history, and the head writes the final
-//            state (the last three raw values of the extended sequence) right after reading it.
+//   pool   = the block that holds a sequence's first row is the only one that reads or writes
+//            its slot (for its channels).  With a pool, tile boundaries that fall on the first
+//            three rows of a sequence move to that sequence's fourth row (or its end), so no
+//            other block ever needs the slot's old history, and the head writes the final state
+//            (the last three raw values of the extended sequence) right after reading it.
 #include "conv1d_device.h"
 
 namespace cconv {
@@ -110,18 +109,6 @@ __device__ __forceinline__ int64_t owner_boundary(const SeqArgs& q, int64_t r, i
   }
 }
 
-// CH consecutive rows starting at q0, every lane active, streamed (non-temporal).  A chunk past
-// the last full one (qlast is that chunk's last row) re-reads the last full chunk: the clamp is
-// one compare per chunk.
-template <int CPL, bool VEC, int CH>
-__device__ __forceinline__ void load_chunk(Pk<CPL> (&buf)[CH], const uint16_t* __restrict__ x, int64_t ld, int64_t q0,
-                                           int64_t qlast, int64_t c0, int64_t C) {
-  const int64_t qs = q0 + CH - 1 <= qlast ? q0 : qlast - (CH - 1);
-  const uint16_t* row = x + qs * ld;
-#pragma unroll
-  for (int r = 0; r < CH; ++r) buf[r] = load_row<CPL, VEC, true>(row + r * ld, c0, C);
-}
-
 // One output row from the ring of R slots: u[(r+1+k)%R] is row t-(R-1)+k and u[r%R] the current
 // row.  z = b, then the W taps in order (FMA), FP32; y = act(z) in bf16.
 template <int CPL, bool SILU, int W, int R = Win<W>::R>
@@ -139,21 +126,6 @@ __device__ __forceinline__ Pk<CPL> stencil_row(const float (&wk)[R][CPL], const 
 }
 
 // ------------------------------------------------------------------ forward kernel
-#ifndef CCONV_FWD_CHUNK
-#define CCONV_FWD_CHUNK 4
-#endif
-// The per-token-ID form streams 8-row chunks: about 5% faster there, while the cu_seqlens form,
-// whose chunks more often hold a sequence start and take the row-by-row path, is faster with 4.
-#ifndef CCONV_FWD_CHUNK_IDX
-#define CCONV_FWD_CHUNK_IDX 8
-#endif
-#ifndef CCONV_FWD_PIPELINE
-#define CCONV_FWD_PIPELINE 1
-#endif
-#ifndef CCONV_FWD_DEPTH
-#define CCONV_FWD_DEPTH 2
-#endif
-
 // The sequence a wave is streaming: its rows, its pool slot, and whether its output is forced to
 // zero (a -1 slot).
 struct FwdSeq {
@@ -239,12 +211,112 @@ __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)
   }
 }
 
+// The window of the row before a tile or range that starts at row ta of sequence cs (ring slots
+// 1..H get rows ta-H .. ta-1): the sequence's history, then the last `dist` input rows of the
+// sequence (wrow holds rows ta-H .. ta-1, loaded before the lookup).  At the sequence's first row
+// this enters the sequence (history, pool write-back); elsewhere only its -1 status matters, and
+// with a pool a tile never starts on a sequence's rows 1 and 2, so the slot is not touched.
+template <int CPL, bool VEC, int MODE, int W, int R = Win<W>::R, int H = Win<W>::H>
+__device__ __forceinline__ void fwd_start(const FwdArgs& a, FwdSeq& cs, int64_t ta, const Pk<CPL> (&wrow)[H],
+                                          int64_t c0, bool active, float (&u)[R][CPL]) {
+  const int64_t dist = ta - cs.sd.s < H ? ta - cs.sd.s : H;
+  float h[H][CPL];
+  if (dist == 0) {
+    fwd_enter<CPL, VEC, MODE, W>(a, cs, c0, active, h);
+  } else {
+    fwd_slot<MODE>(a, cs);
+#pragma unroll
+    for (int j = 0; j < H; ++j)
+#pragma unroll
+      for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
+    if constexpr (MODE != MODE_IDX) {
+      if (!cs.zero && dist < H) load_history<CPL, VEC, W>(a.pool, a.hist, cs.sd.idx, cs.slot, true, c0, a.C, active, h);
+    }
+  }
+  shift_window<CPL, H>(h, wrow, dist);
+#pragma unroll
+  for (int j = 0; j < H; ++j)
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch) u[j + 1][ch] = h[j][ch];
+}
+
+// Taps and bias of a wave whose lanes are all active: straight-line loads, the dtype branches
+// taken once for the wave.
+template <int CPL, int W, int R = Win<W>::R>
+__device__ __forceinline__ void load_taps_full(const FwdArgs& a, int64_t c0, float (&wk)[R][CPL], float (&bias)[CPL]) {
+#pragma unroll
+  for (int k = 0; k < R - W; ++k)
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch) wk[k][ch] = 0.f;
+  if (a.w_f32) {
+    const float* p = static_cast<const float*>(a.w) + c0 * W;
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch)
+#pragma unroll
+      for (int k = 0; k < W; ++k) wk[R - W + k][ch] = p[ch * W + k];
+  } else {
+    const uint16_t* p = static_cast<const uint16_t*>(a.w) + c0 * W;
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch)
+#pragma unroll
+      for (int k = 0; k < W; ++k) wk[R - W + k][ch] = __uint_as_float((uint32_t)p[ch * W + k] << 16);
+  }
+#pragma unroll
+  for (int ch = 0; ch < CPL; ++ch) bias[ch] = 0.f;
+  if (a.b) {
+    if (a.b_f32) {
+#pragma unroll
+      for (int ch = 0; ch < CPL; ++ch) bias[ch] = static_cast<const float*>(a.b)[c0 + ch];
+    } else {
+#pragma unroll
+      for (int ch = 0; ch < CPL; ++ch) bias[ch] = __uint_as_float((uint32_t)static_cast<const uint16_t*>(a.b)[c0 + ch] << 16);
+    }
+  }
+}
+
+// Rows [ta, te) R at a time in a rolled loop (ring slot of row q is (q - ta) mod R), reading each
+// chunk right before it is used: the path for tiles where a sequence starts or the data ends,
+// tiles a pool moved, partly active waves.  The sequence-start code then exists once per kernel.
+template <int CPL, bool VEC, int MODE, bool SILU, int W, int R = Win<W>::R>
+__device__ __forceinline__ void fwd_rolled(const FwdArgs& a, FwdSeq& cs, int64_t ta, int64_t te, int64_t dend,
+                                           int64_t c0, bool active, const float (&wk)[R][CPL],
+                                           const float (&bias)[CPL], float (&u)[R][CPL]) {
+  for (int64_t q0 = ta; q0 < te; q0 += R) {
+    const int n = (int)(te - q0 < R ? te - q0 : R);
+    Pk<CPL> rows[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      rows[r] = zero_pk<CPL>();
+      if (r < n && active) rows[r] = load_row<CPL, VEC>(a.x + (q0 + r) * a.x_ld, c0, a.C);
+    }
+    fwd_chunk<CPL, VEC, MODE, R, SILU, false, W>(a, rows, n, q0, te, dend, cs, c0, active, wk, bias, u);
+  }
+}
+
+// The rows [ta, tb) of one strip by the general path (predicated loads and lanes).
+template <int CPL, bool VEC, int MODE, bool SILU, int W>
+__device__ __forceinline__ void fwd_general(const FwdArgs& a, int64_t ta, int64_t tb, int64_t c0, bool active) {
+  constexpr int R = Win<W>::R, H = Win<W>::H;
+  const int64_t dend = data_end<MODE>(a.seq, a.rows);
+  const int64_t te = tb < dend ? tb : dend;
+  if (ta >= te) return;
+  float wk[R][CPL], bias[CPL];
+  load_taps<CPL, W>(a.w, a.w_f32, a.b, a.b_f32, c0, a.C, wk, bias);
+  Pk<CPL> wrow[H];
+  load_window<CPL, VEC, H>(wrow, a.x, a.x_ld, ta, c0, a.C, active);
+  FwdSeq cs;
+  cs.sd = seq_of_row<MODE, H>(a.seq, ta, dend, te);
+  float u[R][CPL];
+  fwd_start<CPL, VEC, MODE, W>(a, cs, ta, wrow, c0, active, u);
+  fwd_rolled<CPL, VEC, MODE, SILU, W>(a, cs, ta, te, dend, c0, active, wk, bias, u);
+}
+
 template <int CPL, bool VEC, int MODE, bool SILU, int W>
 __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs a) {
   constexpr int R = Win<W>::R, H = Win<W>::H;  // ring slots, history values
-  constexpr int CH0 = MODE == MODE_IDX ? CCONV_FWD_CHUNK_IDX : CCONV_FWD_CHUNK;
-  constexpr int CH = CH0 % R == 0 ? CH0 : R;  // rows per unrolled chunk
-  static_assert(CH % R == 0, "chunks must keep the ring slot of a row fixed");
+  constexpr int RT = kFwdTileRows;              // rows per tile
+  static_assert(RT % R == 0 && RT % 4 == 0, "tiles hold whole ring periods");
+  constexpr int NT = RT / R;                    // register chunks of a tile
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -256,95 +328,88 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
   const int64_t c0 = wc0 + lane * CPL;
   const bool active = c0 < C;
   const bool full = VEC && wc0 + kWaveChannels <= C;  // every lane of the wave is active
+  const bool has_pool = MODE != MODE_IDX && W == 4 && a.pool.ptr != nullptr;
+  const int64_t ta = (int64_t)rb * RT;
+  const int64_t tb = ta + RT < a.rows ? ta + RT : a.rows;
+
+  if (!full) {  // the last strip's partly active wave, or rows that do not allow vectors
+    int64_t ta2 = ta, tb2 = tb;
+    if (has_pool) {
+      const int64_t de = data_end<MODE>(a.seq, a.rows);
+      ta2 = owner_boundary<MODE>(a.seq, ta < de ? ta : de, de);
+      tb2 = owner_boundary<MODE>(a.seq, tb < de ? tb : de, de);
+    }
+    if (ta2 < tb2) fwd_general<CPL, VEC, MODE, SILU, W>(a, ta2, tb2, c0, active);
+    return;
+  }
+
+  // ---- one memory round trip: the sequence lookup's first loads (for both tile ends with a
+  // pool), the taps, the H window rows above the tile (the tile above read them moments ago on
+  // this XCD), every row of the tile (non-temporal; rows past the tile re-read its last row).
+  // Row addresses never wait for the metadata, and the lookup's loads go first, so resolving it
+  // waits for them alone.  The chunk index of every buffer access is a template constant: a
+  // runtime index would move the buffers out of registers.
+  const SeqProbe pa = seq_probe<MODE, H>(a.seq, ta, tb);
+  SeqProbe pb{0, 0};
+  if (has_pool && tb < a.rows) pb = seq_probe<MODE, H>(a.seq, tb, tb);
   const int64_t dend = data_end<MODE>(a.seq, a.rows);
-  const bool has_pool = a.pool.ptr != nullptr;
-
-  int64_t ta = (int64_t)rb * a.range_rows;
-  int64_t tb = ta + a.range_rows;
-  if (has_pool) {
-    ta = owner_boundary<MODE>(a.seq, ta, dend);
-    tb = owner_boundary<MODE>(a.seq, tb, dend);
-  }
-  ta = ta < dend ? ta : dend;
-  tb = tb < dend ? tb : dend;
-  if (ta >= tb) return;
-
   float wk[R][CPL], bias[CPL];
-  load_taps<CPL, W>(a.w, a.w_f32, a.b, a.b_f32, c0, C, wk, bias);
-
-  // full chunks are software-pipelined over the whole range; lanes past the last channel only
-  // occur in the last wave of a strip, which takes the predicated path for everything
-  const int nfull = (full && CCONV_FWD_PIPELINE) ? (int)((tb - ta) / CH) : 0;
-  const int64_t qlast = ta + (int64_t)nfull * CH - 1;
-  int64_t q0 = ta;
-  constexpr int NB = CCONV_FWD_DEPTH;  // register buffers: chunk j + NB - 1 is loading while j computes
-  static_assert(NB >= 2, "at least two buffers");
-  Pk<CPL> buf[NB][CH];
-  if (nfull > 0) {  // in flight during the set-up
-#pragma unroll
-    for (int b = 0; b + 1 < NB; ++b) load_chunk<CPL, VEC, CH>(buf[b], a.x, a.x_ld, q0 + b * CH, qlast, c0, C);
-  }
-
-  // the window rows ta-H .. ta-1 and the sequence holding row ta
+  load_taps_full<CPL, W>(a, c0, wk, bias);
   Pk<CPL> wrow[H];
-  load_window<CPL, VEC, H>(wrow, a.x, a.x_ld, ta, c0, C, active);
-  FwdSeq cs;
-  cs.sd = seq_of_row<MODE, H>(a.seq, ta, dend, tb);
-  const int64_t dist = ta - cs.sd.s < H ? ta - cs.sd.s : H;  // window rows from the same sequence
-  float h[H][CPL];
-  if (dist == 0) {
-    fwd_enter<CPL, VEC, MODE, W>(a, cs, c0, active, h);
-  } else {
-    // mid-sequence start: with a pool, range boundaries never fall on a sequence's rows 1 and 2,
-    // so dist == 3 and the slot is not touched (only its -1 status matters)
-    fwd_slot<MODE>(a, cs);
 #pragma unroll
-    for (int j = 0; j < H; ++j)
-#pragma unroll
-      for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
-    if constexpr (MODE != MODE_IDX) {
-      if (!cs.zero && dist < H) load_history<CPL, VEC, W>(a.pool, a.hist, cs.sd.idx, cs.slot, true, c0, C, active, h);
-    }
+  for (int j = 0; j < H; ++j) {
+    wrow[j] = zero_pk<CPL>();
+    if (ta - H + j >= 0) wrow[j] = load_row<CPL, VEC>(a.x + (ta - H + j) * a.x_ld, c0, C);
   }
-  // window rows ta-H .. ta-1 -> ring slots 1 .. H: the history, then the last `dist` input rows
-  // of the same sequence (the neighbouring range streamed them moments earlier on this XCD, so
-  // they come from L2)
-  shift_window<CPL, H>(h, wrow, dist);
-  float u[R][CPL];
+  Pk<CPL> buf[NT][R];
+  const int64_t qlast = tb - 1;
+  auto load = [&](auto cc) {
+    constexpr int c = decltype(cc)::value;
 #pragma unroll
-  for (int j = 0; j < H; ++j)
-#pragma unroll
-    for (int ch = 0; ch < CPL; ++ch) u[j + 1][ch] = h[j][ch];
+    for (int r = 0; r < R; ++r) {
+      const int64_t q = ta + c * R + r;
+      buf[c][r] = load_row<CPL, VEC, true>(a.x + (q <= qlast ? q : qlast) * a.x_ld, c0, C);
+    }
+  };
+  unroll_steps<NT>(load);
 
-  if (nfull > 0) {
-    // NB register buffers, unrolled by NB chunks: chunk j+NB-1's loads are issued before chunk j's
-    // stores, so waiting for a chunk's data never waits for the stores issued before it (the
-    // vector memory counter is in order).  Look-ahead loads are issued unconditionally; past the
-    // last full chunk they re-read the last row (a cache hit), so every path back to the loop
-    // head carries the same outstanding loads and the compiler's wait counts stay exact.
-    bool more = true;
-    for (int j = 0; more; j += NB) {
+  const int64_t te = tb < dend ? tb : dend;  // rows of the tile that belong to some sequence
+  if (ta >= te) return;
+  FwdSeq cs;
+  cs.sd = seq_resolve<MODE, H>(a.seq, ta, dend, te, pa);
+  if (has_pool) {
+    // tile boundaries on a sequence's rows 1 and 2 move to its row 3: the head tile alone owns
+    // the slot.  A moved tile takes the general path.
+    int64_t ta2 = ta, tb2 = tb;
+    if (ta > 0 && (ta - cs.sd.s == 1 || ta - cs.sd.s == 2)) ta2 = cs.sd.s + 3 < cs.sd.e ? cs.sd.s + 3 : cs.sd.e;
+    if (tb > 0 && tb < dend) {
+      const SeqDesc d = seq_resolve<MODE, H>(a.seq, tb, dend, dend, pb);
+      if (tb - d.s == 1 || tb - d.s == 2) tb2 = d.s + 3 < d.e ? d.s + 3 : d.e;
+    }
+    if (ta2 != ta || tb2 != tb) {
+      if (ta2 < tb2) fwd_general<CPL, VEC, MODE, SILU, W>(a, ta2, tb2, c0, active);
+      return;
+    }
+  }
+  float u[R][CPL];
+  fwd_start<CPL, VEC, MODE, W>(a, cs, ta, wrow, c0, active, u);
+
+  if (te - ta == RT && cs.sd.e >= te) {
+    // ---- the whole tile inside one sequence: one straight stencil (ring slot of row ta+c*R+r is r)
+    auto step = [&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      const int64_t q0 = ta + (int64_t)c * R;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (more) {
-          load_chunk<CPL, VEC, CH>(buf[(b + NB - 1) % NB], a.x, a.x_ld, q0 + (NB - 1) * CH, qlast, c0, C);
-          fwd_chunk<CPL, VEC, MODE, CH, SILU, true, W>(a, buf[b], CH, q0, tb, dend, cs, c0, active, wk, bias, u);
-          q0 += CH;
-          more = j + b + 1 < nfull;
-        }
+      for (int r = 0; r < R; ++r) {
+        unpack(buf[c][r], u[r]);
+        const Pk<CPL> out = cs.zero ? zero_pk<CPL>() : stencil_row<CPL, SILU, W>(wk, bias, u, r);
+        store_row<CPL, VEC, true>(a.y + (q0 + r) * a.y_ld, c0, C, out);
       }
-    }
+    };
+    unroll_steps<NT>(step);
+    return;
   }
-  // the rest (and partially active waves): one chunk at a time with uniform row predicates
-  for (; q0 < tb; q0 += CH) {
-    const int n = (int)(tb - q0 < CH ? tb - q0 : CH);
-#pragma unroll
-    for (int r = 0; r < CH; ++r) {
-      buf[0][r] = zero_pk<CPL>();
-      if (r < n && active) buf[0][r] = load_row<CPL, VEC, true>(a.x + (q0 + r) * a.x_ld, c0, C);
-    }
-    fwd_chunk<CPL, VEC, MODE, CH, SILU, false, W>(a, buf[0], n, q0, tb, dend, cs, c0, active, wk, bias, u);
-  }
+  fwd_rolled<CPL, VEC, MODE, SILU, W>(a, cs, ta, te, dend, c0, active, wk, bias, u);
 }
 
 // ------------------------------------------------------------------ decode / speculative update

@@ -12,17 +12,14 @@
 namespace cconv {
 
 // Tiling.  A block is kWavesPerBlock waves side by side in channels: lane = CPL channels, wave =
-// 64*CPL channels, block = kBlockChannels channels of one row range.  Every wave streams the rows
-// of its range top to bottom, straight across sequence boundaries.  The range length is chosen
-// per launch (range_rows) so that one launch is about kFwdBlocks / kBwdBlocks blocks: with 256
-// CUs that is a single wave of resident blocks of equal work, no tail of late blocks.  A forward
-// over many rows uses short ranges instead (fwd_range_rows).  The backward writes one [5, C]
-// FP32 dweight/dbias partial per range to the workspace.
+// 64*CPL channels, block = kBlockChannels channels (a strip) of some rows.  The forward gives a
+// block one short tile of kFwdTileRows rows and launches many rounds of tiles.  The backward gives
+// a block one row range streamed top to bottom, straight across sequence boundaries; the range
+// length is chosen per launch (range_rows) so that one launch is about kBwdBlocks blocks: with 256
+// CUs that is a single wave of resident blocks of equal work, and one [R + 1, C] FP32
+// dweight/dbias partial per range in the workspace.
 #ifndef CCONV_WAVES_PER_BLOCK
 #define CCONV_WAVES_PER_BLOCK 4
-#endif
-#ifndef CCONV_FWD_BLOCKS
-#define CCONV_FWD_BLOCKS 1024
 #endif
 #ifndef CCONV_BWD_BLOCKS
 #define CCONV_BWD_BLOCKS 1024
@@ -35,15 +32,10 @@ constexpr int kWavesPerBlock = CCONV_WAVES_PER_BLOCK;
 constexpr int kBlockThreads = 64 * kWavesPerBlock;
 constexpr int kWaveChannels = 64 * kChannelsPerLane;
 constexpr int kBlockChannels = kWavesPerBlock * kWaveChannels;
-#ifndef CCONV_FWD_FIXED_ROWS
-#define CCONV_FWD_FIXED_ROWS 0
-#endif
 #ifndef CCONV_BWD_FIXED_ROWS
 #define CCONV_BWD_FIXED_ROWS 0
 #endif
-constexpr int64_t kFwdBlocks = CCONV_FWD_BLOCKS;
 constexpr int64_t kBwdBlocks = CCONV_BWD_BLOCKS;
-constexpr int64_t kFwdFixedRows = CCONV_FWD_FIXED_ROWS;
 constexpr int64_t kBwdFixedRows = CCONV_BWD_FIXED_ROWS;
 #ifndef CCONV_RANGE_ALIGN
 #define CCONV_RANGE_ALIGN 8
@@ -68,25 +60,13 @@ inline int64_t range_rows_for(int64_t rows, int64_t n_strips, int64_t target_blo
   return r > kMinRangeRows ? r : kMinRangeRows;
 }
 
-// The forward's range length.  Up to kFwdLongRows rows per range it is one round of ~kFwdBlocks
-// equal blocks.  Beyond that (large row counts) one round would need long ranges, and several
-// rounds of short ranges dispatched in order stream faster: their resident blocks stay inside a
-// compact band of rows (measured at 32768-131072 rows and 2048-5632 channels: 5.4-5.6 TB/s
-// with 40-row ranges against 4.6-5.1 with one round).  The backward keeps one round, since its
-// per-range partial slab and look-ahead rows grow as ranges shrink.
-#ifndef CCONV_FWD_LONG_ROWS
-#define CCONV_FWD_LONG_ROWS 256
+// The forward's tile: kFwdTileRows rows of one strip per block, a launch of many rounds of them
+// (measured on x [16384, 5632]: 16-row tiles 64.5 us, 32-row 65.4 us, 8-row 72 us, one round of
+// long ranges 72.4 us).
+#ifndef CCONV_FWD_TILE_ROWS
+#define CCONV_FWD_TILE_ROWS 16
 #endif
-#ifndef CCONV_FWD_SHORT_ROWS
-#define CCONV_FWD_SHORT_ROWS 40
-#endif
-constexpr int64_t kFwdLongRows = CCONV_FWD_LONG_ROWS;
-constexpr int64_t kFwdShortRows = CCONV_FWD_SHORT_ROWS;
-
-inline int64_t fwd_range_rows(int64_t rows, int64_t n_strips) {
-  const int64_t r = range_rows_for(rows, n_strips, kFwdBlocks, kFwdFixedRows);
-  return (kFwdFixedRows == 0 && r > kFwdLongRows) ? kFwdShortRows : r;
-}
+constexpr int kFwdTileRows = CCONV_FWD_TILE_ROWS;
 
 // Rows of one range's dweight/dbias partial: a tap slot per register-ring slot (4 up to filter
 // width four, 8 up to width eight; the first R - W are padding), then dbias.
