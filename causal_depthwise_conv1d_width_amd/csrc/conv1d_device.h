@@ -237,6 +237,25 @@ __device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t nb) {
   return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
+// ------------------------------------------------------------------ integer helpers
+// x / L and x mod L for x >= 0, L >= 1 (wave-uniform values): one 32-bit division when both fit
+// (every row count here in practice), the 64-bit sequence otherwise.
+__device__ __forceinline__ int64_t udiv64(int64_t x, int64_t L) {
+  if ((((uint64_t)x | (uint64_t)L) >> 32) == 0) return (int64_t)((uint32_t)x / (uint32_t)L);
+  return x / L;
+}
+__device__ __forceinline__ int64_t umod64(int64_t x, int64_t L) {
+  if ((((uint64_t)x | (uint64_t)L) >> 32) == 0) return (int64_t)((uint32_t)x % (uint32_t)L);
+  return x % L;
+}
+// position of row x in its batch row of L rows, for any x >= -L (rows before the first are taken
+// modulo L as well)
+__device__ __forceinline__ int64_t batch_pos(int64_t x, int64_t L) {
+  if (x >= 0) return umod64(x, L);
+  const int64_t m = umod64(-x, L);
+  return m == 0 ? 0 : L - m;
+}
+
 // ------------------------------------------------------------------ sequence walking
 // All row indices below are wave-uniform: every lane of a wave works on the same row.
 struct SeqDesc {
@@ -266,18 +285,18 @@ __device__ __forceinline__ int64_t cu_at(const SeqArgs& q, int64_t i, int64_t de
 __device__ __forceinline__ int64_t idx_next_start(const SeqArgs& q, int64_t t, int64_t limit) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t L = q.seqlen;
-  int64_t m0 = (t + 1) % L;  // batch-row position of row t + 1
+  int64_t m0 = umod64(t + 1, L);  // batch-row position of row t + 1
   for (int64_t base = t + 1; base < limit; base += kWave) {
     const int64_t r = base + lane;
     bool st = false;
     if (r < limit) {
       const int64_t pos = m0 + lane;
-      const bool bstart = L >= kWave ? (pos == 0 || pos == L) : (pos % L == 0);
+      const bool bstart = L >= kWave ? (pos == 0 || pos == L) : (umod64(pos, L) == 0);
       st = bstart || (q.seq_idx[r] != q.seq_idx[r - 1]);
     }
     const uint64_t m = __ballot(st);
     if (m) return base + (int64_t)__builtin_ctzll(m);
-    m0 = (m0 + kWave) % L;
+    m0 = umod64(m0 + kWave, L);
   }
   return limit;
 }
@@ -300,20 +319,12 @@ __device__ __forceinline__ SeqProbe seq_probe(const SeqArgs& q, int64_t t, int64
     const int64_t off = (int64_t)lane * stride;
     if (off <= n) p.v = q.cu[off];
   } else if constexpr (MODE == MODE_IDX) {
-    // lane l tests row r = t - HB + l: a start where r is a batch-row start or its ID differs.
-    // The batch-row position of lane 0's row is computed once per wave (scalar); a lane's row is a
-    // batch-row start where that position plus the lane is a multiple of seqlen.
-    const int64_t L = q.seqlen;
+    // lane l reads the IDs of row r = t - HB + l and of the row before it (pure loads: whether r
+    // starts a batch row is worked out in seq_resolve)
     const int64_t r = t - HB + lane;
-    int64_t m0 = (t - HB) % L;
-    if (m0 < 0) m0 += L;
-    const int64_t pos = m0 + lane;
-    const bool bstart = L >= kWave ? (pos == 0 || pos == L) : (pos % L == 0);
     if (r >= 0 && (lane <= HB || r < limit)) {
       p.v = q.seq_idx[r];
-      p.w = bstart ? ~p.v : q.seq_idx[r - 1];
-    } else {
-      p.w = p.v;  // not a start
+      p.w = r >= 1 ? q.seq_idx[r - 1] : ~p.v;
     }
   }
   return p;
@@ -354,15 +365,21 @@ __device__ __forceinline__ SeqDesc seq_resolve(const SeqArgs& q, int64_t t, int6
     }
     if (d.e <= t) d.e = t + 1;  // only for metadata that breaks the contract: stay in bounds
   } else if constexpr (MODE == MODE_BATCH) {
-    d.idx = t / q.seqlen;
+    d.idx = udiv64(t, q.seqlen);
     d.s = d.idx * q.seqlen;
     d.e = d.s + q.seqlen;
     if (d.e > dend) d.e = dend;
   } else {
     // only the distance to the sequence start up to HB (the history length) matters
     // (d.s = t - min(dist, HB)), and the next start below `limit`: lane l tests row t - HB + l,
-    // one pass covers rows t-HB .. t+63-HB
-    const uint64_t m = __ballot(p.v != p.w);
+    // one pass covers rows t-HB .. t+63-HB.  A row starts a sequence where it starts a batch row
+    // (its position there, lane 0's plus the lane, is a multiple of seqlen) or its ID differs.
+    const int64_t L = q.seqlen;
+    const int64_t r = t - HB + lane;
+    const int64_t pos = batch_pos(t - HB, L) + lane;
+    const bool bstart = L >= kWave ? (pos == 0 || pos == L) : (umod64(pos, L) == 0);
+    const bool valid = r >= 0 && (lane <= HB || r < limit);
+    const uint64_t m = __ballot(valid && (bstart || p.v != p.w));
     const uint64_t back = m & (((1ull << HB) - 1) << 1);  // rows t-HB+1 .. t
     const int64_t dist = back ? HB - (63 - __builtin_clzll(back)) : HB;
     d.s = t - dist;

@@ -8,7 +8,7 @@
 //
 // Forward tiling (HBM-bound stencil, no MFMA):
 //   block  = kWavesPerBlock waves side by side; lane = CPL consecutive channels; a block covers
-//            kBlockChannels channels (a strip) of kFwdTileRows rows, so each row it touches is
+//            kBlockChannels channels (a strip) of fwd_tile_rows() rows, so each row it touches is
 //            one contiguous segment.  A launch is many rounds of these short tiles, dispatched in
 //            row order (tile = row tile * strips + strip, each XCD one contiguous slice): the
 //            resident blocks sweep a compact band of rows, as a contiguous copy does, and the
@@ -311,10 +311,10 @@ __device__ __forceinline__ void fwd_general(const FwdArgs& a, int64_t ta, int64_
   fwd_rolled<CPL, VEC, MODE, SILU, W>(a, cs, ta, te, dend, c0, active, wk, bias, u);
 }
 
-template <int CPL, bool VEC, int MODE, bool SILU, int W>
+template <int CPL, bool VEC, int MODE, bool SILU, int W, bool POOL>
 __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs a) {
   constexpr int R = Win<W>::R, H = Win<W>::H;  // ring slots, history values
-  constexpr int RT = kFwdTileRows;              // rows per tile
+  constexpr int RT = fwd_tile_rows(MODE, POOL); // rows per tile
   static_assert(RT % R == 0 && RT % 4 == 0, "tiles hold whole ring periods");
   constexpr int NT = RT / R;                    // register chunks of a tile
 
@@ -328,13 +328,14 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
   const int64_t c0 = wc0 + lane * CPL;
   const bool active = c0 < C;
   const bool full = VEC && wc0 + kWaveChannels <= C;  // every lane of the wave is active
-  const bool has_pool = MODE != MODE_IDX && W == 4 && a.pool.ptr != nullptr;
+  constexpr bool has_pool = POOL;  // a slot pool (width four, offsets or batch rows)
+  static_assert(!POOL || (W == 4 && MODE != MODE_IDX), "the pool form is width four with host-known sequences");
   const int64_t ta = (int64_t)rb * RT;
   const int64_t tb = ta + RT < a.rows ? ta + RT : a.rows;
 
   if (!full) {  // the last strip's partly active wave, or rows that do not allow vectors
     int64_t ta2 = ta, tb2 = tb;
-    if (has_pool) {
+    if constexpr (has_pool) {
       const int64_t de = data_end<MODE>(a.seq, a.rows);
       ta2 = owner_boundary<MODE>(a.seq, ta < de ? ta : de, de);
       tb2 = owner_boundary<MODE>(a.seq, tb < de ? tb : de, de);
@@ -377,7 +378,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
   if (ta >= te) return;
   FwdSeq cs;
   cs.sd = seq_resolve<MODE, H>(a.seq, ta, dend, te, pa);
-  if (has_pool) {
+  if constexpr (has_pool) {
     // tile boundaries on a sequence's rows 1 and 2 move to its row 3: the head tile alone owns
     // the slot.  A moved tile takes the general path.
     int64_t ta2 = ta, tb2 = tb;
@@ -409,7 +410,18 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
     unroll_steps<NT>(step);
     return;
   }
-  fwd_rolled<CPL, VEC, MODE, SILU, W>(a, cs, ta, te, dend, c0, active, wk, bias, u);
+  // ---- a tile where a sequence starts or the data ends: the rows already in registers, R at a
+  // time in a rolled loop that shifts the buffer down one chunk per step (static register indices,
+  // one copy of the sequence-start code)
+#pragma unroll 1
+  for (int64_t q0 = ta; q0 < te; q0 += R) {
+    const int n = (int)(te - q0 < R ? te - q0 : R);
+    fwd_chunk<CPL, VEC, MODE, R, SILU, true, W>(a, buf[0], n, q0, te, dend, cs, c0, active, wk, bias, u);
+#pragma unroll
+    for (int c = 0; c + 1 < NT; ++c)
+#pragma unroll
+      for (int r = 0; r < R; ++r) buf[c][r] = buf[c + 1][r];
+  }
 }
 
 // ------------------------------------------------------------------ decode / speculative update
@@ -497,26 +509,32 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_decode_kernel(const Deco
 // ------------------------------------------------------------------ launchers
 constexpr int kCpl = kChannelsPerLane;
 
-template <int MODE, bool VEC, bool SILU, int W>
+template <int MODE, bool VEC, bool SILU, int W, bool POOL>
 static hipError_t fwd_go(const FwdArgs& a, hipStream_t s) {
   const uint32_t blocks = a.n_strips * a.n_rowblocks;
   void* args[] = {const_cast<FwdArgs*>(&a)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&conv1d_fwd_kernel<kCpl, VEC, MODE, SILU, W>), dim3(blocks),
-                         dim3(kBlockThreads), args, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&conv1d_fwd_kernel<kCpl, VEC, MODE, SILU, W, POOL>),
+                         dim3(blocks), dim3(kBlockThreads), args, 0, s);
 }
 
-template <int MODE, int W>
+template <int MODE, int W, bool POOL>
 static hipError_t fwd_mode(const FwdArgs& a, bool vec, bool silu, hipStream_t s) {
-  if (vec) return silu ? fwd_go<MODE, true, true, W>(a, s) : fwd_go<MODE, true, false, W>(a, s);
-  return silu ? fwd_go<MODE, false, true, W>(a, s) : fwd_go<MODE, false, false, W>(a, s);
+  if (vec) return silu ? fwd_go<MODE, true, true, W, POOL>(a, s) : fwd_go<MODE, true, false, W, POOL>(a, s);
+  return silu ? fwd_go<MODE, false, true, W, POOL>(a, s) : fwd_go<MODE, false, false, W, POOL>(a, s);
 }
 
 template <int W>
 static hipError_t fwd_width(const FwdArgs& a, int mode, bool vec, bool silu, hipStream_t s) {
+  if constexpr (W == 4) {
+    if (a.pool.ptr) {  // the pool form: offsets or batch rows
+      if (mode == MODE_CU) return fwd_mode<MODE_CU, 4, true>(a, vec, silu, s);
+      return fwd_mode<MODE_BATCH, 4, true>(a, vec, silu, s);
+    }
+  }
   switch (mode) {
-    case MODE_CU: return fwd_mode<MODE_CU, W>(a, vec, silu, s);
-    case MODE_IDX: return fwd_mode<MODE_IDX, W>(a, vec, silu, s);
-    default: return fwd_mode<MODE_BATCH, W>(a, vec, silu, s);
+    case MODE_CU: return fwd_mode<MODE_CU, W, false>(a, vec, silu, s);
+    case MODE_IDX: return fwd_mode<MODE_IDX, W, false>(a, vec, silu, s);
+    default: return fwd_mode<MODE_BATCH, W, false>(a, vec, silu, s);
   }
 }
 

@@ -13,7 +13,7 @@ namespace cconv {
 
 // Tiling.  A block is kWavesPerBlock waves side by side in channels: lane = CPL channels, wave =
 // 64*CPL channels, block = kBlockChannels channels (a strip) of some rows.  The forward gives a
-// block one short tile of kFwdTileRows rows and launches many rounds of tiles.  The backward gives
+// block one short tile of fwd_tile_rows() rows and launches many rounds of tiles.  The backward gives
 // a block one row range streamed top to bottom, straight across sequence boundaries; the range
 // length is chosen per launch (range_rows) so that one launch is about kBwdBlocks blocks: with 256
 // CUs that is a single wave of resident blocks of equal work, and one [R + 1, C] FP32
@@ -60,13 +60,22 @@ inline int64_t range_rows_for(int64_t rows, int64_t n_strips, int64_t target_blo
   return r > kMinRangeRows ? r : kMinRangeRows;
 }
 
-// The forward's tile: kFwdTileRows rows of one strip per block, a launch of many rounds of them
+// The forward's tile: fwd_tile_rows() rows of one strip per block, a launch of many rounds of them
 // (measured on x [16384, 5632]: 16-row tiles 64.5 us, 32-row 65.4 us, 8-row 72 us, one round of
 // long ranges 72.4 us).
 #ifndef CCONV_FWD_TILE_ROWS
 #define CCONV_FWD_TILE_ROWS 16
 #endif
-constexpr int kFwdTileRows = CCONV_FWD_TILE_ROWS;
+#ifndef CCONV_FWD_TILE_ROWS_IDX
+#define CCONV_FWD_TILE_ROWS_IDX 16
+#endif
+#ifndef CCONV_FWD_TILE_ROWS_POOL
+#define CCONV_FWD_TILE_ROWS_POOL 24
+#endif
+// rows per forward tile by sequence form (MODE_CU, MODE_IDX, MODE_BATCH) and whether a pool is given
+__host__ __device__ constexpr int fwd_tile_rows(int mode, bool pool) {
+  return pool ? CCONV_FWD_TILE_ROWS_POOL : (mode == 1 ? CCONV_FWD_TILE_ROWS_IDX : CCONV_FWD_TILE_ROWS);
+}
 
 // Rows of one range's dweight/dbias partial: a tap slot per register-ring slot (4 up to filter
 // width four, 8 up to width eight; the first R - W are padding), then dbias.
@@ -138,6 +147,7 @@ struct BwdArgs {
   float* db;        // [C] or nullptr
   int64_t range_rows;  // rows per row range
   uint32_t n_strips, n_rowblocks;
+  uint32_t n_cu;       // compute units of the device (0: unknown): a block's arrival slot on its CU
 };
 
 // Channels-first [B, D, T] (T contiguous): every (b, d) row is one sequence with zero history.
@@ -180,5 +190,9 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 // on): its device address on the GPU of `stream`, looked up once per device.
 constexpr size_t kScratchBytes = CONV1D_NOALLOC_SCRATCH_BYTES;
 hipError_t bwd_scratch(hipStream_t stream, void** ptr);
+
+// Compute units of the device that runs `stream` (0 if the runtime cannot say), looked up once
+// per device.
+uint32_t device_cus(hipStream_t stream);
 
 }  // namespace cconv
