@@ -19,9 +19,10 @@ each once (activations read and written, history rows, taps, gradients); halo re
 dweight partial workspace are overhead and not counted.
 
 The same JSON line also carries every other workload (forward of the small and pool-prefill
-workloads, forward and backward of the per-token-ID training workload, a decode step), a plain
-bf16 copy as the practical bandwidth ceiling, the roofline object of the dominant call and the
-CPU oracle timed on the host as a baseline.
+workloads, forward and backward of the per-token-ID training workload, a decode step), copy
+ceilings (torch's bf16 copy; hand-written copies of the step workload's bytes, contiguous and in
+the forward's and backward's own access structure), the roofline object of the dominant call and
+the CPU oracle timed on the host as a baseline.
 """
 import argparse
 import hashlib
@@ -268,6 +269,52 @@ class Gpu:
         return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+    def ceiling_lib(self):
+        """The benchmark's copy kernels (csrc/ceiling.hip), or None when that library was not built."""
+        import ctypes
+        path = os.path.join(ROOT, "causal_depthwise_conv1d_width_amd", "libconv1d_ceiling.so")
+        if not os.path.exists(path):
+            return None
+        lib = ctypes.CDLL(path)
+        lib.ceiling_copy.restype = ctypes.c_int
+        lib.ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p]
+        st = self.stream.cuda_stream
+
+        def call(a, b, d, shape, tr):
+            rows, C = a.shape
+            rc = lib.ceiling_copy(a.data_ptr(), None if b is None else b.data_ptr(), d.data_ptr(), rows, C, shape,
+                                  tr, st)
+            if rc != 0:
+                raise RuntimeError(f"ceiling_copy returned {rc}")
+        return call
+
+    def shaped_ceilings(self, rows, C, nsets=4):
+        """Hand-written copies (libconv1d_ceiling.so) moving the bytes of one forward and one
+        backward call of a [rows, C] bf16 workload, timed like the convolution calls: a contiguous
+        sweep (read once, write once; two reads for the backward's x and dy) and copies with the
+        kernels' own access structure (the forward's short row tiles of 16 rows x 512 channels in
+        row order; the backward's one round of ~1024 long row ranges with a 3-row halo, streamed
+        in chunks of 4 rows as the kernel does, and of 8).  None when the library was not built."""
+        call = self.ceiling_lib()
+        if call is None:
+            return None
+        t = self.torch
+        sets = [tuple(t.empty((rows, C), dtype=t.bfloat16, device=self.dev).normal_() for _ in range(3))
+                for _ in range(nsets)]
+
+        nb1, nb2 = 2 * rows * C * 2, 3 * rows * C * 2
+        res = {}
+        for name, two, shape, tr in (("contiguous_1r1w", False, 0, 0), ("fwd_tiles16_1r1w", False, 1, 16),
+                                     ("contiguous_2r1w", True, 0, 0), ("bwd_ranges_chunk4_2r1w", True, 2, 4),
+                                     ("bwd_ranges_chunk8_2r1w", True, 2, 8)):
+            ms = self.ring([lambda s=s: call(s[0], s[1] if two else None, s[2], shape, tr) for s in sets], 40, 0,
+                           warm_ms=WARM_MS)
+            res[name + "_GBps"] = round(gbps(nb2 if two else nb1, ms), 1)
+        del sets
+        return res
+
+
 def gbps(nbytes, ms):
     return nbytes / (ms * 1e-3) / 1e9
 
@@ -312,7 +359,8 @@ def _cpu_model():
 def layout_counters():
     """28 back-to-back calls of each kind over 4 buffer sets, one kind after another, so that a
     counter run can compare the channel-last kernels (the context-parallel share, x [16384, 5632])
-    with the channels-first ones (x [4, 4096, 4096]) and a contiguous copy of the same size."""
+    with the channels-first ones (x [4, 4096, 4096]), the runtime's copy of the same size and
+    hand-written copies moving the channel-last calls' bytes in their access structure."""
     from causal_depthwise_conv1d_width_amd import workloads as wl
     g = Gpu()
     torch = g.torch
@@ -336,6 +384,14 @@ def layout_counters():
                                                                     workspace=d["ws"]) for d in cf],
         "copy": [lambda a=a: a[1].copy_(a[0]) for a in cp],
     }
+    call = g.ceiling_lib()
+    if call is not None:  # hand-written copies of the channel-last calls' bytes in their access structure
+        calls["forward-shaped copy (16-row tiles, 1 read)"] = [lambda d=d, a=a: call(d["x"], None, a[1], 1, 16)
+                                                              for d, a in zip(cl, cp)]
+        calls["backward-shaped copy (row ranges, 4-row chunks, 2 reads)"] = [
+            lambda d=d, a=a: call(d["x"], d["dy"], a[1], 2, 4) for d, a in zip(cl, cp)]
+        calls["contiguous copy (2 reads)"] = [lambda d=d, a=a: call(d["x"], d["dy"], a[1], 0, 0)
+                                              for d, a in zip(cl, cp)]
     for name, cs in calls.items():
         for i in range(28):
             cs[i % 4]()
@@ -418,6 +474,9 @@ def main():
 
     if not args.no_extras:
         extras = {"copy_ceiling_GBps": round(g.copy_ceiling(), 1)}
+        ceil = g.shaped_ceilings(*case["x"].shape)
+        if ceil is not None:
+            extras["copy_ceilings_" + case["name"]] = ceil
         for make in (wl.single_sequence, wl.varlen_pool, wl.prefill_pool, wl.train_seq_ids):
             c = make()
             nb = fwd_bytes(c)

@@ -23,6 +23,19 @@ def hipcc_flags():
             "-Wall", "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+CEILING_SRC = "ceiling.hip"  # copy kernels for the benchmark's bandwidth ceilings (not the ABI)
+CEILING_LIB = os.path.join(PKG, "libconv1d_ceiling.so")
+
+
+def build_ceiling(out=CEILING_LIB):
+    """The benchmark's copy kernels (csrc/ceiling.hip) as their own small library."""
+    tmp = out + ".tmp"
+    subprocess.run(["hipcc", *hipcc_flags(), "-shared", "-x", "hip", os.path.join(CSRC, CEILING_SRC), "-o", tmp],
+                   check=True, stderr=subprocess.DEVNULL)
+    os.replace(tmp, out)
+    return out
+
+
 def build(out=LIB, jobs=4, verbose=False, defines=()):
     objdir = os.path.join(PKG, "_build", os.path.basename(out))
     os.makedirs(objdir, exist_ok=True)
@@ -53,3 +66,4 @@ def build(out=LIB, jobs=4, verbose=False, defines=()):
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_ceiling())

@@ -365,7 +365,6 @@ static int bwd_common(const void* x, const void* dy, int64_t rows, int64_t C, in
   a.range_rows = rr;
   a.n_strips = ceil_div(C, kBlockChannels);
   a.n_rowblocks = ceil_div(rows, rr);
-  a.n_cu = rows > 0 ? device_cus(stream) : 0;
   return launch_bwd(a, mode, vec, act == CONV1D_ACT_SILU, stream) == hipSuccess ? CONV1D_OK : CONV1D_EHIP;
 }
 

@@ -58,9 +58,7 @@ __device__ __forceinline__ void load_hist_rows(const HistArgs& hist, int64_t idx
 #ifndef CCONV_BWD_DEPTH
 #define CCONV_BWD_DEPTH 2
 #endif
-#ifndef CCONV_BWD_PRIO
-#define CCONV_BWD_PRIO 1
-#endif
+
 
 // Per-lane state of the backward stream (CPL channels) with a ring of R slots.
 template <int CPL, int R>
@@ -305,17 +303,6 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
   const bool active = c0 < C;
   const bool full = VEC && wc0 + kWaveChannels <= C;  // every lane of the wave is active
   const int64_t dend = data_end<MODE>(a.seq, a.rows);
-#if CCONV_BWD_PRIO
-  // A one-round launch deals blocks b, b + n_cu, b + 2 n_cu, ... to one CU, and a CU issues for
-  // its oldest waves first, so later arrivals stream slower and finish last.  Raising the wave
-  // priority with the arrival slot evens out the blocks of a CU.
-  if (a.n_cu) {
-    const uint32_t slot = blockIdx.x / a.n_cu;
-    if (slot == 1) __builtin_amdgcn_s_setprio(1);
-    else if (slot == 2) __builtin_amdgcn_s_setprio(2);
-    else if (slot >= 3) __builtin_amdgcn_s_setprio(3);
-  }
-#endif
 
   int64_t ta = (int64_t)rb * a.range_rows;
   int64_t tb = ta + a.range_rows;
@@ -557,26 +544,6 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (nullptr: not looked up)
 }  // namespace
-
-uint32_t device_cus(hipStream_t stream) {
-  static std::mutex mu;
-  static uint32_t cus[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (stream) {
-    hipDevice_t d = 0;
-    if (hipStreamGetDevice(stream, &d) != hipSuccess) return 0;
-    dev = (int)d;
-  }
-  if (dev < 0 || dev >= kMaxDevices) return 0;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!cus[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
-    cus[dev] = (uint32_t)n;
-  }
-  return cus[dev];
-}
 
 hipError_t bwd_scratch(hipStream_t stream, void** ptr) {
   int cur = 0;

@@ -147,7 +147,6 @@ struct BwdArgs {
   float* db;        // [C] or nullptr
   int64_t range_rows;  // rows per row range
   uint32_t n_strips, n_rowblocks;
-  uint32_t n_cu;       // compute units of the device (0: unknown): a block's arrival slot on its CU
 };
 
 // Channels-first [B, D, T] (T contiguous): every (b, d) row is one sequence with zero history.
@@ -190,9 +189,5 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 // on): its device address on the GPU of `stream`, looked up once per device.
 constexpr size_t kScratchBytes = CONV1D_NOALLOC_SCRATCH_BYTES;
 hipError_t bwd_scratch(hipStream_t stream, void** ptr);
-
-// Compute units of the device that runs `stream` (0 if the runtime cannot say), looked up once
-// per device.
-uint32_t device_cus(hipStream_t stream);
 
 }  // namespace cconv

@@ -12,5 +12,4 @@ hipError_t launch_fwd_cf(const CfArgs&, bool, bool, hipStream_t) { return fail()
 hipError_t launch_bwd_cf(const CfArgs&, bool, bool, hipStream_t) { return fail(); }
 hipError_t launch_combine(const CombineArgs&, hipStream_t) { return fail(); }
 hipError_t bwd_scratch(hipStream_t, void**) { return fail(); }
-uint32_t device_cus(hipStream_t) { return fail(), 0u; }
 }

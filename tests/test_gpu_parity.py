@@ -141,6 +141,43 @@ def test_tile_boundary_sequences_backward(oracle):
         gh.check_bwd(oracle, case)
 
 
+def _tile_edge_lengths(period, n_periods=6, seed=0):
+    """Sequence lengths whose starts land on every offset from -3 to +4 around multiples of `period`
+    (the forward's tile heights: 16 rows, 24 with a slot pool), with sequences of 1..4 rows, so
+    tiles start on a sequence's rows 0..3 and hold one or several sequence starts."""
+    rng = np.random.default_rng(seed)
+    lengths, pos = [], 0
+    for k in range(1, n_periods + 1):
+        target = k * period + int(rng.integers(-3, 5))
+        if target > pos:
+            lengths.append(target - pos)
+            pos = target
+        for n in rng.permutation([1, 2, 3, 4])[: int(rng.integers(1, 4))]:
+            lengths.append(int(n))
+            pos += int(n)
+    lengths.append(0)
+    lengths.append(5)
+    return lengths
+
+
+@pytest.mark.parametrize("period", [16, 24])
+@pytest.mark.parametrize("layout", ["hist", "chan", None])
+def test_sequence_starts_around_tile_edges(oracle, period, layout):
+    """Sequence starts on each row around the tile edges of the forward, with a pool (its tile
+    boundaries move off a sequence's rows 1 and 2) or with history rows; forward and, without a
+    pool, backward against the oracle."""
+    rng = np.random.default_rng(40 + period)
+    for seed in range(4):
+        for C in (512, 1040):
+            case = _boundary_case(rng, C, _tile_edge_lengths(period, seed=seed), layout=layout,
+                                  hist=(layout is None), pad=3)
+            case["name"] = f"tile-edges-p{period}-{layout}-s{seed}-C{C}"
+            _print_case(case["name"], rows=case["x"].shape[0])
+            gh.check_fwd(oracle, case)
+            if layout is None:
+                gh.check_bwd(oracle, case)
+
+
 def test_degenerate_inputs(oracle):
     rng = np.random.default_rng(9)
     C = 16
