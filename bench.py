@@ -295,7 +295,9 @@ class Gpu:
         sweep (read once, write once; two reads for the backward's x and dy) and copies with the
         kernels' own access structure (the forward's short row tiles of 16 rows x 512 channels in
         row order; the backward's one round of ~1024 long row ranges with a 3-row halo, streamed
-        in chunks of 4 rows as the kernel does, and of 8).  None when the library was not built."""
+        in chunks of 4 rows as the kernel does, and of 8, and with its two reads fetched by
+        direct-to-LDS 16-byte loads, a quarter of the load instructions).  None when the library
+        was not built."""
         call = self.ceiling_lib()
         if call is None:
             return None
@@ -307,7 +309,7 @@ class Gpu:
         res = {}
         for name, two, shape, tr in (("contiguous_1r1w", False, 0, 0), ("fwd_tiles16_1r1w", False, 1, 16),
                                      ("contiguous_2r1w", True, 0, 0), ("bwd_ranges_chunk4_2r1w", True, 2, 4),
-                                     ("bwd_ranges_chunk8_2r1w", True, 2, 8)):
+                                     ("bwd_ranges_chunk8_2r1w", True, 2, 8), ("bwd_ranges_lds16B_2r1w", True, 3, 0)):
             ms = self.ring([lambda s=s: call(s[0], s[1] if two else None, s[2], shape, tr) for s in sets], 40, 0,
                            warm_ms=WARM_MS)
             res[name + "_GBps"] = round(gbps(nb2 if two else nb1, ms), 1)
@@ -390,6 +392,8 @@ def layout_counters():
                                                               for d, a in zip(cl, cp)]
         calls["backward-shaped copy (row ranges, 4-row chunks, 2 reads)"] = [
             lambda d=d, a=a: call(d["x"], d["dy"], a[1], 2, 4) for d, a in zip(cl, cp)]
+        calls["backward-shaped copy through direct-to-LDS 16-byte loads (2 reads)"] = [
+            lambda d=d, a=a: call(d["x"], d["dy"], a[1], 3, 0) for d, a in zip(cl, cp)]
         calls["contiguous copy (2 reads)"] = [lambda d=d, a=a: call(d["x"], d["dy"], a[1], 0, 0)
                                               for d, a in zip(cl, cp)]
     for name, cs in calls.items():
@@ -477,6 +481,7 @@ def main():
         ceil = g.shaped_ceilings(*case["x"].shape)
         if ceil is not None:
             extras["copy_ceilings_" + case["name"]] = ceil
+            extras["copy_ceilings_rows16384_C4096"] = g.shaped_ceilings(16384, 4096)  # per-token-ID shape
         for make in (wl.single_sequence, wl.varlen_pool, wl.prefill_pool, wl.train_seq_ids):
             c = make()
             nb = fwd_bytes(c)

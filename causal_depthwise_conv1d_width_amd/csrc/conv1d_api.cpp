@@ -219,6 +219,7 @@ int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void*
   a.range_rows = rr;
   a.n_strips = ceil_div(C, kBlockChannels);
   a.n_rowblocks = ceil_div(rows, rr);
+  a.tile_order = fwd_tile_order(a.n_strips);
   return launch_fwd(a, mode, vec, act == CONV1D_ACT_SILU, stream) == hipSuccess ? CONV1D_OK : CONV1D_EHIP;
 }
 
@@ -365,6 +366,7 @@ static int bwd_common(const void* x, const void* dy, int64_t rows, int64_t C, in
   a.range_rows = rr;
   a.n_strips = ceil_div(C, kBlockChannels);
   a.n_rowblocks = ceil_div(rows, rr);
+  a.tile_order = bwd_tile_order(a.n_strips);
   return launch_bwd(a, mode, vec, act == CONV1D_ACT_SILU, stream) == hipSuccess ? CONV1D_OK : CONV1D_EHIP;
 }
 

@@ -237,6 +237,22 @@ __device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t nb) {
   return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
+// This block's (strip, row block) in a launch of n_strips x n_rowblocks blocks, by tile order.
+__device__ __forceinline__ void block_tile(uint32_t order, uint32_t n_strips, uint32_t n_rowblocks, uint32_t& strip,
+                                           uint32_t& rb) {
+  if (order == kOrderPlain) {
+    tile_coords(blockIdx.x, n_strips, strip, rb);
+    return;
+  }
+  const uint32_t t = xcd_tile(blockIdx.x, gridDim.x);
+  if (order == kOrderXcdStrips) {
+    strip = t / n_rowblocks;
+    rb = t % n_rowblocks;
+  } else {
+    tile_coords(t, n_strips, strip, rb);
+  }
+}
+
 // ------------------------------------------------------------------ integer helpers
 // x / L and x mod L for x >= 0, L >= 1 (wave-uniform values): one 32-bit division when both fit
 // (every row count here in practice), the 64-bit sequence otherwise.

@@ -321,7 +321,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint32_t strip, rb;
-  tile_coords(xcd_tile(blockIdx.x, gridDim.x), a.n_strips, strip, rb);
+  block_tile(a.tile_order, a.n_strips, a.n_rowblocks, strip, rb);
   const int64_t C = a.C;
   const int64_t wc0 = (int64_t)strip * kBlockChannels + (int64_t)wave * kWaveChannels;
   if (wc0 >= C) return;  // the whole wave is past the last channel

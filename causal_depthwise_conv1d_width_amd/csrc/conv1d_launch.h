@@ -77,6 +77,48 @@ __host__ __device__ constexpr int fwd_tile_rows(int mode, bool pool) {
   return pool ? CCONV_FWD_TILE_ROWS_POOL : (mode == 1 ? CCONV_FWD_TILE_ROWS_IDX : CCONV_FWD_TILE_ROWS);
 }
 
+// Block -> tile order of a launch.  The dispatcher deals blocks to the 8 XCDs in turn (block b to
+// XCD b mod 8), and each XCD has its own L2.
+//   kOrderXcdRows:   each XCD takes one contiguous slice of the row-major tile space, a band of
+//                    rows over every strip, so a tile and the one above it share an L2; the 8 XCDs
+//                    stream 8 bands at once;
+//   kOrderPlain:     tile = block in row-major order: the whole GPU streams one band of rows, and
+//                    with a multiple of 8 strips every strip stays on one XCD;
+//   kOrderXcdStrips: each XCD takes one contiguous slice of the strip-major tile space (a part of
+//                    one strip, top to bottom): for 1, 2 or 4 strips.
+// Copies of the forward's tile shape (16 rows, 1 read 1 write, TB/s) by strip count:
+//   strips  rows-order  plain  strips-order
+//      4       5.02     5.31      5.54
+//      8       5.63     6.18      6.22
+//     11       6.00     5.95      5.44
+//     12       6.09     5.99      5.92
+//     16       6.33     6.58      6.65
+// With 8 bands of rows at a power-of-two row pitch, the bands sit a power of two apart and the XCDs
+// meet in the same memory channels.
+enum : uint32_t { kOrderXcdRows = 0, kOrderPlain = 1, kOrderXcdStrips = 2 };
+#ifndef CCONV_FWD_ORDER
+#define CCONV_FWD_ORDER -1
+#endif
+#ifndef CCONV_BWD_ORDER
+#define CCONV_BWD_ORDER -1
+#endif
+inline uint32_t fwd_tile_order(int64_t n_strips) {
+  if (CCONV_FWD_ORDER >= 0) return (uint32_t)CCONV_FWD_ORDER;
+  if (n_strips % 8 == 0) return kOrderPlain;
+  if (8 % n_strips == 0) return kOrderXcdStrips;
+  return kOrderXcdRows;
+}
+// The backward's one round of long row ranges has every range in flight at once, so the order only
+// decides which L2 a range and its neighbours share.  Copies of that shape (2 reads, 1 write, TB/s,
+// rows order / plain) by strip count: 4: 5.28 / 4.82, 6: 5.13 / 5.09, 7: 5.17 / 5.03,
+// 8: 5.77 / 5.39, 9: 5.15 / 5.35, 10: 5.29 / 5.26, 11: 5.32 / 5.50, 12: 5.11 / 4.87,
+// 13: 5.29 / 5.17, 15: 5.12 / 5.06, 16: 5.54 / 4.82.  No rule beats rows order across them.
+inline uint32_t bwd_tile_order(int64_t n_strips) {
+  if (CCONV_BWD_ORDER >= 0) return (uint32_t)CCONV_BWD_ORDER;
+  (void)n_strips;
+  return kOrderXcdRows;
+}
+
 // Rows of one range's dweight/dbias partial: a tap slot per register-ring slot (4 up to filter
 // width four, 8 up to width eight; the first R - W are padding), then dbias.
 constexpr int kMaxWidth = 8;
@@ -116,6 +158,7 @@ struct FwdArgs {
   HistArgs hist;
   int64_t range_rows;  // rows per row range
   uint32_t n_strips, n_rowblocks;
+  uint32_t tile_order;  // kOrder*
 };
 
 struct DecodeArgs {
@@ -147,6 +190,7 @@ struct BwdArgs {
   float* db;        // [C] or nullptr
   int64_t range_rows;  // rows per row range
   uint32_t n_strips, n_rowblocks;
+  uint32_t tile_order;  // kOrder*
 };
 
 // Channels-first [B, D, T] (T contiguous): every (b, d) row is one sequence with zero history.
