@@ -173,7 +173,7 @@ int conv1d_state_update_spec(const void* x, int64_t nseq, int64_t K, int64_t C, 
    row, or to the sequence's d(history) row when the sequence is shorter than W - 1 rows (an
    empty last sequence passes dtail to its d(history) whole).  The last sequence is sequence
    nseq - 1 (cu_seqlens and batch-row forms) or the one holding row rows - 1 (per-token IDs).
-   dw and db are sums of per-tile FP32 partials combined in a fixed order by a second kernel
+   dw and db are sums of per-range FP32 partials combined in a fixed order by a second kernel
    (no atomics), so they are bitwise identical from run to run and independent of the
    workspace address.  ws: device scratch of at least conv1d_bwd_workspace_bytes(rows, C)
    bytes, 16-byte aligned, not overlapping any operand.  The query does not take the filter
