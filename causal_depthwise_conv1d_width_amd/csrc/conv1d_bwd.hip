@@ -60,10 +60,12 @@ __device__ __forceinline__ void load_hist_rows(const HistArgs& hist, int64_t idx
 #endif
 
 
+constexpr float kNegLog2e = -1.44269504088896341f;  // -1 / ln(2)
+
 // Per-lane state of the backward stream (CPL channels) with a ring of R slots.
 template <int CPL, int R>
 struct BwdState {
-  float wk[R][CPL], bias[CPL];
+  float wk[R][CPL], bias[CPL];  // with SiLU: taps and bias times -log2(e) (see bwd_row)
   float u[R][CPL];        // extended-sequence ring, slot = (row - run start) mod R
   float g[R][CPL];        // dz ring, same slots
   float acc[R + 1][CPL];  // dw per tap slot, then db: partial sums over the wave's rows
@@ -71,8 +73,16 @@ struct BwdState {
 
 // One real row q (ring slot r): recompute z, dz = dy * act'(z); dweight/dbias sums when `own`.
 // Tap slot k (k = R-W .. R-1) reads ring slot (r+1+k) % R: rows q-(R-1) .. q.
+// With SiLU the whole stream runs scaled, to save the multiply in front of the exp2: taps and
+// bias hold -log2(e) times their values, so the recompute yields zs = -log2(e) z, the exponent
+// of sigma(z) = 1 / (1 + 2^zs); and the dz ring holds dzs = -ln(2) dz, so a tap times a dz ring
+// value is w dz again (dx, d(history)), while the dweight/dbias sums come out as -ln(2) times
+// theirs and are scaled back once, when the partial is written.
+//   -ln2 (1 + z (1 - sigma)) = zs * ln2^2 (1 - sigma) - ln2,  since z = -ln2 zs.
 template <int CPL, bool SILU, int W, int R = Win<W>::R>
 __device__ __forceinline__ void bwd_row(BwdState<CPL, R>& st, const Pk<CPL>& xr, const Pk<CPL>& gr, int r, bool own) {
+  constexpr float kLn2 = 0.693147180559945309f;
+  constexpr float kLn2Sq = 0.480453013918201424f;
   unpack(xr, st.u[r % R]);
   float dyv[CPL];
   unpack(gr, dyv);
@@ -82,9 +92,10 @@ __device__ __forceinline__ void bwd_row(BwdState<CPL, R>& st, const Pk<CPL>& xr,
 #pragma unroll
     for (int k = R - W; k < R; ++k) z = __builtin_fmaf(st.wk[k][ch], st.u[(r + 1 + k) % R][ch], z);
     float dz = dyv[ch];
-    if (SILU) {
-      const float sg = sigmoid_f32(z);
-      dz = dz * (sg * __builtin_fmaf(z, 1.0f - sg, 1.0f));
+    if constexpr (SILU) {
+      const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z));  // z is zs here
+      const float t = __builtin_fmaf(sg, -kLn2Sq, kLn2Sq);                         // ln2^2 (1 - sigma)
+      dz = dz * (sg * __builtin_fmaf(z, t, -kLn2));                                // dzs
     }
     st.g[r % R][ch] = dz;
   }
@@ -278,10 +289,15 @@ __device__ __forceinline__ void bwd_load(Pk<CPL> (&X)[CH], Pk<CPL> (&G)[CH], con
 #ifndef CCONV_BWD_WAVES_PER_EU
 #define CCONV_BWD_WAVES_PER_EU 4
 #endif
-// The floor holds for widths up to four; the eight-slot ring of wider filters needs more than
-// 128 VGPRs and would spill under it, so those run at the occupancy their registers allow.
+// The floor holds for widths up to four.  The eight-slot ring of wider filters needs more than
+// 128 VGPRs: width five fits 168 (3 waves per SIMD) without spilling except in the per-token-ID
+// form; widths six to eight spill under that floor (and ran 9-20% slower), so the rest run at
+// the occupancy their registers allow.
 #if CCONV_BWD_WAVES_PER_EU > 0
-#define CCONV_BWD_OCCUPANCY __attribute__((amdgpu_waves_per_eu(W <= 4 ? CCONV_BWD_WAVES_PER_EU : 1)))
+#define CCONV_BWD_OCCUPANCY                                                                 \
+  __attribute__((amdgpu_waves_per_eu(W <= 4                           ? CCONV_BWD_WAVES_PER_EU \
+                                     : (W == 5 && MODE != MODE_IDX) ? 3                        \
+                                                                    : 1)))
 #else
 #define CCONV_BWD_OCCUPANCY
 #endif
@@ -317,6 +333,14 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
 
   if (ta < tb) {
     load_taps<CPL, W>(a.w, a.w_f32, a.b, a.b_f32, c0, C, st.wk, st.bias);
+    if constexpr (SILU) {  // the scaled stream of bwd_row
+#pragma unroll
+      for (int ch = 0; ch < CPL; ++ch) {
+#pragma unroll
+        for (int k = R - W; k < R; ++k) st.wk[k][ch] *= kNegLog2e;
+        st.bias[ch] *= kNegLog2e;
+      }
+    }
     const int64_t lim = (tb + H < dend) ? tb + H : dend;  // sequence ends matter up to tb + H
 
     // full chunks of own rows, software-pipelined with NB register buffers (see the forward)
@@ -428,6 +452,12 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
   // ---- this lane's partial sums for its channels over this row range (every range writes one,
   // empty ranges write zeros, so the reduce can read all of them)
   if (active) {
+    if constexpr (SILU) {  // the sums ran on dzs = -ln(2) dz (bwd_row)
+#pragma unroll
+      for (int k = 0; k < R + 1; ++k)
+#pragma unroll
+        for (int ch = 0; ch < CPL; ++ch) st.acc[k][ch] *= kNegLog2e;
+    }
 #pragma unroll
     for (int k = 0; k < R + 1; ++k) {
       float* dst = a.part + ((int64_t)rb * (R + 1) + k) * C + c0;

@@ -280,9 +280,9 @@ def test_batch_rows_with_history(oracle):
 
 @pytest.mark.parametrize("form", ["idx", "batch", "cu"])
 def test_forward_short_ranges_at_large_row_counts(oracle, form):
-    """Past 256 rows per one-round range the forward switches to 40-row ranges (several rounds of
-    blocks): 24584 x 5632 crosses that point.  Sequences of every length, including 1..3 rows,
-    straddle the 40-row range boundaries."""
+    """24584 x 5632 in all three sequence forms: many rounds of 16-row tiles, batch rows of 6146
+    rows (not a multiple of 16), and sequences of every length, including 1..3 rows, straddling the
+    tile boundaries."""
     rng = np.random.default_rng(31)
     C, B = 5632, 4
     rows = B * 6146  # batch rows of 6146 rows: not a multiple of 40
@@ -301,5 +301,32 @@ def test_forward_short_ranges_at_large_row_counts(oracle, form):
         case["seq_idx"] = np.repeat(np.arange(len(lengths)), lengths).astype(np.int32)
     else:
         case["seqlen"] = rows // B
+    _print_case(case["name"], rows=rows, C=C, seqs=len(lengths))
+    gh.check_fwd(oracle, case)
+
+
+@pytest.mark.parametrize("C", [2048, 3600, 4096, 8192])
+@pytest.mark.parametrize("form", ["cu", "idx"])
+def test_forward_block_orders(oracle, C, form):
+    """The forward's block-to-tile order depends on the number of 512-channel strips: slices of the
+    strip-major order per XCD for 4 strips (C = 2048), plain row-major order for 8 and 16 strips
+    (C = 3600 with a partial last strip, 4096, 8192).  Sequences of 1..300 rows over ~1500 rows,
+    history rows in the offsets form, checked against the oracle."""
+    rng = np.random.default_rng(41 + C)
+    lengths, total = [], 0
+    while total < 1500:
+        n = int(rng.choice([1, 2, 3, 5, 17, 40, 300]))
+        lengths.append(n)
+        total += n
+    rows = total
+    case = dict(name=f"block-order-{form}-C{C}", x=wl.normal_bf16(rng, (rows, C)), w=wl.uniform_f32(rng, (C, 4)),
+                b=(rng.standard_normal(C) * 0.1).astype(np.float32), act="silu")
+    if form == "cu":
+        case["cu_seqlens"] = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        case["hist"] = wl.normal_bf16(rng, (len(lengths), 3, C))
+        case["has_history"] = (rng.random(len(lengths)) < 0.6).astype(np.uint8)
+    else:
+        case["seqlen"] = rows
+        case["seq_idx"] = np.repeat(np.arange(len(lengths)), lengths).astype(np.int32)
     _print_case(case["name"], rows=rows, C=C, seqs=len(lengths))
     gh.check_fwd(oracle, case)
