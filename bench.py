@@ -343,8 +343,8 @@ def cpu_baseline(case, max_seconds=30.0):
     nbytes = fwd_bytes(case) + bwd_bytes(case)
     return {"value": round(nbytes / sec / 1e9, 3), "unit": "GB/s", "cores": o.threads(), "kind": "oracle",
             "sample": f"the full step workload (fwd + bwd over x [16384, 5632]), median of {len(times)} timed passes "
-                      f"after one warm pass; {sec:.3f} s per pass",
-            "cpu_model": _cpu_model()}
+                      f"after one warm pass; {sec:.3f} s per pass, min {min(times):.3f} s",
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
 def _cpu_model():

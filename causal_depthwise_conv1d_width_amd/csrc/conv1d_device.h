@@ -221,11 +221,12 @@ __device__ __forceinline__ float sigmoid_f32(float z) {
 }
 
 // ------------------------------------------------------------------ XCD-aware block order
-// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).  Give every XCD one
-// contiguous range of logical tiles, so neighbouring row tiles of a channel strip (which share
-// halo rows) run on the same XCD at about the same time.
-// Logical tiles are ordered row-range major (tile = row_range * n_strips + strip), so the
-// channel strips of the same rows, which share DRAM pages, run side by side.
+// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).  Logical tiles are
+// ordered row-range major (tile = row_range * n_strips + strip), so the channel strips of the
+// same rows, which share DRAM pages, run side by side.  xcd_tile gives every XCD one contiguous
+// range of logical tiles, so neighbouring row tiles of a strip (which share halo rows) run on the
+// same XCD at about the same time; block_tile picks between that and the other orders of a
+// launch (kOrder* in conv1d_launch.h).
 __device__ __forceinline__ void tile_coords(uint32_t tile, uint32_t n_strips, uint32_t& strip, uint32_t& rb) {
   strip = tile % n_strips;
   rb = tile / n_strips;
