@@ -195,7 +195,7 @@ int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void*
   if (rows == 0) return CONV1D_OK;
 
   const bool vec = vec_rows(C, x_ld, x) && vec_rows(C, y_ld, y) && (!use_hist || vec_rows(C, C, hist->ptr));
-  const int64_t rr = fwd_tile_rows(mode, use_pool);
+  const int64_t rr = fwd_tile_rows(mode, use_pool, width);
   const uint64_t nblk = (uint64_t)ceil_div(C, kBlockChannels) * ceil_div(rows, rr);
   if (nblk > 0x7fffffffull) return CONV1D_EINVAL;
 

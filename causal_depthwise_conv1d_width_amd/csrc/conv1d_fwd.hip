@@ -314,7 +314,7 @@ __device__ __forceinline__ void fwd_general(const FwdArgs& a, int64_t ta, int64_
 template <int CPL, bool VEC, int MODE, bool SILU, int W, bool POOL>
 __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs a) {
   constexpr int R = Win<W>::R, H = Win<W>::H;  // ring slots, history values
-  constexpr int RT = fwd_tile_rows(MODE, POOL); // rows per tile
+  constexpr int RT = fwd_tile_rows(MODE, POOL, W);  // rows per tile
   static_assert(RT % R == 0 && RT % 4 == 0, "tiles hold whole ring periods");
   constexpr int NT = RT / R;                    // register chunks of a tile
 

@@ -62,7 +62,9 @@ inline int64_t range_rows_for(int64_t rows, int64_t n_strips, int64_t target_blo
 
 // The forward's tile: fwd_tile_rows() rows of one strip per block, a launch of many rounds of them
 // (measured on x [16384, 5632]: 16-row tiles 64.5 us, 32-row 65.4 us, 8-row 72 us, one round of
-// long ranges 72.4 us).
+// long ranges 72.4 us).  A pool's tiles carry the slot lookup and state write-back: 24 rows
+// (prefill 136 us against 148 us for 16).  Wider filters read W-1 rows above every tile: 24 rows
+// (width 5 / 8: 65.3 / 67.4 us against 67.5 / 72.0 us for 16, the same as 32).
 #ifndef CCONV_FWD_TILE_ROWS
 #define CCONV_FWD_TILE_ROWS 16
 #endif
@@ -72,9 +74,14 @@ inline int64_t range_rows_for(int64_t rows, int64_t n_strips, int64_t target_blo
 #ifndef CCONV_FWD_TILE_ROWS_POOL
 #define CCONV_FWD_TILE_ROWS_POOL 24
 #endif
-// rows per forward tile by sequence form (MODE_CU, MODE_IDX, MODE_BATCH) and whether a pool is given
-__host__ __device__ constexpr int fwd_tile_rows(int mode, bool pool) {
-  return pool ? CCONV_FWD_TILE_ROWS_POOL : (mode == 1 ? CCONV_FWD_TILE_ROWS_IDX : CCONV_FWD_TILE_ROWS);
+#ifndef CCONV_FWD_TILE_ROWS_WIDE
+#define CCONV_FWD_TILE_ROWS_WIDE 24
+#endif
+// rows per forward tile by sequence form (MODE_CU, MODE_IDX, MODE_BATCH), whether a pool is
+// given, and the filter width
+__host__ __device__ constexpr int fwd_tile_rows(int mode, bool pool, int width) {
+  return pool ? CCONV_FWD_TILE_ROWS_POOL
+              : (width > 4 ? CCONV_FWD_TILE_ROWS_WIDE : (mode == 1 ? CCONV_FWD_TILE_ROWS_IDX : CCONV_FWD_TILE_ROWS));
 }
 
 // Block -> tile order of a launch.  The dispatcher deals blocks to the 8 XCDs in turn (block b to
