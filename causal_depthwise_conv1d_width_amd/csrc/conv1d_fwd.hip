@@ -95,7 +95,7 @@ __device__ __forceinline__ void pool_writeback(const FwdArgs& a, int32_t slot, c
         base[(c0 + ch) * a.pool.s_chan + j * a.pool.s_pos] = (uint16_t)(__float_as_uint(v[j][ch]) >> 16);
 }
 
-// With a pool: move a row-range boundary r off the first three rows of its sequence.
+// With a pool: move a tile boundary r off the first three rows of its sequence.
 template <int MODE>
 __device__ __forceinline__ int64_t owner_boundary(const SeqArgs& q, int64_t r, int64_t dend) {
   if constexpr (MODE == MODE_IDX) {
@@ -165,8 +165,8 @@ __device__ __forceinline__ void fwd_enter(const FwdArgs& a, FwdSeq& cs, int64_t 
   }
 }
 
-// n (<= CH) rows starting at q0 from a loaded buffer.  Ring slot of row q is (q - range start)
-// mod 4 = r mod 4, as q0 - range start is a multiple of CH.  A chunk inside one sequence is a
+// n (<= CH) rows starting at q0 from a loaded buffer.  Ring slot of row q is (q - tile start)
+// mod R = r mod R, as q0 - tile start is a multiple of CH.  A chunk inside one sequence is a
 // straight stencil; a chunk where sequences start re-seeds the three window slots from the new
 // sequence's history right before its first row.
 template <int CPL, bool VEC, int MODE, int CH, bool SILU, bool FULL, int W, int R = Win<W>::R>
@@ -211,7 +211,7 @@ __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)
   }
 }
 
-// The window of the row before a tile or range that starts at row ta of sequence cs (ring slots
+// The window of the row before a tile that starts at row ta of sequence cs (ring slots
 // 1..H get rows ta-H .. ta-1): the sequence's history, then the last `dist` input rows of the
 // sequence (wrow holds rows ta-H .. ta-1, loaded before the lookup).  At the sequence's first row
 // this enters the sequence (history, pool write-back); elsewhere only its -1 status matters, and
