@@ -452,6 +452,7 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
   // ---- this lane's partial sums for its channels over this row range (every range writes one,
   // empty ranges write zeros, so the reduce can read all of them)
   if (active) {
+    const int rows_out = a.db ? R + 1 : R;  // the dbias row only when it is wanted
     if constexpr (SILU) {  // the sums ran on dzs = -ln(2) dz (bwd_row)
 #pragma unroll
       for (int k = 0; k < R + 1; ++k)
@@ -460,6 +461,7 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
     }
 #pragma unroll
     for (int k = 0; k < R + 1; ++k) {
+      if (k >= rows_out) break;
       float* dst = a.part + ((int64_t)rb * (R + 1) + k) * C + c0;
       if constexpr (VEC && CPL >= 4) {
 #pragma unroll
@@ -492,11 +494,11 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_bwd_reduce_kernel(const 
   const int64_t gwave = ((int64_t)blockIdx.x * kBlockThreads + threadIdx.x) / kWave;
   const int64_t C = a.C;
   const int R = partial_rows(a.width) - 1;
-  const int64_t nout = (R + 1) * C;
+  const int64_t nout = (R + 1) * C;  // the partial's stride; its dbias row is read only when wanted
   if (gwave < n_red_waves) {
     const int64_t o = gwave * 16 + (lane & 15);
     const int sub = lane >> 4;
-    const bool ok = o < nout;
+    const bool ok = o < (a.db ? nout : R * C);
     const int64_t n = a.n_rowblocks;
     float s = 0.f;
     if (ok) {
@@ -607,6 +609,13 @@ hipError_t bwd_scratch(hipStream_t stream, void** ptr) {
 // ------------------------------------------------------------------ launchers
 constexpr int kCpl = kChannelsPerLane;
 
+// Waves of the ordered reduce: 16 outputs each over the partial rows it reads (the dbias row only
+// when dbias is wanted).
+static int64_t reduce_waves(const BwdArgs& a) {
+  const int64_t rows = partial_rows(a.width) - (a.db ? 0 : 1);
+  return (rows * a.C + 15) / 16;
+}
+
 template <int MODE, bool VEC, bool SILU, int W>
 static hipError_t bwd_go(const BwdArgs& a, hipStream_t s) {
   const uint32_t blocks = a.n_strips * a.n_rowblocks;
@@ -618,7 +627,7 @@ static hipError_t bwd_go(const BwdArgs& a, hipStream_t s) {
   }
   // empty fragments that read history rows still get a (zero) d(history)
   const int64_t nz = (a.dhist && MODE == MODE_CU) ? a.seq.nseq : 0;
-  int64_t n_red_waves = (partial_rows(a.width) * a.C + 15) / 16;
+  int64_t n_red_waves = reduce_waves(a);
   const int64_t threads = n_red_waves * kWave + nz * a.C;
   const uint32_t rblocks = (uint32_t)((threads + kBlockThreads - 1) / kBlockThreads);
   int64_t nz_arg = nz;
@@ -643,7 +652,7 @@ static hipError_t bwd_width(const BwdArgs& a, int mode, bool vec, bool silu, hip
 }
 
 hipError_t launch_reduce(const BwdArgs& a, hipStream_t s) {
-  int64_t n_red_waves = (partial_rows(a.width) * a.C + 15) / 16;
+  int64_t n_red_waves = reduce_waves(a);
   const int64_t threads = n_red_waves * kWave;
   const uint32_t rblocks = (uint32_t)((threads + kBlockThreads - 1) / kBlockThreads);
   int64_t nz_arg = 0;
