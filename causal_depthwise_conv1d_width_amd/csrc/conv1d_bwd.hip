@@ -461,7 +461,8 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
     }
 #pragma unroll
     for (int k = 0; k < R + 1; ++k) {
-      if (k >= rows_out) break;
+      if (k == R && rows_out == R) continue;  // (a compile-time k: a runtime loop bound here moved
+                                              // the sums to scratch at the eight-slot widths)
       float* dst = a.part + ((int64_t)rb * (R + 1) + k) * C + c0;
       if constexpr (VEC && CPL >= 4) {
 #pragma unroll
