@@ -322,19 +322,43 @@ __device__ __forceinline__ int64_t idx_next_start(const SeqArgs& q, int64_t t, i
 // first loads before its row loads and use them after: seq_probe issues them (the first level of
 // the offset search, or the IDs around row t), seq_resolve finishes the lookup with their values.
 // `limit` bounds the IDX-mode forward scan.  seq_of_row does both at once.
+// Up to kDualSeqs sequences the offset search is a single level of two offsets per lane.
+constexpr int64_t kDualSeqs = 2 * kWave - 2;
+
 struct SeqProbe {
-  int32_t v, w;  // CU: raw offset of the first search level; IDX: IDs of rows r and r - 1
+  int32_t v, w;    // CU: raw offsets 2l and 2l+1 (up to kDualSeqs sequences), else the first
+                   // search level's offset; IDX: IDs of rows r and r - 1
+  int32_t s0, s1;  // with a slot array: the slots of sequences 2l and 2l+1 (CU form, up to
+                   // kDualSeqs sequences), or of row t's batch row on every lane (BATCH form)
 };
 
+// `slots` (the pool's cache_indices, or nullptr): fetch the slot with the lookup, so that a tile
+// knows its sequence's slot after one memory round trip (probe_slot).
 template <int MODE, int HB = 3>
-__device__ __forceinline__ SeqProbe seq_probe(const SeqArgs& q, int64_t t, int64_t limit) {
-  SeqProbe p{0, 0};
+__device__ __forceinline__ SeqProbe seq_probe(const SeqArgs& q, int64_t t, int64_t limit,
+                                              const int32_t* slots = nullptr) {
+  SeqProbe p{0, 0, -1, -1};
   const int lane = threadIdx.x & (kWave - 1);
   if constexpr (MODE == MODE_CU) {
     const int64_t n = q.nseq;
-    const int64_t stride = n < kWave ? 1 : (n + kWave - 2) / (kWave - 1);
-    const int64_t off = (int64_t)lane * stride;
-    if (off <= n) p.v = q.cu[off];
+    if (n <= kDualSeqs) {
+      const int64_t o0 = 2 * (int64_t)lane, o1 = o0 + 1;
+      if (o0 <= n) p.v = q.cu[o0];
+      if (o1 <= n) p.w = q.cu[o1];
+      if (slots) {
+        if (o0 < n) p.s0 = slots[o0];
+        if (o1 < n) p.s1 = slots[o1];
+      }
+    } else {
+      const int64_t stride = (n + kWave - 2) / (kWave - 1);
+      const int64_t off = (int64_t)lane * stride;
+      if (off <= n) p.v = q.cu[off];
+    }
+  } else if constexpr (MODE == MODE_BATCH) {
+    if (slots && q.seqlen > 0) {
+      const int64_t i = udiv64(t, q.seqlen);
+      if (i < q.nseq) p.s0 = slots[i];
+    }
   } else if constexpr (MODE == MODE_IDX) {
     // lane l reads the IDs of row r = t - HB + l and of the row before it (pure loads: whether r
     // starts a batch row is worked out in seq_resolve)
@@ -353,13 +377,35 @@ __device__ __forceinline__ SeqDesc seq_resolve(const SeqArgs& q, int64_t t, int6
   SeqDesc d;
   const int lane = threadIdx.x & (kWave - 1);
   if constexpr (MODE == MODE_CU) {
-    // largest i in [0, nseq) with cu[i] <= t, by a 64-ary search: lane l reads cu[lo + l*stride]
-    // (one load per lane per level, a single level while nseq <= 63; the first level's values
-    // come from the probe), the highest lane whose offset is <= t narrows the interval.  Lane 0 is
-    // taken as the floor without a test, as the offsets start at 0.  The last level also hands
-    // over cu[i + 1] from the next lane.
+    // largest i in [0, nseq) with cu[i] <= t.  Up to kDualSeqs sequences lane l holds cu[2l] and
+    // cu[2l+1] from the probe: two ballots give the answer and its end offset at once.  Beyond,
+    // a 64-ary search: lane l reads cu[lo + l*stride] (one load per lane per level; the first
+    // level's values come from the probe), the highest lane whose offset is <= t narrows the
+    // interval.  Lane 0 is taken as the floor without a test, as the offsets start at 0.  The
+    // last level also hands over cu[i + 1] from the next lane.
     int64_t lo = 0, n = q.nseq;  // the answer lies in [lo, lo + n)
     bool first = true;
+    if (n <= kDualSeqs) {
+      const int64_t o0 = 2 * (int64_t)lane, o1 = o0 + 1;
+      const int32_t hi = (int32_t)dend;
+      const int32_t v0 = o0 <= n ? (p.v < 0 ? 0 : (p.v > hi ? hi : p.v)) : 0;
+      const int32_t v1 = o1 <= n ? (p.w < 0 ? 0 : (p.w > hi ? hi : p.w)) : 0;
+      const uint64_t m0 = __ballot(lane == 0 || (o0 < n && v0 <= t));
+      const uint64_t m1 = __ballot(o1 < n && v1 <= t);
+      const int k0 = 63 - __builtin_clzll(m0);
+      const int k1 = m1 ? 63 - __builtin_clzll(m1) : -1;
+      if (k1 >= k0) {  // sequence 2 k1 + 1 (< n, so lane k1 + 1 <= 63 holds its end)
+        d.idx = 2 * (int64_t)k1 + 1;
+        d.s = __builtin_amdgcn_readlane(v1, k1);
+        d.e = __builtin_amdgcn_readlane(v0, k1 + 1 < kWave ? k1 + 1 : k1);
+      } else {  // sequence 2 k0
+        d.idx = 2 * (int64_t)k0;
+        d.s = __builtin_amdgcn_readlane(v0, k0);
+        d.e = __builtin_amdgcn_readlane(v1, k0);
+      }
+      if (d.e <= t) d.e = t + 1;  // only for metadata that breaks the contract: stay in bounds
+      return d;
+    }
     while (true) {
       const int64_t stride = n < kWave ? 1 : (n + kWave - 2) / (kWave - 1);
       const int64_t off = (int64_t)lane * stride;
@@ -411,6 +457,23 @@ __device__ __forceinline__ SeqDesc seq_resolve(const SeqArgs& q, int64_t t, int6
 template <int MODE, int HB = 3>
 __device__ __forceinline__ SeqDesc seq_of_row(const SeqArgs& q, int64_t t, int64_t dend, int64_t limit) {
   return seq_resolve<MODE, HB>(q, t, dend, limit, seq_probe<MODE, HB>(q, t, limit));
+}
+
+// The slot of sequence idx (resolved from the same probe, which was given the slot array) when
+// the probe fetched it: the offsets form up to kDualSeqs sequences, the batch-row form always.
+template <int MODE>
+__device__ __forceinline__ bool probe_slot(const SeqArgs& q, const SeqProbe& p, int64_t idx, int32_t& slot) {
+  if constexpr (MODE == MODE_CU) {
+    if (q.nseq > kDualSeqs || idx < 0 || idx >= q.nseq) return false;
+    slot = __builtin_amdgcn_readlane((idx & 1) ? p.s1 : p.s0, (int)(idx >> 1));
+    return true;
+  } else if constexpr (MODE == MODE_BATCH) {
+    if (idx < 0 || idx >= q.nseq) return false;
+    slot = __builtin_amdgcn_readfirstlane(p.s0);
+    return true;
+  } else {
+    return false;
+  }
 }
 
 // The sequence that starts right where `cur` ended (cur.e < dend).  Empty sequences are skipped.

@@ -132,6 +132,8 @@ struct FwdSeq {
   SeqDesc sd;
   int32_t slot;
   bool zero;
+  int64_t pre_idx = -1;  // the sequence whose slot the lookup already fetched (pre_slot), or -1
+  int32_t pre_slot = -1;
 };
 
 template <int MODE>
@@ -140,7 +142,7 @@ __device__ __forceinline__ void fwd_slot(const FwdArgs& a, FwdSeq& cs) {
   cs.zero = false;
   if constexpr (MODE != MODE_IDX) {
     if (a.pool.ptr) {
-      cs.slot = a.pool.cache_indices[cs.sd.idx];
+      cs.slot = cs.sd.idx == cs.pre_idx ? cs.pre_slot : a.pool.cache_indices[cs.sd.idx];
       cs.zero = !(cs.slot >= 0 && cs.slot < a.pool.slots);  // -1 (other values are out of contract)
     }
   }
@@ -350,7 +352,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
   // Row addresses never wait for the metadata, and the lookup's loads go first, so resolving it
   // waits for them alone.  The chunk index of every buffer access is a template constant: a
   // runtime index would move the buffers out of registers.
-  const SeqProbe pa = seq_probe<MODE, H>(a.seq, ta, tb);
+  const SeqProbe pa = seq_probe<MODE, H>(a.seq, ta, tb, has_pool ? a.pool.cache_indices : nullptr);
   SeqProbe pb{0, 0};
   if (has_pool && tb < a.rows) pb = seq_probe<MODE, H>(a.seq, tb, tb);
   const int64_t dend = data_end<MODE>(a.seq, a.rows);
@@ -378,6 +380,13 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
   if (ta >= te) return;
   FwdSeq cs;
   cs.sd = seq_resolve<MODE, H>(a.seq, ta, dend, te, pa);
+  if constexpr (has_pool) {  // the slot came with the lookup: no dependent load before the stores
+    int32_t sl;
+    if (probe_slot<MODE>(a.seq, pa, cs.sd.idx, sl)) {
+      cs.pre_idx = cs.sd.idx;
+      cs.pre_slot = sl;
+    }
+  }
   if constexpr (has_pool) {
     // tile boundaries on a sequence's rows 1 and 2 move to its row 3: the head tile alone owns
     // the slot.  A moved tile takes the general path.
