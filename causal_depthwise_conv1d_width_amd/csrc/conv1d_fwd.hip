@@ -9,14 +9,14 @@
 // Forward tiling (HBM-bound stencil, no MFMA):
 //   block  = kWavesPerBlock waves side by side; lane = CPL consecutive channels; a block covers
 //            kBlockChannels channels (a strip) of fwd_tile_rows() rows, so each row it touches is
-//            one contiguous segment.  A launch is many rounds of these short tiles, dispatched in
-//            row order (tile = row tile * strips + strip, each XCD one contiguous slice): the
-//            resident blocks sweep a compact band of rows, as a contiguous copy does, and the
-//            dispatcher balances the load to the end of the launch.
+//            one contiguous segment.  A launch is many rounds of these short tiles in an order
+//            chosen by the strip count (block_tile): row-major slices per XCD, plain row-major
+//            order, or strip-major slices per XCD.  The resident blocks sweep bands of rows, as a
+//            copy does, and the dispatcher balances the load to the end of the launch.
 //   loads  = one memory round trip per block: every row of the tile (non-temporal), the H window
-//            rows above it (the tile above read them moments ago on this XCD), the taps and the
-//            sequence offsets, all issued before any of them is used; row addresses never wait
-//            for the metadata.
+//            rows above it (the tile above read them moments ago, mostly on this XCD), the taps,
+//            the sequence offsets and, with a pool, the slots, all issued before any of them is
+//            used; row addresses never wait for the metadata.
 //   window = a ring of R register slots indexed by row mod R inside the unrolled tile, so the
 //            sliding window costs no register moves.  Where a sequence starts inside the tile,
 //            its window slots are re-seeded from that sequence's history (pool positions 0..2,
