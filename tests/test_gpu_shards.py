@@ -173,6 +173,29 @@ def test_two_shards_on_one_gpu(oracle, cut_in):
     gh.assert_w_close(dw.cpu().numpy(), dw_u, "shard-ordered dweight vs unsplit")
 
 
+def test_head_call_gives_the_fragment_d_history(oracle):
+    """The multi-GPU backward's head: conv1d_bwd over the first W-1 rows of a shard's first fragment
+    alone (with its history rows) returns that fragment's d(history) bit for bit, as the full call
+    does, since d(history) takes only the dz of those rows; and it matches the oracle."""
+    whole = wl.cp_share()
+    cu = whole["cu_seqlens"]
+    k = int(np.argmax(np.diff(cu)))
+    cut = int(cu[k]) + 1000
+    _, B = _split(whole, cut)
+    say(f"head call: shard from row {cut}")
+    dB = _dev_case(B)
+    _bwd_dev(dB)
+    head = dict(B, name="head", x=B["x"][:3], dy=B["dy"][:3], cu_seqlens=np.array([0, 3], np.int32),
+                hist=np.ascontiguousarray(B["hist"][:1]), has_history=np.ones(1, np.uint8))
+    dH = _dev_case(head)
+    _bwd_dev(dH)
+    torch.cuda.synchronize()
+    full, part = gh.host_bits(dB["dh"])[0], gh.host_bits(dH["dh"])[0]
+    assert np.array_equal(full, part), "head call d(history) differs from the full call's"
+    _, _, _, dh_ref = gh.oracle_bwd(oracle, head)
+    gh.assert_bf16_close(part, dh_ref[0], "head call d(history) vs oracle")
+
+
 def test_combine_bit_exact_against_oracle(oracle):
     """The ordered sum on seeded partials (values spread over many binades, so the order matters):
     bit-exact against the oracle's ordered sum; one shard is a bit copy; zero shards give zeros."""
