@@ -6,6 +6,8 @@
   form, widths 2, 4 and 8, last sequences shorter than the history and empty.
 - The context-parallel workload (x [16384, 5632], 12 fragments) split into two shards on one GPU:
   shard B's d(history) goes straight (device to device, no host arithmetic) into shard A's d(tail).
+- The head of a multi-GPU backward: the call over a fragment's first W-1 rows alone returns that
+  fragment's d(history) bit for bit, as the full call does.
 - The shard-ordered dweight combine (assert_causal_conv1d_deterministic): bit-exact against the
   oracle's ordered sum, and bitwise stable from run to run.
 """
