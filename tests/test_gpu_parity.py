@@ -330,3 +330,35 @@ def test_forward_block_orders(oracle, C, form):
         case["seq_idx"] = np.repeat(np.arange(len(lengths)), lengths).astype(np.int32)
     _print_case(case["name"], rows=rows, C=C, seqs=len(lengths))
     gh.check_fwd(oracle, case)
+
+
+@pytest.mark.parametrize("nseq", [126, 127, 300])
+def test_sequence_lookup_levels(oracle, nseq):
+    """The offsets lookup is one level of two offsets per lane up to 126 sequences (the forward with
+    a pool also takes every slot from it) and a 64-ary search beyond: 126, 127 and 300 sequences of
+    0..40 rows, with a pool (both layouts, -1 slots, mixed has_initial_state) in the forward and
+    history rows in the backward, against the oracle."""
+    rng = np.random.default_rng(61 + nseq)
+    C = 1032  # three strips, the last one partial
+    lengths = rng.integers(0, 41, size=nseq)
+    lengths[rng.choice(nseq, 5, replace=False)] = rng.integers(1, 4, size=5)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    rows = int(cu[-1]) + 3
+    x = wl.normal_bf16(rng, (rows, C))
+    w = wl.uniform_f32(rng, (C, 4))
+    b = (rng.standard_normal(C) * 0.1).astype(np.float32)
+    for layout in ("hist", "chan"):
+        slots = nseq + 5
+        ci = rng.permutation(slots)[:nseq].astype(np.int32)
+        ci[rng.choice(nseq, 7, replace=False)] = -1
+        case = dict(name=f"lookup-{nseq}-pool-{layout}", x=x, w=w, b=b, act="silu", cu_seqlens=cu,
+                    pool=wl.pool_layout(wl.normal_bf16(rng, (slots, C, 4)), layout), cache_indices=ci,
+                    has_initial_state=(rng.random(nseq) < 0.6).astype(np.uint8))
+        _print_case(case["name"], rows=rows, C=C)
+        gh.check_fwd(oracle, case)
+    case = dict(name=f"lookup-{nseq}-hist", x=x, w=w, b=b, act="silu", cu_seqlens=cu,
+                hist=wl.normal_bf16(rng, (nseq, 3, C)), has_history=(rng.random(nseq) < 0.7).astype(np.uint8),
+                dy=wl.normal_bf16(rng, (rows, C)))
+    _print_case(case["name"], rows=rows, C=C)
+    gh.check_fwd(oracle, case)
+    gh.check_bwd(oracle, case)
