@@ -306,12 +306,13 @@ def test_forward_short_ranges_at_large_row_counts(oracle, form):
 
 
 @pytest.mark.parametrize("C", [2048, 3600, 4096, 8192])
-@pytest.mark.parametrize("form", ["cu", "idx"])
+@pytest.mark.parametrize("form", ["cu", "idx", "pool"])
 def test_forward_block_orders(oracle, C, form):
     """The forward's block-to-tile order depends on the number of 512-channel strips: slices of the
     strip-major order per XCD for 4 strips (C = 2048), plain row-major order for 8 and 16 strips
     (C = 3600 with a partial last strip, 4096, 8192).  Sequences of 1..300 rows over ~1500 rows,
-    history rows in the offsets form, checked against the oracle."""
+    history rows in the offsets form, a slot pool (with -1 slots) in the pool form, checked against
+    the oracle."""
     rng = np.random.default_rng(41 + C)
     lengths, total = [], 0
     while total < 1500:
@@ -325,6 +326,14 @@ def test_forward_block_orders(oracle, C, form):
         case["cu_seqlens"] = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
         case["hist"] = wl.normal_bf16(rng, (len(lengths), 3, C))
         case["has_history"] = (rng.random(len(lengths)) < 0.6).astype(np.uint8)
+    elif form == "pool":  # 24-row tiles, slots taken with the lookup
+        n = len(lengths)
+        case["cu_seqlens"] = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        case["pool"] = wl.pool_layout(wl.normal_bf16(rng, (n + 2, C, 4)), "chan" if C % 3 else "hist")
+        ci = rng.permutation(n + 2)[:n].astype(np.int32)
+        ci[::5] = -1
+        case["cache_indices"] = ci
+        case["has_initial_state"] = (rng.random(n) < 0.7).astype(np.uint8)
     else:
         case["seqlen"] = rows
         case["seq_idx"] = np.repeat(np.arange(len(lengths)), lengths).astype(np.int32)
