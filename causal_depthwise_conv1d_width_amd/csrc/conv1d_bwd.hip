@@ -9,16 +9,18 @@
 //     dw_k   = sum_t dz[t] u[t-(W-1)+k],  db = sum_t dz[t]
 //     dh_j   = sum_{tau <= j} w_{j-tau} dz[s+tau]   (history row j of a continuing fragment)
 //
-// Tiling: as the forward (waves side by side in channels, lane = CPL channels, one launch of
-// about kBwdBlocks equal row ranges).  The window is a ring of R register slots (R = 4 up to
-// width four, 8 up to width eight) with H = R - 1 history rows.  A wave streams x and dy over its
-// own rows [ta, tb) and up to H look-ahead rows of the sequence that holds row tb - 1; the H
+// Tiling: waves side by side in channels as in the forward (lane = CPL channels), but where the
+// forward launches many rounds of short tiles, the backward launches one round of about kBwdBlocks
+// long row ranges, one dweight/dbias partial each.  The window is a ring of R register slots (R = 4
+// up to width four, 8 up to width eight) with H = R - 1 history rows.  A wave streams x and dy over
+// its own rows [ta, tb) and up to H look-ahead rows of the sequence that holds row tb - 1; the H
 // look-behind and the look-ahead rows belong to the neighbouring ranges (cached loads).  The step
-// at row q produces the value of row q - H (at width four: w3 dz[q-3] + w2 dz[q-2] + w1 dz[q-1]
-// + w0 dz[q]): dx when q - H is a row of q's sequence, d(history) row j when it is the
-// sequence's history row j (the dz ring holds zeros before a sequence's start).  Where a
-// sequence ends, the values of its last H rows are flushed with the dz of later rows left out,
-// and the stream goes straight on.
+// at row q produces the value of row q - H (at width four: w3 dz[q-3] + w2 dz[q-2] + w1 dz[q-1] +
+// w0 dz[q]): dx when q - H is a row of q's sequence, d(history) row j when it is the sequence's
+// history row j (the dz ring holds zeros before a sequence's start).  Where a sequence ends, the
+// values of its last H rows are flushed with the dz of later rows left out (plus the caller's
+// d(tail) rows, the gradient arriving from the next fragment, when the sequence is the array's
+// last), and the stream goes straight on.
 //
 // dweight/dbias are deterministic by construction: each lane accumulates its channels over its
 // rows in row order (FP32) and owns those channels for the whole row range, so the range's
