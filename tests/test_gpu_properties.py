@@ -1,6 +1,7 @@
 """GPU properties beyond element-wise parity: determinism, decode = unit prefill, chunked prefill,
 the context-parallel split, HIP-graph capture and replay with edited metadata, strided rows and
-64-bit row offsets.  Everything goes through the C ABI (the torch binding only marshals)."""
+64-bit row offsets (forward and backward, with history rows and per-token IDs).  Everything goes
+through the C ABI (the torch binding only marshals)."""
 import numpy as np
 import pytest
 
@@ -258,3 +259,91 @@ def test_64bit_row_offsets(oracle):
     gh.assert_bf16_close(ys[:4096], yr[:4096], "near rows")
     del x, y
     torch.cuda.empty_cache()
+
+
+def _big_normal(rows, C, seed):
+    t = torch.empty(rows, C, dtype=torch.bfloat16, device="cuda")
+    t.normal_(generator=torch.Generator(device="cuda").manual_seed(seed))
+    return t
+
+
+# Channels are independent in a depthwise filter, so a handful of channels of a huge array is an
+# exact small problem for the oracle: every row of the sampled channels is checked.  At 16384
+# channels row 131072 is element 2^31 and byte 2^32; sequences start on both sides of it.
+_BIG_ROWS, _BIG_C = 4096 * 33, 16384
+_BIG_COLS = np.array([0, 1, 777, 8191, 16383])
+
+
+def test_64bit_row_offsets_backward_with_history(oracle):
+    """The backward with history rows, dbias and d(tail) over rows * C beyond 2^31 elements
+    (4.4 GB per tensor): dx on every row, dweight, dbias and d(history) of sampled channels
+    against the oracle; and the forward with history rows over the same array."""
+    say("64-bit offsets: forward and backward with history rows and d(tail)")
+    rng = np.random.default_rng(37)
+    rows, C, cols = _BIG_ROWS, _BIG_C, _BIG_COLS
+    x, dy = _big_normal(rows, C, 8), _big_normal(rows, C, 9)
+    cu = np.array([0, 5, 70000, 131070, 131073, rows - 3, rows], np.int32)
+    nseq = len(cu) - 1
+    hh = np.array([1, 0, 1, 1, 1, 0], np.uint8)
+    hist = wl.normal_bf16(rng, (nseq, 3, C))
+    w = wl.uniform_f32(rng, (C, 4))
+    b = (rng.standard_normal(C) * 0.1).astype(np.float32)
+    dtail = wl.normal_bf16(rng, (3, C))
+    kw = dict(cu_seqlens=gh.dev_i32(cu), history=gh.dev_bits(hist), has_history=gh.dev_u8(hh))
+    y = cc.conv1d_fwd(x, gh.dev_taps(w), gh.dev_taps(b), **kw)
+    dh = gh.dev_bits(np.full((nseq, 3, C), wl.OUT_FILL, np.uint16))  # rows left untouched keep the marker
+    dx, dw, db, dh = cc.conv1d_bwd(x, dy, gh.dev_taps(w), gh.dev_taps(b), want_dbias=True, dhistory=dh,
+                                   dtail=gh.dev_bits(dtail), **kw)
+    torch.cuda.synchronize()
+    ci = torch.from_numpy(cols).cuda()
+    xs, dys = gh.host_bits(x[:, ci].contiguous()), gh.host_bits(dy[:, ci].contiguous())
+    ys, dxs = gh.host_bits(y[:, ci].contiguous()), gh.host_bits(dx[:, ci].contiguous())
+    dws, dbs = dw[ci].cpu().numpy(), db[ci].cpu().numpy()
+    dhs = gh.host_bits(dh[:, :, ci].contiguous()).reshape(nseq, 3, len(cols))
+    del x, dy, y, dx
+    torch.cuda.empty_cache()
+    hs = np.ascontiguousarray(hist[:, :, cols])
+    wc, bc = np.ascontiguousarray(w[cols]), np.ascontiguousarray(b[cols])
+    yr = oracle.fwd(xs, wc, bc, cu_seqlens=cu, hist=hs, has_history=hh)
+    gh.assert_bf16_close(ys, yr, "far-offset forward y")
+    dxr, dwr, dbr, dhr = oracle.bwd(xs, dys, wc, bc, cu_seqlens=cu, hist=hs, has_history=hh,
+                                    dtail=np.ascontiguousarray(dtail[:, cols]))
+    gh.assert_bf16_close(dxs, dxr, "far-offset dx")
+    gh.assert_w_close(dws, dwr, "far-offset dweight")
+    gh.assert_w_close(dbs, dbr, "far-offset dbias")
+    gh.assert_bf16_close(dhs, dhr, "far-offset d(history)")
+
+
+def test_64bit_row_offsets_per_token_ids(oracle):
+    """Per-token sequence IDs (4096-row batch rows) over rows * C beyond 2^31 elements: y and dx
+    on every row, dweight and dbias of sampled channels against the oracle."""
+    say("64-bit offsets: per-token IDs, forward and backward")
+    rng = np.random.default_rng(38)
+    rows, C, cols, T = _BIG_ROWS, _BIG_C, _BIG_COLS, 4096
+    ids = np.empty(rows, np.int32)
+    nxt = 0
+    for b0 in range(0, rows, T):
+        cuts = np.sort(rng.choice(np.arange(1, T), int(rng.integers(0, 6)), replace=False))
+        bounds = np.concatenate([[0], cuts, [T]])
+        for k in range(len(bounds) - 1):
+            ids[b0 + bounds[k]:b0 + bounds[k + 1]] = nxt
+            nxt += 1
+    x, dy = _big_normal(rows, C, 10), _big_normal(rows, C, 11)
+    w = wl.uniform_f32(rng, (C, 4))
+    b = (rng.standard_normal(C) * 0.1).astype(np.float32)
+    kw = dict(seq_idx=gh.dev_i32(ids), seqlen=T)
+    y = cc.conv1d_fwd(x, gh.dev_taps(w), gh.dev_taps(b), **kw)
+    dx, dw, db, _ = cc.conv1d_bwd(x, dy, gh.dev_taps(w), gh.dev_taps(b), want_dbias=True, **kw)
+    torch.cuda.synchronize()
+    ci = torch.from_numpy(cols).cuda()
+    xs, dys = gh.host_bits(x[:, ci].contiguous()), gh.host_bits(dy[:, ci].contiguous())
+    ys, dxs = gh.host_bits(y[:, ci].contiguous()), gh.host_bits(dx[:, ci].contiguous())
+    dws, dbs = dw[ci].cpu().numpy(), db[ci].cpu().numpy()
+    del x, dy, y, dx
+    torch.cuda.empty_cache()
+    wc, bc = np.ascontiguousarray(w[cols]), np.ascontiguousarray(b[cols])
+    gh.assert_bf16_close(ys, oracle.fwd(xs, wc, bc, seq_idx=ids, seqlen=T), "far-offset per-token-ID y")
+    dxr, dwr, dbr, _ = oracle.bwd(xs, dys, wc, bc, seq_idx=ids, seqlen=T)
+    gh.assert_bf16_close(dxs, dxr, "far-offset per-token-ID dx")
+    gh.assert_w_close(dws, dwr, "far-offset per-token-ID dweight")
+    gh.assert_w_close(dbs, dbr, "far-offset per-token-ID dbias")
