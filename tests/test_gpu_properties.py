@@ -347,3 +347,88 @@ def test_64bit_row_offsets_per_token_ids(oracle):
     gh.assert_bf16_close(dxs, dxr, "far-offset per-token-ID dx")
     gh.assert_w_close(dws, dwr, "far-offset per-token-ID dweight")
     gh.assert_w_close(dbs, dbr, "far-offset per-token-ID dbias")
+
+
+@pytest.mark.parametrize("layout", ["hist", "chan"])
+def test_64bit_pool_offsets(oracle, layout):
+    """A slot pool beyond 2^31 elements (33000 slots x 16384 channels x 4 positions, 4.3 GB; slot
+    32768 starts at element 2^31): a prefill and then a decode step on slots near its end.  y, the
+    decode outputs and the written states of sampled channels against the oracle, which gets only
+    the used slots; a slot between them stays untouched."""
+    say(f"64-bit offsets: slot pool, {layout} layout")
+    rng = np.random.default_rng(39)
+    C, slots, cols = _BIG_C, 33000, _BIG_COLS
+    if layout == "hist":
+        pool = torch.empty(slots, C, 4, dtype=torch.bfloat16, device="cuda")
+    else:
+        pool = torch.empty(slots, 4, C, dtype=torch.bfloat16, device="cuda").permute(0, 2, 1)
+    pool.normal_(generator=torch.Generator(device="cuda").manual_seed(12))
+    lengths = [5, 1, 300, 2, 77]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    ci = np.array([32999, 32768, 31000, -1, 32767], np.int32)
+    hi = np.array([1, 0, 1, 1, 1], np.uint8)
+    live = [int(s) for s in ci if s >= 0]
+    small_ci = np.array([live.index(int(s)) if s >= 0 else -1 for s in ci], np.int32)
+    used = torch.tensor(live, device="cuda")
+    ccol = torch.from_numpy(cols).cuda()
+
+    def used_state():  # [len(live), 5, 4] bits of the used slots at the sampled channels
+        return gh.host_bits(pool[used][:, ccol, :].contiguous()).reshape(len(live), len(cols), 4)
+
+    spare = gh.host_bits(pool[32998].contiguous())
+    small_pool = used_state().copy()
+    x = wl.normal_bf16(rng, (int(cu[-1]), C))
+    w = wl.uniform_f32(rng, (C, 4))
+    b = (rng.standard_normal(C) * 0.1).astype(np.float32)
+    wc, bc = np.ascontiguousarray(w[cols]), np.ascontiguousarray(b[cols])
+    y = cc.conv1d_fwd(gh.dev_bits(x), gh.dev_taps(w), gh.dev_taps(b), cu_seqlens=gh.dev_i32(cu), conv_state=pool,
+                      cache_indices=gh.dev_i32(ci), has_initial_state=gh.dev_u8(hi))
+    torch.cuda.synchronize()
+    yr = oracle.fwd(np.ascontiguousarray(x[:, cols]), wc, bc, cu_seqlens=cu, pool=small_pool,
+                    cache_indices=small_ci, has_initial_state=hi)
+    gh.assert_bf16_close(gh.host_bits(y[:, ccol].contiguous()), yr, f"far-slot prefill y ({layout})")
+    assert np.array_equal(used_state(), small_pool), f"far-slot prefill states ({layout})"
+    # one decode token per sequence on the same slots
+    xt = wl.normal_bf16(rng, (len(ci), C))
+    yt = cc.conv1d_state_update(gh.dev_bits(xt), gh.dev_taps(w), gh.dev_taps(b), conv_state=pool,
+                                cache_indices=gh.dev_i32(ci))
+    torch.cuda.synchronize()
+    ytr = oracle.state_update(np.ascontiguousarray(xt[:, cols]), wc, bc, pool=small_pool, cache_indices=small_ci)
+    gh.assert_bf16_close(gh.host_bits(yt[:, ccol].contiguous()), ytr, f"far-slot decode y ({layout})")
+    assert np.array_equal(used_state(), small_pool), f"far-slot decode states ({layout})"
+    assert np.array_equal(gh.host_bits(pool[32998].contiguous()), spare), "an unused slot was written"
+    del pool
+    torch.cuda.empty_cache()
+
+
+def test_64bit_offsets_channels_first(oracle):
+    """Channels-first x [3, 16384, 65536] (3 * 2^30 elements, 6.4 GB per tensor; batch row 2 starts
+    at element 2^31): forward and backward, y and dx of sampled channels on every step, dweight and
+    dbias of those channels against the oracle."""
+    say("64-bit offsets: channels-first")
+    rng = np.random.default_rng(40)
+    B, D, T = 3, 16384, 65536
+    cols = _BIG_COLS
+    x = torch.empty(B, D, T, dtype=torch.bfloat16, device="cuda")
+    x.normal_(generator=torch.Generator(device="cuda").manual_seed(13))
+    dy = torch.empty_like(x)
+    dy.normal_(generator=torch.Generator(device="cuda").manual_seed(14))
+    w = wl.uniform_f32(rng, (D, 4))
+    b = (rng.standard_normal(D) * 0.1).astype(np.float32)
+    y = cc.conv1d_fwd_cf(x, gh.dev_taps(w), gh.dev_taps(b))
+    dx, dw, db = cc.conv1d_bwd_cf(x, dy, gh.dev_taps(w), gh.dev_taps(b), want_dbias=True)
+    torch.cuda.synchronize()
+    ccol = torch.from_numpy(cols).cuda()
+    xs, dys = gh.host_bits(x[:, ccol, :].contiguous()), gh.host_bits(dy[:, ccol, :].contiguous())
+    ys, dxs = gh.host_bits(y[:, ccol, :].contiguous()), gh.host_bits(dx[:, ccol, :].contiguous())
+    dws, dbs = dw[ccol].cpu().numpy(), db[ccol].cpu().numpy()
+    del x, dy, y, dx
+    torch.cuda.empty_cache()
+    shape = (B, len(cols), T)
+    xs, dys, ys, dxs = xs.reshape(shape), dys.reshape(shape), ys.reshape(shape), dxs.reshape(shape)
+    wc, bc = np.ascontiguousarray(w[cols]), np.ascontiguousarray(b[cols])
+    gh.assert_bf16_close(ys, oracle.fwd_cf(xs, wc, bc), "far-offset channels-first y")
+    dxr, dwr, dbr = oracle.bwd_cf(xs, dys, wc, bc, want_db=True)
+    gh.assert_bf16_close(dxs, dxr, "far-offset channels-first dx")
+    gh.assert_w_close(dws, dwr, "far-offset channels-first dweight")
+    gh.assert_w_close(dbs, dbr, "far-offset channels-first dbias")
