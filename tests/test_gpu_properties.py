@@ -432,3 +432,42 @@ def test_64bit_offsets_channels_first(oracle):
     gh.assert_bf16_close(dxs, dxr, "far-offset channels-first dx")
     gh.assert_w_close(dws, dwr, "far-offset channels-first dweight")
     gh.assert_w_close(dbs, dbr, "far-offset channels-first dbias")
+
+
+def test_sequence_forms_agree_bitwise():
+    """The per-token-ID workload (16384 x 4096, 21 sequences over 4096-row batch rows) and the
+    same sequences given as cu_seqlens offsets; then one sequence per batch row in all three
+    forms: y, dx, dweight and dbias identical bit for bit (the forms only locate the same
+    boundaries; every partial sum covers the same rows)."""
+    say("sequence forms: per-token IDs against the same sequences as offsets")
+    case = wl.train_seq_ids()
+    ids, T = case["seq_idx"].astype(np.int64), case["seqlen"]
+    rows = case["x"].shape[0]
+    starts = [0] + [i for i in range(1, rows) if ids[i] != ids[i - 1] or i % T == 0]
+    cu = np.array(starts + [rows], np.int32)
+    assert len(cu) > 2
+    x, dy = gh.dev_bits(case["x"]), gh.dev_bits(case["dy"])
+    w, b = gh.dev_taps(case["w"]), gh.dev_taps(case.get("b"))
+    out = {}
+    for form, kw in (("idx", dict(seq_idx=gh.dev_i32(case["seq_idx"]), seqlen=T)), ("cu", dict(cu_seqlens=gh.dev_i32(cu)))):
+        y = cc.conv1d_fwd(x, w, b, **kw)
+        dx, dw, db, _ = cc.conv1d_bwd(x, dy, w, b, want_dbias=True, **kw)
+        torch.cuda.synchronize()
+        out[form] = (gh.host_bits(y), gh.host_bits(dx), dw.view(torch.int32).cpu().numpy(),
+                     db.view(torch.int32).cpu().numpy())
+    for name, a, c in zip(("y", "dx", "dweight", "dbias"), out["idx"], out["cu"]):
+        assert np.array_equal(a, c), f"{name} differs between the per-token-ID and offsets forms"
+    # one sequence per batch row: the batch-row form, IDs = batch row, offsets at every T rows
+    forms = (("batch", dict(seqlen=T)),
+             ("idx", dict(seq_idx=gh.dev_i32((np.arange(rows) // T).astype(np.int32)), seqlen=T)),
+             ("cu", dict(cu_seqlens=gh.dev_i32(np.arange(0, rows + 1, T, dtype=np.int32)))))
+    out = {}
+    for form, kw in forms:
+        y = cc.conv1d_fwd(x, w, b, **kw)
+        dx, dw, db, _ = cc.conv1d_bwd(x, dy, w, b, want_dbias=True, **kw)
+        torch.cuda.synchronize()
+        out[form] = (gh.host_bits(y), gh.host_bits(dx), dw.view(torch.int32).cpu().numpy(),
+                     db.view(torch.int32).cpu().numpy())
+    for other in ("idx", "cu"):
+        for name, a, c in zip(("y", "dx", "dweight", "dbias"), out["batch"], out[other]):
+            assert np.array_equal(a, c), f"{name} differs between the batch-row and {other} forms"
