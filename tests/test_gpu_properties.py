@@ -471,3 +471,31 @@ def test_sequence_forms_agree_bitwise():
     for other in ("idx", "cu"):
         for name, a, c in zip(("y", "dx", "dweight", "dbias"), out["batch"], out[other]):
             assert np.array_equal(a, c), f"{name} differs between the batch-row and {other} forms"
+
+
+@pytest.mark.parametrize("layout", ["hist", "chan"])
+def test_pool_state_equals_history_rows(layout):
+    """The prefill workload (32768 x 5632, 64 sequences, 256 padding rows) read its history from a
+    slot pool (positions 0..2, 24-row tiles, slot lookup and write-back) and, with the same values
+    as caller history rows (16-row tiles), gives the same y bits; sequences without initial state
+    start from zeros in both; the padding rows stay untouched in both."""
+    say(f"pool state against history rows ({layout} layout)")
+    case = wl.prefill_pool()
+    rng = np.random.default_rng(41)
+    hi = (rng.random(len(case["cache_indices"])) < 0.7).astype(np.uint8)
+    pool = wl.pool_layout(case["pool"], layout)
+    hist = np.ascontiguousarray(case["pool"][case["cache_indices"]][:, :, 0:3].transpose(0, 2, 1))
+    x = gh.dev_bits(case["x"])
+    w, b = gh.dev_taps(case["w"]), gh.dev_taps(case["b"])
+    cu = gh.dev_i32(case["cu_seqlens"])
+    rows, C = case["x"].shape
+    y_pool = gh.dev_bits(np.full((rows, C), wl.OUT_FILL, np.uint16))
+    y_hist = gh.dev_bits(np.full((rows, C), wl.OUT_FILL, np.uint16))
+    cc.conv1d_fwd(x, w, b, cu_seqlens=cu, conv_state=gh.dev_pool(pool), cache_indices=gh.dev_i32(case["cache_indices"]),
+                  has_initial_state=gh.dev_u8(hi), out=y_pool)
+    cc.conv1d_fwd(x, w, b, cu_seqlens=cu, history=gh.dev_bits(hist), has_history=gh.dev_u8(hi), out=y_hist)
+    torch.cuda.synchronize()
+    a, c = gh.host_bits(y_pool), gh.host_bits(y_hist)
+    end = int(case["cu_seqlens"][-1])
+    assert end < rows and (a[end:] == wl.OUT_FILL).all() and (c[end:] == wl.OUT_FILL).all()
+    assert np.array_equal(a, c), "pool-state and history-row forwards differ"
