@@ -1,6 +1,6 @@
 """Channels-first [B, D, T] forward and backward (conv1d_fwd_cf / conv1d_bwd_cf) on the GPU against
 the oracle: ragged T (the element-wise path), rows longer than one unrolled chunk, strided views,
-empty T, and bitwise-reproducible dweight."""
+empty T, bitwise-reproducible dweight, and the forward bit for bit equal to the channel-last one."""
 import numpy as np
 import pytest
 
@@ -112,3 +112,22 @@ def test_cf_empty_time_axis():
     torch.cuda.synchronize()
     assert y.shape == (2, D, 0) and dx.shape == (2, D, 0)
     assert (dw == 0).all() and (db == 0).all(), "no steps: zero dweight / dbias"
+
+
+@pytest.mark.parametrize("W", [4, 8])
+def test_cf_forward_equals_channel_last(W):
+    """[4, 4096, 4096] channels first against the channel-last forward of the same values
+    transposed to [B * T, D] with one sequence per T-row batch row: the same y bits (both kernels
+    take bias, then taps 0..W-1 as FP32 FMAs, and the same SiLU)."""
+    say(f"channels-first forward against channel-last, width {W}")
+    rng = np.random.default_rng(42 + W)
+    B, D, T = 4, 4096, 4096
+    x = torch.empty(B, D, T, dtype=torch.bfloat16, device="cuda")
+    x.normal_(generator=torch.Generator(device="cuda").manual_seed(15 + W))
+    w = gh.dev_taps(wl.uniform_f32(rng, (D, W)))
+    b = gh.dev_taps((rng.standard_normal(D) * 0.1).astype(np.float32))
+    y_cf = cc.conv1d_fwd_cf(x, w, b)
+    xl = x.transpose(1, 2).contiguous().view(B * T, D)
+    y_cl = cc.conv1d_fwd(xl, w, b, seqlen=T)
+    torch.cuda.synchronize()
+    assert torch.equal(y_cf.transpose(1, 2).contiguous().view(B * T, D).view(torch.int16), y_cl.view(torch.int16))
