@@ -1,7 +1,8 @@
 """Filter widths 2, 3 and 5..8 (taps [C, W], W-1 history rows) on the GPU against the oracle:
 random packed sweeps in both sequence forms, sequences shorter than the history across range
-boundaries, the context-parallel workload at full size (widths 3 and 8), and the channels-first
-layout (widths 2, 3, 5 and 8)."""
+boundaries, the context-parallel workload at full size (widths 3 and 8), the channels-first
+layout (widths 2, 3, 5 and 8), and wide filters with leading zero taps equal to narrow ones bit
+for bit."""
 import numpy as np
 import pytest
 
@@ -97,3 +98,53 @@ def test_width_channels_first(oracle, W):
         assert dw.shape == (D, W)
         gh.assert_w_close(dw.cpu().numpy(), dwr, "cf dw")
         gh.assert_w_close(db.cpu().numpy(), dbr, "cf db")
+
+
+def _run_width(case, w, hist):
+    """y, dx, dweight, dbias, d(history) of the full forward and backward for taps w [C, W]."""
+    x, dy = gh.dev_bits(case["x"]), gh.dev_bits(case["dy"])
+    b = gh.dev_taps(case.get("b"))
+    kw = dict(cu_seqlens=gh.dev_i32(case.get("cu_seqlens")), seq_idx=gh.dev_i32(case.get("seq_idx")),
+              seqlen=case.get("seqlen"))
+    dh = None
+    if hist is not None:
+        kw.update(history=gh.dev_bits(hist), has_history=gh.dev_u8(case["has_history"]))
+        dh = gh.dev_bits(np.full(hist.shape, wl.OUT_FILL, np.uint16))
+    y = cc.conv1d_fwd(x, gh.dev_taps(w), b, **kw)
+    dx, dw, db, dh = cc.conv1d_bwd(x, dy, gh.dev_taps(w), b, want_dbias=b is not None, dhistory=dh, **kw)
+    torch.cuda.synchronize()
+    return (gh.host_bits(y), gh.host_bits(dx), dw.view(torch.int32).cpu().numpy(),
+            None if db is None else db.view(torch.int32).cpu().numpy(),
+            None if dh is None else gh.host_bits(dh).reshape(hist.shape))
+
+
+@pytest.mark.parametrize("wa,wb,work", [(3, 4, "cp"), (4, 5, "cp"), (4, 6, "cp"), (4, 7, "cp"), (4, 8, "cp"),
+                                        (2, 8, "cp"), (3, 4, "ids"), (4, 8, "ids")])
+def test_leading_zero_taps_equal_the_narrow_filter(wa, wb, work):
+    """Width wb with wb - wa leading zero taps is width wa, bit for bit: y, dx, dbias, the last wa
+    columns of dweight and the last wa - 1 rows of d(history) (the first wb - wa rows are zero; the
+    extra history rows meet only zero taps).  Full-size context-parallel share (offsets, history
+    rows) or per-token-ID workload (with bias): a different ring, tile and chunk path against the
+    narrow one, since an FMA with a zero tap leaves the sum unchanged."""
+    say(f"width {wb} with {wb - wa} zero leading taps against width {wa} ({work})")
+    rng = np.random.default_rng(80 + 10 * wa + wb)
+    case = wl.cp_share() if work == "cp" else wl.train_seq_ids()
+    C, k = case["x"].shape[1], wb - wa
+    wa_taps = wl.uniform_f32(rng, (C, wa))
+    wb_taps = np.concatenate([np.zeros((C, k), np.float32), wa_taps], axis=1)
+    ha = hb = None
+    if case.get("hist") is not None:
+        n = case["hist"].shape[0]
+        ha = wl.normal_bf16(rng, (n, wa - 1, C))
+        hb = np.ascontiguousarray(np.concatenate([wl.normal_bf16(rng, (n, k, C)), ha], axis=1))
+    ya, dxa, dwa, dba, dha = _run_width(case, wa_taps, ha)
+    yb, dxb, dwb, dbb, dhb = _run_width(case, wb_taps, hb)
+    assert np.array_equal(ya, yb), "y"
+    assert np.array_equal(dxa, dxb), "dx"
+    assert np.array_equal(dwa, np.ascontiguousarray(dwb[:, k:])), "dweight of the shared taps"
+    if dba is not None:
+        assert np.array_equal(dba, dbb), "dbias"
+    if dha is not None:
+        live = case["has_history"].astype(bool)
+        assert np.array_equal(dha, dhb[:, k:]), "d(history) of the shared history rows"
+        assert (gh.f32(dhb[live][:, :k]) == 0).all(), "d(history) of rows that meet only zero taps"
