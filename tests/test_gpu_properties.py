@@ -499,3 +499,31 @@ def test_pool_state_equals_history_rows(layout):
     end = int(case["cu_seqlens"][-1])
     assert end < rows and (a[end:] == wl.OUT_FILL).all() and (c[end:] == wl.OUT_FILL).all()
     assert np.array_equal(a, c), "pool-state and history-row forwards differ"
+
+
+@pytest.mark.parametrize("work", ["cp", "ids"])
+def test_bf16_and_fp32_taps_agree_bitwise(work):
+    """Taps and bias given as bf16, or as FP32 holding the same (bf16-representable) values: the
+    same y, dx, dweight, dbias and d(history) bits at full size (both widen exactly to FP32)."""
+    say(f"bf16 against FP32 taps ({work})")
+    rng = np.random.default_rng(43)
+    case = wl.cp_share() if work == "cp" else wl.train_seq_ids()
+    C = case["x"].shape[1]
+    wb = wl.to_bf16_bits(wl.uniform_f32(rng, (C, 4)))
+    bb = wl.to_bf16_bits((rng.standard_normal(C) * 0.1).astype(np.float32))
+    x, dy = gh.dev_bits(case["x"]), gh.dev_bits(case["dy"])
+    kw = dict(cu_seqlens=gh.dev_i32(case.get("cu_seqlens")), seq_idx=gh.dev_i32(case.get("seq_idx")),
+              seqlen=case.get("seqlen"))
+    if case.get("hist") is not None:
+        kw.update(history=gh.dev_bits(case["hist"]), has_history=gh.dev_u8(case["has_history"]))
+    out = []
+    for w, b in ((gh.dev_bits(wb), gh.dev_bits(bb)),
+                 (torch.from_numpy(wl.bf16_bits_to_f32(wb)).cuda(), torch.from_numpy(wl.bf16_bits_to_f32(bb)).cuda())):
+        dh = gh.dev_bits(np.full(case["hist"].shape, wl.OUT_FILL, np.uint16)) if case.get("hist") is not None else None
+        y = cc.conv1d_fwd(x, w, b, **kw)
+        dx, dw, db, dh = cc.conv1d_bwd(x, dy, w, b, want_dbias=True, dhistory=dh, **kw)
+        torch.cuda.synchronize()
+        out.append((gh.host_bits(y), gh.host_bits(dx), dw.view(torch.int32).cpu().numpy(),
+                    db.view(torch.int32).cpu().numpy(), None if dh is None else gh.host_bits(dh)))
+    for name, a, c in zip(("y", "dx", "dweight", "dbias", "d(history)"), *out):
+        assert (a is None and c is None) or np.array_equal(a, c), f"{name} differs between bf16 and FP32 taps"
