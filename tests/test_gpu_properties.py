@@ -1,7 +1,8 @@
 """GPU properties beyond element-wise parity: determinism, decode = unit prefill, chunked prefill,
-the context-parallel split, HIP-graph capture and replay with edited metadata, strided rows and
-64-bit row offsets (forward and backward, with history rows and per-token IDs).  Everything goes
-through the C ABI (the torch binding only marshals)."""
+the context-parallel split, HIP-graph capture and replay with edited metadata, strided rows, arrays
+beyond 2^31 elements (forward, backward, slot pool, channels-first), and identities between code
+paths that must give the same bits: the three sequence forms, pool state against history rows,
+bf16 against FP32 taps.  Everything goes through the C ABI (the torch binding only marshals)."""
 import numpy as np
 import pytest
 
