@@ -528,3 +528,50 @@ def test_bf16_and_fp32_taps_agree_bitwise(work):
                     db.view(torch.int32).cpu().numpy(), None if dh is None else gh.host_bits(dh)))
     for name, a, c in zip(("y", "dx", "dweight", "dbias", "d(history)"), *out):
         assert (a is None and c is None) or np.array_equal(a, c), f"{name} differs between bf16 and FP32 taps"
+
+
+def test_graph_replay_equals_eager_at_full_size():
+    """The context-parallel share (16384 x 5632) forward and backward captured once in a HIP graph:
+    three replays, with eager calls on other buffers between them, give the eager call's y, dx,
+    dweight and d(history) bits."""
+    say("graph replay against eager, full size")
+    case = wl.cp_share()
+    x, dy = gh.dev_bits(case["x"]), gh.dev_bits(case["dy"])
+    w = gh.dev_taps(case["w"])
+    kw = dict(cu_seqlens=gh.dev_i32(case["cu_seqlens"]), history=gh.dev_bits(case["hist"]),
+              has_history=gh.dev_u8(case["has_history"]))
+    rows, C = case["x"].shape
+    bufs = dict(y=torch.empty(rows, C, dtype=torch.bfloat16, device="cuda"),
+                dx=torch.empty(rows, C, dtype=torch.bfloat16, device="cuda"),
+                dw=torch.empty(C, 4, dtype=torch.float32, device="cuda"),
+                dh=gh.dev_bits(np.full(case["hist"].shape, wl.OUT_FILL, np.uint16)),
+                ws=torch.empty(cc.conv1d_bwd_workspace_bytes(rows, C), dtype=torch.uint8, device="cuda"))
+
+    def run(o):
+        cc.conv1d_fwd(x, w, None, out=o["y"], **kw)
+        cc.conv1d_bwd(x, dy, w, None, dx=o["dx"], dweight=o["dw"], dhistory=o["dh"], workspace=o["ws"], **kw)
+
+    def bits(o):
+        return (gh.host_bits(o["y"]), gh.host_bits(o["dx"]), o["dw"].view(torch.int32).cpu().numpy(), gh.host_bits(o["dh"]))
+
+    eager = {k: v.clone() for k, v in bufs.items()}
+    run(eager)
+    torch.cuda.synchronize()
+    ref = bits(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(bufs)  # warm up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(bufs)
+    for replay in range(3):
+        for k in ("y", "dx", "dw"):
+            bufs[k].zero_()
+        graph.replay()
+        run(eager)  # eager work between replays, on other buffers
+        torch.cuda.synchronize()
+        for name, a, c in zip(("y", "dx", "dweight", "d(history)"), bits(bufs), ref):
+            assert np.array_equal(a, c), f"replay {replay}: {name} differs from the eager call"
