@@ -70,20 +70,36 @@ __device__ __forceinline__ void load_history(const PoolArgs& pool, const HistArg
 
 // Final state of a live nonempty sequence: pool positions 0..2 <- last three values of the
 // extended sequence u = [h0, h1, h2, x[s], ..., x[e-1]] (raw bits; positions >= 3 untouched).
-template <int CPL, bool VEC>
+// BATCH (kernels launched with a pool): the three candidate rows n-3 .. n-1 are loaded together,
+// one memory round trip alongside the history loads, then shifted in row order.  Kernels without a
+// pool never reach this function; they keep the row-at-a-time loop, which leaves their register
+// allocation as it is (the batched form there cost 8 -> 5 waves per SIMD in the batch-row form).
+template <int CPL, bool VEC, bool BATCH>
 __device__ __forceinline__ void pool_writeback(const FwdArgs& a, int32_t slot, const SeqDesc& sd,
                                                const float (&h)[3][CPL], int64_t c0, bool active) {
   const int64_t n = sd.e - sd.s;
-  // start from the history and shift in the sequence's last min(n, 3) rows
+  // start from the history and shift in the sequence's last min(n, 3) rows, in row order
   float v[3][CPL];
 #pragma unroll
   for (int j = 0; j < 3; ++j)
 #pragma unroll
     for (int ch = 0; ch < CPL; ++ch) v[j][ch] = h[j][ch];
-  for (int64_t k = (n > 3 ? n - 3 : 0); k < n; ++k) {
-    Pk<CPL> p = zero_pk<CPL>();
-    if (active) p = load_row<CPL, VEC>(a.x + (sd.s + k) * a.x_ld, c0, a.C);
-    shift_in<CPL>(v, p);
+  if constexpr (BATCH) {
+    Pk<CPL> last[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      last[j] = zero_pk<CPL>();
+      if (active && n - 3 + j >= 0) last[j] = load_row<CPL, VEC>(a.x + (sd.s + n - 3 + j) * a.x_ld, c0, a.C);
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (n - 3 + j >= 0) shift_in<CPL>(v, last[j]);
+  } else {
+    for (int64_t k = (n > 3 ? n - 3 : 0); k < n; ++k) {
+      Pk<CPL> p = zero_pk<CPL>();
+      if (active) p = load_row<CPL, VEC>(a.x + (sd.s + k) * a.x_ld, c0, a.C);
+      shift_in<CPL>(v, p);
+    }
   }
   if (!active) return;
   uint16_t* base = a.pool.ptr + (int64_t)slot * a.pool.s_slot;
@@ -150,7 +166,8 @@ __device__ __forceinline__ void fwd_slot(const FwdArgs& a, FwdSeq& cs) {
 
 // Row q = cs.sd.s, the first row of a sequence, is next: h <- its history, and with a pool the
 // head writes the sequence's final state (the head wave is the only one that touches the slot).
-template <int CPL, bool VEC, int MODE, int W, int H = Win<W>::H>
+// POOL: the kernel is the one launched with a slot pool (it selects the write-back's load form).
+template <int CPL, bool VEC, int MODE, int W, bool POOL, int H = Win<W>::H>
 __device__ __forceinline__ void fwd_enter(const FwdArgs& a, FwdSeq& cs, int64_t c0, bool active, float (&h)[H][CPL]) {
   fwd_slot<MODE>(a, cs);
 #pragma unroll
@@ -161,7 +178,7 @@ __device__ __forceinline__ void fwd_enter(const FwdArgs& a, FwdSeq& cs, int64_t 
     if (!cs.zero) {
       load_history<CPL, VEC, W>(a.pool, a.hist, cs.sd.idx, cs.slot, true, c0, a.C, active, h);
       if constexpr (W == 4) {
-        if (a.pool.ptr && cs.sd.e > cs.sd.s) pool_writeback<CPL, VEC>(a, cs.slot, cs.sd, h, c0, active);
+        if (a.pool.ptr && cs.sd.e > cs.sd.s) pool_writeback<CPL, VEC, POOL>(a, cs.slot, cs.sd, h, c0, active);
       }
     }
   }
@@ -171,7 +188,7 @@ __device__ __forceinline__ void fwd_enter(const FwdArgs& a, FwdSeq& cs, int64_t 
 // mod R = r mod R, as q0 - tile start is a multiple of CH.  A chunk inside one sequence is a
 // straight stencil; a chunk where sequences start re-seeds the three window slots from the new
 // sequence's history right before its first row.
-template <int CPL, bool VEC, int MODE, int CH, bool SILU, bool FULL, int W, int R = Win<W>::R>
+template <int CPL, bool VEC, int MODE, int CH, bool SILU, bool FULL, int W, bool POOL, int R = Win<W>::R>
 __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)[CH], int n, int64_t q0, int64_t tb,
                                           int64_t dend, FwdSeq& cs, int64_t c0, bool active,
                                           const float (&wk)[R][CPL], const float (&bias)[CPL], float (&u)[R][CPL]) {
@@ -199,7 +216,7 @@ __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)
       if (q == cs.sd.e) {  // a new sequence starts at row q (empty ones are skipped)
         cs.sd = next_seq<MODE>(a.seq, cs.sd, dend, tb);
         float h[H][CPL];
-        fwd_enter<CPL, VEC, MODE, W>(a, cs, c0, active, h);
+        fwd_enter<CPL, VEC, MODE, W, POOL>(a, cs, c0, active, h);
 #pragma unroll
         for (int j = 0; j < H; ++j)
 #pragma unroll
@@ -218,13 +235,13 @@ __device__ __forceinline__ void fwd_chunk(const FwdArgs& a, const Pk<CPL> (&buf)
 // sequence (wrow holds rows ta-H .. ta-1, loaded before the lookup).  At the sequence's first row
 // this enters the sequence (history, pool write-back); elsewhere only its -1 status matters, and
 // with a pool a tile never starts on a sequence's rows 1 and 2, so the slot is not touched.
-template <int CPL, bool VEC, int MODE, int W, int R = Win<W>::R, int H = Win<W>::H>
+template <int CPL, bool VEC, int MODE, int W, bool POOL, int R = Win<W>::R, int H = Win<W>::H>
 __device__ __forceinline__ void fwd_start(const FwdArgs& a, FwdSeq& cs, int64_t ta, const Pk<CPL> (&wrow)[H],
                                           int64_t c0, bool active, float (&u)[R][CPL]) {
   const int64_t dist = ta - cs.sd.s < H ? ta - cs.sd.s : H;
   float h[H][CPL];
   if (dist == 0) {
-    fwd_enter<CPL, VEC, MODE, W>(a, cs, c0, active, h);
+    fwd_enter<CPL, VEC, MODE, W, POOL>(a, cs, c0, active, h);
   } else {
     fwd_slot<MODE>(a, cs);
 #pragma unroll
@@ -279,7 +296,7 @@ __device__ __forceinline__ void load_taps_full(const FwdArgs& a, int64_t c0, flo
 // Rows [ta, te) R at a time in a rolled loop (ring slot of row q is (q - ta) mod R), reading each
 // chunk right before it is used: the path for tiles where a sequence starts or the data ends,
 // tiles a pool moved, partly active waves.  The sequence-start code then exists once per kernel.
-template <int CPL, bool VEC, int MODE, bool SILU, int W, int R = Win<W>::R>
+template <int CPL, bool VEC, int MODE, bool SILU, int W, bool POOL, int R = Win<W>::R>
 __device__ __forceinline__ void fwd_rolled(const FwdArgs& a, FwdSeq& cs, int64_t ta, int64_t te, int64_t dend,
                                            int64_t c0, bool active, const float (&wk)[R][CPL],
                                            const float (&bias)[CPL], float (&u)[R][CPL]) {
@@ -291,12 +308,12 @@ __device__ __forceinline__ void fwd_rolled(const FwdArgs& a, FwdSeq& cs, int64_t
       rows[r] = zero_pk<CPL>();
       if (r < n && active) rows[r] = load_row<CPL, VEC>(a.x + (q0 + r) * a.x_ld, c0, a.C);
     }
-    fwd_chunk<CPL, VEC, MODE, R, SILU, false, W>(a, rows, n, q0, te, dend, cs, c0, active, wk, bias, u);
+    fwd_chunk<CPL, VEC, MODE, R, SILU, false, W, POOL>(a, rows, n, q0, te, dend, cs, c0, active, wk, bias, u);
   }
 }
 
 // The rows [ta, tb) of one strip by the general path (predicated loads and lanes).
-template <int CPL, bool VEC, int MODE, bool SILU, int W>
+template <int CPL, bool VEC, int MODE, bool SILU, int W, bool POOL>
 __device__ __forceinline__ void fwd_general(const FwdArgs& a, int64_t ta, int64_t tb, int64_t c0, bool active) {
   constexpr int R = Win<W>::R, H = Win<W>::H;
   const int64_t dend = data_end<MODE>(a.seq, a.rows);
@@ -309,8 +326,8 @@ __device__ __forceinline__ void fwd_general(const FwdArgs& a, int64_t ta, int64_
   FwdSeq cs;
   cs.sd = seq_of_row<MODE, H>(a.seq, ta, dend, te);
   float u[R][CPL];
-  fwd_start<CPL, VEC, MODE, W>(a, cs, ta, wrow, c0, active, u);
-  fwd_rolled<CPL, VEC, MODE, SILU, W>(a, cs, ta, te, dend, c0, active, wk, bias, u);
+  fwd_start<CPL, VEC, MODE, W, POOL>(a, cs, ta, wrow, c0, active, u);
+  fwd_rolled<CPL, VEC, MODE, SILU, W, POOL>(a, cs, ta, te, dend, c0, active, wk, bias, u);
 }
 
 template <int CPL, bool VEC, int MODE, bool SILU, int W, bool POOL>
@@ -342,7 +359,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
       ta2 = owner_boundary<MODE>(a.seq, ta < de ? ta : de, de);
       tb2 = owner_boundary<MODE>(a.seq, tb < de ? tb : de, de);
     }
-    if (ta2 < tb2) fwd_general<CPL, VEC, MODE, SILU, W>(a, ta2, tb2, c0, active);
+    if (ta2 < tb2) fwd_general<CPL, VEC, MODE, SILU, W, POOL>(a, ta2, tb2, c0, active);
     return;
   }
 
@@ -397,12 +414,12 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
       if (tb - d.s == 1 || tb - d.s == 2) tb2 = d.s + 3 < d.e ? d.s + 3 : d.e;
     }
     if (ta2 != ta || tb2 != tb) {
-      if (ta2 < tb2) fwd_general<CPL, VEC, MODE, SILU, W>(a, ta2, tb2, c0, active);
+      if (ta2 < tb2) fwd_general<CPL, VEC, MODE, SILU, W, POOL>(a, ta2, tb2, c0, active);
       return;
     }
   }
   float u[R][CPL];
-  fwd_start<CPL, VEC, MODE, W>(a, cs, ta, wrow, c0, active, u);
+  fwd_start<CPL, VEC, MODE, W, POOL>(a, cs, ta, wrow, c0, active, u);
 
   if (te - ta == RT && cs.sd.e >= te) {
     // ---- the whole tile inside one sequence: one straight stencil (ring slot of row ta+c*R+r is r)
@@ -425,7 +442,7 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
 #pragma unroll 1
   for (int64_t q0 = ta; q0 < te; q0 += R) {
     const int n = (int)(te - q0 < R ? te - q0 : R);
-    fwd_chunk<CPL, VEC, MODE, R, SILU, true, W>(a, buf[0], n, q0, te, dend, cs, c0, active, wk, bias, u);
+    fwd_chunk<CPL, VEC, MODE, R, SILU, true, W, POOL>(a, buf[0], n, q0, te, dend, cs, c0, active, wk, bias, u);
 #pragma unroll
     for (int c = 0; c + 1 < NT; ++c)
 #pragma unroll
