@@ -317,9 +317,12 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
   const int64_t C = a.C;
   const int64_t wc0 = (int64_t)strip * kBlockChannels + (int64_t)wave * kWaveChannels;
   if (wc0 >= C) return;  // the whole wave is past the last channel: no partial to write
-  const int64_t c0 = wc0 + lane * CPL;
-  const bool active = c0 < C;
-  const bool full = VEC && wc0 + kWaveChannels <= C;  // every lane of the wave is active
+  // With vectors, the lanes of a partly active wave that lie past the last channel work as copies
+  // of the wave's last channel pair: the same loads and arithmetic, and stores of the same bits
+  // (dx, d(history), the range's partial sums) to the same addresses in the same instructions
+  // (lanes never exchange data).  Every wave then streams through the pipeline unpredicated.
+  const int64_t c0 = VEC && wc0 + lane * CPL >= C ? C - CPL : wc0 + lane * CPL;
+  const bool active = VEC || c0 < C;
   const int64_t dend = data_end<MODE>(a.seq, a.rows);
 
   int64_t ta = (int64_t)rb * a.range_rows;
@@ -346,7 +349,7 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
     const int64_t lim = (tb + H < dend) ? tb + H : dend;  // sequence ends matter up to tb + H
 
     // full chunks of own rows, software-pipelined with NB register buffers (see the forward)
-    const int nfull = (full && CCONV_BWD_PIPELINE) ? (int)((tb - ta) / CH) : 0;
+    const int nfull = (VEC && CCONV_BWD_PIPELINE) ? (int)((tb - ta) / CH) : 0;
     const int64_t qlast = ta + (int64_t)nfull * CH - 1;
     int64_t q0 = ta;
     constexpr int NB = CCONV_BWD_DEPTH;

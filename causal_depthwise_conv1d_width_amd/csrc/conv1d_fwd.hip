@@ -293,41 +293,63 @@ __device__ __forceinline__ void load_taps_full(const FwdArgs& a, int64_t c0, flo
   }
 }
 
-// Rows [ta, te) R at a time in a rolled loop (ring slot of row q is (q - ta) mod R), reading each
-// chunk right before it is used: the path for tiles where a sequence starts or the data ends,
-// tiles a pool moved, partly active waves.  The sequence-start code then exists once per kernel.
-template <int CPL, bool VEC, int MODE, bool SILU, int W, bool POOL, int R = Win<W>::R>
-__device__ __forceinline__ void fwd_rolled(const FwdArgs& a, FwdSeq& cs, int64_t ta, int64_t te, int64_t dend,
-                                           int64_t c0, bool active, const float (&wk)[R][CPL],
-                                           const float (&bias)[CPL], float (&u)[R][CPL]) {
-  for (int64_t q0 = ta; q0 < te; q0 += R) {
-    const int n = (int)(te - q0 < R ? te - q0 : R);
-    Pk<CPL> rows[R];
+// Rows q0 .. q0+R-1 of x that lie below te (zeros past te, not loaded).
+template <int CPL, bool VEC, int R>
+__device__ __forceinline__ void fwd_rows(const FwdArgs& a, int64_t q0, int64_t te, int64_t c0, bool active,
+                                         Pk<CPL> (&dst)[R]) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      rows[r] = zero_pk<CPL>();
-      if (r < n && active) rows[r] = load_row<CPL, VEC>(a.x + (q0 + r) * a.x_ld, c0, a.C);
-    }
-    fwd_chunk<CPL, VEC, MODE, R, SILU, false, W, POOL>(a, rows, n, q0, te, dend, cs, c0, active, wk, bias, u);
+  for (int r = 0; r < R; ++r) {
+    dst[r] = zero_pk<CPL>();
+    if (q0 + r < te && active) dst[r] = load_row<CPL, VEC>(a.x + (q0 + r) * a.x_ld, c0, a.C);
   }
 }
 
-// The rows [ta, tb) of one strip by the general path (predicated loads and lanes).
+// Rows [ta, te) R at a time in a rolled loop (ring slot of row q is (q - ta) mod R), each chunk's
+// loads issued one chunk ahead of its use (`rows` arrives holding the chunk at ta): the path for
+// tiles where a sequence starts or the data ends, tiles a pool moved, partly active waves.  The
+// sequence-start code then exists once per kernel.
+template <int CPL, bool VEC, int MODE, bool SILU, int W, bool POOL, int R = Win<W>::R>
+__device__ __forceinline__ void fwd_rolled(const FwdArgs& a, FwdSeq& cs, int64_t ta, int64_t te, int64_t dend,
+                                           int64_t c0, bool active, const float (&wk)[R][CPL],
+                                           const float (&bias)[CPL], float (&u)[R][CPL], Pk<CPL> (&rows)[R]) {
+  for (int64_t q0 = ta; q0 < te; q0 += R) {
+    const int n = (int)(te - q0 < R ? te - q0 : R);
+    Pk<CPL> next[R];
+    fwd_rows<CPL, VEC, R>(a, q0 + R, te, c0, active, next);
+    fwd_chunk<CPL, VEC, MODE, R, SILU, false, W, POOL>(a, rows, n, q0, te, dend, cs, c0, active, wk, bias, u);
+#pragma unroll
+    for (int r = 0; r < R; ++r) rows[r] = next[r];
+  }
+}
+
+// The rows [ta, tb) of one strip by the general path (predicated loads and lanes).  One memory
+// round trip for the set-up, as in the tile path: the lookup's loads (with a pool, the slots too),
+// the taps, the window rows above and the first chunk of rows are all issued before any is used.
 template <int CPL, bool VEC, int MODE, bool SILU, int W, bool POOL>
 __device__ __forceinline__ void fwd_general(const FwdArgs& a, int64_t ta, int64_t tb, int64_t c0, bool active) {
   constexpr int R = Win<W>::R, H = Win<W>::H;
   const int64_t dend = data_end<MODE>(a.seq, a.rows);
   const int64_t te = tb < dend ? tb : dend;
   if (ta >= te) return;
+  const SeqProbe pr = seq_probe<MODE, H>(a.seq, ta, te, POOL ? a.pool.cache_indices : nullptr);
   float wk[R][CPL], bias[CPL];
   load_taps<CPL, W>(a.w, a.w_f32, a.b, a.b_f32, c0, a.C, wk, bias);
   Pk<CPL> wrow[H];
   load_window<CPL, VEC, H>(wrow, a.x, a.x_ld, ta, c0, a.C, active);
+  Pk<CPL> rows[R];
+  fwd_rows<CPL, VEC, R>(a, ta, te, c0, active, rows);
   FwdSeq cs;
-  cs.sd = seq_of_row<MODE, H>(a.seq, ta, dend, te);
+  cs.sd = seq_resolve<MODE, H>(a.seq, ta, dend, te, pr);
+  if constexpr (POOL) {
+    int32_t sl;
+    if (probe_slot<MODE>(a.seq, pr, cs.sd.idx, sl)) {
+      cs.pre_idx = cs.sd.idx;
+      cs.pre_slot = sl;
+    }
+  }
   float u[R][CPL];
   fwd_start<CPL, VEC, MODE, W, POOL>(a, cs, ta, wrow, c0, active, u);
-  fwd_rolled<CPL, VEC, MODE, SILU, W, POOL>(a, cs, ta, te, dend, c0, active, wk, bias, u);
+  fwd_rolled<CPL, VEC, MODE, SILU, W, POOL>(a, cs, ta, te, dend, c0, active, wk, bias, u, rows);
 }
 
 template <int CPL, bool VEC, int MODE, bool SILU, int W, bool POOL>
@@ -344,15 +366,18 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
   const int64_t C = a.C;
   const int64_t wc0 = (int64_t)strip * kBlockChannels + (int64_t)wave * kWaveChannels;
   if (wc0 >= C) return;  // the whole wave is past the last channel
-  const int64_t c0 = wc0 + lane * CPL;
-  const bool active = c0 < C;
-  const bool full = VEC && wc0 + kWaveChannels <= C;  // every lane of the wave is active
+  // With vectors, the lanes of a partly active wave that lie past the last channel work as copies
+  // of the wave's last channel pair: the same loads, history and arithmetic, and stores of the same
+  // bits to the same addresses in the same instructions (lanes never exchange data).  Every wave
+  // then takes the tile path with no per-lane predicate.
+  const int64_t c0 = VEC && wc0 + lane * CPL >= C ? C - CPL : wc0 + lane * CPL;
+  const bool active = VEC || c0 < C;
   constexpr bool has_pool = POOL;  // a slot pool (width four, offsets or batch rows)
   static_assert(!POOL || (W == 4 && MODE != MODE_IDX), "the pool form is width four with host-known sequences");
   const int64_t ta = (int64_t)rb * RT;
   const int64_t tb = ta + RT < a.rows ? ta + RT : a.rows;
 
-  if (!full) {  // the last strip's partly active wave, or rows that do not allow vectors
+  if constexpr (!VEC) {  // rows that do not allow vectors: the general path, predicated per lane
     int64_t ta2 = ta, tb2 = tb;
     if constexpr (has_pool) {
       const int64_t de = data_end<MODE>(a.seq, a.rows);
