@@ -371,3 +371,27 @@ def test_sequence_lookup_levels(oracle, nseq):
     _print_case(case["name"], rows=rows, C=C)
     gh.check_fwd(oracle, case)
     gh.check_bwd(oracle, case)
+
+
+@pytest.mark.parametrize("C", [5630, 1000])
+def test_partly_active_waves_at_full_size(oracle, C):
+    """Channel counts that leave the last wave of every strip row partly active (5630: 63 of 64
+    lanes; 1000: 52 of 64), at the context-parallel share's shape (16384 rows, 12 fragments, 8 with
+    history rows, d(tail)): the lanes past the last channel run as copies of the wave's last channel
+    pair.  Forward and backward against the oracle on every element, dweight/dbias bit for bit
+    across three runs."""
+    rng = np.random.default_rng(77 + C)
+    base = wl.cp_share()
+    rows = base["x"].shape[0]
+    n = len(base["cu_seqlens"]) - 1
+    case = dict(name=f"partial-waves-C{C}", x=wl.normal_bf16(rng, (rows, C)), w=wl.uniform_f32(rng, (C, 4)),
+                b=(rng.standard_normal(C) * 0.1).astype(np.float32), cu_seqlens=base["cu_seqlens"],
+                hist=wl.normal_bf16(rng, (n, 3, C)), has_history=base["has_history"],
+                dy=wl.normal_bf16(rng, (rows, C)), act="silu")
+    dtail = wl.normal_bf16(rng, (3, C))
+    _print_case(case["name"], rows=rows, C=C)
+    gh.check_fwd(oracle, case)
+    _, dw, db, _ = gh.check_bwd(oracle, case, dtail=dtail)
+    for _ in range(2):
+        _, dw2, db2, _ = gh.gpu_bwd(case, dtail=dtail)
+        assert np.array_equal(dw.view(np.int32), dw2.view(np.int32)) and np.array_equal(db.view(np.int32), db2.view(np.int32))
