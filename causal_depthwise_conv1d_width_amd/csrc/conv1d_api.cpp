@@ -49,12 +49,17 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 
 // The channel-last kernels move a lane's kChannelsPerLane channels of a row as one vector when
 // the channel count, every row stride and every row base allow it; otherwise they take the
-// element-wise path (same results).
+// element-wise path (same results).  A pair of channels is one dword access at any 2-byte aligned
+// address, so with pairs any C >= 2 and any row stride will do; with an odd C the last pair
+// overlaps the one before it.  Kernels that update state in place (the slot pool) need C to be a
+// multiple of kChannelsPerLane on top, so that no two lanes own the same channel (vec_inplace).
 constexpr int64_t kVecElems = kChannelsPerLane;
 constexpr uintptr_t kVecBytes = 2 * kChannelsPerLane;
 bool vec_rows(int64_t C, int64_t ld, const void* p) {
+  if (kChannelsPerLane == 2) return C >= 2 && aligned(p, 2);
   return C % kVecElems == 0 && ld % kVecElems == 0 && aligned(p, kVecBytes);
 }
+bool vec_inplace(int64_t C) { return C % kVecElems == 0; }
 
 // Byte extents and element counts are computed in int64.  Sizes and strides whose products could
 // overflow it are rejected up front (no allocation comes near 2^56 elements).
@@ -194,7 +199,8 @@ int conv1d_fwd(const void* x, int64_t rows, int64_t C, int64_t x_ld, const void*
   if (overlap(sy, sp)) return CONV1D_EINVAL;
   if (rows == 0) return CONV1D_OK;
 
-  const bool vec = vec_rows(C, x_ld, x) && vec_rows(C, y_ld, y) && (!use_hist || vec_rows(C, C, hist->ptr));
+  const bool vec = vec_rows(C, x_ld, x) && vec_rows(C, y_ld, y) && (!use_hist || vec_rows(C, C, hist->ptr)) &&
+                   (!use_pool || vec_inplace(C));
   const int64_t rr = fwd_tile_rows(mode, use_pool, width);
   const uint64_t nblk = (uint64_t)ceil_div(C, kBlockChannels) * ceil_div(rows, rr);
   if (nblk > 0x7fffffffull) return CONV1D_EINVAL;
@@ -248,7 +254,7 @@ static int state_update_common(const void* x, int64_t nseq, int64_t K, int64_t C
   if (overlap(sy, sp)) return CONV1D_EINVAL;
   if (nseq == 0) return CONV1D_OK;
   if ((uint64_t)nseq * ceil_div(C, kChannelsPerLane) / kBlockThreads > 0x7fffffffull) return CONV1D_EINVAL;
-  const bool vec = vec_rows(C, x_ld, x) && vec_rows(C, y_ld, y);
+  const bool vec = vec_rows(C, x_ld, x) && vec_rows(C, y_ld, y) && vec_inplace(C);
   DecodeArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.y = static_cast<uint16_t*>(y);

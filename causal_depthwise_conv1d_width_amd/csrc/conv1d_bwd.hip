@@ -321,7 +321,10 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
   // of the wave's last channel pair: the same loads and arithmetic, and stores of the same bits
   // (dx, d(history), the range's partial sums) to the same addresses in the same instructions
   // (lanes never exchange data).  Every wave then streams through the pipeline unpredicated.
-  const int64_t c0 = VEC && wc0 + lane * CPL >= C ? C - CPL : wc0 + lane * CPL;
+  // With an odd C the lane of the lone last channel takes the pair (C-2, C-1); channel C-2 is then
+  // computed twice, perhaps in two waves, over the same rows in the same order, so both store the
+  // same bits.  No output overlaps an input, so the order of those stores does not matter.
+  const int64_t c0 = VEC && wc0 + lane * CPL + (CPL - 1) >= C ? C - CPL : wc0 + lane * CPL;
   const bool active = VEC || c0 < C;
   const int64_t dend = data_end<MODE>(a.seq, a.rows);
 
@@ -474,7 +477,7 @@ __global__ void __launch_bounds__(kBlockThreads) CCONV_BWD_OCCUPANCY conv1d_bwd_
         for (int q = 0; q < CPL; q += 4)
           *reinterpret_cast<f32x4*>(dst + q) = f32x4{st.acc[k][q], st.acc[k][q + 1], st.acc[k][q + 2], st.acc[k][q + 3]};
       } else if constexpr (VEC) {
-        *reinterpret_cast<f32x2*>(dst) = f32x2{st.acc[k][0], st.acc[k][1]};
+        *reinterpret_cast<f32x2_a4*>(dst) = f32x2{st.acc[k][0], st.acc[k][1]};  // c0 may be odd
       } else {
 #pragma unroll
         for (int ch = 0; ch < CPL; ++ch)

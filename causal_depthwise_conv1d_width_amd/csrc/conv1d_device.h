@@ -34,6 +34,7 @@ struct Pk {
 };
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -78,10 +79,14 @@ __device__ __forceinline__ Pk<CPL> zero_pk() {
 #ifndef CCONV_NT_STORES
 #define CCONV_NT_STORES 1
 #endif
-// VEC: C % CPL == 0 and every row start is 16-byte (CPL = 8) / 8-byte (CPL = 4) aligned, so an
-// active lane's CPL channels are one aligned vector.  Otherwise element-wise with bounds.
+// VEC: an active lane's CPL channels are one vector access.  At CPL = 8 / 4 that needs C % CPL == 0
+// and 16- / 8-byte aligned row starts.  At CPL = 2 any row start will do: the pair is one dword
+// access at a 2-byte aligned address, which the hardware serves in the unaligned access mode that
+// the HSA runtime sets (the compiler emits the same single dword instruction for either alignment).
+// Otherwise element-wise with bounds.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32_a2 __attribute__((aligned(2)));
 
 // STREAM: the row is read exactly once here (non-temporal hint: do not keep it in the caches).
 template <int CPL, bool VEC, bool STREAM = false>
@@ -101,7 +106,7 @@ __device__ __forceinline__ Pk<CPL> load_row(const uint16_t* __restrict__ row, in
       else v = *src;
       p.d[0] = v.x; p.d[1] = v.y;
     } else {
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(row + c0);
+      const u32_a2* src = reinterpret_cast<const u32_a2*>(row + c0);
       if constexpr (STREAM && CCONV_NT_LOADS) p.d[0] = __builtin_nontemporal_load(src);
       else p.d[0] = *src;
     }
@@ -130,7 +135,7 @@ __device__ __forceinline__ void store_row(uint16_t* __restrict__ row, int64_t c0
       if constexpr (STREAM && CCONV_NT_STORES) __builtin_nontemporal_store(v, dst);
       else *dst = v;
     } else {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(row + c0);
+      u32_a2* dst = reinterpret_cast<u32_a2*>(row + c0);
       if constexpr (STREAM && CCONV_NT_STORES) __builtin_nontemporal_store(p.d[0], dst);
       else *dst = p.d[0];
     }

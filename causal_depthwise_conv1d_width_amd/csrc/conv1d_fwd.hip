@@ -369,8 +369,11 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_fwd_kernel(const FwdArgs
   // With vectors, the lanes of a partly active wave that lie past the last channel work as copies
   // of the wave's last channel pair: the same loads, history and arithmetic, and stores of the same
   // bits to the same addresses in the same instructions (lanes never exchange data).  Every wave
-  // then takes the tile path with no per-lane predicate.
-  const int64_t c0 = VEC && wc0 + lane * CPL >= C ? C - CPL : wc0 + lane * CPL;
+  // then takes the tile path with no per-lane predicate.  With an odd C (never with a pool: the
+  // slot is updated in place) the lane of the lone last channel takes the pair (C-2, C-1); channel
+  // C-2 is then computed twice, perhaps in two waves, from the same inputs, and both store the same
+  // bits.  No output overlaps an input, so the order of those stores does not matter.
+  const int64_t c0 = VEC && wc0 + lane * CPL + (CPL - 1) >= C ? C - CPL : wc0 + lane * CPL;
   const bool active = VEC || c0 < C;
   constexpr bool has_pool = POOL;  // a slot pool (width four, offsets or batch rows)
   static_assert(!POOL || (W == 4 && MODE != MODE_IDX), "the pool form is width four with host-known sequences");

@@ -39,10 +39,12 @@
  *     [0, rows], a slot outside [0, slots) acts as -1, accepted counts are clamped to the pool.
  *   - Sizes and strides whose products could exceed 2^56 elements (so that byte extents would
  *     overflow 64-bit arithmetic) are rejected with CONV1D_EINVAL.
- *   - Any C >= 1 and any row stride are accepted.  When C and the row strides are even and the
- *     row bases 4-byte aligned (the channels-first calls: T and the strides multiples of 8, bases
- *     16-byte aligned), a lane's channels move as one vector; otherwise an element-wise path
- *     runs.  Results are identical.
+ *   - Any C >= 1 and any row stride are accepted.  In the channel-last calls a lane's two
+ *     channels move as one dword access whenever C >= 2 and the row bases are 2-byte aligned, at
+ *     any row stride (an odd C or odd stride gives unaligned dwords, which the GPU serves), except
+ *     that calls updating the slot pool in place also need an even C.  The channels-first calls
+ *     move vectors when T and the strides are multiples of 8 and the bases 16-byte aligned.
+ *     Otherwise an element-wise path runs.  Results are identical.
  *   - Two calls that run concurrently must not share live slots or workspaces.
  */
 #ifndef CONV1D_H

@@ -15,6 +15,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import gpu_harness as gh  # noqa: E402
+import causal_depthwise_conv1d_width_amd as cc  # noqa: E402
 from causal_depthwise_conv1d_width_amd import workloads as wl  # noqa: E402
 
 
@@ -373,7 +374,7 @@ def test_sequence_lookup_levels(oracle, nseq):
     gh.check_bwd(oracle, case)
 
 
-@pytest.mark.parametrize("C", [5630, 1000])
+@pytest.mark.parametrize("C", [5630, 1000, 5631, 5633])
 def test_partly_active_waves_at_full_size(oracle, C):
     """Channel counts that leave the last wave of every strip row partly active (5630: 63 of 64
     lanes; 1000: 52 of 64), at the context-parallel share's shape (16384 rows, 12 fragments, 8 with
@@ -395,3 +396,63 @@ def test_partly_active_waves_at_full_size(oracle, C):
     for _ in range(2):
         _, dw2, db2, _ = gh.gpu_bwd(case, dtail=dtail)
         assert np.array_equal(dw.view(np.int32), dw2.view(np.int32)) and np.array_equal(db.view(np.int32), db2.view(np.int32))
+
+
+@pytest.mark.parametrize("C", [2, 3, 127, 129, 641, 1537])
+def test_odd_channel_counts(oracle, C):
+    """Odd C: a lane's two channels are one dword access at a 2-byte aligned address, and the lane of
+    the lone last channel takes the pair (C-2, C-1), which overlaps the pair before it.  At C = 129,
+    641 and 1537 (one above a multiple of 128, and of 512) the two pairs sit in different waves, at
+    1537 in different blocks.  Offsets with history rows and d(tail), per-token IDs, batch rows,
+    and the slot pool (which keeps element-wise accesses at odd C, since it is updated in place);
+    dweight/dbias bit for bit across two runs."""
+    rng = np.random.default_rng(900 + C)
+    forms = [("cu", None, True), ("cu", "hist", False), ("cu", "chan", False), ("idx", None, False),
+             ("batch", None, True), ("batch", "chan", False)]
+    for q, (mode, layout, hist) in enumerate(forms):
+        case = wl.random_case(rng, C=C, nseq=int(rng.integers(1, 9)), max_len=int(rng.choice([3, 40, 300])),
+                              mode=mode, pool_layout_name=layout, with_hist=hist, w_f32=bool(q % 2),
+                              act="silu" if q % 3 else "none", sentinel=layout is not None)
+        case["name"] = f"odd-C{C}-{mode}-{layout or ('hist' if hist else 'plain')}"
+        _print_case(case["name"], rows=case["x"].shape[0])
+        gh.check_fwd(oracle, case)
+        if layout is None:
+            dtail = wl.normal_bf16(rng, (3, C))
+            _, dw, db, _ = gh.check_bwd(oracle, case, dtail=dtail)
+            _, dw2, db2, _ = gh.gpu_bwd(case, dtail=dtail)
+            assert np.array_equal(dw.view(np.int32), dw2.view(np.int32))
+            assert db is None or np.array_equal(db.view(np.int32), db2.view(np.int32))
+
+
+@pytest.mark.parametrize("C,ld,off", [(1000, 1001, 1), (5632, 5633, 1), (641, 643, 3)])
+def test_misaligned_rows_backward(oracle, C, ld, off):
+    """Rows that start on odd elements (an odd row stride, or a view one element into a buffer):
+    x, dy and dx rows at 2-byte aligned addresses, against the oracle."""
+    rng = np.random.default_rng(950 + off)
+    rows = 1500
+    cu = np.array([0, 1, 300, 301, 900, 1490], np.int32)
+    n = len(cu) - 1
+    xf, dyf = wl.normal_bf16(rng, (rows, ld + off)), wl.normal_bf16(rng, (rows, ld + off))
+    w = wl.uniform_f32(rng, (C, 4))
+    b = (rng.standard_normal(C) * 0.1).astype(np.float32)
+    hist, hh = wl.normal_bf16(rng, (n, 3, C)), (rng.random(n) < 0.7).astype(np.uint8)
+    dtail = wl.normal_bf16(rng, (3, C))
+    _print_case(f"misaligned-bwd-C{C}-ld{ld}-off{off}", rows=rows)
+    x, dy = gh.dev_bits(xf)[:, off:off + C], gh.dev_bits(dyf)[:, off:off + C]
+    dx_full = torch.full((rows, ld + off), wl.OUT_FILL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    dx = dx_full[:, off:off + C]
+    dh = torch.empty(n, 3, C, dtype=torch.bfloat16, device="cuda")
+    dx, dw, db, dh = cc.conv1d_bwd(x, dy, gh.dev_taps(w), gh.dev_taps(b), cu_seqlens=gh.dev_i32(cu),
+                                   history=gh.dev_bits(hist), has_history=gh.dev_u8(hh), activation="silu",
+                                   dx=dx, dhistory=dh, want_dbias=True, dtail=gh.dev_bits(dtail))
+    torch.cuda.synchronize()
+    dxr, dwr, dbr, dhr = oracle.bwd(np.ascontiguousarray(xf[:, off:off + C]), np.ascontiguousarray(dyf[:, off:off + C]),
+                                    w, b, cu_seqlens=cu, hist=hist, has_history=hh, act="silu", dtail=dtail)
+    gh.assert_bf16_close(gh.host_bits(dx)[: cu[-1]], dxr[: cu[-1]], "dx")
+    gh.assert_w_close(dw.cpu().numpy(), dwr, "dw")
+    gh.assert_w_close(db.cpu().numpy(), dbr, "db")
+    dhg = gh.host_bits(dh).reshape(n, 3, C)
+    for i in np.flatnonzero(hh):
+        gh.assert_bf16_close(dhg[i], dhr[i], f"dhistory {i}")
+    full = gh.host_bits(dx_full)
+    assert (full[:, :off] == np.uint16(wl.OUT_FILL)).all() and (full[:, off + C:] == np.uint16(wl.OUT_FILL)).all()
