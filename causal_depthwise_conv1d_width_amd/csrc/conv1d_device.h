@@ -161,26 +161,57 @@ struct Win {
   static constexpr int H = R - 1;
 };
 
+__device__ __forceinline__ float tap_f32(float v) { return v; }
+__device__ __forceinline__ float tap_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+struct NoBias {};
+
+// The taps and bias of one dtype pair, straight-line: TB = NoBias reads no bias.
+template <typename TW, typename TB, int CPL, int W, int R>
+__device__ __forceinline__ void load_taps_typed(const void* w, const void* b, const int64_t (&cc)[CPL],
+                                                float (&wk)[R][CPL], float (&bias)[CPL]) {
+#pragma unroll
+  for (int ch = 0; ch < CPL; ++ch) {
+    if constexpr (__is_same(TB, NoBias)) bias[ch] = 0.f;
+    else bias[ch] = tap_f32(static_cast<const TB*>(b)[cc[ch]]);
+#pragma unroll
+    for (int k = 0; k < W; ++k) wk[R - W + k][ch] = tap_f32(static_cast<const TW*>(w)[cc[ch] * W + k]);
+  }
+}
+
+// Every load reads an in-range channel (a lane's channels past the last one read channel C-1, and
+// their values are then replaced by zeros), and the dtypes are tested once for the wave, so all the
+// loads go out together and the set-up waits for them once.  A load per tap inside a per-lane test
+// made every bf16 tap its own memory round trip.
 template <int CPL, int W = 4, int R = Win<W>::R>
 __device__ __forceinline__ void load_taps(const void* w, int w_f32, const void* b, int b_f32, int64_t c0,
                                           int64_t C, float (&wk)[R][CPL], float (&bias)[CPL]) {
+  bool ok[CPL];
+  int64_t cc[CPL];
 #pragma unroll
   for (int ch = 0; ch < CPL; ++ch) {
-    const int64_t c = c0 + ch;
-    const bool ok = c < C;
+    ok[ch] = c0 + ch < C;
+    cc[ch] = ok[ch] ? c0 + ch : C - 1;
+  }
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-      float v = 0.f;
-      if (ok && k >= R - W) {
-        const int64_t i = c * W + (k - (R - W));
-        v = w_f32 ? static_cast<const float*>(w)[i] : __uint_as_float((uint32_t)static_cast<const uint16_t*>(w)[i] << 16);
-      }
-      wk[k][ch] = v;
+  for (int k = 0; k < R - W; ++k)
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch) wk[k][ch] = 0.f;
+  if (w_f32) {
+    if (!b) load_taps_typed<float, NoBias, CPL, W, R>(w, b, cc, wk, bias);
+    else if (b_f32) load_taps_typed<float, float, CPL, W, R>(w, b, cc, wk, bias);
+    else load_taps_typed<float, uint16_t, CPL, W, R>(w, b, cc, wk, bias);
+  } else {
+    if (!b) load_taps_typed<uint16_t, NoBias, CPL, W, R>(w, b, cc, wk, bias);
+    else if (b_f32) load_taps_typed<uint16_t, float, CPL, W, R>(w, b, cc, wk, bias);
+    else load_taps_typed<uint16_t, uint16_t, CPL, W, R>(w, b, cc, wk, bias);
+  }
+#pragma unroll
+  for (int ch = 0; ch < CPL; ++ch) {
+    if (!ok[ch]) {
+#pragma unroll
+      for (int k = R - W; k < R; ++k) wk[k][ch] = 0.f;
+      bias[ch] = 0.f;
     }
-    float bv = 0.f;
-    if (ok && b) bv = b_f32 ? static_cast<const float*>(b)[c]
-                            : __uint_as_float((uint32_t)static_cast<const uint16_t*>(b)[c] << 16);
-    bias[ch] = bv;
   }
 }
 

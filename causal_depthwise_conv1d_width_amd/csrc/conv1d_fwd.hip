@@ -493,45 +493,63 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_decode_kernel(const Deco
   const int64_t i = gid / groups;
   const int64_t c0 = (gid - i * groups) * CPL;
   const int64_t C = a.C, K = a.K;
+  // One memory round trip before the slot is known: the slot, the accepted count, the first four
+  // token rows and the taps, none of which depends on the slot.  Only the pool reads wait for it.
+  // The accepted count is read unconditionally (from the slot's own entry when there is none), the
+  // taps last (their dtype test joins with a wait), and a -1 slot selects zeros rather than
+  // branching away, so no load waits behind another.
   const int32_t slot = a.pool.cache_indices[i];
-  if (!(slot >= 0 && slot < a.pool.slots)) {
-    for (int64_t t = 0; t < K; ++t) store_row<CPL, VEC>(a.y + (i * K + t) * a.y_ld, c0, C, zero_pk<CPL>());
-    return;
-  }
-  int64_t o = a.accepted ? (int64_t)a.accepted[i] - 1 : 0;  // first history position
-  const int64_t omax = a.pool.len - 3;                       // out-of-contract counts are clamped
-  o = o < 0 ? 0 : (o > omax ? omax : o);
+  const int32_t acc_raw = (a.accepted ? a.accepted : a.pool.cache_indices)[i];
+  Pk<CPL> xr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) xr[j] = j < K ? load_row<CPL, VEC>(a.x + (i * K + j) * a.x_ld, c0, C) : zero_pk<CPL>();
   float wk[4][CPL], bias[CPL];
   load_taps<CPL>(a.w, a.w_f32, a.b, a.b_f32, c0, C, wk, bias);
-  uint16_t* base = a.pool.ptr + (int64_t)slot * a.pool.s_slot;
+  const int32_t acc = a.accepted ? acc_raw : 1;
+  const bool live = slot >= 0 && slot < a.pool.slots;
+  int64_t o = (int64_t)acc - 1;                // first history position
+  const int64_t omax = a.pool.len - 3;         // out-of-contract counts are clamped
+  o = o < 0 ? 0 : (o > omax ? omax : o);
+  uint16_t* base = a.pool.ptr + (int64_t)(live ? slot : 0) * a.pool.s_slot;
   uint16_t hb[3][CPL];
   float u[3][CPL];
+  // With vectors C is even, so both channels of a lane exist: the three history reads of both go
+  // out together under the one test of the slot.
 #pragma unroll
-  for (int ch = 0; ch < CPL; ++ch) {
-    const int64_t c = c0 + ch;
+  for (int ch = 0; ch < CPL; ++ch)
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      hb[j][ch] = c < C ? base[c * a.pool.s_chan + (o + j) * a.pool.s_pos] : (uint16_t)0;
-      u[j][ch] = __uint_as_float((uint32_t)hb[j][ch] << 16);
+    for (int j = 0; j < 3; ++j) hb[j][ch] = 0;
+  if (live) {
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch) {
+      const int64_t c = c0 + ch;
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (VEC || c < C) hb[j][ch] = base[c * a.pool.s_chan + (o + j) * a.pool.s_pos];
+    }
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch) {
+      const int64_t c = c0 + ch;
+      if (VEC || c < C) {
+        base[c * a.pool.s_chan] = hb[1][ch];
+        base[c * a.pool.s_chan + a.pool.s_pos] = hb[2][ch];
+      }
     }
   }
 #pragma unroll
-  for (int ch = 0; ch < CPL; ++ch) {
-    const int64_t c = c0 + ch;
-    if (c < C) {
-      base[c * a.pool.s_chan] = hb[1][ch];
-      base[c * a.pool.s_chan + a.pool.s_pos] = hb[2][ch];
-    }
-  }
-  // tokens in groups of four: the four row loads are issued together, one round trip per group
+  for (int ch = 0; ch < CPL; ++ch)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) u[j][ch] = __uint_as_float((uint32_t)hb[j][ch] << 16);
+  // tokens in groups of four: the four row loads of a later group are issued together
   for (int64_t t0 = 0; t0 < K; t0 += 4) {
+    if (t0 > 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xr[j] = t0 + j < K ? load_row<CPL, VEC>(a.x + (i * K + t0 + j) * a.x_ld, c0, C) : zero_pk<CPL>();
+    }
     float xv[4][CPL];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      Pk<CPL> p = zero_pk<CPL>();
-      if (t0 + j < K) p = load_row<CPL, VEC>(a.x + (i * K + t0 + j) * a.x_ld, c0, C);
-      unpack(p, xv[j]);
-    }
+    for (int j = 0; j < 4; ++j) unpack(xr[j], xv[j]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (t0 + j < K) {
@@ -544,13 +562,13 @@ __global__ void __launch_bounds__(kBlockThreads) conv1d_decode_kernel(const Deco
           z = __builtin_fmaf(wk[1][ch], u[1][ch], z);
           z = __builtin_fmaf(wk[2][ch], u[2][ch], z);
           z = __builtin_fmaf(wk[3][ch], xv[j][ch], z);
-          out[ch] = SILU ? z * sigmoid_f32(z) : z;
+          out[ch] = live ? (SILU ? z * sigmoid_f32(z) : z) : 0.f;
         }
         store_row<CPL, VEC>(a.y + (i * K + t) * a.y_ld, c0, C, pack(out));
 #pragma unroll
         for (int ch = 0; ch < CPL; ++ch) {
           const int64_t c = c0 + ch;
-          if (c < C) base[c * a.pool.s_chan + (t + 2) * a.pool.s_pos] = (uint16_t)(__float_as_uint(xv[j][ch]) >> 16);
+          if (live && (VEC || c < C)) base[c * a.pool.s_chan + (t + 2) * a.pool.s_pos] = (uint16_t)(__float_as_uint(xv[j][ch]) >> 16);
           u[0][ch] = u[1][ch];
           u[1][ch] = u[2][ch];
           u[2][ch] = xv[j][ch];
