@@ -70,11 +70,9 @@ __device__ __forceinline__ void load_history(const PoolArgs& pool, const HistArg
 
 // Final state of a live nonempty sequence: pool positions 0..2 <- last three values of the
 // extended sequence u = [h0, h1, h2, x[s], ..., x[e-1]] (raw bits; positions >= 3 untouched).
-// BATCH (kernels launched with a pool): the three candidate rows n-3 .. n-1 are loaded together,
-// one memory round trip alongside the history loads, then shifted in row order.  Kernels without a
-// pool never reach this function; they keep the row-at-a-time loop, which leaves their register
-// allocation as it is (the batched form there cost 8 -> 5 waves per SIMD in the batch-row form).
-template <int CPL, bool VEC, bool BATCH>
+// Only kernels launched without a pool contain this (never taken) form, a row at a time, which
+// leaves their register allocation as it is; pool kernels enter sequences through fwd_enter_pool.
+template <int CPL, bool VEC>
 __device__ __forceinline__ void pool_writeback(const FwdArgs& a, int32_t slot, const SeqDesc& sd,
                                                const float (&h)[3][CPL], int64_t c0, bool active) {
   const int64_t n = sd.e - sd.s;
@@ -84,22 +82,10 @@ __device__ __forceinline__ void pool_writeback(const FwdArgs& a, int32_t slot, c
   for (int j = 0; j < 3; ++j)
 #pragma unroll
     for (int ch = 0; ch < CPL; ++ch) v[j][ch] = h[j][ch];
-  if constexpr (BATCH) {
-    Pk<CPL> last[3];
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      last[j] = zero_pk<CPL>();
-      if (active && n - 3 + j >= 0) last[j] = load_row<CPL, VEC>(a.x + (sd.s + n - 3 + j) * a.x_ld, c0, a.C);
-    }
-#pragma unroll
-    for (int j = 0; j < 3; ++j)
-      if (n - 3 + j >= 0) shift_in<CPL>(v, last[j]);
-  } else {
-    for (int64_t k = (n > 3 ? n - 3 : 0); k < n; ++k) {
-      Pk<CPL> p = zero_pk<CPL>();
-      if (active) p = load_row<CPL, VEC>(a.x + (sd.s + k) * a.x_ld, c0, a.C);
-      shift_in<CPL>(v, p);
-    }
+  for (int64_t k = (n > 3 ? n - 3 : 0); k < n; ++k) {
+    Pk<CPL> p = zero_pk<CPL>();
+    if (active) p = load_row<CPL, VEC>(a.x + (sd.s + k) * a.x_ld, c0, a.C);
+    shift_in<CPL>(v, p);
   }
   if (!active) return;
   uint16_t* base = a.pool.ptr + (int64_t)slot * a.pool.s_slot;
@@ -164,11 +150,69 @@ __device__ __forceinline__ void fwd_slot(const FwdArgs& a, FwdSeq& cs) {
   }
 }
 
+// Entering a sequence in a kernel launched with a slot pool (width four, offsets or batch rows).
+// The slot, its has-initial-state flag and the sequence's last three input rows do not depend on
+// one another, so they are read together, from in-range addresses and without tests between them;
+// the old state, which needs the slot, follows in a second round trip, and the final state is
+// written right after it.  With vectors C is even, so both channels of a lane exist.
+template <int CPL, bool VEC, int MODE>
+__device__ __forceinline__ void fwd_enter_pool(const FwdArgs& a, FwdSeq& cs, int64_t c0, bool active, float (&h)[3][CPL]) {
+  const int64_t idx = cs.sd.idx, s = cs.sd.s, n = cs.sd.e - cs.sd.s;
+  const int32_t slot = idx == cs.pre_idx ? cs.pre_slot : a.pool.cache_indices[idx];
+  const uint8_t* hi = a.pool.has_init ? a.pool.has_init : reinterpret_cast<const uint8_t*>(a.pool.cache_indices);
+  const uint8_t init_raw = hi[idx];
+  Pk<CPL> last[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {  // rows s+n-3+j, clamped into the array (used only when >= s)
+    int64_t row = s + n - 3 + j;
+    row = row < s ? s : row;
+    row = row < a.rows ? row : a.rows - 1;
+    last[j] = zero_pk<CPL>();
+    if (VEC || active) last[j] = load_row<CPL, VEC>(a.x + row * a.x_ld, c0, a.C);
+  }
+  cs.slot = slot;
+  cs.zero = !(slot >= 0 && slot < a.pool.slots);  // -1 (other values are out of contract)
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch) h[j][ch] = 0.f;
+  if (cs.zero) return;
+  uint16_t* base = a.pool.ptr + (int64_t)slot * a.pool.s_slot;
+  if (a.pool.has_init && init_raw && (VEC || active)) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int ch = 0; ch < CPL; ++ch)
+        if (VEC || c0 + ch < a.C)
+          h[j][ch] = __uint_as_float((uint32_t)base[(c0 + ch) * a.pool.s_chan + j * a.pool.s_pos] << 16);
+  }
+  if (n <= 0 || !(VEC || active)) return;
+  // final state: the history shifted by the sequence's last min(n, 3) rows, in row order
+  float v[3][CPL];
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch) v[j][ch] = h[j][ch];
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    if (n - 3 + j >= 0) shift_in<CPL>(v, last[j]);
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+#pragma unroll
+    for (int ch = 0; ch < CPL; ++ch)
+      if (VEC || c0 + ch < a.C)
+        base[(c0 + ch) * a.pool.s_chan + j * a.pool.s_pos] = (uint16_t)(__float_as_uint(v[j][ch]) >> 16);
+}
+
 // Row q = cs.sd.s, the first row of a sequence, is next: h <- its history, and with a pool the
 // head writes the sequence's final state (the head wave is the only one that touches the slot).
-// POOL: the kernel is the one launched with a slot pool (it selects the write-back's load form).
+// POOL: the kernel is the one launched with a slot pool.
 template <int CPL, bool VEC, int MODE, int W, bool POOL, int H = Win<W>::H>
 __device__ __forceinline__ void fwd_enter(const FwdArgs& a, FwdSeq& cs, int64_t c0, bool active, float (&h)[H][CPL]) {
+  if constexpr (POOL && MODE != MODE_IDX && W == 4) {
+    fwd_enter_pool<CPL, VEC, MODE>(a, cs, c0, active, h);
+    return;
+  }
   fwd_slot<MODE>(a, cs);
 #pragma unroll
   for (int j = 0; j < H; ++j)
@@ -178,7 +222,7 @@ __device__ __forceinline__ void fwd_enter(const FwdArgs& a, FwdSeq& cs, int64_t 
     if (!cs.zero) {
       load_history<CPL, VEC, W>(a.pool, a.hist, cs.sd.idx, cs.slot, true, c0, a.C, active, h);
       if constexpr (W == 4) {
-        if (a.pool.ptr && cs.sd.e > cs.sd.s) pool_writeback<CPL, VEC, POOL>(a, cs.slot, cs.sd, h, c0, active);
+        if (a.pool.ptr && cs.sd.e > cs.sd.s) pool_writeback<CPL, VEC>(a, cs.slot, cs.sd, h, c0, active);
       }
     }
   }
